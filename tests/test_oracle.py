@@ -1,0 +1,307 @@
+"""Pins for the CPU oracle: each check ties an oracle function to something
+other than itself -- values and shapes the pages fix, closed forms,
+invariants the method guarantees, and brute force in exact rational
+arithmetic on tiny inputs."""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------------------
+# brute force in exact arithmetic (pure Python, tiny sizes)
+# ---------------------------------------------------------------------------
+def _fr(a):
+    return [[Fraction(float(v)) for v in row] for row in np.asarray(a, dtype=np.float64)]
+
+
+def bf_linear(X, W, b=None):
+    """y[i][j] = sum_k X[i][k] * W[j][k] (+ b[j]) exactly."""
+    return [[sum((x * w for x, w in zip(xr, wr)), Fraction(0)) + (b[j] if b else 0)
+             for j, wr in enumerate(W)] for xr in X]
+
+
+def bf_matmul(X, A):
+    return [[sum((X[i][k] * A[k][j] for k in range(len(A))), Fraction(0))
+             for j in range(len(A[0]))] for i in range(len(X))]
+
+
+def _ints(seed, shape, lo=-3, hi=3):
+    return np.random.default_rng(seed).integers(lo, hi + 1, size=shape).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# (a) the worked example's shapes
+# ---------------------------------------------------------------------------
+def test_worked_example_shapes():
+    g = _gold("worked_example.json")
+    X, W1, W2 = synth.worked_example(seed=0)
+    assert list(X.shape) == g["input_shape"]
+    N = g["N"]
+    for r in range(N):
+        assert list(oracle.slice_(W1, 0, 1, N, r).shape) == g["all_to_sharded"]["weight_slice"]
+        assert list(oracle.slice_(W2, 1, 1, N, r).shape) == g["sharded_to_all"]["weight_slice"]
+    y1 = oracle.col(X, W1, P=N)
+    assert list(y1.shape[1:]) == g["all_to_sharded"]["local_output"]
+    y2, z = oracle.row(y1, W2, P=N, partials=True)
+    assert list(z.shape[1:]) == g["sharded_to_all"]["local_result"]
+    assert list(y2.shape) == g["sharded_to_all"]["final_output"]
+    # the chain equals the unsharded two-layer model: one reduction, no gather
+    ref = bf_linear(bf_linear(_fr(X), _fr(W1)), _fr(W2))
+    np.testing.assert_allclose(y2, np.array(ref, dtype=np.float64), rtol=1e-14, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# slicing
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("case", _gold("slices.json")["cases"], ids=lambda c: f"d{c['dim']}S{c['S']}P{c['P']}")
+def test_slice_golden(case):
+    dim, S, P = case["dim"], case["S"], case["P"]
+    cols = 3
+    W = np.arange(dim * cols, dtype=np.int32).reshape(dim, cols)  # entry encodes (row, col)
+    for r, rows in enumerate(case["shards"]):
+        got = oracle.slice_(W, 0, S, P, r)
+        np.testing.assert_array_equal(got, W[rows])
+        got_t = oracle.slice_(np.ascontiguousarray(W.T), 1, S, P, r)
+        np.testing.assert_array_equal(got_t, W.T[:, rows])
+
+
+@pytest.mark.parametrize("dim,S,P", [(24, 3, 4), (16, 2, 8), (30, 3, 5), (7, 1, 7)])
+def test_slice_partition(dim, S, P):
+    """Shards partition the dimension; each shard takes one contiguous run of
+    every segment, in segment order (numpy array_split as a second reading)."""
+    W = np.arange(dim, dtype=np.int64).reshape(dim, 1)
+    seen = []
+    for r in range(P):
+        sh = oracle.slice_(W, 0, S, P, r).ravel()
+        want = np.concatenate([np.array_split(seg, P)[r] for seg in np.array_split(np.arange(dim), S)])
+        np.testing.assert_array_equal(sh, want)
+        seen.extend(sh.tolist())
+    assert sorted(seen) == list(range(dim))
+
+
+def test_slice_bit_exact_16bit():
+    W = synth.uniform(3, (12, 8), 1.0, synth.BF16)
+    for r in range(2):
+        np.testing.assert_array_equal(oracle.slice_(W, 0, 3, 2, r).view(np.uint16),
+                                      W[[x for s in range(3) for x in range(s * 4 + r * 2, s * 4 + r * 2 + 2)]])
+
+
+# ---------------------------------------------------------------------------
+# (c) divisibility rules
+# ---------------------------------------------------------------------------
+def test_rejects_output_not_divisible():
+    X = np.zeros((4, 2))
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.col(X, np.zeros((3, 2)), P=2)  # out = 3 over 2 devices
+    assert e.value.code == 3
+    for P in (2, 4, 8):  # 4096 shards over 2, 4, 8
+        assert oracle.slice_(np.zeros((4096, 1), np.float32), 0, 1, P, 0).shape == (4096 // P, 1)
+
+
+def test_rejects_input_not_divisible():
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.row(np.zeros((3, 1, 1)), np.zeros((2, 5)), P=3)
+    assert e.value.code == 3
+
+
+def test_rejects_segments_not_divisible():
+    with pytest.raises(oracle.OracleError):
+        oracle.col(np.zeros((1, 2)), np.zeros((12, 2)), P=4, S=2)  # 12/2 = 6 not / 4
+    with pytest.raises(oracle.OracleError):
+        oracle.col(np.zeros((1, 2)), np.zeros((10, 2)), P=1, S=3)
+
+
+def test_summa_rejects_bad_grid():
+    with pytest.raises(oracle.OracleError):
+        oracle.summa(np.zeros((6, 4)), np.zeros((4, 4)), q=4)
+
+
+# ---------------------------------------------------------------------------
+# (e) brute force: column / row / summa in exact arithmetic
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("B,inn,out,S,P,gather,bias", [
+    (3, 5, 4, 1, 2, False, False), (2, 4, 12, 3, 2, False, True), (3, 3, 12, 2, 3, True, True),
+    (1, 7, 6, 1, 3, True, False), (4, 2, 2, 1, 1, False, True)])
+def test_col_bruteforce(B, inn, out, S, P, gather, bias):
+    X, W = _ints(1, (B, inn)), _ints(2, (out, inn))
+    b = _ints(3, (out,), 1, 3) if bias else None  # non-zero so a doubled or dropped bias shows
+    got = oracle.col(X, W, P=P, S=S, bias=b, gather=gather)
+    nl = out // P
+    for r in range(P):
+        rows = [s * (out // S) + r * (out // S // P) + i for s in range(S) for i in range(out // S // P)]
+        ref = bf_linear(_fr(X), _fr(W[rows]), [Fraction(float(v)) for v in b[rows]] if bias else None)
+        ref = np.array(ref, dtype=np.float64)
+        blk = got[:, r * nl:(r + 1) * nl] if gather else got[r]
+        np.testing.assert_array_equal(blk, ref)
+
+
+@pytest.mark.parametrize("B,inn,out,P,bias", [(3, 6, 5, 2, False), (2, 8, 3, 4, True), (4, 3, 3, 3, True), (1, 5, 2, 1, False)])
+def test_row_bruteforce(B, inn, out, P, bias):
+    Xf, W = _ints(4, (B, inn)), _ints(5, (out, inn))
+    b = _ints(6, (out,), 1, 3) if bias else None
+    kl = inn // P
+    Xs = np.stack([Xf[:, r * kl:(r + 1) * kl] for r in range(P)])
+    Y, Z = oracle.row(Xs, W, P=P, bias=b, partials=True)
+    for r in range(P):
+        zr = bf_linear(_fr(Xf[:, r * kl:(r + 1) * kl]), _fr(W[:, r * kl:(r + 1) * kl]))
+        np.testing.assert_array_equal(Z[r], np.array(zr, dtype=np.float64))
+    # bias enters once, after the sum
+    ref = bf_linear(_fr(Xf), _fr(W), [Fraction(float(v)) for v in b] if bias else None)
+    np.testing.assert_array_equal(Y, np.array(ref, dtype=np.float64))
+
+
+@pytest.mark.parametrize("M,K,N,q", [(4, 6, 2, 2), (3, 3, 6, 3), (4, 4, 4, 1), (8, 4, 4, 4)])
+def test_summa_bruteforce(M, K, N, q):
+    X, A = _ints(7, (M, K)), _ints(8, (K, N))
+    ref = np.array(bf_matmul(_fr(X), _fr(A)), dtype=np.float64)
+    np.testing.assert_array_equal(oracle.summa(X, A, q), ref)
+
+
+def test_summa_steps_are_equations_1_and_2():
+    """q = 2: the two step products (1) and (2) of the SUMMA derivation, summed
+    block by block, give Y; each block depends only on its own row / column
+    panels."""
+    X, A = _ints(9, (4, 4)), _ints(10, (4, 4))
+    Y = oracle.summa(X, A, 2)
+    step1 = np.zeros((4, 4))
+    step2 = np.zeros((4, 4))
+    for i in range(2):
+        for j in range(2):
+            Xi0, Xi1 = X[2 * i:2 * i + 2, 0:2], X[2 * i:2 * i + 2, 2:4]
+            A0j, A1j = A[0:2, 2 * j:2 * j + 2], A[2:4, 2 * j:2 * j + 2]
+            step1[2 * i:2 * i + 2, 2 * j:2 * j + 2] = np.array(bf_matmul(_fr(Xi0), _fr(A0j)), dtype=float)
+            step2[2 * i:2 * i + 2, 2 * j:2 * j + 2] = np.array(bf_matmul(_fr(Xi1), _fr(A1j)), dtype=float)
+    np.testing.assert_array_equal(Y, step1 + step2)
+
+
+# ---------------------------------------------------------------------------
+# (b) sharded == unsharded on float data, and (d) the SUMMA identity
+# ---------------------------------------------------------------------------
+def test_sharded_equals_unsharded_float():
+    rng = np.random.default_rng(11)
+    X = rng.standard_normal((8, 64))
+    Wg, Wu = rng.uniform(-1 / 8, 1 / 8, (256, 64)), rng.uniform(-1 / 8, 1 / 8, (256, 64))
+    Wd = rng.uniform(-1 / 16, 1 / 16, (64, 256))
+    for P in (1, 2, 4, 8):
+        g = oracle.col(X, Wg, P=P, gather=True)
+        np.testing.assert_allclose(g, X @ Wg.T, rtol=1e-12, atol=1e-13)
+        ys = oracle.mlp(X, Wg, Wu, Wd, P=P, round_dtype="f64")
+        gf, uf = X @ Wg.T, X @ Wu.T
+        h = gf / (1 + np.exp(-gf)) * uf
+        np.testing.assert_allclose(ys, h @ Wd.T, rtol=1e-11, atol=1e-13)
+
+
+@pytest.mark.parametrize("q", [1, 2, 4, 8])
+def test_summa_identity_float(q):
+    rng = np.random.default_rng(12)
+    X, A = rng.standard_normal((16, 24)), rng.standard_normal((24, 32))
+    np.testing.assert_allclose(oracle.summa(X, A, q), X @ A, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# SwiGLU closed forms
+# ---------------------------------------------------------------------------
+def test_swiglu_closed_forms():
+    z = np.array([0.0, 1.0, -1.0, 2.5, -7.0, 40.0, -40.0])
+    s = oracle.swiglu(z, np.ones_like(z))
+    assert s[0] == 0.0
+    assert abs(s[1] - 0.7310585786300049) < 1e-15  # 1 / (1 + 1/e)
+    np.testing.assert_allclose(s[[1, 3]] - oracle.swiglu(-z[[1, 3]], np.ones(2)), z[[1, 3]], rtol=1e-14)  # silu(z) - silu(-z) = z
+    assert abs(s[5] - 40.0) < 1e-15 * 40 + 1e-15 and abs(s[6]) < 1e-15
+    assert np.all(s[[2, 4]] < 0) and np.all(s[[2, 4]] > -0.3)  # silu is bounded below (min ~ -0.278)
+    u = np.array([2.0, -3.0, 0.5, 1.0, 1.0, 1.0, 1.0])
+    np.testing.assert_allclose(oracle.swiglu(z, u), s * u, rtol=1e-15)
+
+
+def test_round_matches_independent_rne():
+    rng = np.random.default_rng(13)
+    v = rng.standard_normal(2000).astype(np.float32)
+    v = np.concatenate([v, np.float32([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 6e-41, -3e-39, 65520.0 / 65536])])
+    want_bf = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(v)).astype(np.float64)
+    got_bf = np.array([oracle.round_to(float(x), "bf16") for x in v])
+    np.testing.assert_array_equal(got_bf, want_bf)
+    w = v[np.abs(v) < 60000]
+    want_h = w.astype(np.float16).astype(np.float64)
+    got_h = np.array([oracle.round_to(float(x), "f16") for x in w])
+    np.testing.assert_array_equal(got_h, want_h)
+
+
+def test_swiglu_rounds_once_to_activation_dtype():
+    rng = np.random.default_rng(14)
+    g, u = rng.standard_normal(500), rng.standard_normal(500)
+    h = oracle.swiglu(g, u, "bf16")
+    exact = oracle.swiglu(g, u, "f64")
+    assert np.all(np.abs(h - exact) <= 0.5 * oracle.ulp(exact, "bf16") * (1 + 1e-12))
+    hb = synth.f32_to_bf16_bits(h.astype(np.float32))
+    np.testing.assert_array_equal(synth.bf16_bits_to_f32(hb).astype(np.float64), h)
+
+
+# ---------------------------------------------------------------------------
+# 4-bit affine
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("case", _gold("q4_words.json")["cases"], ids=lambda c: c["word"])
+def test_deq4_hand_words(case):
+    gs = 8
+    packed = np.array([[int(case["word"], 16)]], dtype=np.uint32)
+    s = np.array([[int(case["scale_f16"], 16)]], dtype=np.uint16)
+    b = np.array([[int(case["bias_f16"], 16)]], dtype=np.uint16)
+    np.testing.assert_array_equal(oracle.deq4(packed, s, b, group_size=gs)[0], np.array(case["w"], dtype=np.float64))
+
+
+def test_deq4_round_trip_and_groups():
+    w = synth.uniform(15, (6, 256), 1 / 64, synth.F32)
+    w[2, 64:128] = np.float32(0.0123)  # a constant group
+    packed, s, b, q = synth.quantize_q4(w, 64)
+    assert q.min() >= 0 and q.max() <= 15
+    d = oracle.deq4(packed, s, b, 64)
+    sc = np.repeat(s.view(np.float16).astype(np.float64), 64, axis=1)
+    bi = np.repeat(b.view(np.float16).astype(np.float64), 64, axis=1)
+    # error of a min/max 4-bit code: half a step, plus the fp16 rounding of scale and bias
+    bound = 0.5 * sc + 15 * sc * 2 ** -11 + np.abs(bi) * 2 ** -11 + 1e-12
+    assert np.all(np.abs(d - w.astype(np.float64)) <= bound)
+    assert np.all(d[2, 64:128] == np.float64(np.float16(np.float32(0.0123))))
+    # group boundaries: each group uses its own (scale, bias)
+    assert np.all((d[:, :64] - bi[:, :64]) / np.where(sc[:, :64] > 0, sc[:, :64], 1) == q[:, :64])
+
+
+def test_deq4_then_linear_matches_bruteforce():
+    packed, s, b, q = synth.quantize_q4(synth.uniform(16, (4, 64), 1 / 8, synth.F32), 64)
+    Wd = oracle.deq4(packed, s, b, 64)
+    X = _ints(17, (2, 64))
+    ref = bf_linear(_fr(X), _fr(Wd))
+    np.testing.assert_array_equal(oracle.col(X, Wd, P=2, gather=True), np.array(ref, dtype=np.float64))
+
+
+# ---------------------------------------------------------------------------
+# decoders and metrics
+# ---------------------------------------------------------------------------
+def test_decoders():
+    bits = np.array([0x3C00, 0xC000, 0x0001, 0x03FF, 0x7BFF, 0x0400], dtype=np.uint16)
+    np.testing.assert_array_equal(oracle.decode(bits, "f16"),
+                                  [1.0, -2.0, 2.0 ** -24, 1023 * 2.0 ** -24, 65504.0, 2.0 ** -14])
+    bb = np.array([0x3F80, 0xBF00, 0x4049, 0x0001], dtype=np.uint16)
+    np.testing.assert_array_equal(oracle.decode(bb, "bf16"), [1.0, -0.5, 3.140625, 2.0 ** -133])
+
+
+def test_ulp_and_metrics():
+    np.testing.assert_array_equal(oracle.ulp(np.array([1.0, 1.5, 0.75]), "bf16"), [2 ** -7, 2 ** -7, 2 ** -8])
+    assert oracle.ulp(np.array([1.0]), "f16")[0] == 2 ** -10
+    assert oracle.ulp(np.array([1.0]), "f32")[0] == 2 ** -23
+    ref = np.array([1.0, -2.0, 0.5])
+    m = oracle.metrics(ref + np.array([2 ** -9, 0, 0]), ref, "bf16")  # within half an ulp
+    assert m["maxabs_ulp"] == 0.0 and m["maxabs"] == 2 ** -9
+    assert oracle.within(m, "bf16")
