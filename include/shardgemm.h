@@ -1,0 +1,159 @@
+/*
+ * shardgemm -- the sharded GEMMs of 1-D tensor parallelism and SUMMA's 2-D
+ * block accumulation, with every shard of a layer held on one MI355X GPU.
+ *
+ * Sources (page title, then the section the entry point follows):
+ *  [MLX]   "MLX 张量并行（Tensor Parallelism）实战指南：用 AllToShardedLinear 与
+ *          ShardedToAllLinear 实现 Llama 多设备推理"
+ *  [HSYM]  "Sharded Matrices and How to Multiply Them 精华笔记"
+ *  [SUMMA] "ColossalAI 2D 张量并行：基于 SUMMA 的二维模型切分原理与实现"
+ *  [EAI]   "拆解EnergonAI的张量并行实现：Linear1D与词表并行的2个关键技巧"
+ *
+ * Conventions shared by every entry point
+ *  - Weights use the (out, in) row-major layout and a linear layer computes
+ *    y = x W^T ([MLX] 2.1 and 2.2).  Activations are row-major (tokens, features).
+ *  - P shards are emulated on the current HIP device: the shard copies of a
+ *    layer live in one allocation, shard r at offset r.
+ *  - Pointers named x, y, X, A, Y, workspace are device pointers owned by the
+ *    caller.  Layer weights passed to the constructors may be host or device
+ *    memory; they are read, never modified ([MLX] 3.1: the source layer is
+ *    only read).
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *    asynchronously; results are ready after the stream synchronises.
+ *  - Validation happens on the host before any device work and returns a
+ *    status; sg_last_error() then describes the failure (thread-local).
+ *    A device fault surfaces at the next synchronisation of the stream.
+ *  - B == 0 tokens is a successful no-op.
+ *  - Results are bitwise identical run to run (fixed reduction order).
+ *  - Accumulation is fp32; the output dtype is the caller's choice.
+ */
+#ifndef SHARDGEMM_H
+#define SHARDGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SG_OK = 0,
+    SG_ERR_INVALID_ARG = 1,   /* null pointer, negative size, bad dtype or epilogue */
+    SG_ERR_BAD_MODE = 2,      /* sharding is neither all-to-sharded nor sharded-to-all */
+    SG_ERR_NOT_DIVISIBLE = 3, /* a dimension does not split evenly */
+    SG_ERR_UNSUPPORTED = 4,   /* valid request this library does not implement */
+    SG_ERR_WORKSPACE = 5,     /* workspace missing or too small */
+    SG_ERR_OOM = 6,           /* device allocation failed */
+    SG_ERR_HIP = 7            /* a HIP runtime call failed */
+} sg_status;
+
+typedef enum { SG_ALL_TO_SHARDED = 0, SG_SHARDED_TO_ALL = 1 } sg_mode;
+typedef enum { SG_F32 = 0, SG_BF16 = 1, SG_F16 = 2 } sg_dtype;
+typedef enum { SG_EPI_NONE = 0, SG_EPI_SWIGLU = 1 } sg_epilogue;
+
+typedef struct sg_layer sg_layer; /* opaque, owned by the library */
+
+/* Shard a dense linear layer over P ranks ([MLX] 3.1 shard_linear; slicing
+ * rule of [MLX] 3.2).
+ *   weight   (out_dims, in_dims) of `dtype`, row-major.
+ *   bias     (out_dims) of `dtype`, or NULL.
+ *   mode     SG_ALL_TO_SHARDED: rank r keeps out_dims/P weight rows and the
+ *            matching bias entries ([MLX] 2.1).  SG_SHARDED_TO_ALL: rank r keeps
+ *            in_dims/P weight columns; the whole bias is added once after the
+ *            cross-rank sum ([MLX] 2.2).  Anything else: SG_ERR_BAD_MODE.
+ *   segments the split dimension is first cut into `segments` equal segments
+ *            (a fused weight such as [Wq; Wk; Wv]); rank r keeps its part of
+ *            every segment, in segment order ([MLX] 3.2).
+ *   P        number of ranks (P >= 1; P == 1 is the unsharded layer).
+ * Errors: SG_ERR_NOT_DIVISIBLE when the split dimension is not divisible by
+ * segments, or dim/segments not by P ([MLX] 2.1 and 6: "Cannot shard the
+ * output of size .. across .. devices").  *out receives the new layer. */
+sg_status sg_shard_linear(const void* weight, sg_dtype dtype, int64_t out_dims, int64_t in_dims,
+                          const void* bias, int mode, int segments, int P, void* stream,
+                          sg_layer** out);
+
+/* Shard a 4-bit affine quantized linear layer ([MLX] 2.3, 6: group_size 64,
+ * bits 4, mode affine).  Stored format: w[o,k] = scale[o,g] * q[o,k] + bias[o,g]
+ * with g = k / group_size; eight 4-bit codes per uint32 along k, element k in
+ * bits [4 (k mod 8), 4 (k mod 8) + 4).
+ *   wq       (out_dims, in_dims/8) uint32.
+ *   scales   (out_dims, in_dims/group_size) fp16 bit patterns.
+ *   qbiases  (out_dims, in_dims/group_size) fp16 bit patterns.
+ *   act      activation dtype of the layer (SG_BF16 or SG_F16).
+ *   bias     (out_dims) of `act`, or NULL (the layer bias, as for sg_shard_linear).
+ * Only group_size 64 and bits 4 are implemented (else SG_ERR_UNSUPPORTED).
+ * Sharded-to-all needs (in_dims/segments/P) % group_size == 0 so that no
+ * quantization group straddles two ranks (SG_ERR_NOT_DIVISIBLE). */
+sg_status sg_shard_quantized_linear(const uint32_t* wq, const uint16_t* scales,
+                                    const uint16_t* qbiases, int64_t out_dims, int64_t in_dims,
+                                    int group_size, int bits, sg_dtype act, const void* bias,
+                                    int mode, int segments, int P, void* stream, sg_layer** out);
+
+/* All-to-sharded forward ([MLX] 2.1; [HSYM] Case 1: no communication).
+ *   x        (B, in_dims) of the layer's dtype, replicated to every rank.
+ *   y        gather == 0: (P, B, n_out/P), rank r's output at offset r
+ *            (the output stays sharded); gather == 1: (B, n_out) with rank r
+ *            in columns [r n_out/P, (r+1) n_out/P) -- the rank-order all-gather
+ *            of the vocabulary-parallel head ([EAI], LM head).
+ *   epilogue SG_EPI_NONE: n_out = out_dims, y = x W_r^T (+ b_r).
+ *            SG_EPI_SWIGLU: the layer must be all-to-sharded with segments == 2
+ *            holding [W_gate; W_up]; n_out = out_dims/2 and
+ *            y_r = silu(x Wg_r^T) * (x Wu_r^T), silu(z) = z / (1 + e^-z), computed
+ *            in fp32 and rounded once ([MLX] 5.2-5.3: the elementwise product
+ *            keeps the sharding).  Bias is not allowed with SWIGLU.
+ *   y_dtype  SG_F32, SG_BF16 or SG_F16. */
+sg_status sg_all_to_sharded(const sg_layer* layer, const void* x, int64_t B, void* y, int gather,
+                            int epilogue, sg_dtype y_dtype, void* stream);
+
+/* Sharded-to-all forward ([MLX] 2.2; [HSYM] Case 3 with AllReduce).
+ *   x_partial (P, B, in_dims/P) of the layer's dtype; slice r is rank r's
+ *            input (columns r of the full activation under the layer's
+ *            segments rule).
+ *   y        (B, out_dims) of y_dtype: sum over r = 0..P-1 of
+ *            x_partial[r] W_r^T, then + bias once.
+ *   workspace device scratch of at least sg_sharded_to_all_workspace(layer, B)
+ *            bytes (NULL allowed when that is 0).  It must be zero-filled
+ *            before its first use; every call leaves it zero-filled again.
+ *            Calls that share a workspace must not run concurrently. */
+sg_status sg_sharded_to_all(const sg_layer* layer, const void* x_partial, int64_t B, void* y,
+                            sg_dtype y_dtype, void* workspace, size_t ws_bytes, void* stream);
+
+/* Bytes of workspace sg_sharded_to_all needs for B tokens (0 on bad input). */
+size_t sg_sharded_to_all_workspace(const sg_layer* layer, int64_t B);
+
+/* SUMMA on a q x q grid ([SUMMA], SUMMA section, equations (1), (2)).
+ *   X (M, K) and A (K, N) row-major of `dtype` (SG_BF16 or SG_F16); Y (M, N)
+ *   fp32.  Both operands are cut into q x q blocks; for t = 0 .. q-1 every
+ *   block performs Y_ij += X_it A_tj.
+ *   accumulate 0: Y = X A; 1: Y += X A.
+ *   fused      0: q launches, step t adds its block products into Y in place
+ *              (the step structure of the derivation); 1: one launch that keeps
+ *              each block's accumulator in registers across the q steps.
+ * Errors: SG_ERR_NOT_DIVISIBLE when q does not divide M, K and N or q < 1
+ * (P = q x q processors). */
+sg_status sg_summa_matmul(const void* X, const void* A, sg_dtype dtype, int64_t M, int64_t K,
+                          int64_t N, int q, float* Y, int accumulate, int fused, void* stream);
+
+/* Layer description (any output pointer may be NULL). */
+sg_status sg_layer_info(const sg_layer* layer, int64_t* out_dims, int64_t* in_dims, int* mode,
+                        int* segments, int* P, sg_dtype* dtype, int* quantized);
+
+/* Copy rank r's stored shard of one layer tensor into dst (device or host).
+ *   what 0: weight (dense: (rows_r, cols_r) of dtype; quantized: packed uint32)
+ *        1: bias (all-to-sharded: out_dims/P entries; sharded-to-all: the full bias)
+ *        2: quantization scales, 3: quantization biases.
+ * Synchronous with respect to `stream`; dst_bytes must be at least the size. */
+sg_status sg_layer_copy_shard(const sg_layer* layer, int r, int what, void* dst, size_t dst_bytes,
+                              void* stream);
+
+/* Release a layer and its device memory (NULL is ignored). */
+void sg_layer_free(sg_layer* layer);
+
+/* Message describing the last failure on this thread ("" if none). */
+const char* sg_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SHARDGEMM_H */

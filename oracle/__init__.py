@@ -118,7 +118,7 @@ def _f64(a, dtype=None):
     if a is None:
         return None
     a = np.ascontiguousarray(a)
-    if a.dtype == np.float64 and dtype in (None, "f64", F64):
+    if a.dtype == np.float64:  # already values (e.g. dequantized weights)
         return a
     return decode(a, dtype)
 

@@ -1,0 +1,242 @@
+"""Python binding of libshardgemm: the sharded GEMMs of 1-D tensor parallelism
+(all-to-sharded, sharded-to-all, their 4-bit affine variants) and SUMMA's
+q-step block accumulation, with all P shards of a layer on one MI355X GPU.
+
+This module only marshals arguments: torch supplies device memory and the
+current HIP stream, every step of the computation runs in the library's
+kernels.  The entry points mirror include/shardgemm.h one to one:
+
+    shard_linear               sg_shard_linear
+    shard_quantized_linear     sg_shard_quantized_linear
+    all_to_sharded             sg_all_to_sharded
+    sharded_to_all             sg_sharded_to_all (+ sg_sharded_to_all_workspace)
+    summa_matmul               sg_summa_matmul
+    Layer.info / Layer.shard   sg_layer_info / sg_layer_copy_shard
+
+There is no fallback: if the library is not built, importing works but the
+first call raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libshardgemm.so")
+
+ALL_TO_SHARDED, SHARDED_TO_ALL = 0, 1
+_MODES = {"all-to-sharded": ALL_TO_SHARDED, "sharded-to-all": SHARDED_TO_ALL}
+F32, BF16, F16 = 0, 1, 2
+_DT = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
+_TORCH_DT = {v: k for k, v in _DT.items()}
+EPI_NONE, EPI_SWIGLU = 0, 1
+
+OK, ERR_INVALID_ARG, ERR_BAD_MODE, ERR_NOT_DIVISIBLE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_OOM, ERR_HIP = range(8)
+
+
+class ShardGemmError(RuntimeError):
+    """A non-zero sg_status; `code` holds it, the message is sg_last_error()."""
+
+    def __init__(self, code: int, message: str):
+        super().__init__(f"[sg_status {code}] {message}")
+        self.code = code
+
+
+class ShardGemmNotBuilt(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (ctypes.CDLL) with every entry point typed."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ShardGemmNotBuilt(
+                f"{LIB_PATH} is missing: build it first (python -m sharded_gemm_alltosharded_amd._build)")
+        L = C.CDLL(LIB_PATH)
+        P, I64, I, SZ = C.c_void_p, C.c_int64, C.c_int, C.c_size_t
+        PP = C.POINTER(C.c_void_p)
+        sig = {
+            "sg_shard_linear": ([P, I, I64, I64, P, I, I, I, P, PP], I),
+            "sg_shard_quantized_linear": ([P, P, P, I64, I64, I, I, I, P, I, I, I, P, PP], I),
+            "sg_all_to_sharded": ([P, P, I64, P, I, I, I, P], I),
+            "sg_sharded_to_all": ([P, P, I64, P, I, P, SZ, P], I),
+            "sg_sharded_to_all_workspace": ([P, I64], SZ),
+            "sg_summa_matmul": ([P, P, I, I64, I64, I64, I, P, I, I, P], I),
+            "sg_layer_info": ([P, P, P, P, P, P, P, P], I),
+            "sg_layer_copy_shard": ([P, I, I, P, SZ, P], I),
+            "sg_layer_free": ([P], None),
+            "sg_last_error": ([], C.c_char_p),
+        }
+        for name, (args, res) in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def _check(rc: int):
+    if rc != OK:
+        raise ShardGemmError(rc, lib().sg_last_error().decode(errors="replace"))
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(device=None):
+    return C.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _mode(sharding) -> int:
+    if isinstance(sharding, int):
+        return sharding
+    # unknown strings reach the library as an invalid mode, which rejects them
+    return _MODES.get(sharding, -1)
+
+
+class Layer:
+    """A sharded layer owned by the library (sg_layer*)."""
+
+    def __init__(self, handle: C.c_void_p, device: torch.device):
+        self._h = handle
+        self.device = device
+        o, i, m, s, p, d, q = (C.c_int64(), C.c_int64(), C.c_int(), C.c_int(), C.c_int(), C.c_int(), C.c_int())
+        _check(lib().sg_layer_info(self._h, C.byref(o), C.byref(i), C.byref(m), C.byref(s), C.byref(p),
+                                   C.byref(d), C.byref(q)))
+        self.out_dims, self.in_dims = o.value, i.value
+        self.mode, self.segments, self.P = m.value, s.value, p.value
+        self.dtype = _TORCH_DT[d.value]
+        self.quantized = bool(q.value)
+
+    @property
+    def handle(self):
+        return self._h
+
+    def free(self):
+        if self._h is not None and _lib is not None:
+            _lib.sg_layer_free(self._h)
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+    def shard(self, r: int, what: int = 0) -> torch.Tensor:
+        """Copy of rank r's stored tensor: 0 weight, 1 bias, 2 scales, 3 biases."""
+        if what == 0:
+            if self.quantized:
+                shape, dt = self._wshape(8), torch.int32
+            else:
+                shape, dt = self._wshape(1), self.dtype
+        elif what == 1:
+            n = self.out_dims // self.P if self.mode == ALL_TO_SHARDED else self.out_dims
+            shape, dt = (n,), self.dtype
+        else:
+            shape, dt = self._wshape(64), torch.int16
+        out = torch.empty(shape, dtype=dt, device=self.device)
+        _check(lib().sg_layer_copy_shard(self._h, r, what, _ptr(out), out.numel() * out.element_size(),
+                                         _stream(self.device)))
+        return out
+
+    def _wshape(self, per):
+        if self.mode == ALL_TO_SHARDED:
+            return (self.out_dims // self.P, self.in_dims // per)
+        return (self.out_dims, self.in_dims // self.P // per)
+
+
+def shard_linear(weight: torch.Tensor, sharding, segments: int = 1, P: int = 1, bias=None) -> Layer:
+    """Shard a dense (out, in) weight over P ranks (sg_shard_linear)."""
+    dt = _DT.get(weight.dtype, -1)
+    out_dims, in_dims = weight.shape
+    weight = weight.contiguous()
+    bias = None if bias is None else bias.contiguous()
+    h = C.c_void_p()
+    dev = weight.device
+    _check(lib().sg_shard_linear(_ptr(weight), dt, out_dims, in_dims, _ptr(bias), _mode(sharding), segments, P,
+                                 _stream(dev) if dev.type == "cuda" else None, C.byref(h)))
+    return Layer(h, dev if dev.type == "cuda" else torch.device("cuda", torch.cuda.current_device()))
+
+
+def shard_quantized_linear(wq: torch.Tensor, scales: torch.Tensor, qbiases: torch.Tensor, in_dims: int, sharding,
+                           segments: int = 1, P: int = 1, group_size: int = 64, bits: int = 4,
+                           act_dtype=torch.bfloat16, bias=None) -> Layer:
+    """Shard a 4-bit affine layer (sg_shard_quantized_linear).  wq: (out, in/8)
+    int32 words; scales, qbiases: (out, in/group_size) 16-bit fp16 patterns."""
+    out_dims = wq.shape[0]
+    wq, scales, qbiases = wq.contiguous(), scales.contiguous(), qbiases.contiguous()
+    bias = None if bias is None else bias.contiguous()
+    dev = wq.device
+    h = C.c_void_p()
+    _check(lib().sg_shard_quantized_linear(_ptr(wq), _ptr(scales), _ptr(qbiases), out_dims, in_dims, group_size, bits,
+                                           _DT.get(act_dtype, -1), _ptr(bias), _mode(sharding), segments, P,
+                                           _stream(dev) if dev.type == "cuda" else None, C.byref(h)))
+    return Layer(h, dev if dev.type == "cuda" else torch.device("cuda", torch.cuda.current_device()))
+
+
+def all_to_sharded(layer: Layer, x: torch.Tensor, gather: bool = False, swiglu: bool = False,
+                   out_dtype=None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """x (B, in) -> (P, B, n/P) sharded, or (B, n) gathered; n = out_dims, or
+    out_dims/2 with the fused SwiGLU epilogue."""
+    B = x.shape[0]
+    n = layer.out_dims // 2 if swiglu else layer.out_dims
+    out_dtype = out_dtype or layer.dtype
+    if out is None:
+        shape = (B, n) if gather else (layer.P, B, n // layer.P)
+        out = torch.empty(shape, dtype=out_dtype, device=x.device)
+    _check(lib().sg_all_to_sharded(layer.handle, _ptr(x), B, _ptr(out), int(gather),
+                                   EPI_SWIGLU if swiglu else EPI_NONE, _DT.get(out.dtype, -1), _stream(x.device)))
+    return out
+
+
+_workspaces: dict = {}
+
+
+def workspace(layer: Layer, B: int, device) -> torch.Tensor | None:
+    """A zero-filled workspace shared by calls on one device (the library
+    leaves it zero-filled after every call)."""
+    need = lib().sg_sharded_to_all_workspace(layer.handle, B)
+    if need == 0:
+        return None
+    key = torch.device(device)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.zeros(need, dtype=torch.uint8, device=key)
+        _workspaces[key] = ws
+    return ws
+
+
+def sharded_to_all(layer: Layer, x_partial: torch.Tensor, out_dtype=None, out: torch.Tensor | None = None,
+                   ws: torch.Tensor | None = None) -> torch.Tensor:
+    """x_partial (P, B, in/P) -> (B, out): the rank partials summed in rank
+    order, bias added once."""
+    B = x_partial.shape[1]
+    out_dtype = out_dtype or layer.dtype
+    if out is None:
+        out = torch.empty((B, layer.out_dims), dtype=out_dtype, device=x_partial.device)
+    if ws is None:
+        ws = workspace(layer, B, x_partial.device)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().sg_sharded_to_all(layer.handle, _ptr(x_partial), B, _ptr(out), _DT.get(out.dtype, -1), _ptr(ws),
+                                   nbytes, _stream(x_partial.device)))
+    return out
+
+
+def summa_matmul(X: torch.Tensor, A: torch.Tensor, q: int, out: torch.Tensor | None = None,
+                 accumulate: bool = False, fused: bool = True) -> torch.Tensor:
+    """Y (M, N) fp32 = X A (or Y += X A) on a q x q block grid."""
+    M, K = X.shape
+    N = A.shape[1]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    _check(lib().sg_summa_matmul(_ptr(X), _ptr(A), _DT.get(X.dtype, -1), M, K, N, q, _ptr(out), int(accumulate),
+                                 int(fused), _stream(X.device)))
+    return out

@@ -1,0 +1,552 @@
+// C-ABI entry points: validation, layer objects, shard slicing and kernel
+// dispatch.  Every check runs on the host before any HIP call, so argument
+// errors never touch the device.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "internal.h"
+
+namespace sg {
+hipError_t q4_repack(uint32_t* w, int64_t n, int forward, hipStream_t s);
+}
+
+struct sg_layer {
+    int mode, segments, P, quantized;
+    sg_dtype dtype;  // weight dtype (dense) or activation dtype (4-bit)
+    int64_t out_dims, in_dims;
+    int64_t rows_r, cols_r;  // one rank's weight shape in elements
+    void* w;                 // dense: P x rows_r x cols_r; 4-bit: P x rows_r x cols_r/8 words
+    uint16_t* qs;            // 4-bit scales: P x rows_r x cols_r/64
+    uint16_t* qb;            // 4-bit biases
+    void* bias;              // all-to-sharded: P x rows_r (rank order); sharded-to-all: out_dims
+    int device;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+sg_status fail(sg_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+sg_status hip_fail(hipError_t e, const char* what) {
+    return fail(e == hipErrorOutOfMemory ? SG_ERR_OOM : SG_ERR_HIP, "%s: %s", what,
+                hipGetErrorString(e));
+}
+
+#define HIP_TRY(expr, what)                        \
+    do {                                           \
+        hipError_t e_ = (expr);                    \
+        if (e_ != hipSuccess) return hip_fail(e_, what); \
+    } while (0)
+
+size_t dtype_size(int dt) { return dt == SG_F32 ? 4 : 2; }
+bool dtype_ok(int dt) { return dt == SG_F32 || dt == SG_BF16 || dt == SG_F16; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Rank r's part of an axis cut into S segments and P parts per segment:
+// offsets s * seg + r * part for s = 0..S-1, each `part` long.
+sg_status check_split(int64_t dim, int S, int P, const char* what) {
+    if (dim % S)
+        return fail(SG_ERR_NOT_DIVISIBLE, "Cannot split the %s of size %lld into %d segments.", what,
+                    (long long)dim, S);
+    if ((dim / S) % P)
+        return fail(SG_ERR_NOT_DIVISIBLE, "Cannot shard the %s of size %lld across %d devices.", what,
+                    (long long)dim, P);
+    return SG_OK;
+}
+
+// Copy rank shards of a row-major (rows, cols) array with element size esz.
+// axis 0: shard r = rows of every segment, stacked (P, rows/P, cols).
+// axis 1: shard r = columns of every segment, stacked (P, rows, cols/P).
+sg_status copy_shards(void* dst, const void* src, int64_t rows, int64_t cols, size_t esz, int axis,
+                      int S, int P, hipStream_t st) {
+    const char* s8 = (const char*)src;
+    char* d8 = (char*)dst;
+    if (axis == 0) {
+        const int64_t seg = rows / S, part = seg / P;
+        for (int r = 0; r < P; ++r)
+            for (int s = 0; s < S; ++s) {
+                const int64_t srow = s * seg + (int64_t)r * part;
+                const int64_t drow = (int64_t)r * S * part + s * part;
+                HIP_TRY(hipMemcpyAsync(d8 + drow * cols * esz, s8 + srow * cols * esz,
+                                       (size_t)(part * cols) * esz, hipMemcpyDefault, st),
+                        "shard copy");
+            }
+    } else {
+        const int64_t seg = cols / S, part = seg / P, cr = S * part;
+        for (int r = 0; r < P; ++r)
+            for (int s = 0; s < S; ++s) {
+                const int64_t scol = s * seg + (int64_t)r * part;
+                HIP_TRY(hipMemcpy2DAsync(d8 + ((int64_t)r * rows * cr + s * part) * esz, cr * esz,
+                                         s8 + scol * esz, cols * esz, part * esz, rows,
+                                         hipMemcpyDefault, st),
+                        "shard copy");
+            }
+    }
+    return SG_OK;
+}
+
+void free_layer(sg_layer* l) {
+    if (!l) return;
+    // kernels queued on any stream may still read the shards
+    (void)hipDeviceSynchronize();
+    if (l->w) (void)hipFree(l->w);
+    if (l->qs) (void)hipFree(l->qs);
+    if (l->qb) (void)hipFree(l->qb);
+    if (l->bias) (void)hipFree(l->bias);
+    delete l;
+}
+
+sg_status common_checks(int mode, int segments, int P, int64_t out_dims, int64_t in_dims, sg_layer** out) {
+    if (!out) return fail(SG_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    if (mode != SG_ALL_TO_SHARDED && mode != SG_SHARDED_TO_ALL)
+        return fail(SG_ERR_BAD_MODE,
+                    "Sharding type %d not supported, choose one of 'all-to-sharded' or 'sharded-to-all'",
+                    mode);
+    if (segments < 1 || P < 1) return fail(SG_ERR_INVALID_ARG, "segments and P must be >= 1");
+    if (out_dims < 1 || in_dims < 1) return fail(SG_ERR_INVALID_ARG, "layer dimensions must be >= 1");
+    if (out_dims > INT32_MAX || in_dims > INT32_MAX)
+        return fail(SG_ERR_UNSUPPORTED, "layer dimensions above 2^31 are not supported");
+    if (mode == SG_ALL_TO_SHARDED) return check_split(out_dims, segments, P, "output");
+    return check_split(in_dims, segments, P, "input");
+}
+
+// ---------------------------------------------------------------------------
+// kernel choice
+// ---------------------------------------------------------------------------
+enum Kind { K_GENERIC, K_TILE0, K_TILE1, K_SKINNY, K_Q4 };
+
+int num_cus() {
+    static int cus = -1;
+    if (cus < 0) {
+        int dev = 0;
+        hipDeviceProp_t prop;
+        cus = (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess)
+                  ? prop.multiProcessorCount
+                  : 256;
+    }
+    return cus;
+}
+
+// dense operands: the MFMA paths need 16-byte rows
+bool mfma_ok(const sg_layer* l, const void* x) {
+    return l->dtype != SG_F32 && l->cols_r % 8 == 0 && aligned16(x) && aligned16(l->w);
+}
+
+Kind choose(const sg_layer* l, int64_t B, const void* x) {
+    if (l->quantized)
+        return (B <= 32 && l->cols_r % 256 == 0 && aligned16(x)) ? K_Q4 : K_GENERIC;
+    if (!mfma_ok(l, x)) return K_GENERIC;
+    if (B <= 32) return K_SKINNY;
+    return B >= 512 ? K_TILE0 : K_TILE1;
+}
+
+// Split sharded-to-all work by rank when the output alone gives too few
+// workgroups to fill the chip.
+sg::SplitLayout split_layout(const sg_layer* l, Kind k, int64_t B);
+
+bool want_split(const sg_layer* l, Kind k, int64_t B) {
+    if (l->P < 2) return false;
+    if (split_layout(l, k, B).counters > sg::kMaxCounters) return false;
+    const int cus = num_cus();
+    switch (k) {
+    case K_SKINNY: return (l->out_dims + 31) / 32 < 4 * cus;
+    case K_Q4: return (l->out_dims + 63) / 64 < 4 * cus;
+    case K_TILE0: return sg::tile_count((int)B, (int)l->out_dims, 0) * 2 <= cus;
+    case K_TILE1: return sg::tile_count((int)B, (int)l->out_dims, 1) * 2 <= cus;
+    default: return false;
+    }
+}
+
+sg::SplitLayout split_layout(const sg_layer* l, Kind k, int64_t B) {
+    switch (k) {
+    case K_SKINNY: return sg::skinny_split_layout((int)B, (int)l->out_dims, l->P);
+    case K_Q4: return sg::q4_split_layout((int)B, (int)l->out_dims, l->P);
+    case K_TILE0: return sg::tile_split_layout((int)B, (int)l->out_dims, l->P, 0);
+    case K_TILE1: return sg::tile_split_layout((int)B, (int)l->out_dims, l->P, 1);
+    default: return {0, 0};
+    }
+}
+
+// kernel family for a sharded-to-all call (alignment of the caller's pointers
+// is checked separately; misaligned pointers fall back to the generic path)
+Kind choose_row(const sg_layer* l, int64_t B) {
+    if (l->quantized) return B <= 32 && l->cols_r % 256 == 0 ? K_Q4 : K_GENERIC;
+    if (l->dtype == SG_F32 || l->cols_r % 8) return K_GENERIC;
+    return B <= 32 ? K_SKINNY : (B >= 512 ? K_TILE0 : K_TILE1);
+}
+
+hipError_t run(const sg::Problem& p, Kind k, hipStream_t st) {
+    switch (k) {
+    case K_TILE0: return sg::launch_tile(p, st, 0);
+    case K_TILE1: return sg::launch_tile(p, st, 1);
+    case K_SKINNY: return sg::launch_skinny(p, st);
+    case K_Q4: return sg::launch_q4(p, st);
+    default: return sg::launch_generic(p, st);
+    }
+}
+
+void set_weights(sg::Problem& p, const sg_layer* l) {
+    if (l->quantized) {
+        p.wq = (const uint32_t*)l->w;
+        p.qs = l->qs;
+        p.qb = l->qb;
+        p.ldq = l->cols_r / 8;
+        p.ldg = l->cols_r / 64;
+        p.q_seg = l->rows_r * p.ldq;
+        p.g_seg = l->rows_r * p.ldg;
+    } else {
+        p.W = l->w;
+        p.ldw = l->cols_r;
+        p.w_seg = l->rows_r * l->cols_r;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sg_last_error(void) { return g_err.c_str(); }
+
+sg_status sg_shard_linear(const void* weight, sg_dtype dtype, int64_t out_dims, int64_t in_dims,
+                          const void* bias, int mode, int segments, int P, void* stream,
+                          sg_layer** out) {
+    g_err.clear();
+    sg_status st = common_checks(mode, segments, P, out_dims, in_dims, out);
+    if (st) return st;
+    if (!weight) return fail(SG_ERR_INVALID_ARG, "weight is NULL");
+    if (!dtype_ok(dtype)) return fail(SG_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+    hipStream_t hs = (hipStream_t)stream;
+    sg_layer* l = new sg_layer{};
+    l->mode = mode;
+    l->segments = segments;
+    l->P = P;
+    l->dtype = dtype;
+    l->out_dims = out_dims;
+    l->in_dims = in_dims;
+    l->rows_r = mode == SG_ALL_TO_SHARDED ? out_dims / P : out_dims;
+    l->cols_r = mode == SG_ALL_TO_SHARDED ? in_dims : in_dims / P;
+    (void)hipGetDevice(&l->device);
+    const size_t esz = dtype_size(dtype);
+    hipError_t e = hipMalloc(&l->w, (size_t)(out_dims * in_dims) * esz);
+    if (e != hipSuccess) {
+        free_layer(l);
+        return hip_fail(e, "weight allocation");
+    }
+    st = copy_shards(l->w, weight, out_dims, in_dims, esz, mode == SG_ALL_TO_SHARDED ? 0 : 1, segments, P, hs);
+    if (!st && bias) {
+        e = hipMalloc(&l->bias, (size_t)out_dims * esz);
+        if (e != hipSuccess) st = hip_fail(e, "bias allocation");
+        else if (mode == SG_ALL_TO_SHARDED)
+            st = copy_shards(l->bias, bias, out_dims, 1, esz, 0, segments, P, hs);
+        else {
+            e = hipMemcpyAsync(l->bias, bias, (size_t)out_dims * esz, hipMemcpyDefault, hs);
+            if (e != hipSuccess) st = hip_fail(e, "bias copy");
+        }
+    }
+    if (!st) {
+        e = hipStreamSynchronize(hs);
+        if (e != hipSuccess) st = hip_fail(e, "shard copy");
+    }
+    if (st) {
+        free_layer(l);
+        return st;
+    }
+    *out = l;
+    return SG_OK;
+}
+
+sg_status sg_shard_quantized_linear(const uint32_t* wq, const uint16_t* scales, const uint16_t* qbiases,
+                                    int64_t out_dims, int64_t in_dims, int group_size, int bits,
+                                    sg_dtype act, const void* bias, int mode, int segments, int P,
+                                    void* stream, sg_layer** out) {
+    g_err.clear();
+    sg_status st = common_checks(mode, segments, P, out_dims, in_dims, out);
+    if (st) return st;
+    if (!wq || !scales || !qbiases) return fail(SG_ERR_INVALID_ARG, "quantized tensors must not be NULL");
+    if (group_size != 64 || bits != 4)
+        return fail(SG_ERR_UNSUPPORTED, "only group_size 64 and bits 4 are implemented (got %d, %d)",
+                    group_size, bits);
+    if (act != SG_BF16 && act != SG_F16) return fail(SG_ERR_INVALID_ARG, "activation dtype must be bf16 or fp16");
+    if (in_dims % group_size) return fail(SG_ERR_NOT_DIVISIBLE, "in_dims %lld is not a multiple of group_size %d", (long long)in_dims, group_size);
+    if (mode == SG_SHARDED_TO_ALL && (in_dims / segments / P) % group_size)
+        return fail(SG_ERR_NOT_DIVISIBLE,
+                    "Cannot shard the input of size %lld across %d devices: a quantization group of %d "
+                    "would straddle two ranks.", (long long)in_dims, P, group_size);
+    hipStream_t hs = (hipStream_t)stream;
+    sg_layer* l = new sg_layer{};
+    l->mode = mode;
+    l->segments = segments;
+    l->P = P;
+    l->quantized = 1;
+    l->dtype = act;
+    l->out_dims = out_dims;
+    l->in_dims = in_dims;
+    l->rows_r = mode == SG_ALL_TO_SHARDED ? out_dims / P : out_dims;
+    l->cols_r = mode == SG_ALL_TO_SHARDED ? in_dims : in_dims / P;
+    (void)hipGetDevice(&l->device);
+    const int axis = mode == SG_ALL_TO_SHARDED ? 0 : 1;
+    const int64_t words = in_dims / 8, groups = in_dims / group_size;
+    hipError_t e = hipMalloc(&l->w, (size_t)(out_dims * words) * 4);
+    if (e == hipSuccess) e = hipMalloc((void**)&l->qs, (size_t)(out_dims * groups) * 2);
+    if (e == hipSuccess) e = hipMalloc((void**)&l->qb, (size_t)(out_dims * groups) * 2);
+    if (e != hipSuccess) {
+        free_layer(l);
+        return hip_fail(e, "quantized weight allocation");
+    }
+    st = copy_shards(l->w, wq, out_dims, words, 4, axis, segments, P, hs);
+    if (!st) st = copy_shards(l->qs, scales, out_dims, groups, 2, axis, segments, P, hs);
+    if (!st) st = copy_shards(l->qb, qbiases, out_dims, groups, 2, axis, segments, P, hs);
+    if (!st) {
+        e = sg::q4_repack((uint32_t*)l->w, out_dims * words, 1, hs);
+        if (e != hipSuccess) st = hip_fail(e, "code reorder");
+    }
+    if (!st && bias) {
+        e = hipMalloc(&l->bias, (size_t)out_dims * 2);
+        if (e != hipSuccess) st = hip_fail(e, "bias allocation");
+        else if (mode == SG_ALL_TO_SHARDED)
+            st = copy_shards(l->bias, bias, out_dims, 1, 2, 0, segments, P, hs);
+        else {
+            e = hipMemcpyAsync(l->bias, bias, (size_t)out_dims * 2, hipMemcpyDefault, hs);
+            if (e != hipSuccess) st = hip_fail(e, "bias copy");
+        }
+    }
+    if (!st) {
+        e = hipStreamSynchronize(hs);
+        if (e != hipSuccess) st = hip_fail(e, "shard copy");
+    }
+    if (st) {
+        free_layer(l);
+        return st;
+    }
+    *out = l;
+    return SG_OK;
+}
+
+sg_status sg_all_to_sharded(const sg_layer* l, const void* x, int64_t B, void* y, int gather,
+                            int epilogue, sg_dtype y_dtype, void* stream) {
+    g_err.clear();
+    if (!l) return fail(SG_ERR_INVALID_ARG, "layer is NULL");
+    if (l->mode != SG_ALL_TO_SHARDED) return fail(SG_ERR_INVALID_ARG, "layer is sharded-to-all; use sg_sharded_to_all");
+    if (B < 0 || B > INT32_MAX) return fail(SG_ERR_INVALID_ARG, "token count %lld out of range", (long long)B);
+    if (gather != 0 && gather != 1) return fail(SG_ERR_INVALID_ARG, "gather must be 0 or 1");
+    if (epilogue != SG_EPI_NONE && epilogue != SG_EPI_SWIGLU) return fail(SG_ERR_INVALID_ARG, "unknown epilogue %d", epilogue);
+    if (!dtype_ok(y_dtype)) return fail(SG_ERR_INVALID_ARG, "unknown output dtype %d", (int)y_dtype);
+    if (epilogue == SG_EPI_SWIGLU && (l->segments != 2 || l->bias))
+        return fail(SG_ERR_INVALID_ARG, "the SwiGLU epilogue needs an all-to-sharded layer with segments == 2 ([gate; up]) and no bias");
+    if (B == 0) return SG_OK;
+    if (!x || !y) return fail(SG_ERR_INVALID_ARG, "x and y must not be NULL");
+    sg::Problem p{};
+    p.A = x;
+    p.lda = l->in_dims;
+    p.M = (int)B;
+    p.Kseg = (int)l->cols_r;
+    p.nseg = 1;
+    p.dtype = l->dtype;
+    set_weights(p, l);
+    p.swiglu = epilogue == SG_EPI_SWIGLU;
+    p.N = (int)(p.swiglu ? l->out_dims / 2 : l->out_dims);
+    p.floc = p.swiglu ? l->rows_r / 2 : 0;
+    p.out = y;
+    p.out_dtype = y_dtype;
+    p.out_map = gather ? sg::OUT_ROWMAJOR : sg::OUT_SHARDED;
+    p.ldo = p.N;
+    p.nloc = p.N / l->P;
+    p.bias = l->bias;
+    Kind k = choose(l, B, x);
+    if (k != K_GENERIC && k != K_Q4 && !aligned16(y)) k = K_GENERIC;
+    hipError_t e = run(p, k, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "all_to_sharded launch");
+    return SG_OK;
+}
+
+size_t sg_sharded_to_all_workspace(const sg_layer* l, int64_t B) {
+    if (!l || l->mode != SG_SHARDED_TO_ALL || B <= 0 || B > INT32_MAX) return 0;
+    const Kind k = choose_row(l, B);
+    return want_split(l, k, B) ? sg::split_workspace_bytes(split_layout(l, k, B)) : 0;
+}
+
+sg_status sg_sharded_to_all(const sg_layer* l, const void* x_partial, int64_t B, void* y, sg_dtype y_dtype,
+                            void* workspace, size_t ws_bytes, void* stream) {
+    g_err.clear();
+    if (!l) return fail(SG_ERR_INVALID_ARG, "layer is NULL");
+    if (l->mode != SG_SHARDED_TO_ALL) return fail(SG_ERR_INVALID_ARG, "layer is all-to-sharded; use sg_all_to_sharded");
+    if (B < 0 || B > INT32_MAX) return fail(SG_ERR_INVALID_ARG, "token count %lld out of range", (long long)B);
+    if (!dtype_ok(y_dtype)) return fail(SG_ERR_INVALID_ARG, "unknown output dtype %d", (int)y_dtype);
+    if (B == 0) return SG_OK;
+    if (!x_partial || !y) return fail(SG_ERR_INVALID_ARG, "x_partial and y must not be NULL");
+    sg::Problem p{};
+    p.A = x_partial;
+    p.lda = l->cols_r;
+    p.a_seg = B * l->cols_r;
+    p.M = (int)B;
+    p.Kseg = (int)l->cols_r;
+    p.nseg = l->P;
+    p.dtype = l->dtype;
+    set_weights(p, l);
+    p.N = (int)l->out_dims;
+    p.out = y;
+    p.out_dtype = y_dtype;
+    p.out_map = sg::OUT_ROWMAJOR;
+    p.ldo = p.N;
+    p.bias = l->bias;
+    Kind k = choose_row(l, B);
+    if (k != K_GENERIC && (!aligned16(x_partial) || !aligned16(l->w) || (k != K_Q4 && !aligned16(y))))
+        k = K_GENERIC;  // the vector paths need 16-byte aligned rows
+    if (want_split(l, k, B)) {
+        const sg::SplitLayout lay = split_layout(l, k, B);
+        const size_t bytes = sg::split_workspace_bytes(lay);
+        if (!workspace || ws_bytes < bytes)
+            return fail(SG_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws_bytes, bytes);
+        if (!aligned16(workspace)) return fail(SG_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+        p.split = 1;
+        p.counters = (unsigned*)workspace;
+        p.ws = (float*)((char*)workspace + sg::kPartialsOffset);
+    }
+    hipError_t e = run(p, k, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "sharded_to_all launch");
+    return SG_OK;
+}
+
+sg_status sg_summa_matmul(const void* X, const void* A, sg_dtype dtype, int64_t M, int64_t K, int64_t N,
+                          int q, float* Y, int accumulate, int fused, void* stream) {
+    g_err.clear();
+    if (!dtype_ok(dtype)) return fail(SG_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+    if (M < 0 || K < 0 || N < 0 || M > INT32_MAX || K > INT32_MAX || N > INT32_MAX)
+        return fail(SG_ERR_INVALID_ARG, "matrix sizes out of range");
+    if (q < 1) return fail(SG_ERR_NOT_DIVISIBLE, "the processor grid must be q x q with q >= 1 (got q = %d)", q);
+    if (M % q || K % q || N % q)
+        return fail(SG_ERR_NOT_DIVISIBLE, "M, K, N (%lld, %lld, %lld) must be divisible by q = %d",
+                    (long long)M, (long long)K, (long long)N, q);
+    if (accumulate != 0 && accumulate != 1) return fail(SG_ERR_INVALID_ARG, "accumulate must be 0 or 1");
+    if (fused != 0 && fused != 1) return fail(SG_ERR_INVALID_ARG, "fused must be 0 or 1");
+    if (M == 0 || N == 0) return SG_OK;
+    if (!X || !A || !Y) return fail(SG_ERR_INVALID_ARG, "X, A and Y must not be NULL");
+    hipStream_t hs = (hipStream_t)stream;
+    const int64_t bk = K / q;
+    const bool mfma = dtype != SG_F32 && N % 8 == 0 && bk % 8 == 0 && aligned16(X) && aligned16(A) && aligned16(Y);
+    const Kind k = !mfma ? K_GENERIC : (M >= 512 ? K_TILE0 : K_TILE1);
+    const size_t esz = dtype_size(dtype);
+    sg::Problem p{};
+    p.M = (int)M;
+    p.N = (int)N;
+    p.dtype = dtype;
+    p.nn = 1;
+    p.lda = K;
+    p.ldw = N;
+    p.out = Y;
+    p.out_dtype = SG_F32;
+    p.out_map = sg::OUT_ROWMAJOR;
+    p.ldo = N;
+    if (K == 0) {
+        if (!accumulate) HIP_TRY(hipMemsetAsync(Y, 0, (size_t)(M * N) * 4, hs), "clear Y");
+        return SG_OK;
+    }
+    if (fused) {
+        // one launch: the K loop visits step t's panel X_it, A_tj for t = 0 .. q-1
+        p.A = X;
+        p.a_seg = bk;
+        p.W = A;
+        p.w_seg = bk * N;
+        p.Kseg = (int)bk;
+        p.nseg = q;
+        p.accumulate = accumulate;
+        hipError_t e = run(p, k, hs);
+        if (e != hipSuccess) return hip_fail(e, "summa launch");
+        return SG_OK;
+    }
+    for (int t = 0; t < q; ++t) {
+        // step t: every block (i, j) adds X_it A_tj into Y_ij in place
+        p.A = (const char*)X + (size_t)(t * bk) * esz;
+        p.W = (const char*)A + (size_t)(t * bk * N) * esz;
+        p.Kseg = (int)bk;
+        p.nseg = 1;
+        p.accumulate = (t > 0) || accumulate;
+        hipError_t e = run(p, k, hs);
+        if (e != hipSuccess) return hip_fail(e, "summa step launch");
+    }
+    return SG_OK;
+}
+
+sg_status sg_layer_info(const sg_layer* l, int64_t* out_dims, int64_t* in_dims, int* mode, int* segments,
+                        int* P, sg_dtype* dtype, int* quantized) {
+    g_err.clear();
+    if (!l) return fail(SG_ERR_INVALID_ARG, "layer is NULL");
+    if (out_dims) *out_dims = l->out_dims;
+    if (in_dims) *in_dims = l->in_dims;
+    if (mode) *mode = l->mode;
+    if (segments) *segments = l->segments;
+    if (P) *P = l->P;
+    if (dtype) *dtype = l->dtype;
+    if (quantized) *quantized = l->quantized;
+    return SG_OK;
+}
+
+sg_status sg_layer_copy_shard(const sg_layer* l, int r, int what, void* dst, size_t dst_bytes, void* stream) {
+    g_err.clear();
+    if (!l || !dst) return fail(SG_ERR_INVALID_ARG, "layer and dst must not be NULL");
+    if (r < 0 || r >= l->P) return fail(SG_ERR_INVALID_ARG, "rank %d out of range [0, %d)", r, l->P);
+    hipStream_t hs = (hipStream_t)stream;
+    const void* src = nullptr;
+    size_t bytes = 0;
+    const size_t esz = dtype_size(l->dtype);
+    switch (what) {
+    case 0:
+        if (l->quantized) {
+            bytes = (size_t)(l->rows_r * (l->cols_r / 8)) * 4;
+            src = (const char*)l->w + r * bytes;
+        } else {
+            bytes = (size_t)(l->rows_r * l->cols_r) * esz;
+            src = (const char*)l->w + r * bytes;
+        }
+        break;
+    case 1:
+        if (!l->bias) return fail(SG_ERR_INVALID_ARG, "layer has no bias");
+        if (l->mode == SG_ALL_TO_SHARDED) {
+            bytes = (size_t)l->rows_r * esz;
+            src = (const char*)l->bias + r * bytes;
+        } else {
+            bytes = (size_t)l->out_dims * esz;
+            src = l->bias;
+        }
+        break;
+    case 2:
+    case 3:
+        if (!l->quantized) return fail(SG_ERR_INVALID_ARG, "layer is not quantized");
+        bytes = (size_t)(l->rows_r * (l->cols_r / 64)) * 2;
+        src = (const char*)(what == 2 ? l->qs : l->qb) + r * bytes;
+        break;
+    default: return fail(SG_ERR_INVALID_ARG, "unknown tensor selector %d", what);
+    }
+    if (dst_bytes < bytes) return fail(SG_ERR_INVALID_ARG, "dst holds %zu bytes, %zu needed", dst_bytes, bytes);
+    if (what == 0 && l->quantized) {
+        // stored codes are in kernel order: restore the standard order
+        void* tmp = nullptr;
+        HIP_TRY(hipMalloc(&tmp, bytes), "staging allocation");
+        hipError_t e = hipMemcpyAsync(tmp, src, bytes, hipMemcpyDeviceToDevice, hs);
+        if (e == hipSuccess) e = sg::q4_repack((uint32_t*)tmp, (int64_t)(bytes / 4), 0, hs);
+        if (e == hipSuccess) e = hipMemcpyAsync(dst, tmp, bytes, hipMemcpyDefault, hs);
+        if (e == hipSuccess) e = hipStreamSynchronize(hs);
+        (void)hipFree(tmp);
+        if (e != hipSuccess) return hip_fail(e, "shard copy");
+        return SG_OK;
+    }
+    HIP_TRY(hipMemcpyAsync(dst, src, bytes, hipMemcpyDefault, hs), "shard copy");
+    HIP_TRY(hipStreamSynchronize(hs), "shard copy");
+    return SG_OK;
+}
+
+void sg_layer_free(sg_layer* l) { free_layer(l); }
+
+}  // extern "C"

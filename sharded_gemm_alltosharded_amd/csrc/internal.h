@@ -1,0 +1,149 @@
+// Internal declarations shared by the host entry points (api.cpp) and the
+// gfx950 kernels.  Nothing here is part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/shardgemm.h"
+
+namespace sg {
+
+// ---------------------------------------------------------------------------
+// one GEMM-shaped problem:  C[m][n] = sum_s sum_k A_s[m][k] * W_s[n][k]
+//
+//  * A_s: activations of segment s (a rank's input slice), row-major
+//    M x Kseg:  A + s * a_seg + m * lda + k.
+//  * W_s: weights.  NT: row-major N_w x Kseg  (W + s * w_seg + n * ldw + k);
+//    NN: row-major Kseg x N  (W + s * w_seg + k * ldw + n), used by SUMMA.
+//  * segments are the ranks of a sharded-to-all layer (nseg = P); the sum over
+//    s is the all_sum.  nseg = 1 otherwise.
+//  * swiglu: W holds P rank blocks of [gate rows (floc); up rows (floc)];
+//    logical output column j (0 .. N-1, N = P * floc) pairs gate row and up row
+//    of rank j / floc, and the kernel stores silu(g) * u.
+// ---------------------------------------------------------------------------
+enum OutMap { OUT_ROWMAJOR = 0, OUT_SHARDED = 1 };
+
+struct Problem {
+    const void* A;
+    int64_t lda, a_seg;
+    const void* W;
+    int64_t ldw, w_seg;
+    // 4-bit weights (when quantized): packed (rows, ldq u32), scales / biases (rows, ldg)
+    const uint32_t* wq;
+    const uint16_t* qs;
+    const uint16_t* qb;
+    int64_t ldq, ldg, q_seg, g_seg;  // per-segment offsets in u32 / group units
+    int M, N, Kseg, nseg;
+    int dtype;      // sg_dtype of A and W
+    int nn;         // W is K x N (SUMMA)
+    int swiglu;     // fused gate/up pairs
+    int64_t floc;   // rank width of the swiglu output (rows per gate block)
+    // epilogue
+    void* out;
+    int out_dtype;
+    int out_map;    // OutMap
+    int64_t ldo;    // OUT_ROWMAJOR row stride
+    int64_t nloc;   // OUT_SHARDED rank width: column n -> rank n / nloc
+    const void* bias;  // per output column, dtype `dtype`; may be null
+    int accumulate; // fp32 output only: out += result
+    // cross-segment reduction through a workspace (split by segment)
+    int split;
+    float* ws;          // nseg partial slabs
+    unsigned* counters; // one per output tile, zero between calls
+};
+
+// launchers (return hipError_t of the launch)
+hipError_t launch_generic(const Problem& p, hipStream_t s);
+hipError_t launch_tile(const Problem& p, hipStream_t s, int variant);
+hipError_t launch_skinny(const Problem& p, hipStream_t s);
+hipError_t launch_q4(const Problem& p, hipStream_t s);
+
+// Workspace of the split-by-segment reduction: a fixed region of arrival
+// counters (one per output tile or row group) at the start, then `floats`
+// partial values (one slab per segment).  The counters sit at the same place
+// for every call, so the zeros one call leaves behind are the zeros the next
+// call (of any shape) starts from; the partial slabs need no clearing.
+struct SplitLayout {
+    size_t floats;
+    size_t counters;
+};
+constexpr size_t kMaxCounters = 4096;
+constexpr size_t kPartialsOffset = kMaxCounters * sizeof(unsigned);
+SplitLayout tile_split_layout(int M, int N, int nseg, int variant);
+SplitLayout skinny_split_layout(int M, int N, int nseg);
+SplitLayout q4_split_layout(int M, int N, int nseg);
+int tile_count(int M, int N, int variant);
+inline size_t split_workspace_bytes(SplitLayout s) { return kPartialsOffset + s.floats * sizeof(float); }
+
+// ---------------------------------------------------------------------------
+// device helpers
+// ---------------------------------------------------------------------------
+#ifdef __HIPCC__
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(((uint32_t)b) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);  // NaN stays NaN
+    u += 0x7fffu + ((u >> 16) & 1u);  // round to nearest, ties to even
+    return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+    _Float16 v;
+    __builtin_memcpy(&v, &h, 2);
+    return (float)v;
+}
+__device__ __forceinline__ uint16_t f32_to_f16(float f) {
+    _Float16 v = (_Float16)f;  // round to nearest even
+    uint16_t h;
+    __builtin_memcpy(&h, &v, 2);
+    return h;
+}
+__device__ __forceinline__ float load_as_f32(const void* p, int dtype, int64_t i) {
+    if (dtype == SG_F32) return ((const float*)p)[i];
+    uint16_t b = ((const uint16_t*)p)[i];
+    return dtype == SG_BF16 ? bf16_to_f32(b) : f16_to_f32(b);
+}
+__device__ __forceinline__ void store_from_f32(void* p, int dtype, int64_t i, float v) {
+    if (dtype == SG_F32)
+        ((float*)p)[i] = v;
+    else
+        ((uint16_t*)p)[i] = dtype == SG_BF16 ? f32_to_bf16(v) : f32_to_f16(v);
+}
+// A 4-bit layer stores each uint32 with its eight codes reordered so that
+// code k (0..7) of the word sits at nibble q4_nibble_pos(k): nibbles e and
+// e + 4 then hold codes 2e and 2e + 1, and one mask-and-or turns a word into
+// four 16-bit pairs in natural k order (see q4.hip).
+__host__ __device__ __forceinline__ int q4_nibble_pos(int k) { return (k >> 1) | ((k & 1) << 2); }
+
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
+
+// output address of logical element (m, n)
+__device__ __forceinline__ int64_t out_index(const Problem& p, int m, int64_t n) {
+    if (p.out_map == OUT_SHARDED) {
+        int64_t r = n / p.nloc;
+        return (r * p.M + m) * p.nloc + (n - r * p.nloc);
+    }
+    return (int64_t)m * p.ldo + n;
+}
+
+// weight row of logical column n (swiglu: `up` selects the up row of the pair)
+__device__ __forceinline__ int64_t weight_row(const Problem& p, int64_t n, int up) {
+    if (!p.swiglu) return n;
+    int64_t r = n / p.floc;
+    return r * 2 * p.floc + (up ? p.floc : 0) + (n - r * p.floc);
+}
+
+// Map a workgroup id to a tile id so that each of the 8 XCDs (which receive
+// workgroups round-robin) works on one contiguous range of tiles: tiles that
+// share operand panels then share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int wg, int total) {
+    const int nx = 8;
+    int x = wg % nx, slot = wg / nx;
+    int q = total / nx, rem = total % nx;
+    return x < rem ? x * (q + 1) + slot : rem * (q + 1) + (x - rem) * q + slot;
+}
+#endif
+
+}  // namespace sg

@@ -1,0 +1,365 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the
+same seeded inputs.  Shapes are small enough for the oracle but span several
+tiles with ragged tails, and exercise every kernel family (generic, MFMA
+tiles 256/128 with and without the rank split, the streaming kernel, the
+4-bit kernel) and every epilogue (sharded / gathered store, SwiGLU, fused
+rank sum, fp32 accumulate)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sharded_gemm_alltosharded_amd as sg
+import synth
+from gpu_util import assert_close, bits, dev, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _cuda():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+    sg.lib()
+
+
+def _print_case(**kw):
+    print("case:", ", ".join(f"{k}={v}" for k, v in kw.items()), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# slicing: stored shards are the oracle's slices, bit for bit
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("mode,out,inn,S,P", [
+    (0, 24, 16, 1, 2), (0, 48, 8, 3, 4), (0, 12, 5, 2, 3), (1, 6, 32, 1, 4), (1, 5, 24, 3, 2), (1, 4, 16, 2, 2)])
+def test_slicing_bit_exact(dtype, mode, out, inn, S, P):
+    _print_case(dtype=dtype, mode=mode, out=out, inn=inn, S=S, P=P)
+    W = synth.uniform(1, (out, inn), 1.0, dtype)
+    b = synth.uniform(2, (out,), 1.0, dtype)
+    layer = sg.shard_linear(to_dev(W, dtype), mode, segments=S, P=P, bias=to_dev(b, dtype))
+    for r in range(P):
+        np.testing.assert_array_equal(bits(layer.shard(r, 0)), oracle.slice_(W, mode, S, P, r))
+        want_b = oracle.slice_(b, 0, S, P, r) if mode == 0 else b
+        np.testing.assert_array_equal(bits(layer.shard(r, 1)), want_b)
+
+
+@pytest.mark.parametrize("mode,out,inn,S,P", [(0, 64, 256, 1, 4), (0, 96, 128, 3, 2), (1, 32, 512, 1, 4), (1, 16, 512, 2, 2)])
+def test_slicing_q4_bit_exact(mode, out, inn, S, P):
+    _print_case(mode=mode, out=out, inn=inn, S=S, P=P)
+    packed, s, b, _ = synth.quantize_q4(synth.uniform(3, (out, inn), 0.1, "f32"), 64)
+    layer = sg.shard_quantized_linear(torch.from_numpy(packed.view(np.int32)).to(dev()),
+                                      torch.from_numpy(s.view(np.int16)).to(dev()),
+                                      torch.from_numpy(b.view(np.int16)).to(dev()), inn, mode, segments=S, P=P)
+    for r in range(P):
+        np.testing.assert_array_equal(layer.shard(r, 0).cpu().numpy().view(np.uint32), oracle.slice_(packed, mode, S, P, r))
+        np.testing.assert_array_equal(bits(layer.shard(r, 2)), oracle.slice_(s, mode, S, P, r))
+        np.testing.assert_array_equal(bits(layer.shard(r, 3)), oracle.slice_(b, mode, S, P, r))
+
+
+# ---------------------------------------------------------------------------
+# config 1: the worked example and the small fp32 MLP
+# ---------------------------------------------------------------------------
+def test_worked_example_fp32():
+    X, W1, W2 = synth.worked_example(seed=0)
+    l1 = sg.shard_linear(to_dev(W1, "f32"), "all-to-sharded", P=2)
+    l2 = sg.shard_linear(to_dev(W2, "f32"), "sharded-to-all", P=2)
+    y1 = sg.all_to_sharded(l1, to_dev(X, "f32"))
+    assert tuple(y1.shape) == (2, 4, 1)  # each device: (4, 1)
+    y2 = sg.sharded_to_all(l2, y1)  # the sharded output feeds the next layer as is
+    assert tuple(y2.shape) == (4, 2)
+    r1 = oracle.col(X, W1, P=2)
+    assert_close(y1, r1, "f32", "l1")
+    assert_close(y2, oracle.row(r1, W2, P=2), "f32", "l2")
+    # and the chain equals the unsharded model
+    assert_close(y2, X.astype(np.float64) @ W1.T.astype(np.float64) @ W2.T.astype(np.float64), "f32", "unsharded")
+
+
+def test_config1_mlp_fp32():
+    inp = synth.mlp_inputs(8, 64, 256, 2, "f32", seed=0)
+    gu = sg.shard_linear(to_dev(np.concatenate([inp.Wg, inp.Wu]), "f32"), "all-to-sharded", segments=2, P=2)
+    dn = sg.shard_linear(to_dev(inp.Wd, "f32"), "sharded-to-all", P=2)
+    h = sg.all_to_sharded(gu, to_dev(inp.X, "f32"), swiglu=True)
+    y = sg.sharded_to_all(dn, h)
+    ref = oracle.mlp(inp.X, inp.Wg, inp.Wu, inp.Wd, 2, round_dtype="f32")
+    assert_close(y, ref, "f32", "mlp fp32")
+
+
+# ---------------------------------------------------------------------------
+# all-to-sharded
+# ---------------------------------------------------------------------------
+COL_CASES = [
+    # dtype, B, in, out, S, P   (path chosen by B: <=32 streaming, <512 tile 128, else tile 256)
+    ("bf16", 1, 256, 96, 1, 2), ("bf16", 5, 512, 192, 3, 2), ("bf16", 16, 4096, 448, 1, 8), ("bf16", 32, 200, 64, 2, 2),
+    ("f16", 17, 1024, 320, 1, 4), ("bf16", 33, 264, 384, 1, 3), ("bf16", 130, 512, 640, 1, 4),
+    ("f16", 300, 128, 1000, 1, 5), ("bf16", 520, 640, 768, 3, 2), ("bf16", 777, 256, 1100, 1, 2),
+    ("bf16", 12, 24, 40, 1, 2), ("bf16", 3, 10, 4, 1, 2),  # K not a multiple of 8: generic path
+]
+
+
+@pytest.mark.parametrize("gather", [False, True])
+@pytest.mark.parametrize("case", COL_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_all_to_sharded(case, gather):
+    dtype, B, inn, out, S, P = case
+    _print_case(dtype=dtype, B=B, inn=inn, out=out, S=S, P=P, gather=gather)
+    X = synth.normal(5, (B, inn), 1.0, dtype)
+    W = synth.uniform(6, (out, inn), 1 / np.sqrt(inn), dtype)
+    bias = synth.uniform(7, (out,), 0.5, dtype) if B % 2 else None
+    layer = sg.shard_linear(to_dev(W, dtype), "all-to-sharded", segments=S, P=P,
+                            bias=None if bias is None else to_dev(bias, dtype))
+    ref = oracle.col(X, W, P=P, S=S, bias=bias, gather=gather, dtype=dtype)
+    y32 = sg.all_to_sharded(layer, to_dev(X, dtype), gather=gather, out_dtype=torch.float32)
+    assert_close(y32, ref, "f32", "fp32 out")
+    y = sg.all_to_sharded(layer, to_dev(X, dtype), gather=gather)
+    assert_close(y, ref, dtype, "16-bit out")
+
+
+SWIGLU_CASES = [("bf16", 1, 256, 128, 2), ("bf16", 16, 512, 448, 4), ("f16", 31, 256, 96, 3),
+                ("bf16", 40, 256, 512, 2), ("bf16", 600, 384, 640, 4), ("f16", 513, 128, 384, 2)]
+
+
+@pytest.mark.parametrize("gather", [False, True])
+@pytest.mark.parametrize("case", SWIGLU_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_swiglu_epilogue(case, gather):
+    dtype, B, D, F, P = case
+    _print_case(dtype=dtype, B=B, D=D, F=F, P=P, gather=gather)
+    inp = synth.mlp_inputs(B, D, F, P, dtype, seed=8)
+    layer = sg.shard_linear(to_dev(np.concatenate([inp.Wg, inp.Wu]), dtype), "all-to-sharded", segments=2, P=P)
+    x = to_dev(inp.X, dtype)
+    g = oracle.col(inp.X, inp.Wg, P=P, gather=gather, dtype=dtype)
+    u = oracle.col(inp.X, inp.Wu, P=P, gather=gather, dtype=dtype)
+    h32 = sg.all_to_sharded(layer, x, gather=gather, swiglu=True, out_dtype=torch.float32)
+    assert_close(h32, oracle.swiglu(g, u, "f64"), "f32", "fp32 h")
+    h = sg.all_to_sharded(layer, x, gather=gather, swiglu=True)
+    assert_close(h, oracle.swiglu(g, u, dtype), dtype, "16-bit h")
+
+
+# ---------------------------------------------------------------------------
+# sharded-to-all (fused rank sum)
+# ---------------------------------------------------------------------------
+ROW_CASES = [
+    ("bf16", 1, 512, 96, 2), ("bf16", 16, 14336 // 4, 256, 8), ("f16", 29, 768, 200, 3), ("bf16", 8, 256, 64, 1),
+    ("bf16", 100, 512, 256, 4),    # tile 128, rank split (2 tiles)
+    ("bf16", 256, 128, 9216, 2),   # tile 128, no split (144 tiles)
+    ("f16", 600, 256, 512, 4),     # tile 256, rank split
+    ("bf16", 2304, 128, 4096, 2),  # tile 256, no split (144 tiles)
+    ("bf16", 7, 12, 9, 2),         # generic
+]
+
+
+@pytest.mark.parametrize("case", ROW_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_sharded_to_all(case):
+    dtype, B, inn, out, P = case
+    _print_case(dtype=dtype, B=B, inn=inn, out=out, P=P)
+    Xf = synth.normal(9, (B, inn), 1.0, dtype)
+    W = synth.uniform(10, (out, inn), 1 / np.sqrt(inn), dtype)
+    bias = synth.uniform(11, (out,), 0.5, dtype) if B % 2 == 0 else None
+    kl = inn // P
+    Xs = np.ascontiguousarray(np.stack([Xf[:, r * kl:(r + 1) * kl] for r in range(P)]))
+    layer = sg.shard_linear(to_dev(W, dtype), "sharded-to-all", P=P, bias=None if bias is None else to_dev(bias, dtype))
+    ref = oracle.row(Xs, W, P=P, bias=bias, dtype=dtype)
+    xs = to_dev(Xs, dtype)
+    y32 = sg.sharded_to_all(layer, xs, out_dtype=torch.float32)
+    assert_close(y32, ref, "f32", "fp32 out")
+    y = sg.sharded_to_all(layer, xs)
+    assert_close(y, ref, dtype, "16-bit out")
+    # deterministic: the same bits on a second call
+    y2 = sg.sharded_to_all(layer, xs, out_dtype=torch.float32)
+    assert torch.equal(y32, y2)
+
+
+def test_mlp_chain_bf16():
+    """column (gate|up, SwiGLU) -> row (down): one fused reduction for the chain."""
+    B, D, F, P = 16, 512, 1024, 8
+    inp = synth.mlp_inputs(B, D, F, P, "bf16", seed=12)
+    gu = sg.shard_linear(to_dev(np.concatenate([inp.Wg, inp.Wu]), "bf16"), "all-to-sharded", segments=2, P=P)
+    dn = sg.shard_linear(to_dev(inp.Wd, "bf16"), "sharded-to-all", P=P)
+    y = sg.sharded_to_all(dn, sg.all_to_sharded(gu, to_dev(inp.X, "bf16"), swiglu=True))
+    ref = oracle.mlp(inp.X, inp.Wg, inp.Wu, inp.Wd, P, round_dtype="bf16", dtype="bf16")
+    assert_close(y, ref, "bf16", "mlp")
+
+
+def test_qkv_segments():
+    """Fused [Wq; Wk; Wv] with segments = 3: rank r holds [Q_r; K_r; V_r]."""
+    B, D, heads, hd, P = 64, 256, 8, 32, 4
+    W = synth.uniform(13, (3 * heads * hd, D), 1 / 16, "bf16")
+    X = synth.normal(14, (B, D), 1.0, "bf16")
+    layer = sg.shard_linear(to_dev(W, "bf16"), "all-to-sharded", segments=3, P=P)
+    y = sg.all_to_sharded(layer, to_dev(X, "bf16"), out_dtype=torch.float32)
+    assert tuple(y.shape) == (P, B, 3 * heads * hd // P)
+    assert_close(y, oracle.col(X, W, P=P, S=3, dtype="bf16"), "f32", "qkv")
+    # rank r's first heads/P*hd columns are its query heads
+    q_full = oracle.col(X, W[:heads * hd], P=P, dtype="bf16")
+    assert_close(y[:, :, :heads * hd // P], q_full, "f32", "q heads")
+
+
+# ---------------------------------------------------------------------------
+# 4-bit affine
+# ---------------------------------------------------------------------------
+def _q4_layer(w, mode, P, S=1):
+    packed, s, b, _ = synth.quantize_q4(w, 64)
+    layer = sg.shard_quantized_linear(torch.from_numpy(packed.view(np.int32)).to(dev()),
+                                      torch.from_numpy(s.view(np.int16)).to(dev()),
+                                      torch.from_numpy(b.view(np.int16)).to(dev()), w.shape[1], mode,
+                                      segments=S, P=P)
+    return layer, oracle.deq4(packed, s, b, 64)
+
+
+@pytest.mark.parametrize("B", [1, 8, 13, 32, 40])
+def test_q4_all_to_sharded(B):
+    _print_case(B=B)
+    D, out, P = 512, 384, 4
+    layer, Wd = _q4_layer(synth.uniform(15, (out, D), 1 / np.sqrt(D), "f32"), 0, P)
+    X = synth.normal(16, (B, D), 1.0, "bf16")
+    ref = oracle.col(X, Wd, P=P, dtype="bf16")
+    assert_close(sg.all_to_sharded(layer, to_dev(X, "bf16"), out_dtype=torch.float32), ref, "f32", "q4 col")
+
+
+@pytest.mark.parametrize("B", [1, 8, 32])
+def test_q4_swiglu_and_row(B):
+    _print_case(B=B)
+    D, F, P = 512, 1024, 4
+    ws = [synth.uniform(17 + i, shp, 1 / np.sqrt(D), "f32") for i, shp in enumerate([(F, D), (F, D), (D, F)])]
+    gu, Wgu = _q4_layer(np.concatenate([ws[0], ws[1]]), 0, P, S=2)
+    dn, Wdn = _q4_layer(ws[2], 1, P)
+    X = synth.normal(20, (B, D), 1.0, "bf16")
+    h = sg.all_to_sharded(gu, to_dev(X, "bf16"), swiglu=True)
+    g = oracle.col(X, Wgu[:F], P=P, dtype="bf16")
+    u = oracle.col(X, Wgu[F:], P=P, dtype="bf16")
+    h_ref = oracle.swiglu(g, u, "bf16")
+    assert_close(h, h_ref, "bf16", "q4 h")
+    # the chain against the oracle's own chain (h stored in bf16 on both sides)
+    y = sg.sharded_to_all(dn, h)
+    assert_close(y, oracle.row(h_ref, Wdn, P=P), "bf16", "q4 down")
+
+
+# ---------------------------------------------------------------------------
+# SUMMA
+# ---------------------------------------------------------------------------
+SUMMA_CASES = [("bf16", 256, 256, 256, 2), ("bf16", 512, 384, 768, 4), ("f16", 320, 512, 256, 1),
+               ("bf16", 1024, 512, 512, 4), ("bf16", 96, 64, 48, 2), ("bf16", 12, 6, 10, 2)]
+
+
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("case", SUMMA_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_summa(case, fused):
+    dtype, M, K, N, q = case
+    _print_case(dtype=dtype, M=M, K=K, N=N, q=q, fused=fused)
+    X = synth.normal(21, (M, K), K ** -0.25, dtype)
+    A = synth.normal(22, (K, N), K ** -0.25, dtype)
+    ref = oracle.summa(X, A, q, dtype=dtype)
+    y = sg.summa_matmul(to_dev(X, dtype), to_dev(A, dtype), q, fused=fused)
+    assert_close(y, ref, "f32", "summa")
+    C0 = synth.normal(23, (M, N), 1.0, "f32")
+    yc = to_dev(C0, "f32")
+    sg.summa_matmul(to_dev(X, dtype), to_dev(A, dtype), q, out=yc, accumulate=True, fused=fused)
+    assert_close(yc, ref + C0.astype(np.float64), "f32", "summa accumulate")
+
+
+# ---------------------------------------------------------------------------
+# exactness on small integers: every product and partial sum is exact in
+# fp32, so the GPU result must equal the oracle bit for bit
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("B", [4, 32, 96, 640])
+def test_integer_exact_dense(B):
+    _print_case(B=B)
+    inn, out, P = 256, 512, 4
+    X = synth.small_ints(24, (B, inn), -2, 2, "bf16")
+    W = synth.small_ints(25, (out, inn), -2, 2, "bf16")
+    lc = sg.shard_linear(to_dev(W, "bf16"), "all-to-sharded", P=P)
+    y = sg.all_to_sharded(lc, to_dev(X, "bf16"), gather=True, out_dtype=torch.float32)
+    np.testing.assert_array_equal(to_np(y), oracle.col(X, W, P=P, gather=True, dtype="bf16"))
+    lr = sg.shard_linear(to_dev(W, "bf16"), "sharded-to-all", P=P)
+    Xs = np.ascontiguousarray(np.stack([X[:, r * 64:(r + 1) * 64] for r in range(P)]))
+    y = sg.sharded_to_all(lr, to_dev(Xs, "bf16"), out_dtype=torch.float32)
+    np.testing.assert_array_equal(to_np(y), oracle.row(Xs, W, P=P, dtype="bf16"))
+
+
+def test_integer_exact_summa():
+    X = synth.small_ints(26, (512, 512), -2, 2, "bf16")
+    A = synth.small_ints(27, (512, 256), -2, 2, "bf16")
+    for fused in (True, False):
+        y = sg.summa_matmul(to_dev(X, "bf16"), to_dev(A, "bf16"), 4, fused=fused)
+        np.testing.assert_array_equal(to_np(y), oracle.summa(X, A, 4, dtype="bf16"))
+
+
+@pytest.mark.parametrize("B", [1, 8, 32])
+def test_integer_exact_q4(B):
+    """Power-of-two scales, integer biases and integer activations: exact."""
+    out, D, P = 128, 512, 2
+    rng = np.random.default_rng(28)
+    q = rng.integers(0, 16, size=(out, D)).astype(np.uint8)
+    packed = synth.pack_q4(q)
+    s = np.float16(rng.choice([0.5, 1.0, 2.0], size=(out, D // 64))).view(np.uint16)
+    b = np.float16(rng.integers(-8, 8, size=(out, D // 64))).view(np.uint16)
+    X = synth.small_ints(29, (B, D), -2, 2, "bf16")
+    for mode in (0, 1):
+        layer = sg.shard_quantized_linear(torch.from_numpy(packed.view(np.int32)).to(dev()),
+                                          torch.from_numpy(s.view(np.int16)).to(dev()),
+                                          torch.from_numpy(b.view(np.int16)).to(dev()), D, mode, P=P)
+        Wd = oracle.deq4(packed, s, b, 64)
+        if mode == 0:
+            y = sg.all_to_sharded(layer, to_dev(X, "bf16"), gather=True, out_dtype=torch.float32)
+            ref = oracle.col(X, Wd, P=P, gather=True, dtype="bf16")
+        else:
+            Xs = np.ascontiguousarray(np.stack([X[:, r * (D // P):(r + 1) * (D // P)] for r in range(P)]))
+            y = sg.sharded_to_all(layer, to_dev(Xs, "bf16"), out_dtype=torch.float32)
+            ref = oracle.row(Xs, Wd, P=P, dtype="bf16")
+        np.testing.assert_array_equal(to_np(y), ref)
+
+
+def test_fp16_subnormal_weights_not_flushed():
+    """fp16 weights k * 2^-24 (subnormal) times small integers: exact results
+    only if the MFMA keeps subnormal operands."""
+    B, inn, out = 32, 256, 256
+    rng = np.random.default_rng(30)
+    W = (rng.integers(-3, 4, size=(out, inn)).astype(np.float64) * 2.0 ** -24)
+    Wb = W.astype(np.float16).view(np.uint16)
+    X = synth.small_ints(31, (B, inn), -3, 3, "f16")
+    for Bt in (B, 64):
+        Xt = np.ascontiguousarray(np.resize(X, (Bt, inn)))
+        layer = sg.shard_linear(to_dev(Wb, "f16"), "all-to-sharded", P=2)
+        y = sg.all_to_sharded(layer, to_dev(Xt, "f16"), gather=True, out_dtype=torch.float32)
+        np.testing.assert_array_equal(to_np(y), oracle.col(Xt, Wb, P=2, gather=True, dtype="f16"))
+
+
+# ---------------------------------------------------------------------------
+# edge cases
+# ---------------------------------------------------------------------------
+def test_empty_batch_is_noop():
+    W = synth.uniform(32, (64, 64), 0.1, "bf16")
+    layer = sg.shard_linear(to_dev(W, "bf16"), "all-to-sharded", P=2)
+    y = torch.full((2, 0, 32), 7.0, dtype=torch.bfloat16, device=dev())
+    sg.all_to_sharded(layer, torch.empty((0, 64), dtype=torch.bfloat16, device=dev()), out=y)
+    lr = sg.shard_linear(to_dev(W, "bf16"), "sharded-to-all", P=2)
+    y2 = sg.sharded_to_all(lr, torch.empty((2, 0, 32), dtype=torch.bfloat16, device=dev()))
+    assert y2.shape == (0, 64)
+
+
+def test_p1_is_the_plain_linear():
+    X = synth.normal(33, (48, 128), 1.0, "bf16")
+    W = synth.uniform(34, (96, 128), 0.1, "bf16")
+    y = sg.all_to_sharded(sg.shard_linear(to_dev(W, "bf16"), "all-to-sharded", P=1), to_dev(X, "bf16"),
+                          out_dtype=torch.float32)
+    assert_close(y[0], oracle.decode(X, "bf16") @ oracle.decode(W, "bf16").T, "f32", "P=1")
+
+
+def test_workspace_too_small_is_rejected():
+    W = synth.uniform(35, (64, 512), 0.1, "bf16")
+    layer = sg.shard_linear(to_dev(W, "bf16"), "sharded-to-all", P=4)
+    xs = to_dev(synth.normal(36, (4, 8, 128), 1.0, "bf16"), "bf16")
+    ws = torch.zeros(16, dtype=torch.uint8, device=dev())
+    with pytest.raises(sg.ShardGemmError) as e:
+        sg.sharded_to_all(layer, xs, ws=ws)
+    assert e.value.code == sg.ERR_WORKSPACE
+
+
+def test_wrong_layer_mode_is_rejected():
+    W = synth.uniform(37, (64, 64), 0.1, "bf16")
+    layer = sg.shard_linear(to_dev(W, "bf16"), "sharded-to-all", P=2)
+    with pytest.raises(sg.ShardGemmError):
+        sg.all_to_sharded(layer, to_dev(synth.normal(38, (4, 64), 1.0, "bf16"), "bf16"))
+    with pytest.raises(sg.ShardGemmError) as e:
+        sg.shard_linear(to_dev(W, "bf16"), "column", P=2)
+    assert e.value.code == sg.ERR_BAD_MODE
