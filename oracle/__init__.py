@@ -80,6 +80,8 @@ def lib():
             f = getattr(L, name)
             f.argtypes = args
             f.restype = C.c_int
+        L.or_threads.argtypes = []
+        L.or_threads.restype = C.c_int
         L.or_round.argtypes = [C.c_double, C.c_int]
         L.or_round.restype = C.c_double
         _lib = L
@@ -121,6 +123,11 @@ def _f64(a, dtype=None):
     if a.dtype == np.float64:  # already values (e.g. dequantized weights)
         return a
     return decode(a, dtype)
+
+
+def threads() -> int:
+    """Threads the oracle's parallel loops run on."""
+    return lib().or_threads()
 
 
 def round_to(x: float, dtype) -> float:

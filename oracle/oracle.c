@@ -38,6 +38,10 @@
 #include <stdlib.h>
 #include <string.h>
 
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
 #define OR_OK 0
 #define OR_INVALID 1
 #define OR_NOT_DIVISIBLE 3
@@ -312,4 +316,13 @@ int or_mlp(const double* X, int64_t B, int64_t D, int64_t F, const double* Wg,
     free(g);
     free(u);
     return rc;
+}
+
+/* Number of threads the parallel loops use (1 without OpenMP). */
+int or_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
 }

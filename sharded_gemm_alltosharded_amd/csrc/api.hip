@@ -144,11 +144,23 @@ bool mfma_ok(const sg_layer* l, const void* x) {
     return l->dtype != SG_F32 && l->cols_r % 8 == 0 && aligned16(x) && aligned16(l->w);
 }
 
-Kind choose(const sg_layer* l, int64_t B, const void* x) {
+// the streaming kernels keep one LDS slot per (rank, part): bounded ranks only
+bool skinny_fits(const sg_layer* l, int64_t B, int swiglu) {
+    const int n = (int)(swiglu ? l->out_dims / 2 : l->out_dims);
+    const int nseg = l->mode == SG_SHARDED_TO_ALL ? l->P : 1;
+    return sg::skinny_shape((int)B, n, nseg, swiglu).lds <= sg::kMaxStreamLds;
+}
+bool q4_fits(const sg_layer* l, int64_t B, int swiglu) {
+    const int n = (int)(swiglu ? l->out_dims / 2 : l->out_dims);
+    const int nseg = l->mode == SG_SHARDED_TO_ALL ? l->P : 1;
+    return sg::q4_shape((int)B, n, nseg, swiglu).lds <= sg::kMaxStreamLds;
+}
+
+Kind choose(const sg_layer* l, int64_t B, const void* x, int swiglu = 0) {
     if (l->quantized)
-        return (B <= 32 && l->cols_r % 256 == 0 && aligned16(x)) ? K_Q4 : K_GENERIC;
+        return (B <= 32 && l->cols_r % 256 == 0 && aligned16(x) && q4_fits(l, B, swiglu)) ? K_Q4 : K_GENERIC;
     if (!mfma_ok(l, x)) return K_GENERIC;
-    if (B <= 32) return K_SKINNY;
+    if (B <= 32 && skinny_fits(l, B, swiglu)) return K_SKINNY;
     return B >= 512 ? K_TILE0 : K_TILE1;
 }
 
@@ -161,8 +173,6 @@ bool want_split(const sg_layer* l, Kind k, int64_t B) {
     if (split_layout(l, k, B).counters > sg::kMaxCounters) return false;
     const int cus = num_cus();
     switch (k) {
-    case K_SKINNY: return (l->out_dims + 31) / 32 < 4 * cus;
-    case K_Q4: return (l->out_dims + 63) / 64 < 4 * cus;
     case K_TILE0: return sg::tile_count((int)B, (int)l->out_dims, 0) * 2 <= cus;
     case K_TILE1: return sg::tile_count((int)B, (int)l->out_dims, 1) * 2 <= cus;
     default: return false;
@@ -171,8 +181,6 @@ bool want_split(const sg_layer* l, Kind k, int64_t B) {
 
 sg::SplitLayout split_layout(const sg_layer* l, Kind k, int64_t B) {
     switch (k) {
-    case K_SKINNY: return sg::skinny_split_layout((int)B, (int)l->out_dims, l->P);
-    case K_Q4: return sg::q4_split_layout((int)B, (int)l->out_dims, l->P);
     case K_TILE0: return sg::tile_split_layout((int)B, (int)l->out_dims, l->P, 0);
     case K_TILE1: return sg::tile_split_layout((int)B, (int)l->out_dims, l->P, 1);
     default: return {0, 0};
@@ -182,9 +190,10 @@ sg::SplitLayout split_layout(const sg_layer* l, Kind k, int64_t B) {
 // kernel family for a sharded-to-all call (alignment of the caller's pointers
 // is checked separately; misaligned pointers fall back to the generic path)
 Kind choose_row(const sg_layer* l, int64_t B) {
-    if (l->quantized) return B <= 32 && l->cols_r % 256 == 0 ? K_Q4 : K_GENERIC;
+    if (l->quantized) return B <= 32 && l->cols_r % 256 == 0 && q4_fits(l, B, 0) ? K_Q4 : K_GENERIC;
     if (l->dtype == SG_F32 || l->cols_r % 8) return K_GENERIC;
-    return B <= 32 ? K_SKINNY : (B >= 512 ? K_TILE0 : K_TILE1);
+    if (B <= 32 && skinny_fits(l, B, 0)) return K_SKINNY;
+    return B >= 512 ? K_TILE0 : K_TILE1;
 }
 
 hipError_t run(const sg::Problem& p, Kind k, hipStream_t st) {
@@ -364,7 +373,7 @@ sg_status sg_all_to_sharded(const sg_layer* l, const void* x, int64_t B, void* y
     p.ldo = p.N;
     p.nloc = p.N / l->P;
     p.bias = l->bias;
-    Kind k = choose(l, B, x);
+    Kind k = choose(l, B, x, p.swiglu);
     if (k != K_GENERIC && k != K_Q4 && !aligned16(y)) k = K_GENERIC;
     hipError_t e = run(p, k, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "all_to_sharded launch");

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "../../include/shardgemm.h"
 
 namespace sg {
@@ -71,8 +73,19 @@ struct SplitLayout {
 constexpr size_t kMaxCounters = 4096;
 constexpr size_t kPartialsOffset = kMaxCounters * sizeof(unsigned);
 SplitLayout tile_split_layout(int M, int N, int nseg, int variant);
-SplitLayout skinny_split_layout(int M, int N, int nseg);
-SplitLayout q4_split_layout(int M, int N, int nseg);
+
+// launch shapes of the streaming kernels (dynamic LDS bytes included)
+struct SkinnyShape {
+    int MT, RB, NW;
+    size_t lds;
+};
+struct Q4Shape {
+    int TB, RB, NW;
+    size_t lds;
+};
+SkinnyShape skinny_shape(int M, int N, int nseg, int swiglu);
+Q4Shape q4_shape(int M, int N, int nseg, int swiglu);
+constexpr size_t kMaxStreamLds = 64 * 1024;
 int tile_count(int M, int N, int variant);
 inline size_t split_workspace_bytes(SplitLayout s) { return kPartialsOffset + s.floats * sizeof(float); }
 
@@ -118,6 +131,18 @@ __device__ __forceinline__ void store_from_f32(void* p, int dtype, int64_t i, fl
 __host__ __device__ __forceinline__ int q4_nibble_pos(int k) { return (k >> 1) | ((k & 1) << 2); }
 
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I = B .. E-1.  Used
+// where register arrays are indexed, so indices stay static even when a loop
+// body is too large for the unroller (a dynamic index would move the whole
+// array to scratch memory).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
 
 // output address of logical element (m, n)
 __device__ __forceinline__ int64_t out_index(const Problem& p, int m, int64_t n) {

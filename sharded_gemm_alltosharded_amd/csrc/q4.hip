@@ -17,11 +17,12 @@
 // = codes of chunks 4h .. 4h+3 of the group; MFMA step u of the group uses
 // chunk 4h + u, and the token fragment of step u holds the same chunk.
 //
-// Workgroup = 4 waves on RB blocks of 32 rows; each wave takes a contiguous
-// quarter of the groups (in runs of 4, so scales and biases arrive 8 bytes at
-// a time).  Wave partials are summed in LDS in wave order.  Sharded-to-all
-// layers split by rank (grid.y = P) and reduce the rank partials in rank
-// order in the last workgroup to arrive, as in the dense streaming kernel.
+// Workgroup = NW waves on RB blocks of 32 rows (a gate/up pair for SwiGLU)
+// across every rank; a wave takes one (row block, rank, part) unit and walks
+// that rank's groups in runs of 4 (so scales and biases arrive 8 bytes at a
+// time), runs j, j + J, ...  Unit partials land in LDS slots and are summed in
+// part order, then rank order -- the fused all_sum, as in the dense streaming
+// kernel -- with no cross-workgroup traffic.
 #include "internal.h"
 
 namespace sg {
@@ -54,155 +55,105 @@ __device__ __forceinline__ u32x4 unpack8(uint32_t w) {
     return r;
 }
 
-template <int TB, int RB, bool F16, bool SWIGLU, bool SPLIT>
-__global__ __launch_bounds__(256) void q4_kernel(Problem p) {
+template <int TB, int RB, int NW, bool F16, bool SWIGLU>
+__global__ __launch_bounds__(NW * 64) void q4_kernel(Problem p) {
     constexpr int ROWS = SWIGLU ? RB / 2 * 32 : RB * 32;  // logical columns per workgroup
     constexpr int NR = 4 * TB;                            // token registers in use
-    constexpr int NV = RB * TB;                           // values per thread after reduction
+    constexpr int SLOT = NR * 64;                         // floats per unit slot
     constexpr float C = F16 ? 1024.f : 128.f;
     static_assert(!SWIGLU || RB % 2 == 0, "gate/up blocks come in pairs");
-    __shared__ float red[4][RB * NR][64];
+    extern __shared__ float slots[];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int rg = blockIdx.x;
-    const int seg_lo = SPLIT ? blockIdx.y : 0;
-    const int seg_cnt = SPLIT ? 1 : p.nseg;
-    const int64_t base = (int64_t)rg * ROWS;
+    const int64_t base = (int64_t)blockIdx.x * ROWS;
     const int h = lane >> 5;
+    const int per_rb = p.nseg >= NW / RB ? p.nseg : (NW / RB / p.nseg) * p.nseg;
+    const int J = per_rb / p.nseg;  // waves per (row block, rank)
+    const int units = RB * per_rb;
+    const int G = p.Kseg / 64;      // groups per rank (a multiple of 4)
+    const int runs = G / 4;
 
-    int64_t qoff[RB], goff[RB];
-    bool wok[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        int64_t row;
-        if constexpr (SWIGLU) {
-            const int64_t j = base + (rb >> 1) * 32 + (lane & 31);
-            wok[rb] = j < p.N;
-            row = weight_row(p, wok[rb] ? j : 0, rb & 1);
-        } else {
-            const int64_t n = base + rb * 32 + (lane & 31);
-            wok[rb] = n < p.N;
-            row = wok[rb] ? n : 0;
-        }
-        qoff[rb] = row * p.ldq + h * 4;
-        goff[rb] = row * p.ldg;
-    }
     const int t = lane & 31;
     const bool xok = t < p.M;
     const int64_t xoff = (int64_t)(xok ? t : 0) * p.lda + h * 32;
-
     const u32x4 ones = F16 ? u32x4{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u}
                            : u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
     const u32x4 zero = {0u, 0u, 0u, 0u};
 
-    f32x16 y[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) y[rb][r] = 0.f;
+    for (int u = wave; u < units; u += NW) {
+        const int rb = u / per_rb, s = (u % per_rb) / J, j = u % J;
+        int64_t row;
+        bool wok;
+        if constexpr (SWIGLU) {
+            const int64_t jj = base + (rb >> 1) * 32 + (lane & 31);
+            wok = jj < p.N;
+            row = weight_row(p, wok ? jj : 0, rb & 1);
+        } else {
+            const int64_t n = base + rb * 32 + (lane & 31);
+            wok = n < p.N;
+            row = wok ? n : 0;
+        }
+        const uint32_t* Qb = p.wq + s * p.q_seg + row * p.ldq + h * 4;
+        const uint16_t* Sb = p.qs + s * p.g_seg + row * p.ldg;
+        const uint16_t* Bb = p.qb + s * p.g_seg + row * p.ldg;
+        const uint16_t* Ab = (const uint16_t*)p.A + s * p.a_seg + xoff;
 
-    const int G = p.Kseg / 64;  // groups per segment (a multiple of 4)
-    const int runs = G / 4;
-    const int r_lo = wave * runs / 4, r_hi = (wave + 1) * runs / 4;
-    for (int s = seg_lo; s < seg_lo + seg_cnt; ++s) {
-        const uint32_t* Qb = p.wq + s * p.q_seg;
-        const uint16_t* Sb = p.qs + s * p.g_seg;
-        const uint16_t* Bb = p.qb + s * p.g_seg;
-        const uint16_t* Ab = (const uint16_t*)p.A + s * p.a_seg;
-        for (int run = r_lo; run < r_hi; ++run) {
+        f32x16 y;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) y[r] = 0.f;
+        for (int run = j; run < runs; run += J) {
             const int g0 = run * 4;
-            u32x4 wv[4][RB];
-            u32x2 sv[RB], bv[RB];
+            u32x4 wv[4];
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-                for (int gi = 0; gi < 4; ++gi)
-                    wv[gi][rb] = wok[rb] ? *(const u32x4*)(Qb + qoff[rb] + (g0 + gi) * 8) : zero;
-                sv[rb] = *(const u32x2*)(Sb + goff[rb] + g0);
-                bv[rb] = *(const u32x2*)(Bb + goff[rb] + g0);
-            }
+            for (int gi = 0; gi < 4; ++gi) wv[gi] = wok ? *(const u32x4*)(Qb + (g0 + gi) * 8) : zero;
+            const u32x2 sv = *(const u32x2*)(Sb + g0);
+            const u32x2 bv = *(const u32x2*)(Bb + g0);
 #pragma unroll
             for (int gi = 0; gi < 4; ++gi) {
                 u32x4 xf[4];
 #pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    xf[u] = xok ? *(const u32x4*)(Ab + xoff + (g0 + gi) * 64 + u * 8) : zero;
-                f32x16 xs;
+                for (int q = 0; q < 4; ++q) xf[q] = xok ? *(const u32x4*)(Ab + (g0 + gi) * 64 + q * 8) : zero;
+                f32x16 xs, acc;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) xs[r] = 0.f;
+                for (int r = 0; r < 16; ++r) xs[r] = acc[r] = 0.f;
 #pragma unroll
-                for (int u = 0; u < 4; ++u) xs = mfma32<F16>(xf[u], ones, xs);
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb) {
-                    f32x16 acc;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) acc = mfma32<F16>(xf[u], unpack8<F16>(wv[gi][rb][u]), acc);
-                    const uint32_t sw = sv[rb][gi >> 1], bw = bv[rb][gi >> 1];
-                    const float sc = f16_to_f32((uint16_t)((gi & 1) ? (sw >> 16) : (sw & 0xFFFFu)));
-                    const float bi = f16_to_f32((uint16_t)((gi & 1) ? (bw >> 16) : (bw & 0xFFFFu)));
-                    const float bp = fmaf(-C, sc, bi);
-#pragma unroll
-                    for (int r = 0; r < NR; ++r) y[rb][r] = fmaf(sc, acc[r], fmaf(bp, xs[r], y[rb][r]));
+                for (int q = 0; q < 4; ++q) {
+                    xs = mfma32<F16>(xf[q], ones, xs);
+                    acc = mfma32<F16>(xf[q], unpack8<F16>(wv[gi][q]), acc);
                 }
+                const uint32_t sw = sv[gi >> 1], bw = bv[gi >> 1];
+                const float sc = f16_to_f32((uint16_t)((gi & 1) ? (sw >> 16) : (sw & 0xFFFFu)));
+                const float bi = f16_to_f32((uint16_t)((gi & 1) ? (bw >> 16) : (bw & 0xFFFFu)));
+                const float bp = fmaf(-C, sc, bi);
+#pragma unroll
+                for (int r = 0; r < NR; ++r) y[r] = fmaf(sc, acc[r], fmaf(bp, xs[r], y[r]));
             }
         }
+        float* slot = slots + (size_t)u * SLOT;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) slot[r * 64 + lane] = y[r];
     }
-
-    // ---- wave partials -> workgroup result (wave order)
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int r = 0; r < NR; ++r) red[wave][rb * NR + r][lane] = y[rb][r];
     __syncthreads();
-    // thread owns register index R = 4 i + tid / 64 (R = rb * NR + r) at lane tid % 64
-    float v[NV];
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const int R = 4 * i + (tid >> 6), ln = tid & 63;
-        v[i] = ((red[0][R][ln] + red[1][R][ln]) + red[2][R][ln]) + red[3][R][ln];
-    }
 
-    if constexpr (SPLIT) {
-        const int nrg = gridDim.x;
-        const int64_t slab = (int64_t)nrg * NV * 256;
-        float* mine = p.ws + blockIdx.y * slab + (int64_t)rg * NV * 256;
-#pragma unroll
-        for (int i = 0; i < NV; ++i) mine[i * 256 + tid] = v[i];
-        __threadfence();
-        __syncthreads();
-        __shared__ int last;
-        if (tid == 0) {
-            const unsigned prev = atomicAdd(&p.counters[rg], 1u);
-            last = prev == (unsigned)p.nseg - 1;
-            if (last) p.counters[rg] = 0u;
-        }
-        __syncthreads();
-        if (!last) return;
-        __threadfence();
-#pragma unroll
-        for (int i = 0; i < NV; ++i) v[i] = 0.f;
-        for (int s = 0; s < p.nseg; ++s) {  // rank order
-            const float* src = p.ws + s * slab + (int64_t)rg * NV * 256;
-#pragma unroll
-            for (int i = 0; i < NV; ++i) v[i] += src[i * 256 + tid];
-        }
-    }
-
-    // ---- epilogue
-    const int ln = tid & 63;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const int R = 4 * i + (tid >> 6);
-        const int rb = R / NR, r = R % NR;
-        if constexpr (SWIGLU) {
-            if (rb & 1) continue;
+    // ---- reduction (parts of a rank in order, then ranks in order) + epilogue
+    constexpr int NE = (SWIGLU ? RB / 2 : RB) * SLOT;
+    for (int idx = tid; idx < NE; idx += NW * 64) {
+        const int ln = idx & 63, r = (idx >> 6) % NR, rbo = (idx >> 6) / NR;
+        const int rb = SWIGLU ? 2 * rbo : rbo;
+        float v = 0.f, vu = 0.f;
+        for (int s = 0; s < p.nseg; ++s) {
+            float zs = 0.f, zu = 0.f;
+            for (int jj = 0; jj < J; ++jj) {
+                zs += slots[(size_t)(rb * per_rb + s * J + jj) * SLOT + r * 64 + ln];
+                if constexpr (SWIGLU) zu += slots[(size_t)((rb + 1) * per_rb + s * J + jj) * SLOT + r * 64 + ln];
+            }
+            v += zs;
+            vu += zu;
         }
         const int m = 8 * (r >> 2) + 4 * (ln >> 5) + (r & 3);
-        const int64_t n = SWIGLU ? base + (rb >> 1) * 32 + (ln & 31) : base + rb * 32 + (ln & 31);
+        const int64_t n = base + rbo * 32 + (ln & 31);
         if (m >= p.M || n >= p.N) continue;
-        float x = SWIGLU ? silu_f32(v[i]) * v[i + TB] : v[i];
+        float x = SWIGLU ? silu_f32(v) * vu : v;
         if (p.bias) x += load_as_f32(p.bias, p.dtype, n);
         const int64_t o = out_index(p, m, n);
         if (p.accumulate && p.out_dtype == SG_F32) x += ((const float*)p.out)[o];
@@ -210,41 +161,56 @@ __global__ __launch_bounds__(256) void q4_kernel(Problem p) {
     }
 }
 
-SplitLayout q4_split_layout(int M, int N, int nseg) {
-    const size_t TB = (M + 7) / 8, RB = 2;
-    const size_t nrg = (N + RB * 32 - 1) / (RB * 32);
-    return {nseg * nrg * RB * TB * 256, nrg};
+// Shape choice: RB row blocks of 32 per workgroup (a gate/up pair for
+// SwiGLU), NW waves, several thousand waves on the chip.
+Q4Shape q4_shape(int M, int N, int nseg, int swiglu) {
+    Q4Shape sh;
+    sh.TB = (M + 7) / 8;
+    sh.RB = swiglu ? 2 : 1;
+    const int rows = swiglu ? N * 2 : N;
+    const int64_t wgs = ((int64_t)rows + sh.RB * 32 - 1) / (sh.RB * 32);
+    int nw = 4;
+    while (nw < 8 && (wgs * nw < 4096 || nw < sh.RB * nseg)) nw *= 2;
+    sh.NW = nw;
+    const int per_rb = nseg >= nw / sh.RB ? nseg : (nw / sh.RB / nseg) * nseg;
+    sh.lds = (size_t)sh.RB * per_rb * 4 * sh.TB * 64 * sizeof(float);
+    return sh;
 }
 
-template <int TB, bool F16>
-static hipError_t launch_tb(const Problem& p, hipStream_t s) {
-    constexpr int RB = 2;
+template <int TB, int NW, bool F16>
+static hipError_t launch_nw(const Problem& p, hipStream_t s, size_t lds) {
     if (p.swiglu) {
-        const int nrg = (p.N + RB / 2 * 32 - 1) / (RB / 2 * 32);
-        hipLaunchKernelGGL((q4_kernel<TB, RB, F16, true, false>), dim3(nrg), dim3(256), 0, s, p);
+        const int nwg = (p.N + 31) / 32;
+        hipLaunchKernelGGL((q4_kernel<TB, 2, NW, F16, true>), dim3(nwg), dim3(NW * 64), lds, s, p);
     } else {
-        const int nrg = (p.N + RB * 32 - 1) / (RB * 32);
-        if (p.split)
-            hipLaunchKernelGGL((q4_kernel<TB, RB, F16, false, true>), dim3(nrg, p.nseg), dim3(256), 0, s, p);
-        else
-            hipLaunchKernelGGL((q4_kernel<TB, RB, F16, false, false>), dim3(nrg), dim3(256), 0, s, p);
+        const int nwg = (p.N + 31) / 32;
+        hipLaunchKernelGGL((q4_kernel<TB, 1, NW, F16, false>), dim3(nwg), dim3(NW * 64), lds, s, p);
     }
     return hipGetLastError();
 }
 
+template <int TB, bool F16>
+static hipError_t launch_tb(const Problem& p, hipStream_t s, const Q4Shape& sh) {
+    switch (sh.NW) {
+    case 4: return launch_nw<TB, 4, F16>(p, s, sh.lds);
+    default: return launch_nw<TB, 8, F16>(p, s, sh.lds);
+    }
+}
+
 template <bool F16>
-static hipError_t launch_f(const Problem& p, hipStream_t s) {
-    switch ((p.M + 7) / 8) {
-    case 1: return launch_tb<1, F16>(p, s);
-    case 2: return launch_tb<2, F16>(p, s);
-    case 3: return launch_tb<3, F16>(p, s);
-    default: return launch_tb<4, F16>(p, s);
+static hipError_t launch_f(const Problem& p, hipStream_t s, const Q4Shape& sh) {
+    switch (sh.TB) {
+    case 1: return launch_tb<1, F16>(p, s, sh);
+    case 2: return launch_tb<2, F16>(p, s, sh);
+    case 3: return launch_tb<3, F16>(p, s, sh);
+    default: return launch_tb<4, F16>(p, s, sh);
     }
 }
 
 hipError_t launch_q4(const Problem& p, hipStream_t s) {
     if (p.M == 0 || p.N == 0) return hipSuccess;
-    return p.dtype == SG_F16 ? launch_f<true>(p, s) : launch_f<false>(p, s);
+    const Q4Shape sh = q4_shape(p.M, p.N, p.nseg, p.swiglu);
+    return p.dtype == SG_F16 ? launch_f<true>(p, s, sh) : launch_f<false>(p, s, sh);
 }
 
 // Reorder the eight codes of every word: forward (standard -> kernel order,

@@ -3,21 +3,22 @@
 // read once, so the kernel is organised around keeping enough 16-byte loads
 // in flight, not around reuse.
 //
-// Workgroup = 4 waves on one group of weight rows (RB blocks of 16 rows);
-// the waves interleave over 32-wide k steps (wave w takes steps w, w+4, ...)
-// so that at any moment the four waves read adjacent 64-byte pieces of the
-// same rows.  Each step is one v_mfma_f32_16x16x32 per (row block, token
-// block): the weight block is the MFMA's row operand (16 rows x 32 k, 16
-// bytes per lane straight from HBM) and the tokens are its column operand.
-// The four wave partials are added in LDS in wave order.
+// One workgroup (NW waves) owns a group of RB x 16 weight rows across every
+// rank of the layer.  The work of that row group is cut into units (rank s,
+// part j): J = max(1, NW / nseg) waves share one rank's k range, taking its
+// 32-wide k steps round robin (step j, j + J, ...), so the waves of one rank
+// read adjacent 64-byte pieces of the same rows at the same time.  Each step
+// is one v_mfma_f32_16x16x32 per (row block, token block): 16 weight rows x
+// 32 k (16 bytes per lane straight from HBM) as the row operand, the tokens
+// as the column operand.  Loads of step t+1 are issued before the MFMAs of
+// step t (register double buffering).
 //
-// Sharded-to-all layers: the workgroups of one row group split by rank
-// (grid.y = P); each forms its rank's partial, writes it to the workspace,
-// and the last workgroup to arrive adds the P partials in rank order, then
-// the bias once -- the all_sum of "MLX 张量并行实战指南" section 2.2 as a
-// fused, deterministic epilogue.  All-to-sharded layers need no reduction;
-// the SwiGLU variant pairs a 16-row gate block with the matching up block so
-// the epilogue can store silu(g) * u directly (sections 5.2-5.3).
+// Every unit's partial goes to its own LDS slot; the epilogue adds the parts
+// of a rank in part order and the ranks in rank order, then the bias once --
+// the all_sum of "MLX 张量并行实战指南" section 2.2, fused into the kernel,
+// deterministic, with no cross-workgroup traffic.  All-to-sharded layers are
+// the one-rank case; the SwiGLU variant pairs a 16-row gate block with the
+// matching up block and stores silu(g) * u (sections 5.2-5.3).
 #include "internal.h"
 
 namespace sg {
@@ -37,19 +38,18 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-template <int MT, int RB, bool F16, bool SWIGLU, bool SPLIT, int U>
-__global__ __launch_bounds__(256) void skinny_kernel(Problem p) {
+template <int MT, int RB, int NW, bool F16, bool SWIGLU, int U>
+__global__ __launch_bounds__(NW * 64) void skinny_kernel(Problem p) {
     constexpr int ROWS = SWIGLU ? RB / 2 * 16 : RB * 16;  // logical columns per workgroup
-    constexpr int NV = RB * MT;                            // values per thread after reduction
+    constexpr int SLOT = RB * MT * 4 * 64;                 // floats per unit slot
     static_assert(!SWIGLU || RB % 2 == 0, "gate/up blocks come in pairs");
-    __shared__ float red[4][NV * 4][64];
+    extern __shared__ float slots[];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int rg = blockIdx.x;
-    const int seg_lo = SPLIT ? blockIdx.y : 0;
-    const int seg_cnt = SPLIT ? 1 : p.nseg;
-    const int64_t base = (int64_t)rg * ROWS;
+    const int64_t base = (int64_t)blockIdx.x * ROWS;
     const int kq = (lane >> 4) * 8;
+    const int J = p.nseg >= NW ? 1 : NW / p.nseg;  // waves per rank
+    const int units = p.nseg * J;
 
     int64_t woff[RB];
     bool wok[RB];
@@ -76,95 +76,90 @@ __global__ __launch_bounds__(256) void skinny_kernel(Problem p) {
         xoff[mt] = (int64_t)(xok[mt] ? m : 0) * p.lda + kq;
     }
 
-    f32x4 acc[RB][MT];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[rb][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
     const u32x4 zero = {0u, 0u, 0u, 0u};
     const int nsteps = (p.Kseg + 31) / 32;
-    for (int s = seg_lo; s < seg_lo + seg_cnt; ++s) {
+
+    for (int u = wave; u < units; u += NW) {
+        const int s = u / J, j = u - s * J;
         const uint16_t* Wb = (const uint16_t*)p.W + s * p.w_seg;
         const uint16_t* Ab = (const uint16_t*)p.A + s * p.a_seg;
-        for (int st = wave; st < nsteps; st += 4 * U) {
-            u32x4 wv[U][RB], xv[U][MT];
+        f32x4 acc[RB][MT];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int k0 = (st + 4 * u) * 32;
-                const bool ok = (st + 4 * u < nsteps) && (k0 + kq < p.Kseg);
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[rb][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        // this unit's steps: j, j + J, ...; U of them per batch, next batch prefetched
+        const int my_steps = nsteps > j ? (nsteps - j + J - 1) / J : 0;
+        const int batches = (my_steps + U - 1) / U;
+        u32x4 wv[2][U][RB], xv[2][U][MT];
+        auto load = [&](int buf, int b) {
+#pragma unroll
+            for (int q = 0; q < U; ++q) {
+                const int idx = b * U + q;
+                const int k0 = (j + idx * J) * 32;
+                const bool ok = idx < my_steps && k0 + kq < p.Kseg;
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
-                    wv[u][rb] = (ok && wok[rb]) ? *(const u32x4*)(Wb + woff[rb] + k0) : zero;
+                    wv[buf][q][rb] = (ok && wok[rb]) ? *(const u32x4*)(Wb + woff[rb] + k0) : zero;
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
-                    xv[u][mt] = (ok && xok[mt]) ? *(const u32x4*)(Ab + xoff[mt] + k0) : zero;
+                    xv[buf][q][mt] = (ok && xok[mt]) ? *(const u32x4*)(Ab + xoff[mt] + k0) : zero;
             }
+        };
+        auto compute = [&](int buf) {
 #pragma unroll
-            for (int u = 0; u < U; ++u)
+            for (int q = 0; q < U; ++q)
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt)
-                        acc[rb][mt] = mfma16<F16>(wv[u][rb], xv[u][mt], acc[rb][mt]);
+                        acc[rb][mt] = mfma16<F16>(wv[buf][q][rb], xv[buf][q][mt], acc[rb][mt]);
+        };
+        if (batches > 0) load(0, 0);
+        int b = 0;
+        for (; b + 1 < batches; b += 2) {
+            load(1, b + 1);
+            compute(0);
+            if (b + 2 < batches) load(0, b + 2);
+            compute(1);
         }
-    }
+        if (b < batches) compute(0);
 
-    // ---- wave partials -> workgroup result (wave order)
+        float* slot = slots + (size_t)u * SLOT;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
+        for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+            for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) red[wave][(rb * MT + mt) * 4 + e][lane] = acc[rb][mt][e];
+                for (int e = 0; e < 4; ++e) slot[((rb * MT + mt) * 4 + e) * 64 + lane] = acc[rb][mt][e];
+    }
     __syncthreads();
-    // thread tid now owns value i = rb * MT + mt of MFMA register e = tid / 64 at lane tid % 64
-    float v[NV];
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const int reg = 4 * i + (tid >> 6), ln = tid & 63;
-        v[i] = ((red[0][reg][ln] + red[1][reg][ln]) + red[2][reg][ln]) + red[3][reg][ln];
-    }
 
-    if constexpr (SPLIT) {
-        const int nrg = gridDim.x;
-        const int64_t slab = (int64_t)nrg * NV * 256;
-        float* mine = p.ws + blockIdx.y * slab + (int64_t)rg * NV * 256;
-#pragma unroll
-        for (int i = 0; i < NV; ++i) mine[i * 256 + tid] = v[i];
-        __threadfence();
-        __syncthreads();
-        __shared__ int last;
-        if (tid == 0) {
-            const unsigned prev = atomicAdd(&p.counters[rg], 1u);
-            last = prev == (unsigned)p.nseg - 1;
-            if (last) p.counters[rg] = 0u;
-        }
-        __syncthreads();
-        if (!last) return;
-        __threadfence();
-#pragma unroll
-        for (int i = 0; i < NV; ++i) v[i] = 0.f;
-        for (int s = 0; s < p.nseg; ++s) {  // rank order
-            const float* src = p.ws + s * slab + (int64_t)rg * NV * 256;
-#pragma unroll
-            for (int i = 0; i < NV; ++i) v[i] += src[i * 256 + tid];
-        }
-    }
-
-    // ---- epilogue
-    const int ln = tid & 63, e = tid >> 6;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const int rb = i / MT, mt = i % MT;
-        if constexpr (SWIGLU) {
-            if (rb & 1) continue;
+    // ---- reduction (parts of a rank in order, then ranks in order) + epilogue
+    // element index: ((rb * MT + mt) * 4 + e) * 64 + ln
+    constexpr int NE = SWIGLU ? SLOT / 2 : SLOT;  // outputs of this workgroup
+    for (int idx = tid; idx < NE; idx += NW * 64) {
+        const int ln = idx & 63, e = (idx >> 6) & 3, bm = idx >> 8;  // bm = rb * MT + mt (gate half for SwiGLU)
+        const int mt = bm % MT;
+        const int rbo = bm / MT;  // row block (SwiGLU: pair index)
+        const int eg = SWIGLU ? (((2 * rbo) * MT + mt) * 4 + e) * 64 + ln : idx;
+        float v = 0.f, vu = 0.f;
+        for (int s = 0; s < p.nseg; ++s) {
+            float zs = 0.f, zu = 0.f;
+            for (int jj = 0; jj < J; ++jj) {
+                const float* sl = slots + (size_t)(s * J + jj) * SLOT;
+                zs += sl[eg];
+                if constexpr (SWIGLU) zu += sl[eg + MT * 256];
+            }
+            v += zs;
+            vu += zu;
         }
         const int m = mt * 16 + (ln & 15);
         const int rowin = 4 * (ln >> 4) + e;
-        const int64_t n = SWIGLU ? base + (rb >> 1) * 16 + rowin : base + rb * 16 + rowin;
+        const int64_t n = base + rbo * 16 + rowin;
         if (m >= p.M || n >= p.N) continue;
-        float x = SWIGLU ? silu_f32(v[i]) * v[i + MT] : v[i];
+        float x = SWIGLU ? silu_f32(v) * vu : v;
         if (p.bias) x += load_as_f32(p.bias, p.dtype, n);
         const int64_t o = out_index(p, m, n);
         if (p.accumulate && p.out_dtype == SG_F32) x += ((const float*)p.out)[o];
@@ -172,33 +167,57 @@ __global__ __launch_bounds__(256) void skinny_kernel(Problem p) {
     }
 }
 
-SplitLayout skinny_split_layout(int M, int N, int nseg) {
-    const size_t MT = M <= 16 ? 1 : 2, RB = 2;
-    const size_t nrg = (N + RB * 16 - 1) / (RB * 16);
-    return {nseg * nrg * RB * MT * 256, nrg};
+// Shape choice: RB row blocks per workgroup, NW waves.  Aim for several
+// thousand waves on the chip, at least one wave per rank.
+SkinnyShape skinny_shape(int M, int N, int nseg, int swiglu) {
+    SkinnyShape sh;
+    sh.MT = M <= 16 ? 1 : 2;
+    const int rows = swiglu ? N * 2 : N;
+    sh.RB = (swiglu || rows / 32 >= 1024) ? 2 : 1;
+    const int64_t wgs = ((int64_t)rows + sh.RB * 16 - 1) / (sh.RB * 16);
+    int nw = 4;
+    while (nw < 8 && (wgs * nw < 4096 || nw < nseg)) nw *= 2;
+    sh.NW = nw;
+    const int J = nseg >= nw ? 1 : nw / nseg;
+    sh.lds = (size_t)nseg * J * sh.RB * sh.MT * 4 * 64 * sizeof(float);
+    return sh;
 }
 
-template <int MT, int RB, bool F16>
-static hipError_t launch_mt(const Problem& p, hipStream_t s) {
-    constexpr int U = 4;
+template <int MT, int RB, int NW, bool F16>
+static hipError_t launch_nw(const Problem& p, hipStream_t s, size_t lds) {
+    constexpr int U = (RB * MT >= 4) ? 2 : 4;
     if (p.swiglu) {
-        const int nrg = (p.N + RB / 2 * 16 - 1) / (RB / 2 * 16);
-        hipLaunchKernelGGL((skinny_kernel<MT, RB, F16, true, false, U>), dim3(nrg), dim3(256), 0, s, p);
+        if constexpr (RB % 2 == 0) {
+            const int nwg = (p.N + RB / 2 * 16 - 1) / (RB / 2 * 16);
+            hipLaunchKernelGGL((skinny_kernel<MT, RB, NW, F16, true, U>), dim3(nwg), dim3(NW * 64), lds, s, p);
+        } else {
+            return hipErrorInvalidValue;
+        }
     } else {
-        const int nrg = (p.N + RB * 16 - 1) / (RB * 16);
-        if (p.split)
-            hipLaunchKernelGGL((skinny_kernel<MT, RB, F16, false, true, U>), dim3(nrg, p.nseg), dim3(256), 0, s, p);
-        else
-            hipLaunchKernelGGL((skinny_kernel<MT, RB, F16, false, false, U>), dim3(nrg), dim3(256), 0, s, p);
+        const int nwg = (p.N + RB * 16 - 1) / (RB * 16);
+        hipLaunchKernelGGL((skinny_kernel<MT, RB, NW, F16, false, U>), dim3(nwg), dim3(NW * 64), lds, s, p);
     }
     return hipGetLastError();
 }
 
+template <int MT, int RB, bool F16>
+static hipError_t launch_rb(const Problem& p, hipStream_t s, const SkinnyShape& sh) {
+    switch (sh.NW) {
+    case 4: return launch_nw<MT, RB, 4, F16>(p, s, sh.lds);
+    default: return launch_nw<MT, RB, 8, F16>(p, s, sh.lds);
+    }
+}
+
+template <bool F16>
+static hipError_t launch_f(const Problem& p, hipStream_t s, const SkinnyShape& sh) {
+    if (sh.MT == 1) return sh.RB == 1 ? launch_rb<1, 1, F16>(p, s, sh) : launch_rb<1, 2, F16>(p, s, sh);
+    return sh.RB == 1 ? launch_rb<2, 1, F16>(p, s, sh) : launch_rb<2, 2, F16>(p, s, sh);
+}
+
 hipError_t launch_skinny(const Problem& p, hipStream_t s) {
     if (p.M == 0 || p.N == 0) return hipSuccess;
-    const bool f16 = p.dtype == SG_F16;
-    if (p.M <= 16) return f16 ? launch_mt<1, 2, true>(p, s) : launch_mt<1, 2, false>(p, s);
-    return f16 ? launch_mt<2, 2, true>(p, s) : launch_mt<2, 2, false>(p, s);
+    const SkinnyShape sh = skinny_shape(p.M, p.N, p.nseg, p.swiglu);
+    return p.dtype == SG_F16 ? launch_f<true>(p, s, sh) : launch_f<false>(p, s, sh);
 }
 
 }  // namespace sg

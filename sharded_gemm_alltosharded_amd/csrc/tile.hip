@@ -68,6 +68,43 @@ __device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[
     }
 }
 
+// Store four consecutive logical columns n .. n+3 of row m (bias, output
+// map, dtype conversion, fp32 accumulate); vector store when they are
+// contiguous and aligned.
+__device__ __forceinline__ void store4(const Problem& p, int m, int64_t n, float (&v)[4]) {
+    if (n >= p.N) return;
+    if (p.bias) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (n + e < p.N) v[e] += load_as_f32(p.bias, p.dtype, n + e);
+    }
+    const bool full = n + 3 < p.N && (p.out_map == OUT_ROWMAJOR ? (p.ldo % 4 == 0) : (p.nloc % 4 == 0));
+    const int64_t o = out_index(p, m, n);
+    if (full && !p.accumulate && p.out_dtype != SG_F32) {
+        u32x2 w;
+        if (p.out_dtype == SG_BF16) {
+            w[0] = f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+            w[1] = f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+        } else {
+            w[0] = f32_to_f16(v[0]) | ((uint32_t)f32_to_f16(v[1]) << 16);
+            w[1] = f32_to_f16(v[2]) | ((uint32_t)f32_to_f16(v[3]) << 16);
+        }
+        *(u32x2*)((uint16_t*)p.out + o) = w;
+    } else if (full && p.out_dtype == SG_F32) {
+        f32x4* dst = (f32x4*)((float*)p.out + o);
+        f32x4 r = {v[0], v[1], v[2], v[3]};
+        if (p.accumulate) r += *dst;
+        *dst = r;
+    } else {
+        for (int e = 0; e < 4 && n + e < p.N; ++e) {
+            const int64_t oe = out_index(p, m, n + e);
+            float x = v[e];
+            if (p.accumulate && p.out_dtype == SG_F32) x += ((const float*)p.out)[oe];
+            store_from_f32(p.out, p.out_dtype, oe, x);
+        }
+    }
+}
+
 template <int BM, int BN, bool F16, int WMODE, bool SPLIT>
 __global__ __launch_bounds__(256) void tile_kernel(Problem p, int tiles_m, int tiles_n) {
     constexpr int WTM = BM / 2, WTN = BN / 2;  // per-wave outputs
@@ -280,17 +317,15 @@ __global__ __launch_bounds__(256) void tile_kernel(Problem p, int tiles_m, int t
 
     // ---- epilogue
     const int hi = lane >> 5;
-#pragma unroll
-    for (int i = 0; i < NBN; ++i) {
-        if constexpr (WMODE == WM_SWIGLU) {
-            if (i & 1) continue;
-        }
-#pragma unroll
-        for (int j = 0; j < NBM; ++j) {
+    static_for<0, NBN>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (WMODE == WM_SWIGLU && (i & 1)) return;
+        static_for<0, NBM>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
             const int m = m0 + wave_m * WTM + j * 32 + (lane & 31);
-            if (m >= p.M) continue;
-#pragma unroll
-            for (int blk = 0; blk < 4; ++blk) {
+            if (m >= p.M) return;
+            static_for<0, 4>([&](auto bc) {
+                constexpr int blk = decltype(bc)::value;
                 int64_t n;
                 float v[4];
                 if constexpr (WMODE == WM_SWIGLU) {
@@ -304,44 +339,10 @@ __global__ __launch_bounds__(256) void tile_kernel(Problem p, int tiles_m, int t
 #pragma unroll
                     for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * blk + e];
                 }
-                if (n >= p.N) continue;
-                if (p.bias) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (n + e < p.N) v[e] += load_as_f32(p.bias, p.dtype, n + e);
-                }
-                const bool full = n + 3 < p.N &&
-                                  (p.out_map == OUT_ROWMAJOR ? (p.ldo % 4 == 0)
-                                                             : (p.nloc % 4 == 0));
-                const int64_t o = out_index(p, m, n);
-                if (full && !p.accumulate && p.out_dtype != SG_F32) {
-                    u32x2 w;
-                    if (p.out_dtype == SG_BF16) {
-                        w[0] = f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-                        w[1] = f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-                    } else {
-                        w[0] = f32_to_f16(v[0]) | ((uint32_t)f32_to_f16(v[1]) << 16);
-                        w[1] = f32_to_f16(v[2]) | ((uint32_t)f32_to_f16(v[3]) << 16);
-                    }
-                    *(u32x2*)((uint16_t*)p.out + o) = w;
-                } else if (full && p.out_dtype == SG_F32) {
-                    f32x4* dst = (f32x4*)((float*)p.out + o);
-                    f32x4 r = {v[0], v[1], v[2], v[3]};
-                    if (p.accumulate) r += *dst;
-                    *dst = r;
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        if (n + e >= p.N) break;
-                        const int64_t oe = out_index(p, m, n + e);
-                        float x = v[e];
-                        if (p.accumulate && p.out_dtype == SG_F32) x += ((const float*)p.out)[oe];
-                        store_from_f32(p.out, p.out_dtype, oe, x);
-                    }
-                }
-            }
-        }
-    }
+                store4(p, m, n, v);
+            });
+        });
+    });
 }
 
 // variant 0: 256 x 256 tiles; variant 1: 128 x 128 tiles

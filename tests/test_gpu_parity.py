@@ -346,9 +346,12 @@ def test_p1_is_the_plain_linear():
 
 
 def test_workspace_too_small_is_rejected():
-    W = synth.uniform(35, (64, 512), 0.1, "bf16")
+    # 100 tokens x 256 outputs: two 128 x 128 tiles, so the ranks are split
+    # over workgroups and reduced through the workspace
+    W = synth.uniform(35, (256, 512), 0.1, "bf16")
     layer = sg.shard_linear(to_dev(W, "bf16"), "sharded-to-all", P=4)
-    xs = to_dev(synth.normal(36, (4, 8, 128), 1.0, "bf16"), "bf16")
+    xs = to_dev(synth.normal(36, (4, 100, 128), 1.0, "bf16"), "bf16")
+    assert sg.lib().sg_sharded_to_all_workspace(layer.handle, 100) > 16
     ws = torch.zeros(16, dtype=torch.uint8, device=dev())
     with pytest.raises(sg.ShardGemmError) as e:
         sg.sharded_to_all(layer, xs, ws=ws)
