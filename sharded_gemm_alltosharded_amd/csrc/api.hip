@@ -8,10 +8,6 @@
 
 #include "internal.h"
 
-namespace sg {
-hipError_t q4_repack(uint32_t* w, int64_t n, int forward, hipStream_t s);
-}
-
 struct sg_layer {
     int mode, segments, P, quantized;
     sg_dtype dtype;  // weight dtype (dense) or activation dtype (4-bit)
@@ -21,6 +17,7 @@ struct sg_layer {
     uint16_t* qs;            // 4-bit scales: P x rows_r x cols_r/64
     uint16_t* qb;            // 4-bit biases
     void* bias;              // all-to-sharded: P x rows_r (rank order); sharded-to-all: out_dims
+    int wfrag;               // dense weights stored fragment-major (sg::frag_offset)
     int device;
 };
 
@@ -219,6 +216,7 @@ void set_weights(sg::Problem& p, const sg_layer* l) {
         p.W = l->w;
         p.ldw = l->cols_r;
         p.w_seg = l->rows_r * l->cols_r;
+        p.wfrag = l->wfrag;
     }
 }
 
@@ -248,12 +246,30 @@ sg_status sg_shard_linear(const void* weight, sg_dtype dtype, int64_t out_dims, 
     l->cols_r = mode == SG_ALL_TO_SHARDED ? in_dims : in_dims / P;
     (void)hipGetDevice(&l->device);
     const size_t esz = dtype_size(dtype);
-    hipError_t e = hipMalloc(&l->w, (size_t)(out_dims * in_dims) * esz);
+    const size_t wbytes = (size_t)(out_dims * in_dims) * esz;
+    // 16-bit weights that tile into 16 x 32 MFMA fragments are stored
+    // fragment-major (one coalesced 1 KB read per fragment).  All-to-sharded
+    // ranks are stacked rows of one (out, in) matrix, so the layout covers the
+    // whole stack; sharded-to-all ranks are separate (out, in/P) matrices.
+    l->wfrag = dtype != SG_F32 && out_dims % 16 == 0 && l->cols_r % 32 == 0;
+    const int frag_mats = mode == SG_ALL_TO_SHARDED ? 1 : P;
+    const int64_t frag_rows = mode == SG_ALL_TO_SHARDED ? out_dims : l->rows_r;
+    void* rowmajor = nullptr;
+    hipError_t e = hipMalloc(&rowmajor, wbytes);
     if (e != hipSuccess) {
         free_layer(l);
         return hip_fail(e, "weight allocation");
     }
-    st = copy_shards(l->w, weight, out_dims, in_dims, esz, mode == SG_ALL_TO_SHARDED ? 0 : 1, segments, P, hs);
+    st = copy_shards(rowmajor, weight, out_dims, in_dims, esz, mode == SG_ALL_TO_SHARDED ? 0 : 1, segments, P, hs);
+    if (!st && l->wfrag) {
+        e = hipMalloc(&l->w, wbytes);
+        if (e == hipSuccess) e = sg::frag_transform(l->w, rowmajor, frag_mats, frag_rows, l->cols_r, 1, hs);
+        if (e == hipSuccess) e = hipStreamSynchronize(hs);
+        (void)hipFree(rowmajor);
+        if (e != hipSuccess) st = hip_fail(e, "weight layout");
+    } else {
+        l->w = rowmajor;
+    }
     if (!st && bias) {
         e = hipMalloc(&l->bias, (size_t)out_dims * esz);
         if (e != hipSuccess) st = hip_fail(e, "bias allocation");
@@ -539,6 +555,21 @@ sg_status sg_layer_copy_shard(const sg_layer* l, int r, int what, void* dst, siz
     default: return fail(SG_ERR_INVALID_ARG, "unknown tensor selector %d", what);
     }
     if (dst_bytes < bytes) return fail(SG_ERR_INVALID_ARG, "dst holds %zu bytes, %zu needed", dst_bytes, bytes);
+    if (what == 0 && l->wfrag) {
+        // stored fragment-major: restore the row-major layout of every rank,
+        // then copy rank r's rows
+        void* tmp = nullptr;
+        const size_t all = bytes * l->P;
+        HIP_TRY(hipMalloc(&tmp, all), "staging allocation");
+        const int mats = l->mode == SG_ALL_TO_SHARDED ? 1 : l->P;
+        const int64_t rows = l->mode == SG_ALL_TO_SHARDED ? l->out_dims : l->rows_r;
+        hipError_t e = sg::frag_transform(tmp, l->w, mats, rows, l->cols_r, 0, hs);
+        if (e == hipSuccess) e = hipMemcpyAsync(dst, (const char*)tmp + r * bytes, bytes, hipMemcpyDefault, hs);
+        if (e == hipSuccess) e = hipStreamSynchronize(hs);
+        (void)hipFree(tmp);
+        if (e != hipSuccess) return hip_fail(e, "shard copy");
+        return SG_OK;
+    }
     if (what == 0 && l->quantized) {
         // stored codes are in kernel order: restore the standard order
         void* tmp = nullptr;

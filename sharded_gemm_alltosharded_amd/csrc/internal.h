@@ -39,6 +39,7 @@ struct Problem {
     int M, N, Kseg, nseg;
     int dtype;      // sg_dtype of A and W
     int nn;         // W is K x N (SUMMA)
+    int wfrag;      // W is stored fragment-major (frag_offset), Kseg % 32 == 0
     int swiglu;     // fused gate/up pairs
     int64_t floc;   // rank width of the swiglu output (rows per gate block)
     // epilogue
@@ -55,11 +56,24 @@ struct Problem {
     unsigned* counters; // one per output tile, zero between calls
 };
 
+// Fragment-major layout of a row-major (rows, K) weight, rows % 16 == 0 and
+// K % 32 == 0: the 16 x 32 block (row block rb, k step st) is 512 contiguous
+// elements ordered (rb, st) with st fastest; inside it lane l of a wave owns
+// elements l * 8 .. l * 8 + 7 = W[16 rb + (l & 15)][32 st + 8 (l >> 4) + 0..7],
+// exactly its operand fragment of a v_mfma_f32_16x16x32.  A wave streaming one
+// k step of a row block then reads 1 KB contiguous.
+__host__ __device__ inline int64_t frag_offset(int64_t row, int64_t k, int64_t nsteps) {
+    return (((row >> 4) * nsteps + (k >> 5)) * 64 + (row & 15) + 16 * ((k >> 3) & 3)) * 8 + (k & 7);
+}
+
 // launchers (return hipError_t of the launch)
 hipError_t launch_generic(const Problem& p, hipStream_t s);
 hipError_t launch_tile(const Problem& p, hipStream_t s, int variant);
 hipError_t launch_skinny(const Problem& p, hipStream_t s);
 hipError_t launch_q4(const Problem& p, hipStream_t s);
+// P stacked (rows, K) 16-bit matrices: row-major -> fragment-major (forward) or back
+hipError_t frag_transform(void* dst, const void* src, int P, int64_t rows, int64_t K, int forward, hipStream_t s);
+hipError_t q4_repack(uint32_t* w, int64_t n, int forward, hipStream_t s);
 
 // Workspace of the split-by-segment reduction: a fixed region of arrival
 // counters (one per output tile or row group) at the start, then `floats`

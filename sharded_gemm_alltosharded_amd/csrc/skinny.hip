@@ -4,7 +4,11 @@
 // in flight, not around reuse.
 //
 // One workgroup (NW waves) owns a group of RB x 16 weight rows across every
-// rank of the layer.  The work of that row group is cut into units (rank s,
+// rank of the layer; each wave streams all RB row blocks for its part of k,
+// so one activation fragment feeds RB MFMAs.  Dense 16-bit layers store their
+// weights fragment-major (frag_offset): the 16 x 32 operand fragment of a row
+// block and k step is one contiguous 1 KB, and each step is one fully
+// coalesced wave-wide read per row block.  The work of that row group is cut into units (rank s,
 // part j): J = max(1, NW / nseg) waves share one rank's k range, taking its
 // 32-wide k steps round robin (step j, j + J, ...), so the waves of one rank
 // read adjacent 64-byte pieces of the same rows at the same time.  Each step
@@ -65,8 +69,11 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Problem p) {
             wok[rb] = n < p.N;
             row = wok[rb] ? n : 0;
         }
-        woff[rb] = row * p.ldw + kq;
+        // row-major: lane's 16 bytes of a step at row * ldw + k; fragment-major:
+        // the block's 1 KB fragment, lane l at l * 8 (one coalesced read per step)
+        woff[rb] = p.wfrag ? frag_offset(row, kq, p.Kseg / 32) : row * p.ldw + kq;
     }
+    const int wstep = p.wfrag ? 512 : 32;  // elements per 32-wide k step
     int64_t xoff[MT];
     bool xok[MT];
 #pragma unroll
@@ -97,11 +104,11 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Problem p) {
 #pragma unroll
             for (int q = 0; q < U; ++q) {
                 const int idx = b * U + q;
-                const int k0 = (j + idx * J) * 32;
+                const int st = j + idx * J, k0 = st * 32;
                 const bool ok = idx < my_steps && k0 + kq < p.Kseg;
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
-                    wv[buf][q][rb] = (ok && wok[rb]) ? *(const u32x4*)(Wb + woff[rb] + k0) : zero;
+                    wv[buf][q][rb] = (ok && wok[rb]) ? *(const u32x4*)(Wb + woff[rb] + (int64_t)st * wstep) : zero;
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
                     xv[buf][q][mt] = (ok && xok[mt]) ? *(const u32x4*)(Ab + xoff[mt] + k0) : zero;
@@ -167,25 +174,41 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Problem p) {
     }
 }
 
-// Shape choice: RB row blocks per workgroup, NW waves.  Aim for several
-// thousand waves on the chip, at least one wave per rank.
+// Shape choice (from a sweep of RB, NW and U on the decode gate|up, down and
+// vocabulary-head shapes): as many row blocks per wave as still leave about
+// 1500 waves on the chip (each activation fragment then serves RB weight
+// fragments), the fewest waves per workgroup that reach that, at least one
+// wave per rank, and LDS slots within kMaxStreamLds.
 SkinnyShape skinny_shape(int M, int N, int nseg, int swiglu) {
     SkinnyShape sh;
     sh.MT = M <= 16 ? 1 : 2;
-    const int rows = swiglu ? N * 2 : N;
-    sh.RB = (swiglu || rows / 32 >= 1024) ? 2 : 1;
-    const int64_t wgs = ((int64_t)rows + sh.RB * 16 - 1) / (sh.RB * 16);
-    int nw = 4;
-    while (nw < 8 && (wgs * nw < 4096 || nw < nseg)) nw *= 2;
-    sh.NW = nw;
-    const int J = nseg >= nw ? 1 : nw / nseg;
-    sh.lds = (size_t)nseg * J * sh.RB * sh.MT * 4 * 64 * sizeof(float);
+    const int64_t rows = swiglu ? 2 * (int64_t)N : N;
+    const int64_t target = 1536;
+    auto lds_of = [&](int rb, int nw) {
+        const int J = nseg >= nw ? 1 : nw / nseg;
+        return (size_t)nseg * J * rb * sh.MT * 4 * 64 * sizeof(float);
+    };
+    sh.RB = swiglu ? 2 : 1;
+    sh.NW = 8;
+    for (int rb : {8, 4, 2, 1}) {
+        if (swiglu && rb < 2) break;
+        const int64_t wgs = (rows + rb * 16 - 1) / (rb * 16);
+        int nw = 2;
+        while (nw < 8 && (wgs * nw < target || nw < nseg || lds_of(rb, nw) > kMaxStreamLds)) nw *= 2;
+        while (nw > 2 && lds_of(rb, nw) > kMaxStreamLds) nw /= 2;
+        if ((wgs * nw >= target && lds_of(rb, nw) <= kMaxStreamLds) || rb == (swiglu ? 2 : 1)) {
+            sh.RB = rb;
+            sh.NW = nw;
+            break;
+        }
+    }
+    sh.lds = lds_of(sh.RB, sh.NW);
     return sh;
 }
 
 template <int MT, int RB, int NW, bool F16>
 static hipError_t launch_nw(const Problem& p, hipStream_t s, size_t lds) {
-    constexpr int U = (RB * MT >= 4) ? 2 : 4;
+    constexpr int U = (MT == 2 && RB >= 8) ? 1 : 2;
     if (p.swiglu) {
         if constexpr (RB % 2 == 0) {
             const int nwg = (p.N + RB / 2 * 16 - 1) / (RB / 2 * 16);
@@ -203,21 +226,27 @@ static hipError_t launch_nw(const Problem& p, hipStream_t s, size_t lds) {
 template <int MT, int RB, bool F16>
 static hipError_t launch_rb(const Problem& p, hipStream_t s, const SkinnyShape& sh) {
     switch (sh.NW) {
+    case 2: return launch_nw<MT, RB, 2, F16>(p, s, sh.lds);
     case 4: return launch_nw<MT, RB, 4, F16>(p, s, sh.lds);
     default: return launch_nw<MT, RB, 8, F16>(p, s, sh.lds);
     }
 }
 
-template <bool F16>
-static hipError_t launch_f(const Problem& p, hipStream_t s, const SkinnyShape& sh) {
-    if (sh.MT == 1) return sh.RB == 1 ? launch_rb<1, 1, F16>(p, s, sh) : launch_rb<1, 2, F16>(p, s, sh);
-    return sh.RB == 1 ? launch_rb<2, 1, F16>(p, s, sh) : launch_rb<2, 2, F16>(p, s, sh);
+template <int MT, bool F16>
+static hipError_t launch_mt(const Problem& p, hipStream_t s, const SkinnyShape& sh) {
+    switch (sh.RB) {
+    case 1: return launch_rb<MT, 1, F16>(p, s, sh);
+    case 2: return launch_rb<MT, 2, F16>(p, s, sh);
+    case 4: return launch_rb<MT, 4, F16>(p, s, sh);
+    default: return launch_rb<MT, 8, F16>(p, s, sh);
+    }
 }
 
 hipError_t launch_skinny(const Problem& p, hipStream_t s) {
     if (p.M == 0 || p.N == 0) return hipSuccess;
     const SkinnyShape sh = skinny_shape(p.M, p.N, p.nseg, p.swiglu);
-    return p.dtype == SG_F16 ? launch_f<true>(p, s, sh) : launch_f<false>(p, s, sh);
+    if (p.dtype == SG_F16) return sh.MT == 1 ? launch_mt<1, true>(p, s, sh) : launch_mt<2, true>(p, s, sh);
+    return sh.MT == 1 ? launch_mt<1, false>(p, s, sh) : launch_mt<2, false>(p, s, sh);
 }
 
 }  // namespace sg

@@ -168,9 +168,12 @@ __global__ __launch_bounds__(256) void tile_kernel(Problem p, int tiles_m, int t
                 wok[i] = n < p.N;
                 row = wok[i] ? n : 0;
             }
-            woff[i] = row * p.ldw + lch * 8;
+            woff[i] = p.wfrag ? frag_offset(row, lch * 8, p.Kseg / 32) : row * p.ldw + lch * 8;
         }
     }
+    // advancing k by one 64-wide tile moves 64 elements (row-major) or two
+    // 512-element fragments (fragment-major)
+    const int wk = p.wfrag ? 1024 / BK : 1;
 
     const int ktiles_seg = (p.Kseg + BK - 1) / BK;
     const int nkt = ktiles_seg * seg_cnt;
@@ -196,7 +199,7 @@ __global__ __launch_bounds__(256) void tile_kernel(Problem p, int tiles_m, int t
         } else {
 #pragma unroll
             for (int i = 0; i < CB; ++i)
-                rb[i] = (wok[i] && kok) ? *(const u32x4*)(Wb + woff[i] + k0) : zero;
+                rb[i] = (wok[i] && kok) ? *(const u32x4*)(Wb + woff[i] + (int64_t)k0 * wk) : zero;
         }
     };
     auto sstore = [&](int buf) {
