@@ -49,6 +49,7 @@ def parse():
     ap.add_argument("--batch", type=int, default=1, help="tokens for the 4-bit workload (1, 8 or 32)")
     ap.add_argument("--summa", default="fused", choices=["fused", "steps"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay measurement")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MiB",
                     help="instead of a workload, time a plain device copy of this size (counter calibration)")
     return ap.parse_args()
@@ -124,10 +125,8 @@ class DecodeMLP(Workload):
         sg = self.sg
         k = i % self.rotate
         if ev:
-            ev[0].record()
+            sg.time_next_launch(*ev)
         sg.all_to_sharded(self.gu[k], self.x, swiglu=True, out=self.h)
-        if ev:
-            ev[1].record()
         sg.sharded_to_all(self.dn[k], self.h, out=self.y, ws=self.ws)
 
     def config(self):
@@ -188,10 +187,8 @@ class PrefillMLP(Workload):
         sg = self.sg
         sg.all_to_sharded(self.qkv, self.x, out=self.q_out)
         if ev:
-            ev[0].record()
+            sg.time_next_launch(*ev)
         sg.all_to_sharded(self.gu, self.x, swiglu=True, out=self.h)
-        if ev:
-            ev[1].record()
         sg.sharded_to_all(self.dn, self.h, out=self.y, ws=self.ws)
 
     def config(self):
@@ -265,10 +262,8 @@ class Q4MLP(Workload):
         sg = self.sg
         k = i % self.rotate
         if ev:
-            ev[0].record()
+            sg.time_next_launch(*ev)
         sg.all_to_sharded(self.gu[k], self.x, swiglu=True, out=self.h)
-        if ev:
-            ev[1].record()
         sg.sharded_to_all(self.dn[k], self.h, out=self.y, ws=self.ws)
 
     def config(self):
@@ -319,10 +314,12 @@ class Summa(Workload):
         self.dom_units = self.units
 
     def step(self, i, ev=None):
-        if ev:
+        if ev and self.fused:
+            self.sg.time_next_launch(*ev)
+        elif ev:
             ev[0].record()
         self.sg.summa_matmul(self.X, self.A, self.q, out=self.Y, fused=self.fused)
-        if ev:
+        if ev and not self.fused:
             ev[1].record()
 
     def config(self):
@@ -371,10 +368,8 @@ class VocabHead(Workload):
 
     def step(self, i, ev=None):
         if ev:
-            ev[0].record()
+            self.sg.time_next_launch(*ev)
         self.sg.all_to_sharded(self.layer, self.x, gather=True, out=self.y)
-        if ev:
-            ev[1].record()
 
     def config(self):
         return {"workload": self.name, "tokens": self.B, "hidden": self.Hd, "vocab": self.V, "P": self.P,
@@ -426,10 +421,8 @@ class Tiny(Workload):
         sg = self.sg
         sg.sharded_to_all(self.l2, sg.all_to_sharded(self.l1, self.x0))
         if ev:
-            ev[0].record()
+            sg.time_next_launch(*ev)
         h = sg.all_to_sharded(self.gu, self.x, swiglu=True)
-        if ev:
-            ev[1].record()
         sg.sharded_to_all(self.dn, h)
 
     def cpu_baseline(self):
@@ -485,6 +478,34 @@ def calib_copy(mib: int, steps: int):
                       "GBps": 2 * n / ms / 1e6}), flush=True)
 
 
+def time_graph(wl: Workload, K: int, W: int):
+    """The same steps captured once per rotated weight copy into HIP graphs
+    and replayed K times (launch overhead and inter-kernel gaps of the host
+    path removed).  None if capture is not possible for the workload."""
+    import torch
+    try:
+        graphs = []
+        cap = torch.cuda.Stream()
+        for r in range(wl.rotate):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                wl.step(r)
+            graphs.append(g)
+    except Exception as e:  # capture unsupported for this workload
+        log(f"[bench] graph capture failed: {e}")
+        return None
+    for i in range(W):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(K):
+        graphs[i % len(graphs)].replay()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / K
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -513,17 +534,31 @@ def main():
         wl.step(i)
     torch.cuda.synchronize()
 
+    # The dominant kernel's start / end events are armed on every `every`-th
+    # timed step only: arming costs a few microseconds of launch overhead, and
+    # sampling keeps that out of the step time.
+    every = max(1, K // 25)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    evs = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for i in range(0, K, every)}
+    for a, b in evs.values():  # create the events before the timed region
+        a.record()
+        b.record()
     torch.cuda.synchronize()
     start.record()
     for i in range(K):
-        wl.step(i, evs[i])
+        wl.step(i, evs.get(i))
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / K
-    dom_ms = sum(a.elapsed_time(b) for a, b in evs) / K
-    log(f"[bench] {ms * 1e3:.1f} us/step; dominant kernel {dom_ms * 1e3:.1f} us")
+    dom_ms = sum(a.elapsed_time(b) for a, b in evs.values()) / len(evs)
+    log(f"[bench] {ms * 1e3:.1f} us/step; dominant kernel {dom_ms * 1e3:.1f} us (its own start/end events)")
+
+    graph_ms = None
+    if not args.no_graph:
+        graph_ms = time_graph(wl, K, W)
+        if graph_ms:
+            log(f"[bench] graph replay {graph_ms * 1e3:.1f} us/step")
 
     scale = 1e9 if wl.unit == "GB/s" else 1e12
     value = wl.units / (ms / 1e3) / scale
@@ -533,7 +568,7 @@ def main():
     traffic = load_traffic(wl, tag)
     roofline = {"bound": wl.bound, "achieved": round(achieved, 2), "peak": peak, "unit": wl.unit,
                 "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": wl.dominant,
-                "kernel_us": round(dom_ms * 1e3, 2),
+                "kernel_us": round(dom_ms * 1e3, 2), "kernel_samples": len(evs),
                 "algorithmic": f"{wl.dom_units / (1e9 if wl.unit == 'GB/s' else 1e12):.4g} "
                                f"{'GB' if wl.unit == 'GB/s' else 'TFLOP'} per launch"}
 
@@ -549,7 +584,9 @@ def main():
     rec = {"metric": wl.metric, "value": round(value, 3), "unit": wl.unit, "n_gpus": 1, "steps": K,
            "warmup": W, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic (seeded; shapes of the pages' workloads)",
-           "config": wl.config(), "roofline": roofline, "cpu_baseline": cpu}
+           "config": wl.config(), "roofline": roofline, "cpu_baseline": cpu,
+           "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 5),
+           "graph_value": None if graph_ms is None else round(wl.units / (graph_ms / 1e3) / scale, 3)}
     print(json.dumps(rec), flush=True)
 
 

@@ -114,8 +114,10 @@ sg_status sg_all_to_sharded(const sg_layer* layer, const void* x, int64_t B, voi
  *            x_partial[r] W_r^T, then + bias once.
  *   workspace device scratch of at least sg_sharded_to_all_workspace(layer, B)
  *            bytes (NULL allowed when that is 0).  It must be zero-filled
- *            before its first use; every call leaves it zero-filled again.
- *            Calls that share a workspace must not run concurrently. */
+ *            before its first use; every call leaves the arrival counters at
+ *            its start zero again, so the same workspace serves later calls of
+ *            any shape.  Calls that share a workspace must not run
+ *            concurrently. */
 sg_status sg_sharded_to_all(const sg_layer* layer, const void* x_partial, int64_t B, void* y,
                             sg_dtype y_dtype, void* workspace, size_t ws_bytes, void* stream);
 
@@ -149,6 +151,14 @@ sg_status sg_layer_copy_shard(const sg_layer* layer, int r, int what, void* dst,
 
 /* Release a layer and its device memory (NULL is ignored). */
 void sg_layer_free(sg_layer* layer);
+
+/* Profiling: arm two hipEvent_t (created with timing enabled; either may be
+ * NULL) for the next kernel this thread launches through the library, which
+ * records start_event when that kernel begins and stop_event when it ends
+ * (hipExtLaunchKernel), so hipEventElapsedTime gives its execution time
+ * without launch overhead.  One-shot: disarmed by that launch.  For entry
+ * points that launch several kernels, the first one is timed. */
+sg_status sg_time_next_launch(void* start_event, void* stop_event);
 
 /* Message describing the last failure on this thread ("" if none). */
 const char* sg_last_error(void);

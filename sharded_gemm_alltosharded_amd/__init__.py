@@ -12,6 +12,7 @@ kernels.  The entry points mirror include/shardgemm.h one to one:
     sharded_to_all             sg_sharded_to_all (+ sg_sharded_to_all_workspace)
     summa_matmul               sg_summa_matmul
     Layer.info / Layer.shard   sg_layer_info / sg_layer_copy_shard
+    time_next_launch           sg_time_next_launch (profiling)
 
 There is no fallback: if the library is not built, importing works but the
 first call raises.
@@ -71,6 +72,7 @@ def lib():
             "sg_layer_info": ([P, P, P, P, P, P, P, P], I),
             "sg_layer_copy_shard": ([P, I, I, P, SZ, P], I),
             "sg_layer_free": ([P], None),
+            "sg_time_next_launch": ([P, P], I),
             "sg_last_error": ([], C.c_char_p),
         }
         for name, (args, res) in sig.items():
@@ -99,6 +101,16 @@ def _mode(sharding) -> int:
         return sharding
     # unknown strings reach the library as an invalid mode, which rejects them
     return _MODES.get(sharding, -1)
+
+
+def time_next_launch(start: "torch.cuda.Event", stop: "torch.cuda.Event"):
+    """Arm two timing events for the next kernel this thread launches
+    through the library (sg_time_next_launch): they are recorded at that
+    kernel's own start and end."""
+    for e in (start, stop):
+        if e.cuda_event == 0:  # torch creates events lazily
+            e.record()
+    _check(lib().sg_time_next_launch(C.c_void_p(start.cuda_event), C.c_void_p(stop.cuda_event)))
 
 
 class Layer:

@@ -18,8 +18,16 @@ struct sg_layer {
     uint16_t* qb;            // 4-bit biases
     void* bias;              // all-to-sharded: P x rows_r (rank order); sharded-to-all: out_dims
     int wfrag;               // dense weights stored fragment-major (sg::frag_offset)
+    int qfrag;               // 4-bit codes / scales / biases fragment-major (sg::q4_*_offset)
     int device;
 };
+
+namespace sg {
+ArmedEvents& armed_events() {
+    static thread_local ArmedEvents ev;
+    return ev;
+}
+}  // namespace sg
 
 namespace {
 
@@ -155,7 +163,7 @@ bool q4_fits(const sg_layer* l, int64_t B, int swiglu) {
 
 Kind choose(const sg_layer* l, int64_t B, const void* x, int swiglu = 0) {
     if (l->quantized)
-        return (B <= 32 && l->cols_r % 256 == 0 && aligned16(x) && q4_fits(l, B, swiglu)) ? K_Q4 : K_GENERIC;
+        return (B <= 32 && l->qfrag && aligned16(x) && q4_fits(l, B, swiglu)) ? K_Q4 : K_GENERIC;
     if (!mfma_ok(l, x)) return K_GENERIC;
     if (B <= 32 && skinny_fits(l, B, swiglu)) return K_SKINNY;
     return B >= 512 ? K_TILE0 : K_TILE1;
@@ -187,7 +195,7 @@ sg::SplitLayout split_layout(const sg_layer* l, Kind k, int64_t B) {
 // kernel family for a sharded-to-all call (alignment of the caller's pointers
 // is checked separately; misaligned pointers fall back to the generic path)
 Kind choose_row(const sg_layer* l, int64_t B) {
-    if (l->quantized) return B <= 32 && l->cols_r % 256 == 0 && q4_fits(l, B, 0) ? K_Q4 : K_GENERIC;
+    if (l->quantized) return B <= 32 && l->qfrag && q4_fits(l, B, 0) ? K_Q4 : K_GENERIC;
     if (l->dtype == SG_F32 || l->cols_r % 8) return K_GENERIC;
     if (B <= 32 && skinny_fits(l, B, 0)) return K_SKINNY;
     return B >= 512 ? K_TILE0 : K_TILE1;
@@ -212,6 +220,7 @@ void set_weights(sg::Problem& p, const sg_layer* l) {
         p.ldg = l->cols_r / 64;
         p.q_seg = l->rows_r * p.ldq;
         p.g_seg = l->rows_r * p.ldg;
+        p.qfrag = l->qfrag;
     } else {
         p.W = l->w;
         p.ldw = l->cols_r;
@@ -336,6 +345,34 @@ sg_status sg_shard_quantized_linear(const uint32_t* wq, const uint16_t* scales, 
     if (!st) {
         e = sg::q4_repack((uint32_t*)l->w, out_dims * words, 1, hs);
         if (e != hipSuccess) st = hip_fail(e, "code reorder");
+    }
+    // codes, scales and biases fragment-major when the rank matrices tile into
+    // 32-row blocks and runs of 4 groups (the streaming kernel's layout)
+    l->qfrag = out_dims % 32 == 0 && l->cols_r % 256 == 0;
+    if (!st && l->qfrag) {
+        const int mats = mode == SG_ALL_TO_SHARDED ? 1 : P;
+        const int64_t rows = mode == SG_ALL_TO_SHARDED ? out_dims : l->rows_r;
+        void *w2 = nullptr, *s2 = nullptr, *b2 = nullptr;
+        e = hipMalloc(&w2, (size_t)(out_dims * words) * 4);
+        if (e == hipSuccess) e = hipMalloc(&s2, (size_t)(out_dims * groups) * 2);
+        if (e == hipSuccess) e = hipMalloc(&b2, (size_t)(out_dims * groups) * 2);
+        if (e == hipSuccess)
+            e = sg::q4_transform((uint32_t*)w2, (const uint32_t*)l->w, (uint16_t*)s2, l->qs, mats, rows, l->cols_r, 1, hs);
+        if (e == hipSuccess) e = sg::q4_transform(nullptr, nullptr, (uint16_t*)b2, l->qb, mats, rows, l->cols_r, 1, hs);
+        if (e == hipSuccess) e = hipStreamSynchronize(hs);
+        if (e == hipSuccess) {
+            (void)hipFree(l->w);
+            (void)hipFree(l->qs);
+            (void)hipFree(l->qb);
+            l->w = w2;
+            l->qs = (uint16_t*)s2;
+            l->qb = (uint16_t*)b2;
+        } else {
+            (void)hipFree(w2);
+            (void)hipFree(s2);
+            (void)hipFree(b2);
+            st = hip_fail(e, "4-bit layout");
+        }
     }
     if (!st && bias) {
         e = hipMalloc(&l->bias, (size_t)out_dims * 2);
@@ -570,6 +607,27 @@ sg_status sg_layer_copy_shard(const sg_layer* l, int r, int what, void* dst, siz
         if (e != hipSuccess) return hip_fail(e, "shard copy");
         return SG_OK;
     }
+    if (l->quantized && l->qfrag && what != 1) {
+        // stored fragment-major: restore the row-major layout of every rank
+        // (codes also back to the standard nibble order), then copy rank r
+        void* tmp = nullptr;
+        const size_t all = bytes * l->P;
+        HIP_TRY(hipMalloc(&tmp, all), "staging allocation");
+        const int mats = l->mode == SG_ALL_TO_SHARDED ? 1 : l->P;
+        const int64_t rows = l->mode == SG_ALL_TO_SHARDED ? l->out_dims : l->rows_r;
+        hipError_t e;
+        if (what == 0) {
+            e = sg::q4_transform((uint32_t*)tmp, (const uint32_t*)l->w, nullptr, nullptr, mats, rows, l->cols_r, 0, hs);
+            if (e == hipSuccess) e = sg::q4_repack((uint32_t*)tmp, (int64_t)(all / 4), 0, hs);
+        } else {
+            e = sg::q4_transform(nullptr, nullptr, (uint16_t*)tmp, what == 2 ? l->qs : l->qb, mats, rows, l->cols_r, 0, hs);
+        }
+        if (e == hipSuccess) e = hipMemcpyAsync(dst, (const char*)tmp + r * bytes, bytes, hipMemcpyDefault, hs);
+        if (e == hipSuccess) e = hipStreamSynchronize(hs);
+        (void)hipFree(tmp);
+        if (e != hipSuccess) return hip_fail(e, "shard copy");
+        return SG_OK;
+    }
     if (what == 0 && l->quantized) {
         // stored codes are in kernel order: restore the standard order
         void* tmp = nullptr;
@@ -588,5 +646,11 @@ sg_status sg_layer_copy_shard(const sg_layer* l, int r, int what, void* dst, siz
 }
 
 void sg_layer_free(sg_layer* l) { free_layer(l); }
+
+sg_status sg_time_next_launch(void* start_event, void* stop_event) {
+    g_err.clear();
+    sg::armed_events() = sg::ArmedEvents{(hipEvent_t)start_event, (hipEvent_t)stop_event};
+    return SG_OK;
+}
 
 }  // extern "C"

@@ -12,9 +12,10 @@ namespace sg {
 
 __device__ __forceinline__ float weight_at(const Problem& p, int s, int64_t row, int k) {
     if (p.wq) {
-        uint32_t word = p.wq[s * p.q_seg + row * p.ldq + (k >> 3)];
+        const int64_t wi = p.qfrag ? q4_word_offset(row, k >> 3, p.ldg) : row * p.ldq + (k >> 3);
+        uint32_t word = p.wq[s * p.q_seg + wi];
         float q = (float)((word >> (4 * q4_nibble_pos(k & 7))) & 0xFu);
-        int64_t g = s * p.g_seg + row * p.ldg + (k >> 6);
+        int64_t g = s * p.g_seg + (p.qfrag ? q4_group_offset(row, k >> 6, p.ldg) : row * p.ldg + (k >> 6));
         return fmaf(f16_to_f32(p.qs[g]), q, f16_to_f32(p.qb[g]));
     }
     if (p.nn) return load_as_f32(p.W, p.dtype, s * p.w_seg + (int64_t)k * p.ldw + row);
@@ -52,7 +53,7 @@ hipError_t launch_generic(const Problem& p, hipStream_t s) {
     int64_t total = (int64_t)p.M * p.N;
     if (total == 0) return hipSuccess;
     int64_t blocks = (total + 255) / 256;
-    hipLaunchKernelGGL(generic_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
+    launch(generic_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

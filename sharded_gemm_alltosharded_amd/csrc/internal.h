@@ -2,6 +2,7 @@
 // gfx950 kernels.  Nothing here is part of the public C ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -40,6 +41,7 @@ struct Problem {
     int dtype;      // sg_dtype of A and W
     int nn;         // W is K x N (SUMMA)
     int wfrag;      // W is stored fragment-major (frag_offset), Kseg % 32 == 0
+    int qfrag;      // 4-bit codes / scales / biases stored fragment-major (q4 offsets)
     int swiglu;     // fused gate/up pairs
     int64_t floc;   // rank width of the swiglu output (rows per gate block)
     // epilogue
@@ -66,6 +68,40 @@ __host__ __device__ inline int64_t frag_offset(int64_t row, int64_t k, int64_t n
     return (((row >> 4) * nsteps + (k >> 5)) * 64 + (row & 15) + 16 * ((k >> 3) & 3)) * 8 + (k & 7);
 }
 
+// Events armed by sg_time_next_launch for the calling thread: the next kernel
+// the library launches records them at its own start and end.
+struct ArmedEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+ArmedEvents& armed_events();
+
+#ifdef __HIPCC__
+template <typename K, typename... Args>
+inline void launch(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, Args... args) {
+    ArmedEvents& ev = armed_events();
+    if (ev.start || ev.stop) {
+        hipExtLaunchKernelGGL(kernel, grid, block, lds, s, ev.start, ev.stop, 0, args...);
+        ev = ArmedEvents{};
+    } else {
+        hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+    }
+}
+#endif
+
+// Fragment-major layout of 4-bit layers, rows % 32 == 0 and G = K / 64 groups
+// with G % 4 == 0.  Codes: the 32 rows x 8 words of (row block rb, group g)
+// are 256 contiguous words; lane l of a wave owns words l * 4 .. l * 4 + 3 =
+// words 4 (l >> 5) .. 4 (l >> 5) + 3 of group g of row 32 rb + (l & 31), its
+// operand of one group in v_mfma_f32_32x32x16.  Scales and biases: the 32 rows
+// x 4 groups of (rb, run g / 4) are 128 contiguous halves, row-major.
+__host__ __device__ inline int64_t q4_word_offset(int64_t row, int64_t word, int64_t groups) {
+    const int64_t g = word >> 3, wi = word & 7;
+    return (((row >> 5) * groups + g) * 64 + (row & 31) + 32 * (wi >> 2)) * 4 + (wi & 3);
+}
+__host__ __device__ inline int64_t q4_group_offset(int64_t row, int64_t g, int64_t groups) {
+    return (((row >> 5) * (groups >> 2) + (g >> 2)) * 32 + (row & 31)) * 4 + (g & 3);
+}
+
 // launchers (return hipError_t of the launch)
 hipError_t launch_generic(const Problem& p, hipStream_t s);
 hipError_t launch_tile(const Problem& p, hipStream_t s, int variant);
@@ -74,6 +110,10 @@ hipError_t launch_q4(const Problem& p, hipStream_t s);
 // P stacked (rows, K) 16-bit matrices: row-major -> fragment-major (forward) or back
 hipError_t frag_transform(void* dst, const void* src, int P, int64_t rows, int64_t K, int forward, hipStream_t s);
 hipError_t q4_repack(uint32_t* w, int64_t n, int forward, hipStream_t s);
+// P stacked 4-bit matrices (rows, K): codes (rows, K/8 words) and scales or
+// biases (rows, K/64), row-major <-> fragment-major
+hipError_t q4_transform(uint32_t* dst_w, const uint32_t* src_w, uint16_t* dst_g, const uint16_t* src_g, int P,
+                        int64_t rows, int64_t K, int forward, hipStream_t s);
 
 // Workspace of the split-by-segment reduction: a fixed region of arrival
 // counters (one per output tile or row group) at the start, then `floats`

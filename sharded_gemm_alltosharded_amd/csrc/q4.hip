@@ -15,12 +15,14 @@
 // 32 weight rows the column operand, so each lane owns one weight row and
 // needs one (scale, bias) pair per group.  Lane (row j, half h) loads 16 bytes
 // = codes of chunks 4h .. 4h+3 of the group; MFMA step u of the group uses
-// chunk 4h + u, and the token fragment of step u holds the same chunk.
+// chunk 4h + u, and the token fragment of step u holds the same chunk.  The
+// layer stores codes, scales and biases fragment-major (q4_word_offset,
+// q4_group_offset), so every one of these loads is a coalesced wave-wide read.
 //
-// Workgroup = NW waves on RB blocks of 32 rows (a gate/up pair for SwiGLU)
-// across every rank; a wave takes one (row block, rank, part) unit and walks
-// that rank's groups in runs of 4 (so scales and biases arrive 8 bytes at a
-// time), runs j, j + J, ...  Unit partials land in LDS slots and are summed in
+// Workgroup = NW waves on RB blocks of 32 rows (gate/up pairs for SwiGLU)
+// across every rank; a wave takes one (rank, part) unit for all RB row blocks
+// (one activation fragment serves RB of them) and walks that rank's groups in
+// runs of 4 (scales and biases arrive 8 bytes at a time), runs j, j + J, ...  Unit partials land in LDS slots and are summed in
 // part order, then rank order -- the fused all_sum, as in the dense streaming
 // kernel -- with no cross-workgroup traffic.
 #include "internal.h"
@@ -55,11 +57,11 @@ __device__ __forceinline__ u32x4 unpack8(uint32_t w) {
     return r;
 }
 
-template <int TB, int RB, int NW, bool F16, bool SWIGLU>
+template <int TB, int RB, int NW, bool F16, bool SWIGLU, bool PF, bool XH>
 __global__ __launch_bounds__(NW * 64) void q4_kernel(Problem p) {
     constexpr int ROWS = SWIGLU ? RB / 2 * 32 : RB * 32;  // logical columns per workgroup
     constexpr int NR = 4 * TB;                            // token registers in use
-    constexpr int SLOT = NR * 64;                         // floats per unit slot
+    constexpr int SLOT = RB * NR * 64;                    // floats per unit slot
     constexpr float C = F16 ? 1024.f : 128.f;
     static_assert(!SWIGLU || RB % 2 == 0, "gate/up blocks come in pairs");
     extern __shared__ float slots[];
@@ -67,12 +69,28 @@ __global__ __launch_bounds__(NW * 64) void q4_kernel(Problem p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t base = (int64_t)blockIdx.x * ROWS;
     const int h = lane >> 5;
-    const int per_rb = p.nseg >= NW / RB ? p.nseg : (NW / RB / p.nseg) * p.nseg;
-    const int J = per_rb / p.nseg;  // waves per (row block, rank)
-    const int units = RB * per_rb;
-    const int G = p.Kseg / 64;      // groups per rank (a multiple of 4)
+    const int J = p.nseg >= NW ? 1 : NW / p.nseg;  // waves per rank
+    const int units = p.nseg * J;
+    const int G = p.Kseg / 64;                     // groups per rank (a multiple of 4)
     const int runs = G / 4;
 
+    int64_t qoff[RB], goff[RB];
+    bool wok[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        int64_t row;
+        if constexpr (SWIGLU) {
+            const int64_t jj = base + (rb >> 1) * 32 + (lane & 31);
+            wok[rb] = jj < p.N;
+            row = weight_row(p, wok[rb] ? jj : 0, rb & 1);
+        } else {
+            const int64_t n = base + rb * 32 + (lane & 31);
+            wok[rb] = n < p.N;
+            row = wok[rb] ? n : 0;
+        }
+        qoff[rb] = q4_word_offset(row, 4 * h, G);  // group g at + 256 g
+        goff[rb] = q4_group_offset(row, 0, G);     // run r at + 128 r
+    }
     const int t = lane & 31;
     const bool xok = t < p.M;
     const int64_t xoff = (int64_t)(xok ? t : 0) * p.lda + h * 32;
@@ -81,71 +99,106 @@ __global__ __launch_bounds__(NW * 64) void q4_kernel(Problem p) {
     const u32x4 zero = {0u, 0u, 0u, 0u};
 
     for (int u = wave; u < units; u += NW) {
-        const int rb = u / per_rb, s = (u % per_rb) / J, j = u % J;
-        int64_t row;
-        bool wok;
-        if constexpr (SWIGLU) {
-            const int64_t jj = base + (rb >> 1) * 32 + (lane & 31);
-            wok = jj < p.N;
-            row = weight_row(p, wok ? jj : 0, rb & 1);
-        } else {
-            const int64_t n = base + rb * 32 + (lane & 31);
-            wok = n < p.N;
-            row = wok ? n : 0;
-        }
-        const uint32_t* Qb = p.wq + s * p.q_seg + row * p.ldq + h * 4;
-        const uint16_t* Sb = p.qs + s * p.g_seg + row * p.ldg;
-        const uint16_t* Bb = p.qb + s * p.g_seg + row * p.ldg;
+        const int s = u / J, j = u % J;
+        const uint32_t* Qb = p.wq + s * p.q_seg;
+        const uint16_t* Sb = p.qs + s * p.g_seg;
+        const uint16_t* Bb = p.qb + s * p.g_seg;
         const uint16_t* Ab = (const uint16_t*)p.A + s * p.a_seg + xoff;
-
-        f32x16 y;
+        f32x16 y[RB];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) y[r] = 0.f;
-        for (int run = j; run < runs; run += J) {
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) y[rb][r] = 0.f;
+        // codes, scales and biases of a run of 4 groups; with PF the next run's
+        // are in flight while this one is computed (register double buffer)
+        constexpr int NB = PF ? 2 : 1;
+        u32x4 wv[NB][4][RB];
+        u32x2 sv[NB][RB], bv[NB][RB];
+        auto load = [&](int buf, int run) {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+                for (int gi = 0; gi < 4; ++gi)
+                    wv[buf][gi][rb] = wok[rb] ? *(const u32x4*)(Qb + qoff[rb] + (int64_t)(run * 4 + gi) * 256) : zero;
+                sv[buf][rb] = *(const u32x2*)(Sb + goff[rb] + (int64_t)run * 128);
+                bv[buf][rb] = *(const u32x2*)(Bb + goff[rb] + (int64_t)run * 128);
+            }
+        };
+        auto compute = [&](int buf, int run) {
             const int g0 = run * 4;
-            u32x4 wv[4];
+            // XH: the run's activation fragments are loaded up front (one L2
+            // round trip per run instead of one per group)
+            u32x4 xr[XH ? 4 : 1][4];
+            if constexpr (XH) {
 #pragma unroll
-            for (int gi = 0; gi < 4; ++gi) wv[gi] = wok ? *(const u32x4*)(Qb + (g0 + gi) * 8) : zero;
-            const u32x2 sv = *(const u32x2*)(Sb + g0);
-            const u32x2 bv = *(const u32x2*)(Bb + g0);
+                for (int gi = 0; gi < 4; ++gi)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) xr[gi][q] = xok ? *(const u32x4*)(Ab + (g0 + gi) * 64 + q * 8) : zero;
+            }
 #pragma unroll
             for (int gi = 0; gi < 4; ++gi) {
                 u32x4 xf[4];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) xf[q] = xok ? *(const u32x4*)(Ab + (g0 + gi) * 64 + q * 8) : zero;
-                f32x16 xs, acc;
+                for (int q = 0; q < 4; ++q)
+                    xf[q] = XH ? xr[XH ? gi : 0][q] : (xok ? *(const u32x4*)(Ab + (g0 + gi) * 64 + q * 8) : zero);
+                f32x16 xs;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) xs[r] = acc[r] = 0.f;
+                for (int r = 0; r < 16; ++r) xs[r] = 0.f;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    xs = mfma32<F16>(xf[q], ones, xs);
-                    acc = mfma32<F16>(xf[q], unpack8<F16>(wv[gi][q]), acc);
+                for (int q = 0; q < 4; ++q) xs = mfma32<F16>(xf[q], ones, xs);
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    f32x16 acc;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acc = mfma32<F16>(xf[q], unpack8<F16>(wv[buf][gi][rb][q]), acc);
+                    const uint32_t sw = sv[buf][rb][gi >> 1], bw = bv[buf][rb][gi >> 1];
+                    const float sc = f16_to_f32((uint16_t)((gi & 1) ? (sw >> 16) : (sw & 0xFFFFu)));
+                    const float bi = f16_to_f32((uint16_t)((gi & 1) ? (bw >> 16) : (bw & 0xFFFFu)));
+                    const float bp = fmaf(-C, sc, bi);
+#pragma unroll
+                    for (int r = 0; r < NR; ++r) y[rb][r] = fmaf(sc, acc[r], fmaf(bp, xs[r], y[rb][r]));
                 }
-                const uint32_t sw = sv[gi >> 1], bw = bv[gi >> 1];
-                const float sc = f16_to_f32((uint16_t)((gi & 1) ? (sw >> 16) : (sw & 0xFFFFu)));
-                const float bi = f16_to_f32((uint16_t)((gi & 1) ? (bw >> 16) : (bw & 0xFFFFu)));
-                const float bp = fmaf(-C, sc, bi);
-#pragma unroll
-                for (int r = 0; r < NR; ++r) y[r] = fmaf(sc, acc[r], fmaf(bp, xs[r], y[r]));
+            }
+        };
+        if constexpr (PF) {
+            int run = j;
+            if (run < runs) load(0, run);
+            for (; run + J < runs; run += 2 * J) {
+                load(1, run + J);
+                compute(0, run);
+                if (run + 2 * J < runs) load(0, run + 2 * J);
+                compute(1, run + J);
+            }
+            if (run < runs) compute(0, run);
+        } else {
+            for (int run = j; run < runs; run += J) {
+                load(0, run);
+                compute(0, run);
             }
         }
         float* slot = slots + (size_t)u * SLOT;
 #pragma unroll
-        for (int r = 0; r < NR; ++r) slot[r * 64 + lane] = y[r];
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int r = 0; r < NR; ++r) slot[(rb * NR + r) * 64 + lane] = y[rb][r];
     }
     __syncthreads();
 
     // ---- reduction (parts of a rank in order, then ranks in order) + epilogue
-    constexpr int NE = (SWIGLU ? RB / 2 : RB) * SLOT;
+    constexpr int NE = (SWIGLU ? RB / 2 : RB) * NR * 64;
     for (int idx = tid; idx < NE; idx += NW * 64) {
         const int ln = idx & 63, r = (idx >> 6) % NR, rbo = (idx >> 6) / NR;
         const int rb = SWIGLU ? 2 * rbo : rbo;
+        const int off = (rb * NR + r) * 64 + ln;
         float v = 0.f, vu = 0.f;
         for (int s = 0; s < p.nseg; ++s) {
             float zs = 0.f, zu = 0.f;
             for (int jj = 0; jj < J; ++jj) {
-                zs += slots[(size_t)(rb * per_rb + s * J + jj) * SLOT + r * 64 + ln];
-                if constexpr (SWIGLU) zu += slots[(size_t)((rb + 1) * per_rb + s * J + jj) * SLOT + r * 64 + ln];
+                const float* sl = slots + (size_t)(s * J + jj) * SLOT;
+                zs += sl[off];
+                if constexpr (SWIGLU) zu += sl[off + NR * 64];
             }
             v += zs;
             vu += zu;
@@ -161,39 +214,66 @@ __global__ __launch_bounds__(NW * 64) void q4_kernel(Problem p) {
     }
 }
 
-// Shape choice: RB row blocks of 32 per workgroup (a gate/up pair for
-// SwiGLU), NW waves, several thousand waves on the chip.
+// Shape choice: RB row blocks of 32 per wave (a gate/up pair for SwiGLU; more
+// share each activation fragment), NW waves, about 1500 waves on the chip, at
+// least one wave per rank, LDS slots within kMaxStreamLds.
 Q4Shape q4_shape(int M, int N, int nseg, int swiglu) {
     Q4Shape sh;
     sh.TB = (M + 7) / 8;
+    const int64_t rows = swiglu ? 2 * (int64_t)N : N;
+    auto lds_of = [&](int rb, int nw) {
+        const int J = nseg >= nw ? 1 : nw / nseg;
+        return (size_t)nseg * J * rb * 4 * sh.TB * 64 * sizeof(float);
+    };
     sh.RB = swiglu ? 2 : 1;
-    const int rows = swiglu ? N * 2 : N;
-    const int64_t wgs = ((int64_t)rows + sh.RB * 32 - 1) / (sh.RB * 32);
-    int nw = 4;
-    while (nw < 8 && (wgs * nw < 4096 || nw < sh.RB * nseg)) nw *= 2;
-    sh.NW = nw;
-    const int per_rb = nseg >= nw / sh.RB ? nseg : (nw / sh.RB / nseg) * nseg;
-    sh.lds = (size_t)sh.RB * per_rb * 4 * sh.TB * 64 * sizeof(float);
+    sh.NW = 8;
+    for (int rb : {4, 2, 1}) {
+        if (swiglu && rb < 2) break;
+        const int64_t wgs = (rows + rb * 32 - 1) / (rb * 32);
+        int nw = 4;
+        while (nw < 8 && (wgs * nw < 1536 || nw < nseg)) nw *= 2;
+        if (lds_of(rb, nw) > kMaxStreamLds && nw > 4) nw = 4;
+        if ((wgs * nw >= 1536 && lds_of(rb, nw) <= kMaxStreamLds) || rb == (swiglu ? 2 : 1)) {
+            sh.RB = rb;
+            sh.NW = nw;
+            break;
+        }
+    }
+    sh.lds = lds_of(sh.RB, sh.NW);
     return sh;
 }
 
-template <int TB, int NW, bool F16>
-static hipError_t launch_nw(const Problem& p, hipStream_t s, size_t lds) {
+template <int TB, int RB, int NW, bool F16, bool PF = false, bool XH = false>
+hipError_t launch_q4_variant(const Problem& p, hipStream_t s, size_t lds) {
     if (p.swiglu) {
-        const int nwg = (p.N + 31) / 32;
-        hipLaunchKernelGGL((q4_kernel<TB, 2, NW, F16, true>), dim3(nwg), dim3(NW * 64), lds, s, p);
+        if constexpr (RB % 2 == 0) {
+            const int nwg = (p.N + RB / 2 * 32 - 1) / (RB / 2 * 32);
+            launch(q4_kernel<TB, RB, NW, F16, true, PF, XH>, dim3(nwg), dim3(NW * 64), lds, s, p);
+        } else {
+            return hipErrorInvalidValue;
+        }
     } else {
-        const int nwg = (p.N + 31) / 32;
-        hipLaunchKernelGGL((q4_kernel<TB, 1, NW, F16, false>), dim3(nwg), dim3(NW * 64), lds, s, p);
+        const int nwg = (p.N + RB * 32 - 1) / (RB * 32);
+        launch(q4_kernel<TB, RB, NW, F16, false, PF, XH>, dim3(nwg), dim3(NW * 64), lds, s, p);
     }
     return hipGetLastError();
 }
 
+template <int TB, int RB, bool F16>
+static hipError_t launch_rb(const Problem& p, hipStream_t s, const Q4Shape& sh) {
+    // up to 8 tokens the run's activation fragments are hoisted (measured
+    // faster); beyond that their registers cost more than the latency saved
+    constexpr bool XH = TB == 1;
+    return sh.NW == 4 ? launch_q4_variant<TB, RB, 4, F16, false, XH>(p, s, sh.lds)
+                      : launch_q4_variant<TB, RB, 8, F16, false, XH>(p, s, sh.lds);
+}
+
 template <int TB, bool F16>
 static hipError_t launch_tb(const Problem& p, hipStream_t s, const Q4Shape& sh) {
-    switch (sh.NW) {
-    case 4: return launch_nw<TB, 4, F16>(p, s, sh.lds);
-    default: return launch_nw<TB, 8, F16>(p, s, sh.lds);
+    switch (sh.RB) {
+    case 1: return launch_rb<TB, 1, F16>(p, s, sh);
+    case 2: return launch_rb<TB, 2, F16>(p, s, sh);
+    default: return launch_rb<TB, 4, F16>(p, s, sh);
     }
 }
 
@@ -209,6 +289,7 @@ static hipError_t launch_f(const Problem& p, hipStream_t s, const Q4Shape& sh) {
 
 hipError_t launch_q4(const Problem& p, hipStream_t s) {
     if (p.M == 0 || p.N == 0) return hipSuccess;
+    if (!p.qfrag) return hipErrorInvalidValue;  // the streaming kernel reads the fragment layout
     const Q4Shape sh = q4_shape(p.M, p.N, p.nseg, p.swiglu);
     return p.dtype == SG_F16 ? launch_f<true>(p, s, sh) : launch_f<false>(p, s, sh);
 }
@@ -230,7 +311,7 @@ __global__ void q4_repack_kernel(uint32_t* w, int64_t n, int forward) {
 
 hipError_t q4_repack(uint32_t* w, int64_t n, int forward, hipStream_t s) {
     if (n == 0) return hipSuccess;
-    hipLaunchKernelGGL(q4_repack_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, w, n, forward);
+    launch(q4_repack_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, w, n, forward);
     return hipGetLastError();
 }
 

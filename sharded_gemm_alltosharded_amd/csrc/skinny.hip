@@ -212,13 +212,13 @@ static hipError_t launch_nw(const Problem& p, hipStream_t s, size_t lds) {
     if (p.swiglu) {
         if constexpr (RB % 2 == 0) {
             const int nwg = (p.N + RB / 2 * 16 - 1) / (RB / 2 * 16);
-            hipLaunchKernelGGL((skinny_kernel<MT, RB, NW, F16, true, U>), dim3(nwg), dim3(NW * 64), lds, s, p);
+            launch((skinny_kernel<MT, RB, NW, F16, true, U>), dim3(nwg), dim3(NW * 64), lds, s, p);
         } else {
             return hipErrorInvalidValue;
         }
     } else {
         const int nwg = (p.N + RB * 16 - 1) / (RB * 16);
-        hipLaunchKernelGGL((skinny_kernel<MT, RB, NW, F16, false, U>), dim3(nwg), dim3(NW * 64), lds, s, p);
+        launch((skinny_kernel<MT, RB, NW, F16, false, U>), dim3(nwg), dim3(NW * 64), lds, s, p);
     }
     return hipGetLastError();
 }

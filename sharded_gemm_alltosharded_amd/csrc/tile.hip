@@ -364,7 +364,7 @@ static hipError_t launch_one(const Problem& p, hipStream_t s) {
     const int nout = WMODE == WM_SWIGLU ? BN / 2 : BN;
     const int tm = (p.M + BM - 1) / BM, tn = (p.N + nout - 1) / nout;
     dim3 grid(tm * tn, SPLIT ? p.nseg : 1);
-    hipLaunchKernelGGL((tile_kernel<BM, BN, F16, WMODE, SPLIT>), grid, dim3(256), 0, s, p, tm, tn);
+    launch((tile_kernel<BM, BN, F16, WMODE, SPLIT>), grid, dim3(256), 0, s, p, tm, tn);
     return hipGetLastError();
 }
 

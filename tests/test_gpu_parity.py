@@ -45,7 +45,8 @@ def test_slicing_bit_exact(dtype, mode, out, inn, S, P):
         np.testing.assert_array_equal(bits(layer.shard(r, 1)), want_b)
 
 
-@pytest.mark.parametrize("mode,out,inn,S,P", [(0, 64, 256, 1, 4), (0, 96, 128, 3, 2), (1, 32, 512, 1, 4), (1, 16, 512, 2, 2)])
+@pytest.mark.parametrize("mode,out,inn,S,P", [(0, 64, 256, 1, 4), (0, 96, 128, 3, 2), (1, 32, 512, 1, 4), (1, 16, 512, 2, 2),
+                                               (1, 64, 1024, 1, 4), (0, 128, 512, 2, 2)])
 def test_slicing_q4_bit_exact(mode, out, inn, S, P):
     _print_case(mode=mode, out=out, inn=inn, S=S, P=P)
     packed, s, b, _ = synth.quantize_q4(synth.uniform(3, (out, inn), 0.1, "f32"), 64)
