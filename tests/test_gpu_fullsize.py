@@ -1,0 +1,132 @@
+"""Full-size parity: every workload at the shapes bench.py times, in the same
+launch configuration (same layers, same kernels), against the oracle on all
+tokens where the oracle finishes in seconds, else on sampled tokens / rows
+(the oracle computes those rows exactly; rows are independent)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sharded_gemm_alltosharded_amd as sg
+import synth
+from gpu_util import assert_close, dev, to_dev
+
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(600)]
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _cuda():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+    sg.lib()
+
+
+def _case(msg):
+    print("case:", msg, flush=True)
+
+
+def test_decode_mlp_full():
+    """B=16, D=4096, F=14336, P=8, bf16: every token against the oracle."""
+    _case("decode MLP B=16 D=4096 F=14336 P=8")
+    B, D, F, P = 16, 4096, 14336, 8
+    inp = synth.mlp_inputs(B, D, F, P, "bf16", seed=0)
+    gu = sg.shard_linear(to_dev(np.concatenate([inp.Wg, inp.Wu]), "bf16"), "all-to-sharded", segments=2, P=P)
+    dn = sg.shard_linear(to_dev(inp.Wd, "bf16"), "sharded-to-all", P=P)
+    x = to_dev(inp.X, "bf16")
+    h = sg.all_to_sharded(gu, x, swiglu=True)
+    y = sg.sharded_to_all(dn, h)
+    X, Wg, Wu, Wd = (oracle.decode(a, "bf16") for a in (inp.X, inp.Wg, inp.Wu, inp.Wd))
+    g, u = oracle.col(X, Wg, P=P), oracle.col(X, Wu, P=P)
+    # h against the exact product; the next layer's reference consumes h rounded
+    # to bf16 once, as stored between the layers
+    assert_close(h, oracle.swiglu(g, u, "f64"), "bf16", "h")
+    assert_close(y, oracle.row(oracle.swiglu(g, u, "bf16"), Wd, P=P), "bf16", "y")
+    # the fused rank sum is deterministic
+    y2 = sg.sharded_to_all(dn, h)
+    assert torch.equal(y, y2)
+
+
+def test_prefill_full_sampled():
+    """B=4096, P=4: QKV (segments 3) + MLP on the full batch; 8 sampled tokens."""
+    _case("prefill B=4096 D=4096 F=14336 P=4 + QKV")
+    B, D, F, P = 4096, 4096, 14336, 4
+    inp = synth.mlp_inputs(B, D, F, P, "bf16", seed=0)
+    wqkv = synth.qkv_weight(D, 32, 128, seed=10)
+    x = to_dev(inp.X, "bf16")
+    qkv = sg.all_to_sharded(sg.shard_linear(to_dev(wqkv, "bf16"), "all-to-sharded", segments=3, P=P), x)
+    gu = sg.shard_linear(to_dev(np.concatenate([inp.Wg, inp.Wu]), "bf16"), "all-to-sharded", segments=2, P=P)
+    dn = sg.shard_linear(to_dev(inp.Wd, "bf16"), "sharded-to-all", P=P)
+    h = sg.all_to_sharded(gu, x, swiglu=True)
+    y = sg.sharded_to_all(dn, h)
+    idx = np.array([0, 1, 255, 256, 1000, 2047, 3333, 4095])
+    Xs = oracle.decode(inp.X[idx], "bf16")
+    Wg, Wu, Wd, Wq = (oracle.decode(a, "bf16") for a in (inp.Wg, inp.Wu, inp.Wd, wqkv))
+    assert_close(qkv[:, idx, :], oracle.col(Xs, Wq, P=P, S=3), "bf16", "qkv")
+    g, u = oracle.col(Xs, Wg, P=P), oracle.col(Xs, Wu, P=P)
+    assert_close(h[:, idx, :], oracle.swiglu(g, u, "f64"), "bf16", "h")
+    assert_close(y[idx], oracle.row(oracle.swiglu(g, u, "bf16"), Wd, P=P), "bf16", "y")
+
+
+@pytest.fixture(scope="module")
+def q4_weights():
+    return synth.q4_mlp_weights(4096, 14336, seed=20)
+
+
+@pytest.mark.parametrize("B", [1, 8, 32])
+def test_q4_mlp_full(q4_weights, B):
+    """4-bit affine MLP, D=4096, F=14336, P=4 (sampled tokens at B=32)."""
+    _case(f"4-bit MLP B={B}")
+    D, F, P = 4096, 14336, 4
+    q = q4_weights
+
+    def t32(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int32)).to(dev())
+
+    def t16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev())
+
+    gu = sg.shard_quantized_linear(t32(np.concatenate([q["gate"][0], q["up"][0]])),
+                                   t16(np.concatenate([q["gate"][1], q["up"][1]])),
+                                   t16(np.concatenate([q["gate"][2], q["up"][2]])), D, "all-to-sharded",
+                                   segments=2, P=P)
+    dn = sg.shard_quantized_linear(t32(q["down"][0]), t16(q["down"][1]), t16(q["down"][2]), F, "sharded-to-all", P=P)
+    X = synth.normal(0, (B, D), 1.0, "bf16")
+    h = sg.all_to_sharded(gu, to_dev(X, "bf16"), swiglu=True)
+    y = sg.sharded_to_all(dn, h)
+    idx = np.arange(B) if B <= 8 else np.array([0, 5, 16, 31])
+    W = {k: oracle.deq4(*q[k][:3], 64) for k in ("gate", "up", "down")}
+    Xs = oracle.decode(X[idx], "bf16")
+    g, u = oracle.col(Xs, W["gate"], P=P), oracle.col(Xs, W["up"], P=P)
+    assert_close(h[:, idx, :], oracle.swiglu(g, u, "f64"), "bf16", "h")
+    assert_close(y[idx], oracle.row(oracle.swiglu(g, u, "bf16"), W["down"], P=P), "bf16", "y")
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_summa_full_sampled(fused):
+    """Y = X A, 8192^3 bf16, q = 4, fp32 Y: 8 sampled rows (two per block row)."""
+    _case(f"SUMMA 8192 q=4 fused={fused}")
+    n, q = 8192, 4
+    Xh, Ah = synth.summa_inputs(n, seed=30)
+    Y = sg.summa_matmul(to_dev(Xh, "bf16"), to_dev(Ah, "bf16"), q, fused=fused)
+    idx = np.array([0, 2047, 2048, 4000, 4096, 6143, 6144, 8191])
+    ref = oracle.summa(oracle.decode(Xh[idx], "bf16"), oracle.decode(Ah, "bf16"), q)
+    assert_close(Y[idx], ref, "f32", "summa")
+
+
+def test_vocab_head_full_sampled():
+    """fp16 vocabulary head, 32 x 12288 against 50272 x 12288, P = 8 ranks of
+    6284 rows, gathered logits: 3 sampled tokens, every vocabulary entry."""
+    _case("vocab head B=32 H=12288 V=50272 P=8")
+    B, H, V, P = 32, 12288, 50272, 8
+    Xh, Wh = synth.vocab_head_inputs(B, H, V, seed=40)
+    layer = sg.shard_linear(to_dev(Wh, "f16"), "all-to-sharded", P=P)
+    logits = sg.all_to_sharded(layer, to_dev(Xh, "f16"), gather=True)
+    assert tuple(logits.shape) == (B, V)
+    idx = np.array([0, 17, 31])
+    ref = oracle.col(oracle.decode(Xh[idx], "f16"), oracle.decode(Wh, "f16"), P=P, gather=True)
+    assert_close(logits[idx], ref, "f16", "logits")
+    # the gathered columns of rank r are rank r's sharded output
+    sharded = sg.all_to_sharded(layer, to_dev(Xh, "f16"))
+    for r in (0, 7):
+        assert torch.equal(sharded[r], logits[:, r * (V // P):(r + 1) * (V // P)])
