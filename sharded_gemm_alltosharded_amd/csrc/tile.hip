@@ -378,11 +378,12 @@ static hipError_t launch_mode(const Problem& p, hipStream_t s) {
 }
 
 hipError_t launch_tile_dma(const Problem& p, hipStream_t s);
+bool tile_dma_fits(const Problem& p);
 
 hipError_t launch_tile(const Problem& p, hipStream_t s, int variant) {
     if (p.M == 0 || p.N == 0) return hipSuccess;
     // 256 x 256 weight tiles: the direct-to-LDS pipeline (tile_dma.hip)
-    if (variant == 0 && !p.nn && !p.split && p.Kseg % 32 == 0) return launch_tile_dma(p, s);
+    if (variant == 0 && tile_dma_fits(p)) return launch_tile_dma(p, s);
     const bool f16 = p.dtype == SG_F16;
     if (variant == 0) return f16 ? launch_mode<256, 256, true>(p, s) : launch_mode<256, 256, false>(p, s);
     return f16 ? launch_mode<128, 128, true>(p, s) : launch_mode<128, 128, false>(p, s);

@@ -1,22 +1,42 @@
-// MFMA tile GEMM for gfx950 with direct global -> LDS loads (prefill-shaped
-// sharded GEMMs).  Same product and epilogues as tile.hip's NT / SWIGLU modes;
-// what differs is the feed:
+// MFMA tile GEMM for gfx950 fed by direct global -> LDS loads (the
+// prefill-shaped sharded GEMMs: many tokens against a rank's weight rows).
+// Same product and epilogues as tile.hip's NT / SWIGLU modes; 256 x 256 output
+// tiles (SwiGLU: 256 tokens x 128 outputs from 256 interleaved gate/up rows),
+// BK = 32, 512 threads.
 //
-//  * global_load_lds_dwordx4: each lane's 16 bytes go straight from memory to
-//    LDS slot (M0 + 16 lane) with no staging registers and no ds_write, so the
-//    LDS can hold a 4-stage pipeline (BK = 32, 32 KB per stage): three k tiles
-//    are in flight while the MFMAs consume the fourth, which covers the global
-//    latency a single register-staged prefetch could not.
-//  * each wave-wide load fills 16 tile rows x 64 bytes; a lane picks its
-//    global chunk so that the row's four 16-byte chunks land XOR-swizzled by
-//    (row >> 1) & 3, which keeps the MFMA fragment reads conflict-free.  With
-//    fragment-major weights those 16 rows x 64 bytes are one contiguous 1 KB.
-//  * the k loop is unrolled over the 4 stages so every LDS buffer is a
-//    distinct array (the waits before a stage's reads then cover only that
-//    stage's loads); one barrier per k tile.
+// Schedule (ping-pong).  The 8 waves form two groups of four, waves 0-3 and
+// 4-7, so every SIMD hosts one wave of each.  Time runs in phases separated by
+// workgroup barriers.  In a memory phase a wave reads the 12 MFMA operand
+// fragments of one k tile from LDS into registers and then issues its share of
+// the global -> LDS loads of the k tile three ahead; in a compute phase it
+// runs the 16 MFMAs of the k tile it read (a 128 x 64 block of the tile).
+// Group 0 works on k tile t in phases 2t (memory) and 2t + 1 (compute), group 1
+// one phase later, so on each SIMD one wave feeds the matrix unit while the
+// other waits on memory.  Measured on MI355X, the alternatives lose:
+//  * one group with both roles per wave (one barrier per k tile) exposes the
+//    LDS latency after every barrier on all waves at once;
+//  * issuing the global -> LDS loads from a wave that is running MFMAs, even
+//    one at a time between them, stalls that wave for ~150 cycles per load:
+//    the loads stay in the memory phase, after the fragment reads.
 //
-// Rows past M or N read a clamped valid row (their outputs are never
-// stored); K must be a multiple of 32.
+// Loads.  buffer_load_dwordx4 ... lds puts each lane's 16 bytes straight into
+// LDS slot (M0 + 16 lane), so the LDS holds 4 stages of 32 KB.  The operands
+// are addressed through buffer resources: the per-lane byte offset is computed
+// once and stays in one VGPR, the k advance is a scalar offset.  (With 64-bit
+// per-lane addresses the compiler reuses those registers for the fragments
+// read next, and such a write stalls the wave until the queued load has read
+// its address.)  Offsets past a resource's range read zeros.
+//
+// LDS layout.  A wave-wide load fills 16 tile rows x 64 bytes (with
+// fragment-major weights one contiguous 1 KB); the lane that owns LDS chunk c
+// of row r fetches global chunk c ^ ((r >> 2) & 3).  A ds_read_b128 is served
+// 16 lanes (16 rows) per 256 bytes, four 64-byte rows wide: row & 3 selects the
+// quarter and the swizzle gives each row >> 2 its own chunk, so the fragment
+// reads are conflict-free (swizzling by (r >> 1) & 3 measured at half rate).
+//
+// Rows past M or N read a clamped valid row (their outputs are never stored).
+// Requirements (tile_dma_fits): NT or SwiGLU weights, K a multiple of 32, no
+// split, operand extents below 2 GiB.
 #include "internal.h"
 
 namespace sg {
@@ -40,11 +60,21 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ int swz4(int row) { return (row >> 1) & 3; }
+__device__ __forceinline__ int swz4(int row) { return (row >> 2) & 3; }
 
-__device__ __forceinline__ void dma16(const uint16_t* g, uint16_t* lds) {
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                     (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+// one wave-wide 16-byte-per-lane load into LDS (dest + 16 lane)
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint16_t* lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+
+// byte extents of the operands (A: rows x segments; W: the rows the tiles address)
+__host__ __device__ inline int64_t a_extent(const Problem& p) {
+    return ((int64_t)(p.nseg - 1) * p.a_seg + (int64_t)(p.M - 1) * p.lda + p.Kseg) * 2;
+}
+__host__ __device__ inline int64_t w_extent(const Problem& p) {
+    const int64_t rows = p.swiglu ? 2 * (int64_t)p.N : p.N;
+    const int64_t seg = p.wfrag ? rows * p.Kseg : (rows - 1) * p.ldw + p.Kseg;
+    return ((int64_t)(p.nseg - 1) * p.w_seg + seg) * 2;
 }
 
 // LDS fragment read issued as inline assembly: the compiler's wait insertion
@@ -58,14 +88,10 @@ __device__ __forceinline__ u32x4 lds_read16(const uint16_t* p) {
     return r;
 }
 
-template <int NWF, int NXF>
-__device__ __forceinline__ void wait_lds(u32x4 (&w)[NWF], u32x4 (&x)[NXF]) {
-    static_assert(NXF == 4 && (NWF == 4 || NWF == 2), "fragments of one k step");
-    if constexpr (NWF == 4)
-        asm volatile("s_waitcnt lgkmcnt(0)"
-                     : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]), "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]));
-    else
-        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(w[0]), "+v"(w[1]), "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]));
+// wait for every outstanding LDS read; ties the six fragments of one k step so
+// that no use of them is scheduled before the wait
+__device__ __forceinline__ void wait_lds(u32x4 (&w)[2], u32x4 (&x)[4]) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(w[0]), "+v"(w[1]), "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]));
 }
 
 // s_waitcnt vmcnt(n) (n <= 63), other counters untouched
@@ -110,42 +136,49 @@ __device__ __forceinline__ void store4(const Problem& p, int m, int64_t n, float
 
 }  // namespace
 
-template <bool F16, bool SWIGLU, int NW>
-__global__ __launch_bounds__(NW * 64) void tile_dma_kernel(Problem p, int tiles_m, int tiles_n) {
-    constexpr int BM = 256, BN = 256, BK = 32;
-    // NW = 4: 2 x 2 waves of 128 x 128; NW = 8: 2 x 4 waves of 128 x 64 (two
-    // waves per SIMD, so one wave's barrier or LDS wait overlaps the other's MFMAs)
-    constexpr int WN = NW / 2;
-    constexpr int WTM = BM / 2, WTN = BN / WN, NBM = WTM / 32, NBN = WTN / 32;
-    constexpr int LPT = 1024 / (NW * 64);  // 16-byte loads per thread per operand and stage
+// Buffers and waits of the ping-pong loop:
+//  * k tile t lives in LDS stage t mod 4.  Its loads are issued at the end of
+//    the memory phases of k tile t - 3 (each group its rows), into the stage
+//    of k tile t - 1, whose last reader (group 1, phase 2t - 3) finished its
+//    reads before the barrier that ends that phase.
+//  * before each barrier that starts an even phase 2t, every wave waits until
+//    its own loads of k tile t have landed (those of the two later k tiles may
+//    stay in flight); the barrier then publishes k tile t to all waves.
+//  * every wave passes the same 2 nkt + 2 barriers.
+template <bool F16, bool SWIGLU>
+__global__ __launch_bounds__(512) void tile_pp_kernel(Problem p, int tiles_m, int tiles_n) {
+    constexpr int BM = 256, BN = 256, BK = 32, NW = 8, NS = 4;
+    constexpr int WTM = 128, WTN = 64, NBM = WTM / 32, NBN = WTN / 32;
+    constexpr int LPT = 2;  // loads per thread per operand and k tile
     constexpr int NOUT = SWIGLU ? BN / 2 : BN;
-    constexpr int TILE = BM * BK;  // elements of one operand stage (16 KB)
-    __shared__ __attribute__((aligned(1024))) uint16_t sA0[TILE], sA1[TILE], sA2[TILE], sA3[TILE];
-    __shared__ __attribute__((aligned(1024))) uint16_t sB0[TILE], sB1[TILE], sB2[TILE], sB3[TILE];
+    constexpr int TILE = BM * BK;
+    __shared__ __attribute__((aligned(1024))) uint16_t sA[NS * TILE], sB[NS * TILE];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wave_m = wave / WN, wave_n = wave % WN;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
+    const int group = wave >> 2;
+    const int wave_m = wave & 1, wave_n = wave >> 1;
 
     const int ntiles = tiles_m * tiles_n;
     const int tile = xcd_remap(blockIdx.x, ntiles);
     constexpr int GM = 4;
-    const int group = tile / (GM * tiles_n);
-    const int first_m = group * GM;
+    const int gidx = tile / (GM * tiles_n);
+    const int first_m = gidx * GM;
     const int gsz = min(GM, tiles_m - first_m);
-    const int tin = tile - group * GM * tiles_n;
+    const int tin = tile - gidx * GM * tiles_n;
     const int m0 = (first_m + tin % gsz) * BM;
     const int64_t n0 = (int64_t)(tin / gsz) * NOUT;
 
-    // ---- load descriptors: instruction i of this wave fills tile rows
-    // (NW i + wave) * 16 .. +16; lane -> (row lr, LDS chunk lc)
+    // load descriptors: load i of wave w fills tile rows (8 i + w) * 16 .. +16;
+    // lane -> (row lr, LDS chunk lc); byte offsets from the operand base
     const int lr = lane >> 2, lc = lane & 3;
-    int64_t aoff[LPT], boff[LPT];
+    uint32_t aoff[LPT], boff[LPT];
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
         const int row = (NW * i + wave) * 16 + lr;
         const int ch = lc ^ swz4(row);
         const int m = min(m0 + row, p.M - 1);
-        aoff[i] = (int64_t)m * p.lda + ch * 8;
+        aoff[i] = (uint32_t)(((int64_t)m * p.lda + ch * 8) * 2);
         int64_t wrow;
         if constexpr (SWIGLU) {
             const int64_t j = min(n0 + (row >> 6) * 32 + (row & 31), (int64_t)p.N - 1);
@@ -153,24 +186,34 @@ __global__ __launch_bounds__(NW * 64) void tile_dma_kernel(Problem p, int tiles_
         } else {
             wrow = min(n0 + row, (int64_t)p.N - 1);
         }
-        boff[i] = p.wfrag ? frag_offset(wrow, ch * 8, p.Kseg / 32) : wrow * p.ldw + ch * 8;
+        boff[i] = (uint32_t)((p.wfrag ? frag_offset(wrow, ch * 8, p.Kseg / 32) : wrow * p.ldw + ch * 8) * 2);
     }
     const int bk_step = p.wfrag ? 16 : 1;  // elements of W per element of k
-    const uint16_t* Ag = (const uint16_t*)p.A;
-    const uint16_t* Wg = (const uint16_t*)p.W;
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)p.A, 0, (int)a_extent(p), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)p.W, 0, (int)w_extent(p), 0x00020000);
     const int ktiles_seg = p.Kseg / BK;
     const int nkt = ktiles_seg * p.nseg;
 
-    auto issue = [&](int kt, uint16_t* a, uint16_t* b) {
+    auto issue = [&](int kt) {
         const int s = kt / ktiles_seg;
         const int k0 = (kt - s * ktiles_seg) * BK;
-        const uint16_t* Ab = Ag + s * p.a_seg + k0;
-        const uint16_t* Wb = Wg + s * p.w_seg + (int64_t)k0 * bk_step;
+        const uint32_t sa = (uint32_t)((s * p.a_seg + k0) * 2);
+        const uint32_t sw = (uint32_t)((s * p.w_seg + (int64_t)k0 * bk_step) * 2);
+        uint16_t* a = sA + (kt % NS) * TILE;
+        uint16_t* b = sB + (kt % NS) * TILE;
 #pragma unroll
         for (int i = 0; i < LPT; ++i) {
-            dma16(Ab + aoff[i], a + (NW * i + wave) * 16 * BK);
-            dma16(Wb + boff[i], b + (NW * i + wave) * 16 * BK);
+            dma16(ra, aoff[i], sa, a + (NW * i + wave) * 16 * BK);
+            dma16(rw, boff[i], sw, b + (NW * i + wave) * 16 * BK);
         }
+    };
+    // wait until this wave's loads of k tile t have landed; it has issued
+    // those of every k tile up to min(t + 2, nkt - 1)
+    auto wait_tile = [&](int t) {
+        const int later = min(t + 2, nkt - 1) - t;
+        if (later >= 2) wait_vm<4 * LPT>();
+        else if (later == 1) wait_vm<2 * LPT>();
+        else wait_vm<0>();
     };
 
     f32x16 acc[NBN][NBM];
@@ -182,55 +225,60 @@ __global__ __launch_bounds__(NW * 64) void tile_dma_kernel(Problem p, int tiles_
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
     const int frow = lane & 31, fch = lane >> 5;
-    auto compute = [&](const uint16_t* a, const uint16_t* b) {
+    u32x4 w0[NBN], x0[NBM], w1[NBN], x1[NBM];
+    auto read = [&](int t, int kk, u32x4 (&wf)[NBN], u32x4 (&xf)[NBM]) {
+        const uint16_t* a = sA + (t % NS) * TILE;
+        const uint16_t* b = sB + (t % NS) * TILE;
+        const int c = kk * 2 + fch;
 #pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-            const int c = kk * 2 + fch;
-            u32x4 wf[NBN], xf[NBM];
+        for (int i = 0; i < NBN; ++i) {
+            const int row = wave_n * WTN + i * 32 + frow;
+            wf[i] = lds_read16(b + row * BK + ((c ^ swz4(row)) << 3));
+        }
 #pragma unroll
-            for (int i = 0; i < NBN; ++i) {
-                const int row = wave_n * WTN + i * 32 + frow;
-                wf[i] = lds_read16(b + row * BK + ((c ^ swz4(row)) << 3));
-            }
-#pragma unroll
-            for (int j = 0; j < NBM; ++j) {
-                const int row = wave_m * WTM + j * 32 + frow;
-                xf[j] = lds_read16(a + row * BK + ((c ^ swz4(row)) << 3));
-            }
-            wait_lds(wf, xf);
-#pragma unroll
-            for (int i = 0; i < NBN; ++i)
-#pragma unroll
-                for (int j = 0; j < NBM; ++j) acc[i][j] = mfma32<F16>(wf[i], xf[j], acc[i][j]);
+        for (int j = 0; j < NBM; ++j) {
+            const int row = wave_m * WTM + j * 32 + frow;
+            xf[j] = lds_read16(a + row * BK + ((c ^ swz4(row)) << 3));
         }
     };
-
-    // stage t: wait for its loads (2 LPT per thread per stage; up to two later
-    // stages may stay in flight), barrier, refill the buffer consumed in the
-    // previous iteration with stage t + 3, compute stage t.
-    auto step = [&](int t, const uint16_t* a, const uint16_t* b, uint16_t* na, uint16_t* nb) {
-        const int later = min(2, nkt - 1 - t);
-        if (later >= 2) wait_vm<4 * LPT>();
-        else if (later == 1) wait_vm<2 * LPT>();
-        else wait_vm<0>();
-        // every wave has its own loads of stage t in LDS; a plain barrier (no
-        // release fence, which would wait for the later stages too) publishes them
+    auto barrier = [] {
+        __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_barrier();
-        if (t + 3 < nkt) issue(t + 3, na, nb);
-        compute(a, b);
+        __builtin_amdgcn_sched_barrier(0);
     };
 
-    if (nkt > 0) issue(0, sA0, sB0);
-    if (nkt > 1) issue(1, sA1, sB1);
-    if (nkt > 2) issue(2, sA2, sB2);
-    for (int kt = 0; kt < nkt; kt += 4) {
-        step(kt, sA0, sB0, sA3, sB3);
-        if (kt + 1 < nkt) step(kt + 1, sA1, sB1, sA0, sB0);
-        if (kt + 2 < nkt) step(kt + 2, sA2, sB2, sA1, sB1);
-        if (kt + 3 < nkt) step(kt + 3, sA3, sB3, sA2, sB2);
+    for (int t = 0; t < NS - 1 && t < nkt; ++t) issue(t);
+    if (nkt > 0) wait_tile(0);
+    __builtin_amdgcn_s_barrier();
+    // phase 0 of group 1 is idle: one extra barrier puts it one phase behind
+    if (group == 1) __builtin_amdgcn_s_barrier();
+    for (int t = 0; t < nkt; ++t) {
+        // memory phase of k tile t: fragment reads first, then the loads of
+        // k tile t + 3 (a load queued ahead of the reads would hold them up)
+        read(t, 0, w0, x0);
+        read(t, 1, w1, x1);
+        if (t + NS - 1 < nkt) issue(t + NS - 1);
+        wait_lds(w0, x0);
+        wait_lds(w1, x1);
+        // for group 1 the next barrier starts phase 2t + 2: k tile t + 1 must land
+        if (group == 1 && t + 1 < nkt) wait_tile(t + 1);
+        barrier();
+        // compute phase of k tile t
+#pragma unroll
+        for (int i = 0; i < NBN; ++i)
+#pragma unroll
+            for (int j = 0; j < NBM; ++j) acc[i][j] = mfma32<F16>(w0[i], x0[j], acc[i][j]);
+#pragma unroll
+        for (int i = 0; i < NBN; ++i)
+#pragma unroll
+            for (int j = 0; j < NBM; ++j) acc[i][j] = mfma32<F16>(w1[i], x1[j], acc[i][j]);
+        if (group == 0 && t + 1 < nkt) wait_tile(t + 1);
+        barrier();
     }
+    if (group == 0) __builtin_amdgcn_s_barrier();
 
-    // ---- epilogue (as tile.hip)
+    // epilogue: lane l of a 32 x 32 block holds column l & 31 (token) and rows
+    // 8 blk + 4 (l >> 5) + e (weight rows) of the block
     const int hi = lane >> 5;
     static_for<0, NBN>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
@@ -244,6 +292,7 @@ __global__ __launch_bounds__(NW * 64) void tile_dma_kernel(Problem p, int tiles_
                 int64_t n;
                 float v[4];
                 if constexpr (SWIGLU) {
+                    // 32-row blocks alternate gate / up of the same 32 outputs
                     const int blk32 = wave_n * NBN + i;
                     n = n0 + (blk32 >> 1) * 32 + 8 * blk + 4 * hi;
 #pragma unroll
@@ -260,27 +309,25 @@ __global__ __launch_bounds__(NW * 64) void tile_dma_kernel(Problem p, int tiles_
     });
 }
 
-template <int NW>
-hipError_t launch_tile_dma_nw(const Problem& p, hipStream_t s) {
-    const int nout = p.swiglu ? 128 : 256;
-    const int tm = (p.M + 255) / 256, tn = (p.N + nout - 1) / nout;
-    const bool f16 = p.dtype == SG_F16;
-    const dim3 grid(tm * tn), block(NW * 64);
-    if (p.swiglu) {
-        if (f16) launch(tile_dma_kernel<true, true, NW>, grid, block, 0, s, p, tm, tn);
-        else launch(tile_dma_kernel<false, true, NW>, grid, block, 0, s, p, tm, tn);
-    } else {
-        if (f16) launch(tile_dma_kernel<true, false, NW>, grid, block, 0, s, p, tm, tn);
-        else launch(tile_dma_kernel<false, false, NW>, grid, block, 0, s, p, tm, tn);
-    }
-    return hipGetLastError();
+bool tile_dma_fits(const Problem& p) {
+    return !p.nn && !p.split && p.Kseg % 32 == 0 && a_extent(p) < (1LL << 31) && w_extent(p) < (1LL << 31);
 }
-template hipError_t launch_tile_dma_nw<4>(const Problem& p, hipStream_t s);
 
 hipError_t launch_tile_dma(const Problem& p, hipStream_t s) {
     if (p.M == 0 || p.N == 0) return hipSuccess;
-    if (p.Kseg % 32 || p.nn || p.split) return hipErrorInvalidValue;
-    return launch_tile_dma_nw<4>(p, s);
+    if (!tile_dma_fits(p)) return hipErrorInvalidValue;
+    const int nout = p.swiglu ? 128 : 256;
+    const int tm = (p.M + 255) / 256, tn = (p.N + nout - 1) / nout;
+    const bool f16 = p.dtype == SG_F16;
+    const dim3 grid(tm * tn), block(512);
+    if (p.swiglu) {
+        if (f16) launch(tile_pp_kernel<true, true>, grid, block, 0, s, p, tm, tn);
+        else launch(tile_pp_kernel<false, true>, grid, block, 0, s, p, tm, tn);
+    } else {
+        if (f16) launch(tile_pp_kernel<true, false>, grid, block, 0, s, p, tm, tn);
+        else launch(tile_pp_kernel<false, false>, grid, block, 0, s, p, tm, tn);
+    }
+    return hipGetLastError();
 }
 
 }  // namespace sg
