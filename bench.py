@@ -158,8 +158,8 @@ class PrefillMLP(Workload):
     unit = "TFLOP/s"
     bound = "mfma"
     steps, warmup = 20, 3
-    dominant = "tile_kernel 256x256 (gate|up all-to-sharded + SwiGLU)"
-    dominant_src = ("tile.hip", "internal.h")
+    dominant = "tile_pp_kernel 256x256 (gate|up all-to-sharded + SwiGLU)"
+    dominant_src = ("tile_dma.hip", "internal.h")
 
     def setup(self):
         import numpy as np
@@ -295,12 +295,12 @@ class Summa(Workload):
     unit = "TFLOP/s"
     bound = "mfma"
     steps, warmup = 20, 3
-    dominant_src = ("tile.hip", "internal.h")
+    dominant_src = ("tile_dma.hip", "internal.h")
 
     def __init__(self, fused):
         self.fused = fused
-        self.dominant = ("tile_kernel 256x256 NN (one launch, q steps in registers)" if fused
-                         else "tile_kernel 256x256 NN (q in-place step launches)")
+        self.dominant = ("tile_pp_kernel 256x256 on the A_t^T copy (one launch, q steps in registers)" if fused
+                         else "whole call: A_t^T copy + q in-place tile_pp_kernel step launches")
 
     def setup(self):
         import torch
@@ -309,6 +309,9 @@ class Summa(Workload):
         self.Xh, self.Ah = synth.summa_inputs(self.n, seed=30)
         self.X, self.A = _dev_tensor(self.Xh, "bf16"), _dev_tensor(self.Ah, "bf16")
         self.Y = torch.empty((self.n, self.n), dtype=torch.float32, device="cuda")
+        # the A_t^T copy's workspace is allocated once, as a caller that reuses it would
+        self.ws = torch.empty(sg.summa_workspace(torch.bfloat16, self.n, self.n, self.q), dtype=torch.uint8,
+                              device="cuda")
         self.sg = sg
         self.units = 2 * self.n ** 3
         self.dom_units = self.units
@@ -318,7 +321,7 @@ class Summa(Workload):
             self.sg.time_next_launch(*ev)
         elif ev:
             ev[0].record()
-        self.sg.summa_matmul(self.X, self.A, self.q, out=self.Y, fused=self.fused)
+        self.sg.summa_matmul(self.X, self.A, self.q, out=self.Y, fused=self.fused, workspace=self.ws)
         if ev and not self.fused:
             ev[1].record()
 

@@ -132,10 +132,23 @@ size_t sg_sharded_to_all_workspace(const sg_layer* layer, int64_t B);
  *   fused      0: q launches, step t adds its block products into Y in place
  *              (the step structure of the derivation); 1: one launch that keeps
  *              each block's accumulator in registers across the q steps.
+ *   workspace  device scratch of at least sg_summa_workspace(dtype, K, N, q)
+ *              bytes, or NULL.  With it, each call first writes A_t^T for every
+ *              t into the workspace in the fragment-major layout the matrix-core
+ *              kernels read (as for a linear layer's weights); without it they
+ *              read A in place, more slowly.  Contents need no initialisation;
+ *              calls that share a workspace must not run concurrently.
  * Errors: SG_ERR_NOT_DIVISIBLE when q does not divide M, K and N or q < 1
- * (P = q x q processors). */
+ * (P = q x q processors); SG_ERR_WORKSPACE when workspace is not NULL and
+ * ws_bytes is below the required size. */
 sg_status sg_summa_matmul(const void* X, const void* A, sg_dtype dtype, int64_t M, int64_t K,
-                          int64_t N, int q, float* Y, int accumulate, int fused, void* stream);
+                          int64_t N, int q, float* Y, int accumulate, int fused, void* workspace,
+                          size_t ws_bytes, void* stream);
+
+/* Bytes of workspace sg_summa_matmul can use for these sizes: K N element
+ * sizes for SG_BF16 / SG_F16 when N % 16 == 0 and (K / q) % 32 == 0, else 0
+ * (the call then reads A in place whatever workspace it is given). */
+size_t sg_summa_workspace(sg_dtype dtype, int64_t K, int64_t N, int q);
 
 /* Layer description (any output pointer may be NULL). */
 sg_status sg_layer_info(const sg_layer* layer, int64_t* out_dims, int64_t* in_dims, int* mode,

@@ -10,7 +10,7 @@ kernels.  The entry points mirror include/shardgemm.h one to one:
     shard_quantized_linear     sg_shard_quantized_linear
     all_to_sharded             sg_all_to_sharded
     sharded_to_all             sg_sharded_to_all (+ sg_sharded_to_all_workspace)
-    summa_matmul               sg_summa_matmul
+    summa_matmul               sg_summa_matmul (+ sg_summa_workspace)
     Layer.info / Layer.shard   sg_layer_info / sg_layer_copy_shard
     time_next_launch           sg_time_next_launch (profiling)
 
@@ -68,7 +68,8 @@ def lib():
             "sg_all_to_sharded": ([P, P, I64, P, I, I, I, P], I),
             "sg_sharded_to_all": ([P, P, I64, P, I, P, SZ, P], I),
             "sg_sharded_to_all_workspace": ([P, I64], SZ),
-            "sg_summa_matmul": ([P, P, I, I64, I64, I64, I, P, I, I, P], I),
+            "sg_summa_matmul": ([P, P, I, I64, I64, I64, I, P, I, I, P, SZ, P], I),
+            "sg_summa_workspace": ([I, I64, I64, I], SZ),
             "sg_layer_info": ([P, P, P, P, P, P, P, P], I),
             "sg_layer_copy_shard": ([P, I, I, P, SZ, P], I),
             "sg_layer_free": ([P], None),
@@ -242,13 +243,30 @@ def sharded_to_all(layer: Layer, x_partial: torch.Tensor, out_dtype=None, out: t
     return out
 
 
+def summa_workspace(dtype: torch.dtype, K: int, N: int, q: int) -> int:
+    """Bytes of workspace summa_matmul can use (0: it reads A in place)."""
+    return int(lib().sg_summa_workspace(_DT.get(dtype, -1), K, N, q))
+
+
 def summa_matmul(X: torch.Tensor, A: torch.Tensor, q: int, out: torch.Tensor | None = None,
-                 accumulate: bool = False, fused: bool = True) -> torch.Tensor:
-    """Y (M, N) fp32 = X A (or Y += X A) on a q x q block grid."""
+                 accumulate: bool = False, fused: bool = True, workspace="auto") -> torch.Tensor:
+    """Y (M, N) fp32 = X A (or Y += X A) on a q x q block grid.
+
+    workspace: "auto" takes summa_workspace(...) bytes from torch's caching
+    allocator for this call (stream-ordered, so the memory is reused only by
+    later work on the same stream); None makes the kernels read A in place; or
+    a uint8 device tensor of at least that size."""
     M, K = X.shape
     N = A.shape[1]
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto', None or a tensor")
+        need = summa_workspace(X.dtype, K, N, q)
+        workspace = torch.empty(need, dtype=torch.uint8, device=X.device) if need else None
+    ws_ptr = _ptr(workspace) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().sg_summa_matmul(_ptr(X), _ptr(A), _DT.get(X.dtype, -1), M, K, N, q, _ptr(out), int(accumulate),
-                                 int(fused), _stream(X.device)))
+                                 int(fused), ws_ptr, ws_bytes, _stream(X.device)))
     return out

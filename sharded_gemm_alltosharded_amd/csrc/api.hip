@@ -481,8 +481,21 @@ sg_status sg_sharded_to_all(const sg_layer* l, const void* x_partial, int64_t B,
     return SG_OK;
 }
 
+// bytes of the transposed fragment-major copy of A the MFMA path reads
+static size_t summa_ws_bytes(sg_dtype dtype, int64_t K, int64_t N, int q) {
+    if (dtype != SG_BF16 && dtype != SG_F16) return 0;
+    if (q < 1 || K <= 0 || N <= 0 || K % q || (K / q) % 32 || N % 16) return 0;
+    return (size_t)(K * N) * 2;
+}
+
+size_t sg_summa_workspace(sg_dtype dtype, int64_t K, int64_t N, int q) {
+    if (K > INT32_MAX || N > INT32_MAX) return 0;
+    return summa_ws_bytes(dtype, K, N, q);
+}
+
 sg_status sg_summa_matmul(const void* X, const void* A, sg_dtype dtype, int64_t M, int64_t K, int64_t N,
-                          int q, float* Y, int accumulate, int fused, void* stream) {
+                          int q, float* Y, int accumulate, int fused, void* workspace, size_t ws_bytes,
+                          void* stream) {
     g_err.clear();
     if (!dtype_ok(dtype)) return fail(SG_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
     if (M < 0 || K < 0 || N < 0 || M > INT32_MAX || K > INT32_MAX || N > INT32_MAX)
@@ -493,20 +506,24 @@ sg_status sg_summa_matmul(const void* X, const void* A, sg_dtype dtype, int64_t 
                     (long long)M, (long long)K, (long long)N, q);
     if (accumulate != 0 && accumulate != 1) return fail(SG_ERR_INVALID_ARG, "accumulate must be 0 or 1");
     if (fused != 0 && fused != 1) return fail(SG_ERR_INVALID_ARG, "fused must be 0 or 1");
+    const size_t need = summa_ws_bytes(dtype, K, N, q);
+    if (workspace && ws_bytes < need)
+        return fail(SG_ERR_WORKSPACE, "SUMMA workspace of %zu bytes, %zu needed", ws_bytes, need);
     if (M == 0 || N == 0) return SG_OK;
     if (!X || !A || !Y) return fail(SG_ERR_INVALID_ARG, "X, A and Y must not be NULL");
     hipStream_t hs = (hipStream_t)stream;
     const int64_t bk = K / q;
     const bool mfma = dtype != SG_F32 && N % 8 == 0 && bk % 8 == 0 && aligned16(X) && aligned16(A) && aligned16(Y);
     const Kind k = !mfma ? K_GENERIC : (M >= 512 ? K_TILE0 : K_TILE1);
+    // with a workspace the MFMA kernels read A_t^T fragment-major, as they read
+    // a linear layer's weights; without one the tile kernels read A in place
+    const bool frag = k != K_GENERIC && need > 0 && workspace && aligned16(workspace);
     const size_t esz = dtype_size(dtype);
     sg::Problem p{};
     p.M = (int)M;
     p.N = (int)N;
     p.dtype = dtype;
-    p.nn = 1;
     p.lda = K;
-    p.ldw = N;
     p.out = Y;
     p.out_dtype = SG_F32;
     p.out_map = sg::OUT_ROWMAJOR;
@@ -515,12 +532,22 @@ sg_status sg_summa_matmul(const void* X, const void* A, sg_dtype dtype, int64_t 
         if (!accumulate) HIP_TRY(hipMemsetAsync(Y, 0, (size_t)(M * N) * 4, hs), "clear Y");
         return SG_OK;
     }
+    if (frag) {
+        HIP_TRY(sg::nn_to_frag(workspace, A, K, N, q, hs), "SUMMA operand transform");
+        p.wfrag = 1;
+        p.ldw = bk;
+    } else {
+        p.nn = 1;
+        p.ldw = N;
+    }
+    // block t of the right operand: rows [t bk, (t + 1) bk) of A, or its transposed copy
+    const int64_t w_block = bk * N;
     if (fused) {
         // one launch: the K loop visits step t's panel X_it, A_tj for t = 0 .. q-1
         p.A = X;
         p.a_seg = bk;
-        p.W = A;
-        p.w_seg = bk * N;
+        p.W = frag ? workspace : A;
+        p.w_seg = w_block;
         p.Kseg = (int)bk;
         p.nseg = q;
         p.accumulate = accumulate;
@@ -531,7 +558,7 @@ sg_status sg_summa_matmul(const void* X, const void* A, sg_dtype dtype, int64_t 
     for (int t = 0; t < q; ++t) {
         // step t: every block (i, j) adds X_it A_tj into Y_ij in place
         p.A = (const char*)X + (size_t)(t * bk) * esz;
-        p.W = (const char*)A + (size_t)(t * bk * N) * esz;
+        p.W = (const char*)(frag ? workspace : A) + (size_t)(t * w_block) * esz;
         p.Kseg = (int)bk;
         p.nseg = 1;
         p.accumulate = (t > 0) || accumulate;

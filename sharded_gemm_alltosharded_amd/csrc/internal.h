@@ -109,6 +109,8 @@ hipError_t launch_skinny(const Problem& p, hipStream_t s);
 hipError_t launch_q4(const Problem& p, hipStream_t s);
 // P stacked (rows, K) 16-bit matrices: row-major -> fragment-major (forward) or back
 hipError_t frag_transform(void* dst, const void* src, int P, int64_t rows, int64_t K, int forward, hipStream_t s);
+// SUMMA's A (K, N) -> q fragment-major blocks of A_t^T (N, K / q); N % 16 == 0, (K / q) % 32 == 0
+hipError_t nn_to_frag(void* dst, const void* A, int64_t K, int64_t N, int q, hipStream_t s);
 hipError_t q4_repack(uint32_t* w, int64_t n, int forward, hipStream_t s);
 // P stacked 4-bit matrices (rows, K): codes (rows, K/8 words) and scales or
 // biases (rows, K/64), row-major <-> fragment-major

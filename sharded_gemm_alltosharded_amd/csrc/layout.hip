@@ -1,5 +1,6 @@
-// Weight layout transforms (one-time, at layer construction and shard
-// copy-out): row-major <-> fragment-major (see frag_offset in internal.h).
+// Layout transforms: row-major <-> fragment-major weights (one-time, at layer
+// construction and shard copy-out; see frag_offset in internal.h), and SUMMA's
+// (K, N) right operand into fragment-major transposed blocks (per call).
 #include "internal.h"
 
 namespace sg {
@@ -70,6 +71,42 @@ hipError_t q4_transform(uint32_t* dst_w, const uint32_t* src_w, uint16_t* dst_g,
         if (total) launch(q4_groups_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, src_g, dst_g, rows,
                           K / 64, total, forward);
     }
+    return hipGetLastError();
+}
+
+// SUMMA's A (K, N) row-major -> q fragment-major matrices B_t = A_t^T, where
+// A_t holds rows [t bk, (t + 1) bk) of A: element (n, kk) of B_t goes to
+// t N bk + frag_offset(n, kk, bk / 32).  The MFMA tile kernels then read the
+// blocks exactly like the (out, in) weights of a linear layer.  One workgroup
+// per 32 (k) x 64 (n) tile: 16-byte reads of 32 rows x 128 bytes into LDS, then
+// each thread gathers the 8 k values of one fragment lane slot and writes them
+// as 16 contiguous bytes.  Needs N % 16 == 0 and bk % 32 == 0.
+__global__ __launch_bounds__(256) void nn_frag_kernel(const uint16_t* A, uint16_t* dst, int64_t N, int64_t bk) {
+    __shared__ __attribute__((aligned(16))) uint16_t tile[32][64 + 8];
+    const int tid = threadIdx.x;
+    const int64_t n0 = (int64_t)blockIdx.x * 64, k0 = (int64_t)blockIdx.y * 32;
+    {
+        const int r = tid >> 3, c = tid & 7;
+        if (n0 + c * 8 < N) *(u32x4*)&tile[r][c * 8] = *(const u32x4*)(A + (k0 + r) * N + n0 + c * 8);
+    }
+    __syncthreads();
+    const int b = tid >> 6, l = tid & 63;
+    if (n0 + b * 16 >= N) return;
+    const int n = b * 16 + (l & 15), kq = 8 * (l >> 4);
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = tile[kq + 2 * i][n] | ((uint32_t)tile[kq + 2 * i + 1][n] << 16);
+    const int64_t t = k0 / bk, kin = k0 - t * bk;
+    const int64_t off = t * N * bk + (((n0 / 16 + b) * (bk / 32) + kin / 32) * 64 + l) * 8;
+    *(u32x4*)(dst + off) = u32x4{w[0], w[1], w[2], w[3]};
+}
+
+hipError_t nn_to_frag(void* dst, const void* A, int64_t K, int64_t N, int q, hipStream_t s) {
+    if (K == 0 || N == 0) return hipSuccess;
+    if (q < 1 || K % q || (K / q) % 32 || N % 16) return hipErrorInvalidValue;
+    // launched directly: a layout pass is never the kernel sg_time_next_launch times
+    hipLaunchKernelGGL(nn_frag_kernel, dim3((unsigned)((N + 63) / 64), (unsigned)(K / 32)), dim3(256), 0, s,
+                       (const uint16_t*)A, (uint16_t*)dst, N, K / q);
     return hipGetLastError();
 }
 

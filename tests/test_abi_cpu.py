@@ -111,13 +111,27 @@ def test_forward_calls_validate_first(L):
 
 def test_summa_rules(L):
     X = C.c_void_p(0x1000)
-    assert L.sg_summa_matmul(X, X, sg.BF16, 8, 8, 8, 0, X, 0, 1, None) == sg.ERR_NOT_DIVISIBLE  # q < 1
-    assert L.sg_summa_matmul(X, X, sg.BF16, 6, 8, 8, 4, X, 0, 1, None) == sg.ERR_NOT_DIVISIBLE
-    assert L.sg_summa_matmul(X, X, sg.BF16, 8, 6, 8, 4, X, 0, 1, None) == sg.ERR_NOT_DIVISIBLE
-    assert L.sg_summa_matmul(X, X, 7, 8, 8, 8, 2, X, 0, 1, None) == sg.ERR_INVALID_ARG
-    assert L.sg_summa_matmul(X, X, sg.BF16, 8, 8, 8, 2, X, 2, 1, None) == sg.ERR_INVALID_ARG
+    assert L.sg_summa_matmul(X, X, sg.BF16, 8, 8, 8, 0, X, 0, 1, None, 0, None) == sg.ERR_NOT_DIVISIBLE  # q < 1
+    assert L.sg_summa_matmul(X, X, sg.BF16, 6, 8, 8, 4, X, 0, 1, None, 0, None) == sg.ERR_NOT_DIVISIBLE
+    assert L.sg_summa_matmul(X, X, sg.BF16, 8, 6, 8, 4, X, 0, 1, None, 0, None) == sg.ERR_NOT_DIVISIBLE
+    assert L.sg_summa_matmul(X, X, 7, 8, 8, 8, 2, X, 0, 1, None, 0, None) == sg.ERR_INVALID_ARG
+    assert L.sg_summa_matmul(X, X, sg.BF16, 8, 8, 8, 2, X, 2, 1, None, 0, None) == sg.ERR_INVALID_ARG
     # empty output: nothing to do, no device work
-    assert L.sg_summa_matmul(None, None, sg.BF16, 0, 8, 8, 2, None, 0, 1, None) == sg.OK
+    assert L.sg_summa_matmul(None, None, sg.BF16, 0, 8, 8, 2, None, 0, 1, None, 0, None) == sg.OK
+    # a workspace below the required size is rejected before any device work
+    assert L.sg_summa_matmul(None, None, sg.BF16, 0, 64, 16, 2, None, 0, 1, X, 100, None) == sg.ERR_WORKSPACE
+
+
+def test_summa_workspace_sizes(L):
+    # the transposed fragment-major copy of A: K N 16-bit elements
+    assert L.sg_summa_workspace(sg.BF16, 8192, 8192, 4) == 8192 * 8192 * 2
+    assert L.sg_summa_workspace(sg.F16, 64, 48, 2) == 64 * 48 * 2
+    # no copy where the fragment layout does not apply
+    assert L.sg_summa_workspace(sg.F32, 64, 64, 2) == 0       # no fp32 MFMA path
+    assert L.sg_summa_workspace(sg.BF16, 64, 40, 2) == 0      # N % 16
+    assert L.sg_summa_workspace(sg.BF16, 96, 64, 2) == 0      # K / q = 48, not a multiple of 32
+    assert L.sg_summa_workspace(sg.BF16, 64, 64, 3) == 0      # q does not divide K
+    assert L.sg_summa_workspace(sg.BF16, 64, 64, 0) == 0
 
 
 def test_binding_maps_sharding_names():

@@ -239,23 +239,37 @@ def test_q4_swiglu_and_row(B):
 # SUMMA
 # ---------------------------------------------------------------------------
 SUMMA_CASES = [("bf16", 256, 256, 256, 2), ("bf16", 512, 384, 768, 4), ("f16", 320, 512, 256, 1),
-               ("bf16", 1024, 512, 512, 4), ("bf16", 96, 64, 48, 2), ("bf16", 12, 6, 10, 2)]
+               ("bf16", 1024, 512, 512, 4), ("bf16", 600, 256, 272, 2), ("bf16", 96, 64, 48, 2),
+               ("bf16", 12, 6, 10, 2)]
 
 
+@pytest.mark.parametrize("ws", ["auto", None], ids=["transposed-copy", "in-place"])
 @pytest.mark.parametrize("fused", [True, False])
 @pytest.mark.parametrize("case", SUMMA_CASES, ids=lambda c: "-".join(map(str, c)))
-def test_summa(case, fused):
+def test_summa(case, fused, ws):
+    """Both operand paths: A copied to fragment-major A_t^T blocks in a
+    workspace (where the sizes allow), or read in place."""
     dtype, M, K, N, q = case
-    _print_case(dtype=dtype, M=M, K=K, N=N, q=q, fused=fused)
+    _print_case(dtype=dtype, M=M, K=K, N=N, q=q, fused=fused, ws=ws)
     X = synth.normal(21, (M, K), K ** -0.25, dtype)
     A = synth.normal(22, (K, N), K ** -0.25, dtype)
     ref = oracle.summa(X, A, q, dtype=dtype)
-    y = sg.summa_matmul(to_dev(X, dtype), to_dev(A, dtype), q, fused=fused)
+    y = sg.summa_matmul(to_dev(X, dtype), to_dev(A, dtype), q, fused=fused, workspace=ws)
     assert_close(y, ref, "f32", "summa")
     C0 = synth.normal(23, (M, N), 1.0, "f32")
     yc = to_dev(C0, "f32")
-    sg.summa_matmul(to_dev(X, dtype), to_dev(A, dtype), q, out=yc, accumulate=True, fused=fused)
+    sg.summa_matmul(to_dev(X, dtype), to_dev(A, dtype), q, out=yc, accumulate=True, fused=fused, workspace=ws)
     assert_close(yc, ref + C0.astype(np.float64), "f32", "summa accumulate")
+
+
+def test_summa_workspace_reuse():
+    """One workspace tensor serves calls of different shapes (no initialisation needed)."""
+    ws = torch.full((sg.summa_workspace(torch.bfloat16, 512, 768, 4),), 0x7f, dtype=torch.uint8, device=dev())
+    for (M, K, N, q) in ((512, 512, 768, 4), (256, 256, 256, 2)):
+        X = synth.normal(31, (M, K), K ** -0.25, "bf16")
+        A = synth.normal(32, (K, N), K ** -0.25, "bf16")
+        y = sg.summa_matmul(to_dev(X, "bf16"), to_dev(A, "bf16"), q, workspace=ws)
+        assert_close(y, oracle.summa(X, A, q, dtype="bf16"), "f32", "summa")
 
 
 # ---------------------------------------------------------------------------
@@ -281,8 +295,9 @@ def test_integer_exact_summa():
     X = synth.small_ints(26, (512, 512), -2, 2, "bf16")
     A = synth.small_ints(27, (512, 256), -2, 2, "bf16")
     for fused in (True, False):
-        y = sg.summa_matmul(to_dev(X, "bf16"), to_dev(A, "bf16"), 4, fused=fused)
-        np.testing.assert_array_equal(to_np(y), oracle.summa(X, A, 4, dtype="bf16"))
+        for ws in ("auto", None):
+            y = sg.summa_matmul(to_dev(X, "bf16"), to_dev(A, "bf16"), 4, fused=fused, workspace=ws)
+            np.testing.assert_array_equal(to_np(y), oracle.summa(X, A, 4, dtype="bf16"))
 
 
 @pytest.mark.parametrize("B", [1, 8, 32])
