@@ -567,7 +567,8 @@ def main():
     value = wl.units / (ms / 1e3) / scale
     achieved = wl.dom_units / (dom_ms / 1e3) / scale
     peak = HBM_PEAK_GBS if wl.bound == "hbm" else MFMA_PEAK_TFLOPS[wl.dtype]
-    tag = wl.name + (f"-b{wl.B}" if isinstance(wl, Q4MLP) else "")
+    tag = wl.name + (f"-b{wl.B}" if isinstance(wl, Q4MLP) else "") + (
+        "-steps" if isinstance(wl, Summa) and not wl.fused else "")
     traffic = load_traffic(wl, tag)
     roofline = {"bound": wl.bound, "achieved": round(achieved, 2), "peak": peak, "unit": wl.unit,
                 "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": wl.dominant,
