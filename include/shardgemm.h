@@ -51,6 +51,9 @@ typedef enum {
 typedef enum { SG_ALL_TO_SHARDED = 0, SG_SHARDED_TO_ALL = 1 } sg_mode;
 typedef enum { SG_F32 = 0, SG_BF16 = 1, SG_F16 = 2 } sg_dtype;
 typedef enum { SG_EPI_NONE = 0, SG_EPI_SWIGLU = 1 } sg_epilogue;
+/* activation layouts across ranks ([HSYM] Cases 1-3) */
+typedef enum { SG_IN_FULL = 0, SG_IN_SHARDED = 1 } sg_in_layout;   /* (B, in) | (P, B, in/P) */
+typedef enum { SG_OUT_FULL = 0, SG_OUT_SHARDED = 1 } sg_out_layout; /* (B, n) | (P, B, n/P) */
 
 typedef struct sg_layer sg_layer; /* opaque, owned by the library */
 
@@ -106,6 +109,20 @@ sg_status sg_shard_quantized_linear(const uint32_t* wq, const uint16_t* scales,
 sg_status sg_all_to_sharded(const sg_layer* layer, const void* x, int64_t B, void* y, int gather,
                             int epilogue, sg_dtype y_dtype, void* stream);
 
+/* All-to-sharded forward with explicit activation layouts ([HSYM] Cases 1 and 2).
+ *   in_layout  SG_IN_FULL: x (B, in_dims), replicated to every rank (Case 1).
+ *              SG_IN_SHARDED: x (P, B, in_dims/P), slice r holding columns
+ *              [r in/P, (r+1) in/P) of the activation; every rank all-gathers it
+ *              before its matmul (Case 2), which here is the K loop walking the P
+ *              slices in order.  Dense layers only (SG_ERR_UNSUPPORTED for 4-bit
+ *              layers, and for fragment-stored weights when (in_dims/P) % 32 != 0);
+ *              SG_ERR_NOT_DIVISIBLE when P does not divide in_dims.
+ *   out_layout SG_OUT_SHARDED: y (P, B, n_out/P) (gather = 0 of sg_all_to_sharded);
+ *              SG_OUT_FULL: y (B, n_out), the rank-order all-gather (gather = 1).
+ * Everything else as sg_all_to_sharded. */
+sg_status sg_all_to_sharded_ex(const sg_layer* layer, const void* x, int in_layout, int64_t B, void* y,
+                               int out_layout, int epilogue, sg_dtype y_dtype, void* stream);
+
 /* Sharded-to-all forward ([MLX] 2.2; [HSYM] Case 3 with AllReduce).
  *   x_partial (P, B, in_dims/P) of the layer's dtype; slice r is rank r's
  *            input (columns r of the full activation under the layer's
@@ -120,6 +137,16 @@ sg_status sg_all_to_sharded(const sg_layer* layer, const void* x, int64_t B, voi
  *            concurrently. */
 sg_status sg_sharded_to_all(const sg_layer* layer, const void* x_partial, int64_t B, void* y,
                             sg_dtype y_dtype, void* workspace, size_t ws_bytes, void* stream);
+
+/* Sharded-to-all forward with an explicit output layout ([HSYM] Case 3).
+ *   out_layout SG_OUT_FULL: y (B, out_dims), the all-reduce (= sg_sharded_to_all).
+ *              SG_OUT_SHARDED: y (P, B, out_dims/P), the reduce-scatter: slice r
+ *              holds columns [r out/P, (r+1) out/P) of the same rank-order sum
+ *              (+ bias once); SG_ERR_NOT_DIVISIBLE when P does not divide out_dims.
+ * Everything else, the workspace included, as sg_sharded_to_all. */
+sg_status sg_sharded_to_all_ex(const sg_layer* layer, const void* x_partial, int64_t B, void* y,
+                               int out_layout, sg_dtype y_dtype, void* workspace, size_t ws_bytes,
+                               void* stream);
 
 /* Bytes of workspace sg_sharded_to_all needs for B tokens (0 on bad input). */
 size_t sg_sharded_to_all_workspace(const sg_layer* layer, int64_t B);

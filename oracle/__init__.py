@@ -18,6 +18,9 @@ row         sharded-to-all linear: partials, rank-order sum, bias   brute force,
 deq4        4-bit affine dequantisation                             hand-packed words, round trip
 summa       q-step block accumulation Y_ij += X_it A_tj             brute force, q-independence
 mlp         col(gate), col(up) -> swiglu -> row(down)               composition of the above
+all_gather  input shards (P, B, k) -> (B, P k), rank order          index arrays, brute force
+reduce_     summed (B, n) result -> (P, B, n/P), rank r's columns   index arrays, brute force
+ scatter
 ==========  =====================================================  ============================
 
 Every function accepts stored arrays (float32, float64, or uint16 bit
@@ -210,6 +213,35 @@ def mlp(X, Wg, Wu, Wd, P, round_dtype="bf16", dtype=None) -> np.ndarray:
     Y = np.empty((B, D), dtype=np.float64)
     _check(lib().or_mlp(_p(X), B, D, F, _p(Wg), _p(Wu), _p(Wd), P, _DT[round_dtype], _p(Y)), "mlp")
     return Y
+
+
+def all_gather(Xs) -> np.ndarray:
+    """AllGather of activation shards ("Sharded Matrices and How to Multiply
+    Them", Case 2 and the collective-primitive table: AllGather_X(A[I, J_X])
+    -> A[I, J]): Xs (P, B, k), shard r holding feature columns [r k, (r+1) k),
+    -> (B, P k).  A pure copy, so stored bit patterns pass through unchanged."""
+    Xs = np.asarray(Xs)
+    P, B, k = Xs.shape
+    out = np.empty((B, P * k), dtype=Xs.dtype)
+    for r in range(P):
+        out[:, r * k:(r + 1) * k] = Xs[r]
+    return out
+
+
+def reduce_scatter(Y, P) -> np.ndarray:
+    """ReduceScatter of the summed result (same page, Case 3 and the primitive
+    table: ReduceScatter_{X,K}(C[I, K]{U_X}) -> C[I, K_X]): the reduction is
+    done by ``row``; this hands rank r the output columns [r n/P, (r+1) n/P)
+    as slice r of (P, B, n/P)."""
+    Y = np.asarray(Y)
+    B, n = Y.shape
+    if n % P:
+        raise OracleError(3, "reduce_scatter")
+    k = n // P
+    out = np.empty((P, B, k), dtype=Y.dtype)
+    for r in range(P):
+        out[r] = Y[:, r * k:(r + 1) * k]
+    return out
 
 
 # ---------------------------------------------------------------------------

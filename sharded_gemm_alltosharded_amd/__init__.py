@@ -8,8 +8,9 @@ kernels.  The entry points mirror include/shardgemm.h one to one:
 
     shard_linear               sg_shard_linear
     shard_quantized_linear     sg_shard_quantized_linear
-    all_to_sharded             sg_all_to_sharded
-    sharded_to_all             sg_sharded_to_all (+ sg_sharded_to_all_workspace)
+    all_to_sharded             sg_all_to_sharded_ex (sg_all_to_sharded's layouts + a sharded input)
+    sharded_to_all             sg_sharded_to_all_ex (+ sg_sharded_to_all_workspace; all-reduce or
+                               reduce-scatter output)
     summa_matmul               sg_summa_matmul (+ sg_summa_workspace)
     Layer.info / Layer.shard   sg_layer_info / sg_layer_copy_shard
     time_next_launch           sg_time_next_launch (profiling)
@@ -28,6 +29,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libshardgemm.so")
 
 ALL_TO_SHARDED, SHARDED_TO_ALL = 0, 1
+IN_FULL, IN_SHARDED = 0, 1
+OUT_FULL, OUT_SHARDED = 0, 1
 _MODES = {"all-to-sharded": ALL_TO_SHARDED, "sharded-to-all": SHARDED_TO_ALL}
 F32, BF16, F16 = 0, 1, 2
 _DT = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
@@ -66,7 +69,9 @@ def lib():
             "sg_shard_linear": ([P, I, I64, I64, P, I, I, I, P, PP], I),
             "sg_shard_quantized_linear": ([P, P, P, I64, I64, I, I, I, P, I, I, I, P, PP], I),
             "sg_all_to_sharded": ([P, P, I64, P, I, I, I, P], I),
+            "sg_all_to_sharded_ex": ([P, P, I, I64, P, I, I, I, P], I),
             "sg_sharded_to_all": ([P, P, I64, P, I, P, SZ, P], I),
+            "sg_sharded_to_all_ex": ([P, P, I64, P, I, I, P, SZ, P], I),
             "sg_sharded_to_all_workspace": ([P, I64], SZ),
             "sg_summa_matmul": ([P, P, I, I64, I64, I64, I, P, I, I, P, SZ, P], I),
             "sg_summa_workspace": ([I, I64, I64, I], SZ),
@@ -196,17 +201,19 @@ def shard_quantized_linear(wq: torch.Tensor, scales: torch.Tensor, qbiases: torc
 
 
 def all_to_sharded(layer: Layer, x: torch.Tensor, gather: bool = False, swiglu: bool = False,
-                   out_dtype=None, out: torch.Tensor | None = None) -> torch.Tensor:
+                   out_dtype=None, out: torch.Tensor | None = None, x_sharded: bool = False) -> torch.Tensor:
     """x (B, in) -> (P, B, n/P) sharded, or (B, n) gathered; n = out_dims, or
-    out_dims/2 with the fused SwiGLU epilogue."""
-    B = x.shape[0]
+    out_dims/2 with the fused SwiGLU epilogue.  x_sharded: x is (P, B, in/P),
+    all-gathered inside the matmul."""
+    B = x.shape[1] if x_sharded else x.shape[0]
     n = layer.out_dims // 2 if swiglu else layer.out_dims
     out_dtype = out_dtype or layer.dtype
     if out is None:
         shape = (B, n) if gather else (layer.P, B, n // layer.P)
         out = torch.empty(shape, dtype=out_dtype, device=x.device)
-    _check(lib().sg_all_to_sharded(layer.handle, _ptr(x), B, _ptr(out), int(gather),
-                                   EPI_SWIGLU if swiglu else EPI_NONE, _DT.get(out.dtype, -1), _stream(x.device)))
+    _check(lib().sg_all_to_sharded_ex(layer.handle, _ptr(x), IN_SHARDED if x_sharded else IN_FULL, B, _ptr(out),
+                                      OUT_FULL if gather else OUT_SHARDED, EPI_SWIGLU if swiglu else EPI_NONE,
+                                      _DT.get(out.dtype, -1), _stream(x.device)))
     return out
 
 
@@ -228,18 +235,19 @@ def workspace(layer: Layer, B: int, device) -> torch.Tensor | None:
 
 
 def sharded_to_all(layer: Layer, x_partial: torch.Tensor, out_dtype=None, out: torch.Tensor | None = None,
-                   ws: torch.Tensor | None = None) -> torch.Tensor:
+                   ws: torch.Tensor | None = None, scatter: bool = False) -> torch.Tensor:
     """x_partial (P, B, in/P) -> (B, out): the rank partials summed in rank
-    order, bias added once."""
+    order, bias added once; scatter: the reduce-scatter (P, B, out/P)."""
     B = x_partial.shape[1]
     out_dtype = out_dtype or layer.dtype
     if out is None:
-        out = torch.empty((B, layer.out_dims), dtype=out_dtype, device=x_partial.device)
+        shape = (layer.P, B, layer.out_dims // layer.P) if scatter else (B, layer.out_dims)
+        out = torch.empty(shape, dtype=out_dtype, device=x_partial.device)
     if ws is None:
         ws = workspace(layer, B, x_partial.device)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(lib().sg_sharded_to_all(layer.handle, _ptr(x_partial), B, _ptr(out), _DT.get(out.dtype, -1), _ptr(ws),
-                                   nbytes, _stream(x_partial.device)))
+    _check(lib().sg_sharded_to_all_ex(layer.handle, _ptr(x_partial), B, _ptr(out), OUT_SHARDED if scatter else OUT_FULL,
+                                      _DT.get(out.dtype, -1), _ptr(ws), nbytes, _stream(x_partial.device)))
     return out
 
 

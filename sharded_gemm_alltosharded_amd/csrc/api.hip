@@ -150,9 +150,10 @@ bool mfma_ok(const sg_layer* l, const void* x) {
 }
 
 // the streaming kernels keep one LDS slot per (rank, part): bounded ranks only
-bool skinny_fits(const sg_layer* l, int64_t B, int swiglu) {
+// nseg: K segments of the call (ranks of a sharded-to-all layer, or the input
+// shards of an all-to-sharded call whose input arrives sharded)
+bool skinny_fits(const sg_layer* l, int64_t B, int swiglu, int nseg) {
     const int n = (int)(swiglu ? l->out_dims / 2 : l->out_dims);
-    const int nseg = l->mode == SG_SHARDED_TO_ALL ? l->P : 1;
     return sg::skinny_shape((int)B, n, nseg, swiglu).lds <= sg::kMaxStreamLds;
 }
 bool q4_fits(const sg_layer* l, int64_t B, int swiglu) {
@@ -161,11 +162,11 @@ bool q4_fits(const sg_layer* l, int64_t B, int swiglu) {
     return sg::q4_shape((int)B, n, nseg, swiglu).lds <= sg::kMaxStreamLds;
 }
 
-Kind choose(const sg_layer* l, int64_t B, const void* x, int swiglu = 0) {
+Kind choose(const sg_layer* l, int64_t B, const void* x, int swiglu = 0, int nseg = 1) {
     if (l->quantized)
         return (B <= 32 && l->qfrag && aligned16(x) && q4_fits(l, B, swiglu)) ? K_Q4 : K_GENERIC;
     if (!mfma_ok(l, x)) return K_GENERIC;
-    if (B <= 32 && skinny_fits(l, B, swiglu)) return K_SKINNY;
+    if (B <= 32 && skinny_fits(l, B, swiglu, nseg)) return K_SKINNY;
     return B >= 512 ? K_TILE0 : K_TILE1;
 }
 
@@ -197,7 +198,7 @@ sg::SplitLayout split_layout(const sg_layer* l, Kind k, int64_t B) {
 Kind choose_row(const sg_layer* l, int64_t B) {
     if (l->quantized) return B <= 32 && l->qfrag && q4_fits(l, B, 0) ? K_Q4 : K_GENERIC;
     if (l->dtype == SG_F32 || l->cols_r % 8) return K_GENERIC;
-    if (B <= 32 && skinny_fits(l, B, 0)) return K_SKINNY;
+    if (B <= 32 && skinny_fits(l, B, 0, l->P)) return K_SKINNY;
     return B >= 512 ? K_TILE0 : K_TILE1;
 }
 
@@ -226,6 +227,7 @@ void set_weights(sg::Problem& p, const sg_layer* l) {
         p.ldw = l->cols_r;
         p.w_seg = l->rows_r * l->cols_r;
         p.wfrag = l->wfrag;
+        p.wsteps = l->cols_r / 32;
     }
 }
 
@@ -396,41 +398,77 @@ sg_status sg_shard_quantized_linear(const uint32_t* wq, const uint16_t* scales, 
     return SG_OK;
 }
 
-sg_status sg_all_to_sharded(const sg_layer* l, const void* x, int64_t B, void* y, int gather,
-                            int epilogue, sg_dtype y_dtype, void* stream) {
+sg_status sg_all_to_sharded_ex(const sg_layer* l, const void* x, int in_layout, int64_t B, void* y,
+                               int out_layout, int epilogue, sg_dtype y_dtype, void* stream) {
     g_err.clear();
     if (!l) return fail(SG_ERR_INVALID_ARG, "layer is NULL");
     if (l->mode != SG_ALL_TO_SHARDED) return fail(SG_ERR_INVALID_ARG, "layer is sharded-to-all; use sg_sharded_to_all");
     if (B < 0 || B > INT32_MAX) return fail(SG_ERR_INVALID_ARG, "token count %lld out of range", (long long)B);
-    if (gather != 0 && gather != 1) return fail(SG_ERR_INVALID_ARG, "gather must be 0 or 1");
+    if (in_layout != SG_IN_FULL && in_layout != SG_IN_SHARDED)
+        return fail(SG_ERR_INVALID_ARG, "unknown input layout %d", in_layout);
+    if (out_layout != SG_OUT_FULL && out_layout != SG_OUT_SHARDED)
+        return fail(SG_ERR_INVALID_ARG, "unknown output layout %d", out_layout);
     if (epilogue != SG_EPI_NONE && epilogue != SG_EPI_SWIGLU) return fail(SG_ERR_INVALID_ARG, "unknown epilogue %d", epilogue);
     if (!dtype_ok(y_dtype)) return fail(SG_ERR_INVALID_ARG, "unknown output dtype %d", (int)y_dtype);
     if (epilogue == SG_EPI_SWIGLU && (l->segments != 2 || l->bias))
         return fail(SG_ERR_INVALID_ARG, "the SwiGLU epilogue needs an all-to-sharded layer with segments == 2 ([gate; up]) and no bias");
+    const bool xsh = in_layout == SG_IN_SHARDED;
+    if (xsh) {
+        if (l->in_dims % l->P)
+            return fail(SG_ERR_NOT_DIVISIBLE, "Cannot shard the input of size %lld across %d devices.",
+                        (long long)l->in_dims, l->P);
+        if (l->quantized)
+            return fail(SG_ERR_UNSUPPORTED, "a sharded input is implemented for dense layers only");
+        if (l->wfrag && (l->in_dims / l->P) % 32)
+            return fail(SG_ERR_UNSUPPORTED, "a sharded input needs in_dims / P to be a multiple of 32 (got %lld)",
+                        (long long)(l->in_dims / l->P));
+    }
     if (B == 0) return SG_OK;
     if (!x || !y) return fail(SG_ERR_INVALID_ARG, "x and y must not be NULL");
     sg::Problem p{};
     p.A = x;
-    p.lda = l->in_dims;
     p.M = (int)B;
-    p.Kseg = (int)l->cols_r;
-    p.nseg = 1;
     p.dtype = l->dtype;
     set_weights(p, l);
+    if (xsh) {
+        // [HSYM] Case 2: the all-gather of the input shards is the K loop
+        // walking shard r's columns for r = 0 .. P-1
+        const int64_t kr = l->in_dims / l->P;
+        p.lda = kr;
+        p.a_seg = B * kr;
+        p.Kseg = (int)kr;
+        p.nseg = l->P;
+        p.w_seg = l->wfrag ? kr * 16 : kr;  // next k range of every weight row
+    } else {
+        p.lda = l->in_dims;
+        p.Kseg = (int)l->cols_r;
+        p.nseg = 1;
+    }
     p.swiglu = epilogue == SG_EPI_SWIGLU;
     p.N = (int)(p.swiglu ? l->out_dims / 2 : l->out_dims);
     p.floc = p.swiglu ? l->rows_r / 2 : 0;
     p.out = y;
     p.out_dtype = y_dtype;
-    p.out_map = gather ? sg::OUT_ROWMAJOR : sg::OUT_SHARDED;
+    p.out_map = out_layout == SG_OUT_FULL ? sg::OUT_ROWMAJOR : sg::OUT_SHARDED;
     p.ldo = p.N;
     p.nloc = p.N / l->P;
     p.bias = l->bias;
-    Kind k = choose(l, B, x, p.swiglu);
+    Kind k = choose(l, B, x, p.swiglu, p.nseg);
+    if (xsh && (p.Kseg % 8)) k = K_GENERIC;  // 16-byte input rows for the vector paths
     if (k != K_GENERIC && k != K_Q4 && !aligned16(y)) k = K_GENERIC;
     hipError_t e = run(p, k, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "all_to_sharded launch");
     return SG_OK;
+}
+
+sg_status sg_all_to_sharded(const sg_layer* l, const void* x, int64_t B, void* y, int gather,
+                            int epilogue, sg_dtype y_dtype, void* stream) {
+    if (gather != 0 && gather != 1) {
+        g_err.clear();
+        return fail(SG_ERR_INVALID_ARG, "gather must be 0 or 1");
+    }
+    return sg_all_to_sharded_ex(l, x, SG_IN_FULL, B, y, gather ? SG_OUT_FULL : SG_OUT_SHARDED, epilogue,
+                                y_dtype, stream);
 }
 
 size_t sg_sharded_to_all_workspace(const sg_layer* l, int64_t B) {
@@ -439,12 +477,17 @@ size_t sg_sharded_to_all_workspace(const sg_layer* l, int64_t B) {
     return want_split(l, k, B) ? sg::split_workspace_bytes(split_layout(l, k, B)) : 0;
 }
 
-sg_status sg_sharded_to_all(const sg_layer* l, const void* x_partial, int64_t B, void* y, sg_dtype y_dtype,
-                            void* workspace, size_t ws_bytes, void* stream) {
+sg_status sg_sharded_to_all_ex(const sg_layer* l, const void* x_partial, int64_t B, void* y, int out_layout,
+                               sg_dtype y_dtype, void* workspace, size_t ws_bytes, void* stream) {
     g_err.clear();
     if (!l) return fail(SG_ERR_INVALID_ARG, "layer is NULL");
     if (l->mode != SG_SHARDED_TO_ALL) return fail(SG_ERR_INVALID_ARG, "layer is all-to-sharded; use sg_all_to_sharded");
     if (B < 0 || B > INT32_MAX) return fail(SG_ERR_INVALID_ARG, "token count %lld out of range", (long long)B);
+    if (out_layout != SG_OUT_FULL && out_layout != SG_OUT_SHARDED)
+        return fail(SG_ERR_INVALID_ARG, "unknown output layout %d", out_layout);
+    if (out_layout == SG_OUT_SHARDED && l->out_dims % l->P)
+        return fail(SG_ERR_NOT_DIVISIBLE, "Cannot shard the output of size %lld across %d devices.",
+                    (long long)l->out_dims, l->P);
     if (!dtype_ok(y_dtype)) return fail(SG_ERR_INVALID_ARG, "unknown output dtype %d", (int)y_dtype);
     if (B == 0) return SG_OK;
     if (!x_partial || !y) return fail(SG_ERR_INVALID_ARG, "x_partial and y must not be NULL");
@@ -460,8 +503,11 @@ sg_status sg_sharded_to_all(const sg_layer* l, const void* x_partial, int64_t B,
     p.N = (int)l->out_dims;
     p.out = y;
     p.out_dtype = y_dtype;
-    p.out_map = sg::OUT_ROWMAJOR;
+    // SG_OUT_SHARDED: [HSYM]'s reduce-scatter -- rank r receives columns
+    // [r out/P, (r+1) out/P) of the summed result
+    p.out_map = out_layout == SG_OUT_FULL ? sg::OUT_ROWMAJOR : sg::OUT_SHARDED;
     p.ldo = p.N;
+    p.nloc = p.N / l->P;
     p.bias = l->bias;
     Kind k = choose_row(l, B);
     if (k != K_GENERIC && (!aligned16(x_partial) || !aligned16(l->w) || (k != K_Q4 && !aligned16(y))))
@@ -479,6 +525,11 @@ sg_status sg_sharded_to_all(const sg_layer* l, const void* x_partial, int64_t B,
     hipError_t e = run(p, k, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "sharded_to_all launch");
     return SG_OK;
+}
+
+sg_status sg_sharded_to_all(const sg_layer* l, const void* x_partial, int64_t B, void* y, sg_dtype y_dtype,
+                            void* workspace, size_t ws_bytes, void* stream) {
+    return sg_sharded_to_all_ex(l, x_partial, B, y, SG_OUT_FULL, y_dtype, workspace, ws_bytes, stream);
 }
 
 // bytes of the transposed fragment-major copy of A the MFMA path reads
@@ -535,6 +586,7 @@ sg_status sg_summa_matmul(const void* X, const void* A, sg_dtype dtype, int64_t 
     if (frag) {
         HIP_TRY(sg::nn_to_frag(workspace, A, K, N, q, hs), "SUMMA operand transform");
         p.wfrag = 1;
+        p.wsteps = bk / 32;
         p.ldw = bk;
     } else {
         p.nn = 1;

@@ -19,7 +19,7 @@ __device__ __forceinline__ float weight_at(const Problem& p, int s, int64_t row,
         return fmaf(f16_to_f32(p.qs[g]), q, f16_to_f32(p.qb[g]));
     }
     if (p.nn) return load_as_f32(p.W, p.dtype, s * p.w_seg + (int64_t)k * p.ldw + row);
-    if (p.wfrag) return load_as_f32(p.W, p.dtype, s * p.w_seg + frag_offset(row, k, p.Kseg / 32));
+    if (p.wfrag) return load_as_f32(p.W, p.dtype, s * p.w_seg + frag_offset(row, k, p.wsteps));
     return load_as_f32(p.W, p.dtype, s * p.w_seg + row * p.ldw + k);
 }
 

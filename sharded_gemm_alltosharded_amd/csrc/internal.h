@@ -41,6 +41,7 @@ struct Problem {
     int dtype;      // sg_dtype of A and W
     int nn;         // W is K x N (SUMMA)
     int wfrag;      // W is stored fragment-major (frag_offset), Kseg % 32 == 0
+    int64_t wsteps; // fragment-major W: 32-wide k steps per stored row (frag_offset's nsteps)
     int qfrag;      // 4-bit codes / scales / biases stored fragment-major (q4 offsets)
     int swiglu;     // fused gate/up pairs
     int64_t floc;   // rank width of the swiglu output (rows per gate block)

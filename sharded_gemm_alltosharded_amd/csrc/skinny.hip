@@ -73,7 +73,7 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Problem p) {
         }
         // row-major: lane's 16 bytes of a step at row * ldw + k; fragment-major:
         // the block's 1 KB fragment, lane l at l * 8 (one coalesced read per step)
-        woff[rb] = p.wfrag ? frag_offset(row, kq, p.Kseg / 32) : row * p.ldw + kq;
+        woff[rb] = p.wfrag ? frag_offset(row, kq, p.wsteps) : row * p.ldw + kq;
     }
     const int wstep = p.wfrag ? 512 : 32;  // elements per 32-wide k step
     int64_t xoff[MT];

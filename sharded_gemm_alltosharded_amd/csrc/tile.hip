@@ -168,7 +168,7 @@ __global__ __launch_bounds__(256) void tile_kernel(Problem p, int tiles_m, int t
                 wok[i] = n < p.N;
                 row = wok[i] ? n : 0;
             }
-            woff[i] = p.wfrag ? frag_offset(row, lch * 8, p.Kseg / 32) : row * p.ldw + lch * 8;
+            woff[i] = p.wfrag ? frag_offset(row, lch * 8, p.wsteps) : row * p.ldw + lch * 8;
         }
     }
     // advancing k by one 64-wide tile moves 64 elements (row-major) or two

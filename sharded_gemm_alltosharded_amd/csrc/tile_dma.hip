@@ -73,7 +73,8 @@ __host__ __device__ inline int64_t a_extent(const Problem& p) {
 }
 __host__ __device__ inline int64_t w_extent(const Problem& p) {
     const int64_t rows = p.swiglu ? 2 * (int64_t)p.N : p.N;
-    const int64_t seg = p.wfrag ? rows * p.Kseg : (rows - 1) * p.ldw + p.Kseg;
+    // fragment-major: the last segment's k steps of the last 16-row block
+    const int64_t seg = p.wfrag ? (((rows - 1) >> 4) * p.wsteps + p.Kseg / 32) * 512 : (rows - 1) * p.ldw + p.Kseg;
     return ((int64_t)(p.nseg - 1) * p.w_seg + seg) * 2;
 }
 
@@ -186,7 +187,7 @@ __global__ __launch_bounds__(512) void tile_pp_kernel(Problem p, int tiles_m, in
         } else {
             wrow = min(n0 + row, (int64_t)p.N - 1);
         }
-        boff[i] = (uint32_t)((p.wfrag ? frag_offset(wrow, ch * 8, p.Kseg / 32) : wrow * p.ldw + ch * 8) * 2);
+        boff[i] = (uint32_t)((p.wfrag ? frag_offset(wrow, ch * 8, p.wsteps) : wrow * p.ldw + ch * 8) * 2);
     }
     const int bk_step = p.wfrag ? 16 : 1;  // elements of W per element of k
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)p.A, 0, (int)a_extent(p), 0x00020000);

@@ -382,3 +382,103 @@ def test_wrong_layer_mode_is_rejected():
     with pytest.raises(sg.ShardGemmError) as e:
         sg.shard_linear(to_dev(W, "bf16"), "column", P=2)
     assert e.value.code == sg.ERR_BAD_MODE
+
+
+# ---------------------------------------------------------------------------
+# collective layouts ("Sharded Matrices and How to Multiply Them", Cases 2 and
+# 3): an all-to-sharded layer fed sharded activations (all-gathered inside the
+# K loop), and a sharded-to-all layer whose summed output is reduce-scattered
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("B", [1, 16, 40, 600])
+@pytest.mark.parametrize("P", [2, 4])
+def test_all_gather_input(B, P):
+    _print_case(B=B, P=P)
+    out, inn = 512, 1024
+    Xs = synth.normal(45, (P, B, inn // P), 1.0, "bf16")
+    W = synth.uniform(46, (out, inn), inn ** -0.5, "bf16")
+    b = synth.uniform(47, (out,), 0.5, "bf16")
+    layer = sg.shard_linear(to_dev(W, "bf16"), "all-to-sharded", P=P, bias=to_dev(b, "bf16"))
+    xg = oracle.all_gather(Xs)
+    for gather in (False, True):
+        y = sg.all_to_sharded(layer, to_dev(Xs, "bf16"), x_sharded=True, gather=gather, out_dtype=torch.float32)
+        assert_close(y, oracle.col(xg, W, P=P, bias=b, gather=gather, dtype="bf16"), "f32", "gathered-input col")
+    # the same numbers as gathering first, bit for bit only where the same kernel runs both
+    yb = sg.all_to_sharded(layer, to_dev(Xs, "bf16"), x_sharded=True)
+    assert_close(yb, oracle.col(xg, W, P=P, bias=b, dtype="bf16"), "bf16", "gathered-input col bf16")
+
+
+@pytest.mark.parametrize("B", [16, 600])
+def test_all_gather_input_swiglu(B):
+    _print_case(B=B)
+    D, F, P = 512, 1024, 4
+    Wg = synth.uniform(48, (F, D), D ** -0.5, "bf16")
+    Wu = synth.uniform(49, (F, D), D ** -0.5, "bf16")
+    Xs = synth.normal(50, (P, B, D // P), 1.0, "bf16")
+    gu = sg.shard_linear(to_dev(np.concatenate([Wg, Wu]), "bf16"), "all-to-sharded", segments=2, P=P)
+    h = sg.all_to_sharded(gu, to_dev(Xs, "bf16"), x_sharded=True, swiglu=True)
+    xg = oracle.all_gather(Xs)
+    ref = oracle.swiglu(oracle.col(xg, Wg, P=P, dtype="bf16"), oracle.col(xg, Wu, P=P, dtype="bf16"), "f64")
+    assert_close(h, ref, "bf16", "gathered-input swiglu")
+
+
+def test_all_gather_input_row_major_weights():
+    """out % 16 != 0: the weights stay row-major."""
+    B, out, inn, P = 24, 72, 256, 2
+    Xs = synth.normal(51, (P, B, inn // P), 1.0, "bf16")
+    W = synth.uniform(52, (out, inn), inn ** -0.5, "bf16")
+    layer = sg.shard_linear(to_dev(W, "bf16"), "all-to-sharded", P=P)
+    y = sg.all_to_sharded(layer, to_dev(Xs, "bf16"), x_sharded=True, out_dtype=torch.float32)
+    assert_close(y, oracle.col(oracle.all_gather(Xs), W, P=P, dtype="bf16"), "f32", "row-major gathered input")
+
+
+def test_all_gather_input_rejections():
+    W = synth.uniform(53, (64, 96), 0.1, "bf16")
+    layer = sg.shard_linear(to_dev(W, "bf16"), "all-to-sharded", P=2)  # in / P = 48: not 32-aligned
+    with pytest.raises(sg.ShardGemmError) as e:
+        sg.all_to_sharded(layer, to_dev(synth.normal(54, (2, 4, 48), 1.0, "bf16"), "bf16"), x_sharded=True)
+    assert e.value.code == sg.ERR_UNSUPPORTED
+    layer3 = sg.shard_linear(to_dev(synth.uniform(55, (66, 64), 0.1, "bf16"), "bf16"), "all-to-sharded", P=3)
+    with pytest.raises(sg.ShardGemmError) as e:  # 64 input features over 3 ranks
+        sg.all_to_sharded(layer3, to_dev(synth.normal(56, (3, 4, 21), 1.0, "bf16"), "bf16"), x_sharded=True)
+    assert e.value.code == sg.ERR_NOT_DIVISIBLE
+    lq, _ = _q4_layer(synth.uniform(57, (128, 256), 1 / 16, "f32"), 0, 2)
+    with pytest.raises(sg.ShardGemmError) as e:
+        sg.all_to_sharded(lq, to_dev(synth.normal(58, (2, 4, 128), 1.0, "bf16"), "bf16"), x_sharded=True)
+    assert e.value.code == sg.ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("B", [1, 16, 100, 600, 2048])
+@pytest.mark.parametrize("P", [2, 4])
+def test_reduce_scatter_output(B, P):
+    """B = 100 and 2048 take the rank-split workspace path of the tile kernels."""
+    _print_case(B=B, P=P)
+    out, inn = 512, 1024
+    Xs = synth.normal(59, (P, B, inn // P), 1.0, "bf16")
+    W = synth.uniform(60, (out, inn), inn ** -0.5, "bf16")
+    b = synth.uniform(61, (out,), 0.5, "bf16")
+    layer = sg.shard_linear(to_dev(W, "bf16"), "sharded-to-all", P=P, bias=to_dev(b, "bf16"))
+    ref = oracle.reduce_scatter(oracle.row(Xs, W, P=P, bias=b, dtype="bf16"), P)
+    y = sg.sharded_to_all(layer, to_dev(Xs, "bf16"), scatter=True, out_dtype=torch.float32)
+    assert tuple(y.shape) == (P, B, out // P)
+    assert_close(y, ref, "f32", "reduce-scatter")
+    # the same rank-order sum as the all-reduce output, bit for bit
+    yf = sg.sharded_to_all(layer, to_dev(Xs, "bf16"), out_dtype=torch.float32)
+    for r in range(P):
+        assert torch.equal(y[r], yf[:, r * (out // P):(r + 1) * (out // P)])
+
+
+@pytest.mark.parametrize("B", [1, 8, 32])
+def test_reduce_scatter_q4(B):
+    _print_case(B=B)
+    D, F, P = 512, 1024, 4
+    dn, Wdn = _q4_layer(synth.uniform(62, (D, F), 1 / np.sqrt(F), "f32"), 1, P)
+    Xs = synth.normal(63, (P, B, F // P), 1.0, "bf16")
+    y = sg.sharded_to_all(dn, to_dev(Xs, "bf16"), scatter=True, out_dtype=torch.float32)
+    assert_close(y, oracle.reduce_scatter(oracle.row(Xs, Wdn, P=P, dtype="bf16"), P), "f32", "q4 reduce-scatter")
+
+
+def test_reduce_scatter_rejections():
+    layer = sg.shard_linear(to_dev(synth.uniform(64, (66, 64), 0.1, "bf16"), "bf16"), "sharded-to-all", P=4)
+    with pytest.raises(sg.ShardGemmError) as e:  # 66 outputs over 4 ranks
+        sg.sharded_to_all(layer, to_dev(synth.normal(65, (4, 4, 16), 1.0, "bf16"), "bf16"), scatter=True)
+    assert e.value.code == sg.ERR_NOT_DIVISIBLE

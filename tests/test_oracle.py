@@ -164,6 +164,66 @@ def test_row_bruteforce(B, inn, out, P, bias):
     np.testing.assert_array_equal(Y, np.array(ref, dtype=np.float64))
 
 
+# ---------------------------------------------------------------------------
+# collective layouts of "Sharded Matrices and How to Multiply Them": AllGather
+# of the input shards (Case 2) and ReduceScatter of the summed output (Case 3)
+# ---------------------------------------------------------------------------
+def test_all_gather_index_layout():
+    P, B, k = 3, 2, 4
+    Xs = np.array([[[100 * r + 10 * b + j for j in range(k)] for b in range(B)] for r in range(P)], dtype=np.float64)
+    got = oracle.all_gather(Xs)
+    assert got.shape == (B, P * k)
+    for b in range(B):
+        for c in range(P * k):
+            assert got[b, c] == 100 * (c // k) + 10 * b + c % k  # column c of shard c // k
+
+
+def test_reduce_scatter_index_layout():
+    P, B, n = 4, 3, 8
+    Y = np.array([[10 * b + c for c in range(n)] for b in range(B)], dtype=np.float64)
+    got = oracle.reduce_scatter(Y, P)
+    assert got.shape == (P, B, n // P)
+    for r in range(P):
+        for b in range(B):
+            for j in range(n // P):
+                assert got[r, b, j] == 10 * b + r * (n // P) + j
+    with pytest.raises(oracle.OracleError):
+        oracle.reduce_scatter(np.zeros((2, 6)), 4)
+
+
+@pytest.mark.parametrize("B,inn,out,P", [(3, 6, 4, 2), (2, 9, 6, 3), (1, 8, 8, 4)])
+def test_all_gather_then_col_bruteforce(B, inn, out, P):
+    """Case 2: y_r = AllGather(x) W_r^T, written out as a sum over the input
+    shards straight from the shard arrays."""
+    k = inn // P
+    Xs, W = _ints(40, (P, B, k)), _ints(41, (out, inn))
+    got = oracle.col(oracle.all_gather(Xs), W, P=P)
+    nl = out // P
+    for r in range(P):
+        for i in range(B):
+            for j in range(nl):
+                ref = sum((Fraction(float(Xs[s, i, kk])) * Fraction(float(W[r * nl + j, s * k + kk]))
+                           for s in range(P) for kk in range(k)), Fraction(0))
+                assert got[r, i, j] == float(ref)
+
+
+@pytest.mark.parametrize("B,inn,out,P", [(2, 6, 4, 2), (3, 6, 9, 3)])
+def test_row_then_reduce_scatter_bruteforce(B, inn, out, P):
+    """Case 3 with ReduceScatter: rank r receives its output columns of the
+    rank-order sum, the bias added once."""
+    k = inn // P
+    Xs, W, b = _ints(42, (P, B, k)), _ints(43, (out, inn)), _ints(44, (out,), 1, 3)
+    got = oracle.reduce_scatter(oracle.row(Xs, W, P=P, bias=b), P)
+    nl = out // P
+    for r in range(P):
+        for i in range(B):
+            for j in range(nl):
+                c = r * nl + j
+                ref = sum((Fraction(float(Xs[s, i, kk])) * Fraction(float(W[c, s * k + kk]))
+                           for s in range(P) for kk in range(k)), Fraction(0)) + Fraction(float(b[c]))
+                assert got[r, i, j] == float(ref)
+
+
 @pytest.mark.parametrize("M,K,N,q", [(4, 6, 2, 2), (3, 3, 6, 3), (4, 4, 4, 1), (8, 4, 4, 4)])
 def test_summa_bruteforce(M, K, N, q):
     X, A = _ints(7, (M, K)), _ints(8, (K, N))
