@@ -108,6 +108,7 @@ hipError_t launch_generic(const Problem& p, hipStream_t s);
 hipError_t launch_tile(const Problem& p, hipStream_t s, int variant);
 hipError_t launch_skinny(const Problem& p, hipStream_t s);
 hipError_t launch_q4(const Problem& p, hipStream_t s);
+hipError_t launch_q4s(const Problem& p, hipStream_t s);  // 16-row blocks, M <= 32, Kseg % 256 == 0
 // P stacked (rows, K) 16-bit matrices: row-major -> fragment-major (forward) or back
 hipError_t frag_transform(void* dst, const void* src, int P, int64_t rows, int64_t K, int forward, hipStream_t s);
 // SUMMA's A (K, N) -> q fragment-major blocks of A_t^T (N, K / q); N % 16 == 0, (K / q) % 32 == 0
@@ -142,6 +143,7 @@ struct Q4Shape {
 };
 SkinnyShape skinny_shape(int M, int N, int nseg, int swiglu);
 Q4Shape q4_shape(int M, int N, int nseg, int swiglu);
+SkinnyShape q4s_shape(int M, int N, int nseg, int swiglu);
 constexpr size_t kMaxStreamLds = 64 * 1024;
 int tile_count(int M, int N, int variant);
 inline size_t split_workspace_bytes(SplitLayout s) { return kPartialsOffset + s.floats * sizeof(float); }
