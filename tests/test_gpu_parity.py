@@ -482,3 +482,32 @@ def test_reduce_scatter_rejections():
     with pytest.raises(sg.ShardGemmError) as e:  # 66 outputs over 4 ranks
         sg.sharded_to_all(layer, to_dev(synth.normal(65, (4, 4, 16), 1.0, "bf16"), "bf16"), scatter=True)
     assert e.value.code == sg.ERR_NOT_DIVISIBLE
+
+
+@pytest.mark.parametrize("B", [4, 600])
+def test_attention_projections_end_to_end(B):
+    """Fused QKV column shards (segments = 3: rank r holds heads of Q, K and V)
+    feeding the row-sharded output projection with a bias, as in the MLX
+    attention example ([MLX] 5.4).  The attention core is not on this path:
+    rank r's V shard stands in for its heads' attention output, which has the
+    same layout (tokens, D/P) per rank."""
+    _print_case(B=B)
+    D, heads, hd, P = 512, 8, 64, 4
+    X = synth.normal(66, (B, D), 1.0, "bf16")
+    Wqkv = synth.uniform(67, (3 * D, D), D ** -0.5, "bf16")
+    Wo = synth.uniform(68, (D, D), D ** -0.5, "bf16")
+    bo = synth.uniform(69, (D,), 0.5, "bf16")
+    qkv = sg.shard_linear(to_dev(Wqkv, "bf16"), "all-to-sharded", segments=3, P=P)
+    wo = sg.shard_linear(to_dev(Wo, "bf16"), "sharded-to-all", P=P, bias=to_dev(bo, "bf16"))
+    y = sg.all_to_sharded(qkv, to_dev(X, "bf16"))            # (P, B, 3 D / P) = [Q_r | K_r | V_r]
+    v = y[:, :, 2 * D // P:].contiguous()                   # (P, B, D / P)
+    out = sg.sharded_to_all(wo, v, out_dtype=torch.float32)
+    # oracle: V_r = X Wv_r^T from the segments rule, then the rank-order sum + bias
+    ref_qkv = oracle.col(X, Wqkv, P=P, S=3, dtype="bf16")
+    assert_close(y, ref_qkv, "bf16", "qkv")
+    v_ref = np.ascontiguousarray(ref_qkv[:, :, 2 * D // P:])
+    Wv = Wqkv[2 * D:]
+    np.testing.assert_array_equal(v_ref, oracle.col(X, Wv, P=P, dtype="bf16"))  # segment 2 of every rank is V
+    # the row layer consumes V as stored between the layers (bf16)
+    ref = oracle.row(bits(v), Wo, P=P, bias=bo, dtype="bf16")
+    assert_close(out, ref, "f32", "wo(v)")
