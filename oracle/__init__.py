@@ -16,6 +16,7 @@ col         all-to-sharded linear, sharded or gathered output       brute force,
 swiglu      silu(g) * u, rounded once to the activation dtype       closed forms
 row         sharded-to-all linear: partials, rank-order sum, bias   brute force, unsharded identity
 deq4        4-bit affine dequantisation                             hand-packed words, round trip
+deq_mx8     MX FP8 dequantisation (E4M3 x E8M0 per 32)              closed forms, hand bytes
 summa       q-step block accumulation Y_ij += X_it A_tj             brute force, q-independence
 mlp         col(gate), col(up) -> swiglu -> row(down)               composition of the above
 all_gather  input shards (P, B, k) -> (B, P k), rank order          index arrays, brute force
@@ -76,6 +77,7 @@ def lib():
             "or_swiglu": [P, P, I64, I, P],
             "or_row": [P, I64, I64, P, I64, P, I, P, P],
             "or_deq4": [P, P, P, I64, I64, I, P],
+            "or_deqmx8": [P, P, I64, I64, I, P],
             "or_summa": [P, P, I64, I64, I64, I, P],
             "or_mlp": [P, I64, I64, I64, P, P, P, I, I, P],
         }
@@ -87,6 +89,9 @@ def lib():
         L.or_threads.restype = C.c_int
         L.or_round.argtypes = [C.c_double, C.c_int]
         L.or_round.restype = C.c_double
+        for name in ("or_e4m3", "or_e8m0"):
+            getattr(L, name).argtypes = [C.c_uint8]
+            getattr(L, name).restype = C.c_double
         _lib = L
     return _lib
 
@@ -193,6 +198,24 @@ def deq4(packed, scales, biases, group_size=64) -> np.ndarray:
     inn = packed.shape[1] * 8
     W = np.empty((out, inn), dtype=np.float64)
     _check(lib().or_deq4(_p(packed), _p(scales), _p(biases), out, inn, group_size, _p(W)), "deq4")
+    return W
+
+
+def e4m3(b: int) -> float:
+    return float(lib().or_e4m3(int(b)))
+
+
+def e8m0(x: int) -> float:
+    return float(lib().or_e8m0(int(x)))
+
+
+def deq_mx8(codes, scales, block=32) -> np.ndarray:
+    """w[o, k] = 2^(scales[o, k / block] - 127) * e4m3(codes[o, k])."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    out, inn = codes.shape
+    W = np.empty((out, inn), dtype=np.float64)
+    _check(lib().or_deqmx8(_p(codes), _p(scales), out, inn, block, _p(W)), "deq_mx8")
     return W
 
 

@@ -267,6 +267,31 @@ int or_deq4(const uint32_t* Wq, const uint16_t* scales, const uint16_t* biases, 
 }
 
 /* ------------------------------------------------------------------ */
+/* O5b: MX FP8 dequantisation ([MLX] 2.3: non-affine mode "mxfp8", and 4: */
+/* such a layer has no biases).  Read as the OCP Microscaling format:      */
+/* FP8 E4M3 elements, one E8M0 power-of-two scale per block of inputs.    */
+/* ------------------------------------------------------------------ */
+/* E4M3: sign, exponent e (4 bits, bias 7), mantissa m (3 bits); e = 0 is
+ * subnormal (m 2^-9); e = 15 with m = 7 is NaN (no infinity). */
+double or_e4m3(uint8_t b) {
+    int s = b >> 7, e = (b >> 3) & 15, m = b & 7;
+    if (e == 15 && m == 7) return NAN;
+    double v = e ? ldexp(8.0 + m, e - 10) : ldexp((double)m, -9);
+    return s ? -v : v;
+}
+/* E8M0: 2^(x - 127); 255 is NaN. */
+double or_e8m0(uint8_t x) { return x == 255 ? NAN : ldexp(1.0, (int)x - 127); }
+
+int or_deqmx8(const uint8_t* codes, const uint8_t* scales, int64_t out, int64_t in, int block, double* W) {
+    if (!codes || !scales || !W || out < 0 || in < 0 || block < 1) return OR_INVALID;
+    if (in % block) return OR_NOT_DIVISIBLE;
+    for (int64_t o = 0; o < out; ++o)
+        for (int64_t k = 0; k < in; ++k)
+            W[o * in + k] = or_e8m0(scales[o * (in / block) + k / block]) * or_e4m3(codes[o * in + k]);
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------ */
 /* O6: SUMMA ([SUMMA] "SUMMA 算法", equations (1), (2) and their sum)   */
 /* ------------------------------------------------------------------ */
 /* Y = X A with X (M, K), A (K, N), both cut into q x q blocks.  For every

@@ -147,6 +147,48 @@ def quantize_q4(w: np.ndarray, group_size: int = 64):
     return packed, scale.view(np.uint16), bias.view(np.uint16), q
 
 
+def e4m3_encode(v) -> np.ndarray:
+    """Round-to-nearest-even, saturating encode of float values to FP8 E4M3
+    (OCP: 1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no infinity;
+    0x7F / 0xFF are NaN, so the largest finite magnitude 448 = 0x7E)."""
+    v = np.asarray(v, dtype=np.float64)
+    sign = np.signbit(v).astype(np.int64)
+    a = np.abs(v)
+    _, e2 = np.frexp(np.where(a > 0, a, 1.0))          # a = m 2^e2, m in [0.5, 1)
+    ex = np.clip(e2 - 1, -6, 8)                         # exponent; -6 also covers subnormals
+    q = np.rint(a / np.ldexp(1.0, ex - 3))              # significand in units of 2^(ex-3)
+    carry = q >= 16
+    ex = np.where(carry, ex + 1, ex)
+    q = np.where(carry, 8.0, q)
+    code = np.where(q >= 8, ((ex + 7) << 3) | (q.astype(np.int64) - 8), q.astype(np.int64))
+    code = np.minimum(code, 0x7E)
+    return (code | (sign << 7)).astype(np.uint8)
+
+
+def quantize_mxfp8(w: np.ndarray, block: int = 32):
+    """MX FP8 quantizer (OCP Microscaling: FP8 E4M3 elements, one E8M0 scale
+    per block of ``block`` consecutive inputs of a row).  Per block:
+    ``X = floor(log2(max |w|)) - 8`` (8 = exponent of E4M3's largest normal),
+    clamped to [-127, 127]; scale byte ``X + 127``; elements
+    ``e4m3_rne_saturating(w / 2^X)``.  An all-zero block gets X = -127.
+
+    The pages name the mode ("MLX 张量并行实战指南" section 2.3: non-affine
+    modes such as mode="mxfp8"; section 4: an mxfp8 layer has no biases) but
+    not its format; this is the OCP MX reading, and both the oracle and the
+    kernels decode it themselves.
+
+    Returns (codes uint8 (out, in), scales uint8 (out, in / block))."""
+    w = np.asarray(w, dtype=np.float32).astype(np.float64)
+    out, inn = w.shape
+    assert inn % block == 0
+    g = w.reshape(out, inn // block, block)
+    amax = np.abs(g).max(axis=2)
+    _, e2 = np.frexp(np.where(amax > 0, amax, 1.0))
+    X = np.where(amax > 0, np.clip(e2 - 1 - 8, -127, 127), -127)
+    codes = e4m3_encode(g / np.ldexp(1.0, X)[..., None])
+    return codes.reshape(out, inn), (X + 127).astype(np.uint8)
+
+
 def pack_q4(q: np.ndarray) -> np.ndarray:
     q = np.asarray(q, dtype=np.uint32)
     out, inn = q.shape

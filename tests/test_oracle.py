@@ -365,3 +365,74 @@ def test_ulp_and_metrics():
     m = oracle.metrics(ref + np.array([2 ** -9, 0, 0]), ref, "bf16")  # within half an ulp
     assert m["maxabs_ulp"] == 0.0 and m["maxabs"] == 2 ** -9
     assert oracle.within(m, "bf16")
+
+
+# ---------------------------------------------------------------------------
+# MX FP8 ("MLX 张量并行实战指南" 2.3 mode "mxfp8", read as OCP MX: E4M3 elements,
+# one E8M0 scale per 32 inputs, no biases)
+# ---------------------------------------------------------------------------
+def test_e4m3_closed_forms():
+    table = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x09: 1.125 * 2.0 ** -6,
+             0x38: 1.0, 0x3C: 1.5, 0x40: 2.0, 0x77: 240.0, 0x7E: 448.0, 0x80: -0.0, 0xB8: -1.0, 0xFE: -448.0}
+    for b, v in table.items():
+        assert oracle.e4m3(b) == v, hex(b)
+    assert math.isnan(oracle.e4m3(0x7F)) and math.isnan(oracle.e4m3(0xFF))
+
+
+def test_e4m3_monotone_over_every_finite_code():
+    vals = [oracle.e4m3(b) for b in range(0x7F)]
+    assert all(a < b for a, b in zip(vals, vals[1:]))          # no gap or overlap between binades
+    assert [oracle.e4m3(0x80 | b) for b in range(0x7F)] == [-v for v in vals]
+
+
+def test_e8m0():
+    assert oracle.e8m0(127) == 1.0 and oracle.e8m0(128) == 2.0 and oracle.e8m0(120) == 2.0 ** -7
+    assert oracle.e8m0(0) == 2.0 ** -127 and oracle.e8m0(254) == 2.0 ** 127
+    assert math.isnan(oracle.e8m0(255))
+
+
+def test_deq_mx8_hand_bytes():
+    codes = np.array([[0x38, 0xB8] + [0x00] * 30 + [0x7E] + [0x01] * 31], dtype=np.uint8)  # 1 row, 2 blocks
+    scales = np.array([[126, 130]], dtype=np.uint8)                                          # 2^-1, 2^3
+    W = oracle.deq_mx8(codes, scales)
+    assert W[0, 0] == 0.5 and W[0, 1] == -0.5 and W[0, 2] == 0.0
+    assert W[0, 32] == 448.0 * 8 and W[0, 33] == 2.0 ** -9 * 8
+
+
+def test_quantize_mxfp8_bounds():
+    w = synth.uniform(70, (6, 128), 1 / 64, "f32").astype(np.float64)
+    w[2, 32:64] = 0.0                                      # an all-zero block
+    codes, scales = synth.quantize_mxfp8(w)
+    assert codes.shape == (6, 128) and scales.shape == (6, 4)
+    assert not np.any((codes & 0x7F) == 0x7F)               # never NaN
+    assert scales[2, 1] == 0 and np.all(codes[2, 32:64] & 0x7F == 0)
+    W = oracle.deq_mx8(codes, scales)
+    X = scales.astype(np.int64) - 127
+    for o in range(6):
+        for blk in range(4):
+            g = w[o, 32 * blk:32 * (blk + 1)]
+            if not np.any(g):
+                continue
+            amax = np.abs(g).max()
+            assert 2.0 ** (X[o, blk] + 8) <= amax < 2.0 ** (X[o, blk] + 9)   # block max in E4M3's top binade
+            for k in range(32):
+                a = abs(g[k])
+                e = max(math.floor(math.log2(a)), X[o, blk] - 6) if a > 0 else X[o, blk] - 6
+                # half a unit in the last place of the element's binade (3 mantissa bits);
+                # the block max may also saturate from (448, 512) x 2^X down to 448 x 2^X
+                bound = max(2.0 ** (e - 4), amax - 448 * 2.0 ** X[o, blk])
+                assert abs(W[o, 32 * blk + k] - g[k]) <= bound
+
+
+def test_deq_mx8_then_linear_matches_bruteforce():
+    codes = np.random.default_rng(71).integers(0, 0x7F, size=(4, 64)).astype(np.uint8)
+    codes[1, 5] = 0x80 | 0x3C
+    scales = np.array([[120, 134], [127, 127], [122, 131], [127, 125]], dtype=np.uint8)  # sums stay exact in fp64
+    X = _ints(72, (3, 64))
+    W = oracle.deq_mx8(codes, scales)
+    got = oracle.col(X, W, P=2)
+    Wf = [[Fraction(oracle.e4m3(codes[o, k])) * Fraction(2) ** (int(scales[o, k // 32]) - 127) for k in range(64)]
+          for o in range(4)]
+    ref = bf_linear(_fr(X), Wf)
+    for r in range(2):
+        np.testing.assert_array_equal(got[r], np.array([row[2 * r:2 * r + 2] for row in ref], dtype=np.float64))
