@@ -93,6 +93,24 @@ sg_status sg_shard_quantized_linear(const uint32_t* wq, const uint16_t* scales,
                                     int group_size, int bits, sg_dtype act, const void* bias,
                                     int mode, int segments, int P, void* stream, sg_layer** out);
 
+/* Shard an MX FP8 layer ([MLX] 2.3: the non-affine quantization mode
+ * "mxfp8"; [MLX] 4: such a layer has no quantization biases).  Format read as
+ * the OCP Microscaling one: w[o,k] = 2^(scales[o, k/32] - 127) * e4m3(codes[o,k]),
+ * codes FP8 E4M3 (sign, 4 exponent bits with bias 7, 3 mantissa bits, 0x7F /
+ * 0xFF NaN), scales E8M0 (255 NaN), one per block of 32 inputs of a row.
+ *   codes    (out_dims, in_dims) uint8.   scales (out_dims, in_dims/32) uint8.
+ *   act      activation dtype: SG_BF16 only (else SG_ERR_UNSUPPORTED).
+ *   bias     (out_dims) bf16, or NULL (the layer bias, as for sg_shard_linear).
+ * SG_ERR_NOT_DIVISIBLE when in_dims % 32, or for sharded-to-all when a scale
+ * block would straddle two ranks ((in_dims/segments/P) % 32).  Up to 32 tokens
+ * run on the streaming kernel (codes converted to bf16 in registers) when the
+ * shards tile into 16-row blocks and in/P (sharded-to-all) or in is a multiple
+ * of 128; other calls take the generic kernel.  sg_layer_copy_shard returns
+ * codes (what 0) and scales (what 2); sg_layer_info reports quantized = 2. */
+sg_status sg_shard_mxfp8_linear(const uint8_t* codes, const uint8_t* scales, int64_t out_dims,
+                                int64_t in_dims, sg_dtype act, const void* bias, int mode, int segments,
+                                int P, void* stream, sg_layer** out);
+
 /* All-to-sharded forward ([MLX] 2.1; [HSYM] Case 1: no communication).
  *   x        (B, in_dims) of the layer's dtype, replicated to every rank.
  *   y        gather == 0: (P, B, n_out/P), rank r's output at offset r
@@ -177,7 +195,8 @@ sg_status sg_summa_matmul(const void* X, const void* A, sg_dtype dtype, int64_t 
  * (the call then reads A in place whatever workspace it is given). */
 size_t sg_summa_workspace(sg_dtype dtype, int64_t K, int64_t N, int q);
 
-/* Layer description (any output pointer may be NULL). */
+/* Layer description (any output pointer may be NULL); quantized: 0 dense,
+ * 1 4-bit affine, 2 MX FP8. */
 sg_status sg_layer_info(const sg_layer* layer, int64_t* out_dims, int64_t* in_dims, int* mode,
                         int* segments, int* P, sg_dtype* dtype, int* quantized);
 

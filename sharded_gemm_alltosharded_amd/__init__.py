@@ -8,6 +8,7 @@ kernels.  The entry points mirror include/shardgemm.h one to one:
 
     shard_linear               sg_shard_linear
     shard_quantized_linear     sg_shard_quantized_linear
+    shard_mxfp8_linear         sg_shard_mxfp8_linear
     all_to_sharded             sg_all_to_sharded_ex (sg_all_to_sharded's layouts + a sharded input)
     sharded_to_all             sg_sharded_to_all_ex (+ sg_sharded_to_all_workspace; all-reduce or
                                reduce-scatter output)
@@ -68,6 +69,7 @@ def lib():
         sig = {
             "sg_shard_linear": ([P, I, I64, I64, P, I, I, I, P, PP], I),
             "sg_shard_quantized_linear": ([P, P, P, I64, I64, I, I, I, P, I, I, I, P, PP], I),
+            "sg_shard_mxfp8_linear": ([P, P, I64, I64, I, P, I, I, I, P, PP], I),
             "sg_all_to_sharded": ([P, P, I64, P, I, I, I, P], I),
             "sg_all_to_sharded_ex": ([P, P, I, I64, P, I, I, I, P], I),
             "sg_sharded_to_all": ([P, P, I64, P, I, P, SZ, P], I),
@@ -132,6 +134,7 @@ class Layer:
         self.mode, self.segments, self.P = m.value, s.value, p.value
         self.dtype = _TORCH_DT[d.value]
         self.quantized = bool(q.value)
+        self.mx = q.value == 2  # MX FP8 layer
 
     @property
     def handle(self):
@@ -151,13 +154,17 @@ class Layer:
     def shard(self, r: int, what: int = 0) -> torch.Tensor:
         """Copy of rank r's stored tensor: 0 weight, 1 bias, 2 scales, 3 biases."""
         if what == 0:
-            if self.quantized:
+            if self.mx:
+                shape, dt = self._wshape(1), torch.uint8
+            elif self.quantized:
                 shape, dt = self._wshape(8), torch.int32
             else:
                 shape, dt = self._wshape(1), self.dtype
         elif what == 1:
             n = self.out_dims // self.P if self.mode == ALL_TO_SHARDED else self.out_dims
             shape, dt = (n,), self.dtype
+        elif self.mx:
+            shape, dt = self._wshape(32), torch.uint8
         else:
             shape, dt = self._wshape(64), torch.int16
         out = torch.empty(shape, dtype=dt, device=self.device)
@@ -181,6 +188,21 @@ def shard_linear(weight: torch.Tensor, sharding, segments: int = 1, P: int = 1, 
     dev = weight.device
     _check(lib().sg_shard_linear(_ptr(weight), dt, out_dims, in_dims, _ptr(bias), _mode(sharding), segments, P,
                                  _stream(dev) if dev.type == "cuda" else None, C.byref(h)))
+    return Layer(h, dev if dev.type == "cuda" else torch.device("cuda", torch.cuda.current_device()))
+
+
+def shard_mxfp8_linear(codes: torch.Tensor, scales: torch.Tensor, sharding, segments: int = 1, P: int = 1,
+                       act_dtype=torch.bfloat16, bias=None) -> Layer:
+    """Shard an MX FP8 layer (sg_shard_mxfp8_linear).  codes: (out, in) uint8
+    E4M3; scales: (out, in/32) uint8 E8M0."""
+    out_dims, in_dims = codes.shape
+    codes, scales = codes.contiguous(), scales.contiguous()
+    bias = None if bias is None else bias.contiguous()
+    dev = codes.device
+    h = C.c_void_p()
+    _check(lib().sg_shard_mxfp8_linear(_ptr(codes), _ptr(scales), out_dims, in_dims, _DT.get(act_dtype, -1),
+                                       _ptr(bias), _mode(sharding), segments, P,
+                                       _stream(dev) if dev.type == "cuda" else None, C.byref(h)))
     return Layer(h, dev if dev.type == "cuda" else torch.device("cuda", torch.cuda.current_device()))
 
 

@@ -19,6 +19,8 @@ struct sg_layer {
     void* bias;              // all-to-sharded: P x rows_r (rank order); sharded-to-all: out_dims
     int wfrag;               // dense weights stored fragment-major (sg::frag_offset)
     int qfrag;               // 4-bit codes / scales / biases fragment-major (sg::q4_*_offset)
+    int mx;                  // MX FP8 layer: w holds E4M3 code bytes (dense layouts, wfrag), ms its scales
+    uint8_t* ms;             // MX FP8 E8M0 scales: P x rows_r x cols_r/32 (sg::mx_scale_offset when wfrag)
     int device;
 };
 
@@ -108,6 +110,7 @@ void free_layer(sg_layer* l) {
     if (l->w) (void)hipFree(l->w);
     if (l->qs) (void)hipFree(l->qs);
     if (l->qb) (void)hipFree(l->qb);
+    if (l->ms) (void)hipFree(l->ms);
     if (l->bias) (void)hipFree(l->bias);
     delete l;
 }
@@ -162,7 +165,15 @@ bool q4_fits(const sg_layer* l, int64_t B, int swiglu) {
     return sg::q4_shape((int)B, n, nseg, swiglu).lds <= sg::kMaxStreamLds;
 }
 
+// MX FP8 layers: the streaming kernel when the codes are fragment-major,
+// else the generic kernel (the tile kernels take 16-bit weights only)
+Kind choose_mx(const sg_layer* l, int64_t B, const void* x, int swiglu, int nseg) {
+    const bool ok = B <= 32 && l->wfrag && (l->cols_r / 32) % 4 == 0 && aligned16(x) && aligned16(l->w);
+    return ok && skinny_fits(l, B, swiglu, nseg) ? K_SKINNY : K_GENERIC;
+}
+
 Kind choose(const sg_layer* l, int64_t B, const void* x, int swiglu = 0, int nseg = 1) {
+    if (l->mx) return choose_mx(l, B, x, swiglu, nseg);
     if (l->quantized)
         return (B <= 32 && l->qfrag && aligned16(x) && q4_fits(l, B, swiglu)) ? K_Q4 : K_GENERIC;
     if (!mfma_ok(l, x)) return K_GENERIC;
@@ -196,6 +207,7 @@ sg::SplitLayout split_layout(const sg_layer* l, Kind k, int64_t B) {
 // kernel family for a sharded-to-all call (alignment of the caller's pointers
 // is checked separately; misaligned pointers fall back to the generic path)
 Kind choose_row(const sg_layer* l, int64_t B) {
+    if (l->mx) return choose_mx(l, B, l->w, 0, l->P);
     if (l->quantized) return B <= 32 && l->qfrag && q4_fits(l, B, 0) ? K_Q4 : K_GENERIC;
     if (l->dtype == SG_F32 || l->cols_r % 8) return K_GENERIC;
     if (B <= 32 && skinny_fits(l, B, 0, l->P)) return K_SKINNY;
@@ -228,6 +240,11 @@ void set_weights(sg::Problem& p, const sg_layer* l) {
         p.w_seg = l->rows_r * l->cols_r;
         p.wfrag = l->wfrag;
         p.wsteps = l->cols_r / 32;
+        if (l->mx) {
+            p.fp8 = 1;
+            p.ms = l->ms;
+            p.ms_seg = l->rows_r * (l->cols_r / 32);
+        }
     }
 }
 
@@ -398,6 +415,86 @@ sg_status sg_shard_quantized_linear(const uint32_t* wq, const uint16_t* scales, 
     return SG_OK;
 }
 
+sg_status sg_shard_mxfp8_linear(const uint8_t* codes, const uint8_t* scales, int64_t out_dims, int64_t in_dims,
+                                sg_dtype act, const void* bias, int mode, int segments, int P, void* stream,
+                                sg_layer** out) {
+    g_err.clear();
+    sg_status st = common_checks(mode, segments, P, out_dims, in_dims, out);
+    if (st) return st;
+    if (!codes || !scales) return fail(SG_ERR_INVALID_ARG, "codes and scales must not be NULL");
+    if (act != SG_BF16) return fail(SG_ERR_UNSUPPORTED, "MX FP8 layers take bf16 activations");
+    if (in_dims % 32) return fail(SG_ERR_NOT_DIVISIBLE, "in_dims %lld is not a multiple of the block of 32", (long long)in_dims);
+    if (mode == SG_SHARDED_TO_ALL && (in_dims / segments / P) % 32)
+        return fail(SG_ERR_NOT_DIVISIBLE,
+                    "Cannot shard the input of size %lld across %d devices: a scale block of 32 would straddle "
+                    "two ranks.", (long long)in_dims, P);
+    hipStream_t hs = (hipStream_t)stream;
+    sg_layer* l = new sg_layer{};
+    l->mode = mode;
+    l->segments = segments;
+    l->P = P;
+    l->mx = 1;
+    l->dtype = act;
+    l->out_dims = out_dims;
+    l->in_dims = in_dims;
+    l->rows_r = mode == SG_ALL_TO_SHARDED ? out_dims / P : out_dims;
+    l->cols_r = mode == SG_ALL_TO_SHARDED ? in_dims : in_dims / P;
+    (void)hipGetDevice(&l->device);
+    const int axis = mode == SG_ALL_TO_SHARDED ? 0 : 1;
+    const int64_t blocks = in_dims / 32;
+    hipError_t e = hipMalloc(&l->w, (size_t)(out_dims * in_dims));
+    if (e == hipSuccess) e = hipMalloc((void**)&l->ms, (size_t)(out_dims * blocks));
+    if (e != hipSuccess) {
+        free_layer(l);
+        return hip_fail(e, "MX FP8 allocation");
+    }
+    st = copy_shards(l->w, codes, out_dims, in_dims, 1, axis, segments, P, hs);
+    if (!st) st = copy_shards(l->ms, scales, out_dims, blocks, 1, axis, segments, P, hs);
+    // codes and scales fragment-major when the rank matrices tile into 16-row
+    // blocks and runs of 4 scale blocks (the streaming kernel's layout)
+    l->wfrag = out_dims % 16 == 0 && l->cols_r % 128 == 0 && (mode == SG_ALL_TO_SHARDED || l->rows_r % 16 == 0);
+    if (!st && l->wfrag) {
+        const int mats = mode == SG_ALL_TO_SHARDED ? 1 : P;
+        const int64_t rows = mode == SG_ALL_TO_SHARDED ? out_dims : l->rows_r;
+        void *c2 = nullptr, *s2 = nullptr;
+        e = hipMalloc(&c2, (size_t)(out_dims * in_dims));
+        if (e == hipSuccess) e = hipMalloc(&s2, (size_t)(out_dims * blocks));
+        if (e == hipSuccess)
+            e = sg::mx_transform((uint8_t*)c2, (const uint8_t*)l->w, (uint8_t*)s2, l->ms, mats, rows, l->cols_r, 1, hs);
+        if (e == hipSuccess) e = hipStreamSynchronize(hs);
+        if (e == hipSuccess) {
+            (void)hipFree(l->w);
+            (void)hipFree(l->ms);
+            l->w = c2;
+            l->ms = (uint8_t*)s2;
+        } else {
+            (void)hipFree(c2);
+            (void)hipFree(s2);
+            st = hip_fail(e, "MX FP8 layout");
+        }
+    }
+    if (!st && bias) {
+        e = hipMalloc(&l->bias, (size_t)out_dims * 2);
+        if (e != hipSuccess) st = hip_fail(e, "bias allocation");
+        else if (mode == SG_ALL_TO_SHARDED)
+            st = copy_shards(l->bias, bias, out_dims, 1, 2, 0, segments, P, hs);
+        else {
+            e = hipMemcpyAsync(l->bias, bias, (size_t)out_dims * 2, hipMemcpyDefault, hs);
+            if (e != hipSuccess) st = hip_fail(e, "bias copy");
+        }
+    }
+    if (!st) {
+        e = hipStreamSynchronize(hs);
+        if (e != hipSuccess) st = hip_fail(e, "shard copy");
+    }
+    if (st) {
+        free_layer(l);
+        return st;
+    }
+    *out = l;
+    return SG_OK;
+}
+
 sg_status sg_all_to_sharded_ex(const sg_layer* l, const void* x, int in_layout, int64_t B, void* y,
                                int out_layout, int epilogue, sg_dtype y_dtype, void* stream) {
     g_err.clear();
@@ -417,7 +514,7 @@ sg_status sg_all_to_sharded_ex(const sg_layer* l, const void* x, int in_layout, 
         if (l->in_dims % l->P)
             return fail(SG_ERR_NOT_DIVISIBLE, "Cannot shard the input of size %lld across %d devices.",
                         (long long)l->in_dims, l->P);
-        if (l->quantized)
+        if (l->quantized || l->mx)
             return fail(SG_ERR_UNSUPPORTED, "a sharded input is implemented for dense layers only");
         if (l->wfrag && (l->in_dims / l->P) % 32)
             return fail(SG_ERR_UNSUPPORTED, "a sharded input needs in_dims / P to be a multiple of 32 (got %lld)",
@@ -630,7 +727,7 @@ sg_status sg_layer_info(const sg_layer* l, int64_t* out_dims, int64_t* in_dims, 
     if (segments) *segments = l->segments;
     if (P) *P = l->P;
     if (dtype) *dtype = l->dtype;
-    if (quantized) *quantized = l->quantized;
+    if (quantized) *quantized = l->mx ? 2 : l->quantized;
     return SG_OK;
 }
 
@@ -646,6 +743,9 @@ sg_status sg_layer_copy_shard(const sg_layer* l, int r, int what, void* dst, siz
     case 0:
         if (l->quantized) {
             bytes = (size_t)(l->rows_r * (l->cols_r / 8)) * 4;
+            src = (const char*)l->w + r * bytes;
+        } else if (l->mx) {
+            bytes = (size_t)(l->rows_r * l->cols_r);
             src = (const char*)l->w + r * bytes;
         } else {
             bytes = (size_t)(l->rows_r * l->cols_r) * esz;
@@ -664,6 +764,12 @@ sg_status sg_layer_copy_shard(const sg_layer* l, int r, int what, void* dst, siz
         break;
     case 2:
     case 3:
+        if (l->mx && what == 2) {
+            bytes = (size_t)(l->rows_r * (l->cols_r / 32));
+            src = (const char*)l->ms + r * bytes;
+            break;
+        }
+        if (l->mx) return fail(SG_ERR_INVALID_ARG, "an MX FP8 layer has no quantization biases");
         if (!l->quantized) return fail(SG_ERR_INVALID_ARG, "layer is not quantized");
         bytes = (size_t)(l->rows_r * (l->cols_r / 64)) * 2;
         src = (const char*)(what == 2 ? l->qs : l->qb) + r * bytes;
@@ -671,6 +777,23 @@ sg_status sg_layer_copy_shard(const sg_layer* l, int r, int what, void* dst, siz
     default: return fail(SG_ERR_INVALID_ARG, "unknown tensor selector %d", what);
     }
     if (dst_bytes < bytes) return fail(SG_ERR_INVALID_ARG, "dst holds %zu bytes, %zu needed", dst_bytes, bytes);
+    if (l->mx && l->wfrag && what != 1) {
+        // stored fragment-major: restore the row-major codes or scales of every
+        // rank, then copy rank r's
+        void* tmp = nullptr;
+        const size_t all = bytes * l->P;
+        HIP_TRY(hipMalloc(&tmp, all), "staging allocation");
+        const int mats = l->mode == SG_ALL_TO_SHARDED ? 1 : l->P;
+        const int64_t rows = l->mode == SG_ALL_TO_SHARDED ? l->out_dims : l->rows_r;
+        hipError_t e = what == 0
+                           ? sg::mx_transform((uint8_t*)tmp, (const uint8_t*)l->w, nullptr, nullptr, mats, rows, l->cols_r, 0, hs)
+                           : sg::mx_transform(nullptr, nullptr, (uint8_t*)tmp, l->ms, mats, rows, l->cols_r, 0, hs);
+        if (e == hipSuccess) e = hipMemcpyAsync(dst, (const char*)tmp + r * bytes, bytes, hipMemcpyDefault, hs);
+        if (e == hipSuccess) e = hipStreamSynchronize(hs);
+        (void)hipFree(tmp);
+        if (e != hipSuccess) return hip_fail(e, "shard copy");
+        return SG_OK;
+    }
     if (what == 0 && l->wfrag) {
         // stored fragment-major: restore the row-major layout of every rank,
         // then copy rank r's rows

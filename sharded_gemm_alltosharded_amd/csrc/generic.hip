@@ -1,8 +1,8 @@
 // Generic sharded GEMM: one thread per output element, fp32 accumulation.
 //
 // Serves the fp32 layers (the plumbing case of the two-device worked
-// example), shapes whose rows are not 16-byte aligned, and 4-bit layers with
-// more tokens than the 4-bit streaming kernel takes.  Structure follows the
+// example), shapes whose rows are not 16-byte aligned, and 4-bit and MX FP8
+// layers with more tokens than the streaming kernels take.  Structure follows the
 // method literally: each rank's partial product is formed over its own input
 // slice, and the partials are summed in rank order before the bias is added
 // once ("MLX 张量并行实战指南" section 2.2).
@@ -17,6 +17,11 @@ __device__ __forceinline__ float weight_at(const Problem& p, int s, int64_t row,
         float q = (float)((word >> (4 * q4_nibble_pos(k & 7))) & 0xFu);
         int64_t g = s * p.g_seg + (p.qfrag ? q4_group_offset(row, k >> 6, p.ldg) : row * p.ldg + (k >> 6));
         return fmaf(f16_to_f32(p.qs[g]), q, f16_to_f32(p.qb[g]));
+    }
+    if (p.fp8) {
+        const int64_t ci = p.wfrag ? frag_offset(row, k, p.wsteps) : row * p.ldw + k;
+        const int64_t si = p.wfrag ? mx_scale_offset(row, k >> 5, p.wsteps) : row * (p.ldw >> 5) + (k >> 5);
+        return e8m0_to_f32(p.ms[s * p.ms_seg + si]) * e4m3_to_f32(((const uint8_t*)p.W)[s * p.w_seg + ci]);
     }
     if (p.nn) return load_as_f32(p.W, p.dtype, s * p.w_seg + (int64_t)k * p.ldw + row);
     if (p.wfrag) return load_as_f32(p.W, p.dtype, s * p.w_seg + frag_offset(row, k, p.wsteps));

@@ -42,6 +42,12 @@ struct Problem {
     int nn;         // W is K x N (SUMMA)
     int wfrag;      // W is stored fragment-major (frag_offset), Kseg % 32 == 0
     int64_t wsteps; // fragment-major W: 32-wide k steps per stored row (frag_offset's nsteps)
+    // MX FP8 weights (fp8): W holds E4M3 codes, one byte each, in the dense
+    // layouts above; ms their E8M0 scales, one per 32 inputs of a row
+    // (fragment-major: mx_scale_offset; row-major: row * ldw / 32 + k / 32)
+    int fp8;
+    const uint8_t* ms;
+    int64_t ms_seg;
     int qfrag;      // 4-bit codes / scales / biases stored fragment-major (q4 offsets)
     int swiglu;     // fused gate/up pairs
     int64_t floc;   // rank width of the swiglu output (rows per gate block)
@@ -67,6 +73,12 @@ struct Problem {
 // k step of a row block then reads 1 KB contiguous.
 __host__ __device__ inline int64_t frag_offset(int64_t row, int64_t k, int64_t nsteps) {
     return (((row >> 4) * nsteps + (k >> 5)) * 64 + (row & 15) + 16 * ((k >> 3) & 3)) * 8 + (k & 7);
+}
+
+// E8M0 scales of a fragment-major MX FP8 layer: for each 16-row block and run
+// of 4 k steps, 16 rows x 4 bytes (a row's scales of the 4 steps adjacent).
+__host__ __device__ inline int64_t mx_scale_offset(int64_t row, int64_t st, int64_t nsteps) {
+    return (((row >> 4) * (nsteps >> 2) + (st >> 2)) * 16 + (row & 15)) * 4 + (st & 3);
 }
 
 // Events armed by sg_time_next_launch for the calling thread: the next kernel
@@ -113,6 +125,10 @@ hipError_t launch_q4s(const Problem& p, hipStream_t s);  // 16-row blocks, M <= 
 hipError_t frag_transform(void* dst, const void* src, int P, int64_t rows, int64_t K, int forward, hipStream_t s);
 // SUMMA's A (K, N) -> q fragment-major blocks of A_t^T (N, K / q); N % 16 == 0, (K / q) % 32 == 0
 hipError_t nn_to_frag(void* dst, const void* A, int64_t K, int64_t N, int q, hipStream_t s);
+// MX FP8: P stacked (rows, K) code bytes and (rows, K/32) scales <-> fragment-major
+// (either pair of pointers may be null); rows % 16 == 0, K % 128 == 0
+hipError_t mx_transform(uint8_t* dst_codes, const uint8_t* src_codes, uint8_t* dst_scales,
+                        const uint8_t* src_scales, int P, int64_t rows, int64_t K, int forward, hipStream_t s);
 hipError_t q4_repack(uint32_t* w, int64_t n, int forward, hipStream_t s);
 // P stacked 4-bit matrices (rows, K): codes (rows, K/8 words) and scales or
 // biases (rows, K/64), row-major <-> fragment-major
@@ -188,6 +204,19 @@ __device__ __forceinline__ void store_from_f32(void* p, int dtype, int64_t i, fl
 // e + 4 then hold codes 2e and 2e + 1, and one mask-and-or turns a word into
 // four 16-bit pairs in natural k order (see q4.hip).
 __host__ __device__ __forceinline__ int q4_nibble_pos(int k) { return (k >> 1) | ((k & 1) << 2); }
+
+// FP8 E4M3 (sign, 4 exponent bits with bias 7, 3 mantissa bits; exponent 0 is
+// subnormal, 0x7F / 0xFF NaN) and E8M0 (2^(x - 127), 255 NaN), exact in fp32
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+    const uint32_t s = (b >> 7) & 1u, e = (b >> 3) & 15u, m = b & 7u;
+    if (e == 15u && m == 7u) return __builtin_nanf("");
+    const float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+    return s ? -v : v;
+}
+__device__ __forceinline__ float e8m0_to_f32(uint32_t x) {
+    if (x == 255u) return __builtin_nanf("");
+    return x ? __uint_as_float(x << 23) : __uint_as_float(0x00400000u);  // 2^-127 is subnormal
+}
 
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
 

@@ -110,4 +110,55 @@ hipError_t nn_to_frag(void* dst, const void* A, int64_t K, int64_t N, int q, hip
     return hipGetLastError();
 }
 
+// MX FP8 layers: P stacked (rows, K) byte matrices of E4M3 codes <-> the
+// fragment-major byte layout (frag_offset on bytes: a 16-row x 32-k fragment
+// is 512 contiguous bytes, lane l's 8 codes at 8 l), and their (rows, K/32)
+// E8M0 scales <-> mx_scale_offset.  One thread per 8 codes / per scale.
+__global__ void mx_codes_kernel(const uint8_t* src, uint8_t* dst, int64_t rows, int64_t K, int64_t chunks,
+                                int forward) {
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= chunks) return;
+    const int64_t per = rows * (K / 8);
+    const int64_t mat = c / per, rem = c - mat * per;
+    const int64_t row = rem / (K / 8), k = (rem - row * (K / 8)) * 8;
+    const int64_t lin = mat * rows * K + row * K + k;
+    const int64_t frg = mat * rows * K + frag_offset(row, k, K / 32);
+    if (forward)
+        *(uint64_t*)(dst + frg) = *(const uint64_t*)(src + lin);
+    else
+        *(uint64_t*)(dst + lin) = *(const uint64_t*)(src + frg);
+}
+
+__global__ void mx_scales_kernel(const uint8_t* src, uint8_t* dst, int64_t rows, int64_t steps, int64_t total,
+                                 int forward) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= total) return;
+    const int64_t per = rows * steps, mat = i / per, rem = i - mat * per;
+    const int64_t row = rem / steps, st = rem - row * steps;
+    const int64_t lin = mat * per + row * steps + st;
+    const int64_t frg = mat * per + mx_scale_offset(row, st, steps);
+    if (forward)
+        dst[frg] = src[lin];
+    else
+        dst[lin] = src[frg];
+}
+
+hipError_t mx_transform(uint8_t* dst_codes, const uint8_t* src_codes, uint8_t* dst_scales,
+                        const uint8_t* src_scales, int P, int64_t rows, int64_t K, int forward, hipStream_t s) {
+    if (rows % 16 || K % 128) return hipErrorInvalidValue;
+    if (dst_codes) {
+        const int64_t chunks = (int64_t)P * rows * (K / 8);
+        if (chunks)
+            launch(mx_codes_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, s, src_codes, dst_codes,
+                   rows, K, chunks, forward);
+    }
+    if (dst_scales) {
+        const int64_t total = (int64_t)P * rows * (K / 32);
+        if (total)
+            launch(mx_scales_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, src_scales, dst_scales,
+                   rows, K / 32, total, forward);
+    }
+    return hipGetLastError();
+}
+
 }  // namespace sg

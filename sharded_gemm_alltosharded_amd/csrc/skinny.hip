@@ -33,6 +33,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <bool F16>
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
@@ -44,8 +45,22 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-template <int MT, int RB, int NW, bool F16, bool SWIGLU, int U>
+// MX FP8 weights (FP8): the lane's 8 codes of a step are 8 bytes of the
+// fragment, its row's E8M0 scale one byte; v_cvt_scalef32_pk_bf16_fp8 turns
+// them into the bf16 operand (exact: 4 significant bits times a power of two).
+__device__ __forceinline__ u32x4 mx8_to_bf16(u32x2 c, uint32_t scale_byte) {
+    const float sc = scale_byte ? __uint_as_float(scale_byte << 23) : __uint_as_float(0x00400000u);
+    u32x4 r;
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[0], sc, false));
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[0], sc, true));
+    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[1], sc, false));
+    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[1], sc, true));
+    return r;
+}
+
+template <int MT, int RB, int NW, bool F16, bool SWIGLU, int U, bool FP8 = false>
 __global__ __launch_bounds__(NW * 64) void skinny_kernel(Problem p) {
+    static_assert(!(FP8 && F16), "MX FP8 layers take bf16 activations");
     constexpr int ROWS = SWIGLU ? RB / 2 * 16 : RB * 16;  // logical columns per workgroup
     constexpr int SLOT = RB * MT * 4 * 64;                 // floats per unit slot
     static_assert(!SWIGLU || RB % 2 == 0, "gate/up blocks come in pairs");
@@ -57,7 +72,7 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Problem p) {
     const int J = p.nseg >= NW ? 1 : NW / p.nseg;  // waves per rank
     const int units = p.nseg * J;
 
-    int64_t woff[RB];
+    int64_t woff[RB], soff[RB];  // soff: FP8 scales (step st at + (st >> 2) 64 + (st & 3))
     bool wok[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -74,6 +89,7 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Problem p) {
         // row-major: lane's 16 bytes of a step at row * ldw + k; fragment-major:
         // the block's 1 KB fragment, lane l at l * 8 (one coalesced read per step)
         woff[rb] = p.wfrag ? frag_offset(row, kq, p.wsteps) : row * p.ldw + kq;
+        if constexpr (FP8) soff[rb] = mx_scale_offset(row, 0, p.wsteps);
     }
     const int wstep = p.wfrag ? 512 : 32;  // elements per 32-wide k step
     int64_t xoff[MT];
@@ -91,6 +107,8 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Problem p) {
     for (int u = wave; u < units; u += NW) {
         const int s = u / J, j = u - s * J;
         const uint16_t* Wb = (const uint16_t*)p.W + s * p.w_seg;
+        const uint8_t* Wb8 = (const uint8_t*)p.W + s * p.w_seg;
+        const uint8_t* Sb8 = p.ms + s * p.ms_seg;
         const uint16_t* Ab = (const uint16_t*)p.A + s * p.a_seg;
         f32x4 acc[RB][MT];
 #pragma unroll
@@ -102,6 +120,8 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Problem p) {
         const int my_steps = nsteps > j ? (nsteps - j + J - 1) / J : 0;
         const int batches = (my_steps + U - 1) / U;
         u32x4 wv[2][U][RB], xv[2][U][MT];
+        u32x2 wc[2][U][RB];       // FP8 codes
+        uint32_t wsc[2][U][RB];   // FP8 scale bytes
         auto load = [&](int buf, int b) {
 #pragma unroll
             for (int q = 0; q < U; ++q) {
@@ -109,10 +129,18 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Problem p) {
                 const int st = j + idx * J, k0 = st * 32;
                 const bool ok = idx < my_steps && k0 + kq < p.Kseg;
 #pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
-                    wv[buf][q][rb] = (ok && wok[rb])
-                                         ? __builtin_nontemporal_load((const u32x4*)(Wb + woff[rb] + (int64_t)st * wstep))
-                                         : zero;
+                for (int rb = 0; rb < RB; ++rb) {
+                    if constexpr (FP8) {
+                        wc[buf][q][rb] = (ok && wok[rb])
+                                             ? __builtin_nontemporal_load((const u32x2*)(Wb8 + woff[rb] + (int64_t)st * wstep))
+                                             : u32x2{0u, 0u};
+                        wsc[buf][q][rb] = (ok && wok[rb]) ? Sb8[soff[rb] + (int64_t)(st >> 2) * 64 + (st & 3)] : 127u;
+                    } else {
+                        wv[buf][q][rb] = (ok && wok[rb])
+                                             ? __builtin_nontemporal_load((const u32x4*)(Wb + woff[rb] + (int64_t)st * wstep))
+                                             : zero;
+                    }
+                }
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
                     xv[buf][q][mt] = (ok && xok[mt]) ? *(const u32x4*)(Ab + xoff[mt] + k0) : zero;
@@ -122,10 +150,11 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Problem p) {
 #pragma unroll
             for (int q = 0; q < U; ++q)
 #pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
+                for (int rb = 0; rb < RB; ++rb) {
+                    const u32x4 w = FP8 ? mx8_to_bf16(wc[buf][q][rb], wsc[buf][q][rb]) : wv[buf][q][rb];
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt)
-                        acc[rb][mt] = mfma16<F16>(wv[buf][q][rb], xv[buf][q][mt], acc[rb][mt]);
+                    for (int mt = 0; mt < MT; ++mt) acc[rb][mt] = mfma16<F16>(w, xv[buf][q][mt], acc[rb][mt]);
+                }
         };
         if (batches > 0) load(0, 0);
         int b = 0;
@@ -210,45 +239,56 @@ SkinnyShape skinny_shape(int M, int N, int nseg, int swiglu) {
     return sh;
 }
 
-template <int MT, int RB, int NW, bool F16>
+template <int MT, int RB, int NW, bool F16, bool FP8 = false>
 static hipError_t launch_nw(const Problem& p, hipStream_t s, size_t lds) {
     constexpr int U = (MT == 2 && RB >= 8) ? 1 : 2;
     if (p.swiglu) {
         if constexpr (RB % 2 == 0) {
             const int nwg = (p.N + RB / 2 * 16 - 1) / (RB / 2 * 16);
-            launch((skinny_kernel<MT, RB, NW, F16, true, U>), dim3(nwg), dim3(NW * 64), lds, s, p);
+            launch((skinny_kernel<MT, RB, NW, F16, true, U, FP8>), dim3(nwg), dim3(NW * 64), lds, s, p);
         } else {
             return hipErrorInvalidValue;
         }
     } else {
         const int nwg = (p.N + RB * 16 - 1) / (RB * 16);
-        launch((skinny_kernel<MT, RB, NW, F16, false, U>), dim3(nwg), dim3(NW * 64), lds, s, p);
+        launch((skinny_kernel<MT, RB, NW, F16, false, U, FP8>), dim3(nwg), dim3(NW * 64), lds, s, p);
     }
     return hipGetLastError();
 }
 
-template <int MT, int RB, bool F16>
+template <int MT, int RB, bool F16, bool FP8>
 static hipError_t launch_rb(const Problem& p, hipStream_t s, const SkinnyShape& sh) {
     switch (sh.NW) {
-    case 2: return launch_nw<MT, RB, 2, F16>(p, s, sh.lds);
-    case 4: return launch_nw<MT, RB, 4, F16>(p, s, sh.lds);
-    default: return launch_nw<MT, RB, 8, F16>(p, s, sh.lds);
+    case 2: return launch_nw<MT, RB, 2, F16, FP8>(p, s, sh.lds);
+    case 4: return launch_nw<MT, RB, 4, F16, FP8>(p, s, sh.lds);
+    default: return launch_nw<MT, RB, 8, F16, FP8>(p, s, sh.lds);
     }
 }
 
-template <int MT, bool F16>
+template <int MT, bool F16, bool FP8 = false>
 static hipError_t launch_mt(const Problem& p, hipStream_t s, const SkinnyShape& sh) {
     switch (sh.RB) {
-    case 1: return launch_rb<MT, 1, F16>(p, s, sh);
-    case 2: return launch_rb<MT, 2, F16>(p, s, sh);
-    case 4: return launch_rb<MT, 4, F16>(p, s, sh);
-    default: return launch_rb<MT, 8, F16>(p, s, sh);
+    case 1: return launch_rb<MT, 1, F16, FP8>(p, s, sh);
+    case 2: return launch_rb<MT, 2, F16, FP8>(p, s, sh);
+    case 4: return launch_rb<MT, 4, F16, FP8>(p, s, sh);
+    default: return launch_rb<MT, 8, F16, FP8>(p, s, sh);
     }
 }
 
 hipError_t launch_skinny(const Problem& p, hipStream_t s) {
     if (p.M == 0 || p.N == 0) return hipSuccess;
     const SkinnyShape sh = skinny_shape(p.M, p.N, p.nseg, p.swiglu);
+    if (p.fp8) {
+        // fragment-major codes and scales, bf16 activations, 4-step scale runs
+        if (!p.wfrag || p.dtype != SG_BF16 || p.wsteps % 4) return hipErrorInvalidValue;
+        SkinnyShape f = sh;
+        if (f.RB == 8 && f.NW == 8) {  // the scale registers would spill at 8 waves
+            f.NW = 4;
+            const int J = p.nseg >= 4 ? 1 : 4 / p.nseg;
+            f.lds = (size_t)p.nseg * J * f.RB * f.MT * 4 * 64 * sizeof(float);
+        }
+        return f.MT == 1 ? launch_mt<1, false, true>(p, s, f) : launch_mt<2, false, true>(p, s, f);
+    }
     if (p.dtype == SG_F16) return sh.MT == 1 ? launch_mt<1, true>(p, s, sh) : launch_mt<2, true>(p, s, sh);
     return sh.MT == 1 ? launch_mt<1, false>(p, s, sh) : launch_mt<2, false>(p, s, sh);
 }

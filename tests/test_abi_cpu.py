@@ -105,6 +105,8 @@ def test_forward_calls_validate_first(L):
     assert L.sg_sharded_to_all(None, None, 4, None, sg.BF16, None, 0, None) == sg.ERR_INVALID_ARG
     assert L.sg_sharded_to_all_workspace(None, 4) == 0
     assert L.sg_all_to_sharded_ex(None, None, 0, 4, None, 0, 0, sg.BF16, None) == sg.ERR_INVALID_ARG
+    h = C.c_void_p()
+    assert L.sg_shard_mxfp8_linear(None, None, 64, 64, sg.BF16, None, 0, 1, 1, None, C.byref(h)) == sg.ERR_INVALID_ARG
     assert L.sg_sharded_to_all_ex(None, None, 4, None, 0, sg.BF16, None, 0, None) == sg.ERR_INVALID_ARG
     assert L.sg_layer_info(None, None, None, None, None, None, None, None) == sg.ERR_INVALID_ARG
     assert L.sg_layer_copy_shard(None, 0, 0, None, 0, None) == sg.ERR_INVALID_ARG

@@ -511,3 +511,96 @@ def test_attention_projections_end_to_end(B):
     # the row layer consumes V as stored between the layers (bf16)
     ref = oracle.row(bits(v), Wo, P=P, bias=bo, dtype="bf16")
     assert_close(out, ref, "f32", "wo(v)")
+
+
+# ---------------------------------------------------------------------------
+# MX FP8 layers ("MLX 张量并行实战指南" 2.3 mode "mxfp8"; OCP MX reading:
+# E4M3 codes, one E8M0 scale per 32 inputs, no biases)
+# ---------------------------------------------------------------------------
+def _mx_layer(w, mode, P, S=1, bias=None):
+    codes, scales = synth.quantize_mxfp8(w)
+    layer = sg.shard_mxfp8_linear(torch.from_numpy(codes).to(dev()), torch.from_numpy(scales).to(dev()), mode,
+                                  segments=S, P=P, bias=bias)
+    return layer, codes, scales, oracle.deq_mx8(codes, scales)
+
+
+@pytest.mark.parametrize("mode,out,inn,S,P", [(0, 384, 512, 1, 4), (0, 768, 256, 3, 2), (1, 256, 1024, 1, 4),
+                                              (0, 72, 128, 1, 2), (1, 40, 256, 2, 2)])
+def test_slicing_mx_bit_exact(mode, out, inn, S, P):
+    _print_case(mode=mode, out=out, inn=inn, S=S, P=P)
+    w = synth.uniform(73, (out, inn), inn ** -0.5, "f32")
+    layer, codes, scales, _ = _mx_layer(w, mode, P, S)
+    for r in range(P):
+        np.testing.assert_array_equal(to_np(layer.shard(r, 0)).astype(np.uint8), oracle.slice_(codes, mode, S, P, r))
+        np.testing.assert_array_equal(to_np(layer.shard(r, 2)).astype(np.uint8), oracle.slice_(scales, mode, S, P, r))
+    with pytest.raises(sg.ShardGemmError):
+        layer.shard(0, 3)  # no quantization biases
+
+
+@pytest.mark.parametrize("B", [1, 8, 16, 32, 40])
+def test_mx_all_to_sharded(B):
+    _print_case(B=B)
+    D, out, P = 512, 384, 4
+    layer, _, _, Wd = _mx_layer(synth.uniform(74, (out, D), 1 / np.sqrt(D), "f32"), 0, P)
+    X = synth.normal(75, (B, D), 1.0, "bf16")
+    for gather in (False, True):
+        y = sg.all_to_sharded(layer, to_dev(X, "bf16"), gather=gather, out_dtype=torch.float32)
+        assert_close(y, oracle.col(X, Wd, P=P, gather=gather, dtype="bf16"), "f32", "mx col")
+
+
+@pytest.mark.parametrize("B", [1, 16, 32])
+def test_mx_swiglu_and_row(B):
+    _print_case(B=B)
+    D, F, P = 512, 1024, 4
+    ws = [synth.uniform(76 + i, shp, 1 / np.sqrt(D), "f32") for i, shp in enumerate([(F, D), (F, D), (D, F)])]
+    bd = synth.uniform(79, (D,), 0.5, "bf16")
+    gu, _, _, Wgu = _mx_layer(np.concatenate([ws[0], ws[1]]), 0, P, S=2)
+    dn, _, _, Wdn = _mx_layer(ws[2], 1, P, bias=to_dev(bd, "bf16"))
+    X = synth.normal(80, (B, D), 1.0, "bf16")
+    h = sg.all_to_sharded(gu, to_dev(X, "bf16"), swiglu=True)
+    g, u = oracle.col(X, Wgu[:F], P=P, dtype="bf16"), oracle.col(X, Wgu[F:], P=P, dtype="bf16")
+    assert_close(h, oracle.swiglu(g, u, "f64"), "bf16", "mx h")
+    y = sg.sharded_to_all(dn, h, out_dtype=torch.float32)
+    assert_close(y, oracle.row(bits(h), Wdn, P=P, bias=bd, dtype="bf16"), "f32", "mx y")
+
+
+def test_mx_row_major_layout():
+    """out % 16 != 0: codes stay row-major and the generic kernel runs."""
+    B, out, D, P = 4, 72, 256, 2
+    layer, _, _, Wd = _mx_layer(synth.uniform(81, (out, D), D ** -0.5, "f32"), 0, P)
+    X = synth.normal(82, (B, D), 1.0, "bf16")
+    y = sg.all_to_sharded(layer, to_dev(X, "bf16"), gather=True, out_dtype=torch.float32)
+    assert_close(y, oracle.col(X, Wd, P=P, gather=True, dtype="bf16"), "f32", "mx row-major")
+
+
+@pytest.mark.parametrize("B", [1, 8, 32])
+def test_integer_exact_mx(B):
+    """Integer-valued E4M3 codes at scale 2^0 and 2^1, integer activations: exact."""
+    out, D, P = 128, 512, 2
+    rng = np.random.default_rng(83)
+    ints = np.array([0x00, 0x38, 0x40, 0x44, 0x48, 0xB8, 0xC0, 0xC4], dtype=np.uint8)  # 0, 1, 2, 3, 4, -1, -2, -3
+    codes = ints[rng.integers(0, len(ints), size=(out, D))]
+    scales = rng.choice(np.array([127, 128], dtype=np.uint8), size=(out, D // 32))
+    X = synth.small_ints(84, (B, D), -2, 2, "bf16")
+    for mode in (0, 1):
+        layer = sg.shard_mxfp8_linear(torch.from_numpy(codes).to(dev()), torch.from_numpy(scales).to(dev()), mode, P=P)
+        Wd = oracle.deq_mx8(codes, scales)
+        if mode == 0:
+            y = sg.all_to_sharded(layer, to_dev(X, "bf16"), gather=True, out_dtype=torch.float32)
+            ref = oracle.col(X, Wd, P=P, gather=True, dtype="bf16")
+        else:
+            Xs = np.ascontiguousarray(np.stack([X[:, r * (D // P):(r + 1) * (D // P)] for r in range(P)]))
+            y = sg.sharded_to_all(layer, to_dev(Xs, "bf16"), out_dtype=torch.float32)
+            ref = oracle.row(Xs, Wd, P=P, dtype="bf16")
+        np.testing.assert_array_equal(to_np(y), ref)
+
+
+def test_mx_rejections():
+    codes = torch.zeros((64, 96), dtype=torch.uint8, device=dev())
+    scales = torch.full((64, 3), 127, dtype=torch.uint8, device=dev())
+    with pytest.raises(sg.ShardGemmError) as e:  # a scale block would straddle the two ranks (96 / 2 = 48)
+        sg.shard_mxfp8_linear(codes, scales, "sharded-to-all", P=2)
+    assert e.value.code == sg.ERR_NOT_DIVISIBLE
+    with pytest.raises(sg.ShardGemmError) as e:
+        sg.shard_mxfp8_linear(codes, scales, "all-to-sharded", P=2, act_dtype=torch.float16)
+    assert e.value.code == sg.ERR_UNSUPPORTED
