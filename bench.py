@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Throughput of the sharded-GEMM hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2|3|4|5a|5b|1]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2|3|4|5a|5b|6|1]
 
 A step is one pass of the workload's whole sharded path over one batch of
 synthetic inputs already resident in HBM.  The default workload is the
@@ -13,6 +13,8 @@ down sharded-to-all with the fused rank sum.  Other workloads:
     4   4-bit affine MLP (group 64), B in {1, 8, 32} (--batch), P=4
     5a  SUMMA Y = X A, 8192^3 bf16, q=4 (--summa fused|steps)
     5b  vocabulary-parallel head, fp16, 32 x 12288 . (50272 x 12288)^T, P=8
+    6   the decode MLP of the default workload with MX FP8 weights (E4M3 codes,
+        one E8M0 scale per 32 inputs)
     1   the fp32 worked example + the D=64 MLP (launch-bound, for completeness)
 
 Prints ONE JSON line on stdout; progress goes to stderr.  Weight copies are
@@ -45,7 +47,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--config", default="2", choices=["1", "2", "3", "4", "5a", "5b"])
+    ap.add_argument("--config", default="2", choices=["1", "2", "3", "4", "5a", "5b", "6"])
     ap.add_argument("--batch", type=int, default=1, help="tokens for the 4-bit workload (1, 8 or 32)")
     ap.add_argument("--summa", default="fused", choices=["fused", "steps"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -441,10 +443,74 @@ class Tiny(Workload):
         return self.units / t_step / 1e9, t_step, f"the whole step x{n}"
 
 
+class MxfpDecodeMLP(Workload):
+    """Gated MLP decode with MX FP8 weights (E4M3 + E8M0 per 32): B=16, D=4096,
+    F=14336, P=8, bf16 activations -- the decode shape of config 2 on the
+    quantized mode the MLX pages name besides affine."""
+    B, D, F, P = 16, 4096, 14336, 8
+    name = "llama-mlp-mxfp8-decode"
+    metric = "sharded-MLP decode GB/s (% HBM peak)"
+    rotate = 2
+    dominant = "skinny_kernel FP8 (gate|up all-to-sharded + SwiGLU)"
+    dominant_src = ("skinny.hip", "internal.h")
+
+    def setup(self):
+        import numpy as np
+        import torch
+        import sharded_gemm_alltosharded_amd as sg
+        import synth
+        B, D, F, P = self.B, self.D, self.F, self.P
+        self.X = synth.normal(90, (B, D), 1.0, synth.BF16)
+        self.x = _dev_tensor(self.X, "bf16")
+        ws = [synth.uniform(91 + i, shp, 1 / 64, "f32") for i, shp in enumerate([(F, D), (F, D), (D, F)])]
+        gc, gs = synth.quantize_mxfp8(np.concatenate([ws[0], ws[1]]))
+        dc, ds = synth.quantize_mxfp8(ws[2])
+        self.q = (gc, gs, dc, ds)
+        t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        self.gu = [sg.shard_mxfp8_linear(t(gc), t(gs), "all-to-sharded", segments=2, P=P) for _ in range(self.rotate)]
+        self.dn = [sg.shard_mxfp8_linear(t(dc), t(ds), "sharded-to-all", P=P) for _ in range(self.rotate)]
+        self.h = torch.empty((P, B, F // P), dtype=torch.bfloat16, device="cuda")
+        self.y = torch.empty((B, D), dtype=torch.bfloat16, device="cuda")
+        self.sg = sg
+        codes = 2 * F * D + D * F
+        w = codes + codes // 32  # E4M3 codes + E8M0 scales, read once
+        a = 2 * (B * D + 2 * B * F + B * D)
+        self.units = w + a
+        self.dom_units = (2 * F * D) * 33 // 32 + 2 * (B * D + B * F)
+
+    def step(self, i, ev=None):
+        sg = self.sg
+        k = i % self.rotate
+        if ev:
+            sg.time_next_launch(*ev)
+        sg.all_to_sharded(self.gu[k], self.x, swiglu=True, out=self.h)
+        sg.sharded_to_all(self.dn[k], self.h, out=self.y)
+
+    def config(self):
+        return {"workload": self.name, "tokens": self.B, "D": self.D, "F": self.F, "P": self.P,
+                "weights": "mxfp8 (E4M3, E8M0 per 32)", "weight_copies_rotated": self.rotate}
+
+    def cpu_baseline(self):
+        import oracle
+        gc, gs, dc, ds = self.q
+        t0 = time.perf_counter()
+        Wgu, Wd = oracle.deq_mx8(gc, gs), oracle.deq_mx8(dc, ds)
+        X = oracle.decode(self.X, "bf16")
+        t_dec = time.perf_counter() - t0
+        S = 4
+        t0 = time.perf_counter()
+        oracle.mlp(X[:S], Wgu[:self.F], Wgu[self.F:], Wd, self.P, round_dtype="bf16")
+        t_cmp = time.perf_counter() - t0
+        t_step = t_dec + t_cmp * self.B / S
+        return self.units / t_step / 1e9, t_step, (
+            f"oracle MLP on {S} of {self.B} tokens ({t_cmp:.2f} s) scaled x{self.B // S}, plus the fp64 "
+            f"dequantisation of all weights ({t_dec:.2f} s); step-equivalent {t_step:.2f} s")
+
+
 def make(args) -> Workload:
     return {"1": lambda: Tiny(), "2": lambda: DecodeMLP(), "3": lambda: PrefillMLP(),
             "4": lambda: Q4MLP(args.batch), "5a": lambda: Summa(args.summa == "fused"),
-            "5b": lambda: VocabHead()}[args.config]()
+            "5b": lambda: VocabHead(), "6": lambda: MxfpDecodeMLP()}[args.config]()
 
 
 # ---------------------------------------------------------------------------

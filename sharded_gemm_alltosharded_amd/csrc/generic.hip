@@ -19,7 +19,7 @@ __device__ __forceinline__ float weight_at(const Problem& p, int s, int64_t row,
         return fmaf(f16_to_f32(p.qs[g]), q, f16_to_f32(p.qb[g]));
     }
     if (p.fp8) {
-        const int64_t ci = p.wfrag ? frag_offset(row, k, p.wsteps) : row * p.ldw + k;
+        const int64_t ci = p.wfrag ? mx_code_offset(row, k, p.wsteps) : row * p.ldw + k;
         const int64_t si = p.wfrag ? mx_scale_offset(row, k >> 5, p.wsteps) : row * (p.ldw >> 5) + (k >> 5);
         return e8m0_to_f32(p.ms[s * p.ms_seg + si]) * e4m3_to_f32(((const uint8_t*)p.W)[s * p.w_seg + ci]);
     }

@@ -75,6 +75,15 @@ __host__ __device__ inline int64_t frag_offset(int64_t row, int64_t k, int64_t n
     return (((row >> 4) * nsteps + (k >> 5)) * 64 + (row & 15) + 16 * ((k >> 3) & 3)) * 8 + (k & 7);
 }
 
+// E4M3 codes of a fragment-major MX FP8 layer: for each 16-row block and pair
+// of 32-wide k steps, 1 KB in which lane l (row l & 15, chunk c = l >> 4) owns
+// 16 bytes: its 8 codes of the even step, then its 8 codes of the odd step
+// (k = 64 sp + 32 h + 8 c + e).  One 16-byte load per lane feeds two MFMAs.
+__host__ __device__ inline int64_t mx_code_offset(int64_t row, int64_t k, int64_t nsteps) {
+    return (((row >> 4) * (nsteps >> 1) + (k >> 6)) * 64 + (row & 15) + 16 * ((k >> 3) & 3)) * 16 +
+           8 * ((k >> 5) & 1) + (k & 7);
+}
+
 // E8M0 scales of a fragment-major MX FP8 layer: for each 16-row block and run
 // of 4 k steps, 16 rows x 4 bytes (a row's scales of the 4 steps adjacent).
 __host__ __device__ inline int64_t mx_scale_offset(int64_t row, int64_t st, int64_t nsteps) {

@@ -111,9 +111,8 @@ hipError_t nn_to_frag(void* dst, const void* A, int64_t K, int64_t N, int q, hip
 }
 
 // MX FP8 layers: P stacked (rows, K) byte matrices of E4M3 codes <-> the
-// fragment-major byte layout (frag_offset on bytes: a 16-row x 32-k fragment
-// is 512 contiguous bytes, lane l's 8 codes at 8 l), and their (rows, K/32)
-// E8M0 scales <-> mx_scale_offset.  One thread per 8 codes / per scale.
+// fragment-major byte layout (mx_code_offset), and their (rows, K/32) E8M0
+// scales <-> mx_scale_offset.  One thread per 8 codes / per scale.
 __global__ void mx_codes_kernel(const uint8_t* src, uint8_t* dst, int64_t rows, int64_t K, int64_t chunks,
                                 int forward) {
     const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -122,7 +121,7 @@ __global__ void mx_codes_kernel(const uint8_t* src, uint8_t* dst, int64_t rows, 
     const int64_t mat = c / per, rem = c - mat * per;
     const int64_t row = rem / (K / 8), k = (rem - row * (K / 8)) * 8;
     const int64_t lin = mat * rows * K + row * K + k;
-    const int64_t frg = mat * rows * K + frag_offset(row, k, K / 32);
+    const int64_t frg = mat * rows * K + mx_code_offset(row, k, K / 32);
     if (forward)
         *(uint64_t*)(dst + frg) = *(const uint64_t*)(src + lin);
     else

@@ -45,9 +45,10 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// MX FP8 weights (FP8): the lane's 8 codes of a step are 8 bytes of the
-// fragment, its row's E8M0 scale one byte; v_cvt_scalef32_pk_bf16_fp8 turns
-// them into the bf16 operand (exact: 4 significant bits times a power of two).
+// MX FP8 weights (FP8): a step covers two 32-wide k steps; the lane's 16 code
+// bytes of the pair are one load (mx_code_offset), its row's two E8M0 scales
+// two bytes of one word; v_cvt_scalef32_pk_bf16_fp8 turns each 8 codes into
+// the bf16 operand (exact: 4 significant bits times a power of two).
 __device__ __forceinline__ u32x4 mx8_to_bf16(u32x2 c, uint32_t scale_byte) {
     const float sc = scale_byte ? __uint_as_float(scale_byte << 23) : __uint_as_float(0x00400000u);
     u32x4 r;
@@ -72,7 +73,7 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Problem p) {
     const int J = p.nseg >= NW ? 1 : NW / p.nseg;  // waves per rank
     const int units = p.nseg * J;
 
-    int64_t woff[RB], soff[RB];  // soff: FP8 scales (step st at + (st >> 2) 64 + (st & 3))
+    int64_t woff[RB], soff[RB];  // soff: FP8 scales (pair step st: the word at + (st >> 1) 64)
     bool wok[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -89,9 +90,15 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Problem p) {
         // row-major: lane's 16 bytes of a step at row * ldw + k; fragment-major:
         // the block's 1 KB fragment, lane l at l * 8 (one coalesced read per step)
         woff[rb] = p.wfrag ? frag_offset(row, kq, p.wsteps) : row * p.ldw + kq;
-        if constexpr (FP8) soff[rb] = mx_scale_offset(row, 0, p.wsteps);
+        if constexpr (FP8) {
+            woff[rb] = mx_code_offset(row, kq, p.wsteps);
+            soff[rb] = mx_scale_offset(row, 0, p.wsteps);
+        }
     }
-    const int wstep = p.wfrag ? 512 : 32;  // elements per 32-wide k step
+    // elements (FP8: bytes) per step; an FP8 step is a pair of 32-wide k steps
+    const int wstep = FP8 ? 1024 : (p.wfrag ? 512 : 32);
+    constexpr int KS = FP8 ? 64 : 32;  // k per step
+    constexpr int XF = FP8 ? 2 : 1;    // activation fragments per step
     int64_t xoff[MT];
     bool xok[MT];
 #pragma unroll
@@ -102,7 +109,7 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Problem p) {
     }
 
     const u32x4 zero = {0u, 0u, 0u, 0u};
-    const int nsteps = (p.Kseg + 31) / 32;
+    const int nsteps = (p.Kseg + KS - 1) / KS;
 
     for (int u = wave; u < units; u += NW) {
         const int s = u / J, j = u - s * J;
@@ -119,22 +126,23 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Problem p) {
         // this unit's steps: j, j + J, ...; U of them per batch, next batch prefetched
         const int my_steps = nsteps > j ? (nsteps - j + J - 1) / J : 0;
         const int batches = (my_steps + U - 1) / U;
-        u32x4 wv[2][U][RB], xv[2][U][MT];
-        u32x2 wc[2][U][RB];       // FP8 codes
-        uint32_t wsc[2][U][RB];   // FP8 scale bytes
+        u32x4 wv[2][U][RB], xv[2][U][MT][XF];
+        uint32_t wsc[2][U][RB];   // FP8: the step pair's two scale bytes
         auto load = [&](int buf, int b) {
 #pragma unroll
             for (int q = 0; q < U; ++q) {
                 const int idx = b * U + q;
-                const int st = j + idx * J, k0 = st * 32;
+                const int st = j + idx * J, k0 = st * KS;
                 const bool ok = idx < my_steps && k0 + kq < p.Kseg;
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb) {
                     if constexpr (FP8) {
-                        wc[buf][q][rb] = (ok && wok[rb])
-                                             ? __builtin_nontemporal_load((const u32x2*)(Wb8 + woff[rb] + (int64_t)st * wstep))
-                                             : u32x2{0u, 0u};
-                        wsc[buf][q][rb] = (ok && wok[rb]) ? Sb8[soff[rb] + (int64_t)(st >> 2) * 64 + (st & 3)] : 127u;
+                        wv[buf][q][rb] = (ok && wok[rb])
+                                             ? __builtin_nontemporal_load((const u32x4*)(Wb8 + woff[rb] + (int64_t)st * wstep))
+                                             : zero;
+                        const uint32_t sw = (ok && wok[rb]) ? *(const uint32_t*)(Sb8 + soff[rb] + (int64_t)(st >> 1) * 64)
+                                                            : 0x7F7F7F7Fu;
+                        wsc[buf][q][rb] = (sw >> (16 * (st & 1))) & 0xFFFFu;
                     } else {
                         wv[buf][q][rb] = (ok && wok[rb])
                                              ? __builtin_nontemporal_load((const u32x4*)(Wb + woff[rb] + (int64_t)st * wstep))
@@ -143,7 +151,9 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Problem p) {
                 }
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
-                    xv[buf][q][mt] = (ok && xok[mt]) ? *(const u32x4*)(Ab + xoff[mt] + k0) : zero;
+#pragma unroll
+                    for (int f = 0; f < XF; ++f)
+                        xv[buf][q][mt][f] = (ok && xok[mt]) ? *(const u32x4*)(Ab + xoff[mt] + k0 + 32 * f) : zero;
             }
         };
         auto compute = [&](int buf) {
@@ -151,9 +161,20 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Problem p) {
             for (int q = 0; q < U; ++q)
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb) {
-                    const u32x4 w = FP8 ? mx8_to_bf16(wc[buf][q][rb], wsc[buf][q][rb]) : wv[buf][q][rb];
+                    if constexpr (FP8) {
+                        const u32x4 c = wv[buf][q][rb];
+                        const u32x4 w0 = mx8_to_bf16(u32x2{c[0], c[1]}, wsc[buf][q][rb] & 0xFFu);
+                        const u32x4 w1 = mx8_to_bf16(u32x2{c[2], c[3]}, wsc[buf][q][rb] >> 8);
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) acc[rb][mt] = mfma16<F16>(w, xv[buf][q][mt], acc[rb][mt]);
+                        for (int mt = 0; mt < MT; ++mt) {
+                            acc[rb][mt] = mfma16<F16>(w0, xv[buf][q][mt][0], acc[rb][mt]);
+                            acc[rb][mt] = mfma16<F16>(w1, xv[buf][q][mt][XF - 1], acc[rb][mt]);
+                        }
+                    } else {
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt)
+                            acc[rb][mt] = mfma16<F16>(wv[buf][q][rb], xv[buf][q][mt][0], acc[rb][mt]);
+                    }
                 }
         };
         if (batches > 0) load(0, 0);
@@ -241,7 +262,7 @@ SkinnyShape skinny_shape(int M, int N, int nseg, int swiglu) {
 
 template <int MT, int RB, int NW, bool F16, bool FP8 = false>
 static hipError_t launch_nw(const Problem& p, hipStream_t s, size_t lds) {
-    constexpr int U = (MT == 2 && RB >= 8) ? 1 : 2;
+    constexpr int U = (FP8 || (MT == 2 && RB >= 8)) ? 1 : 2;  // an FP8 step already spans 64 k
     if (p.swiglu) {
         if constexpr (RB % 2 == 0) {
             const int nwg = (p.N + RB / 2 * 16 - 1) / (RB / 2 * 16);
@@ -282,7 +303,7 @@ hipError_t launch_skinny(const Problem& p, hipStream_t s) {
         // fragment-major codes and scales, bf16 activations, 4-step scale runs
         if (!p.wfrag || p.dtype != SG_BF16 || p.wsteps % 4) return hipErrorInvalidValue;
         SkinnyShape f = sh;
-        if (f.RB == 8 && f.NW == 8) {  // the scale registers would spill at 8 waves
+        if (f.MT == 2 && f.RB == 8 && f.NW == 8) {  // two token tiles would spill at 8 waves
             f.NW = 4;
             const int J = p.nseg >= 4 ? 1 : 4 / p.nseg;
             f.lds = (size_t)p.nseg * J * f.RB * f.MT * 4 * 64 * sizeof(float);
