@@ -217,7 +217,7 @@ def test_q4_all_to_sharded(B):
     assert_close(sg.all_to_sharded(layer, to_dev(X, "bf16"), out_dtype=torch.float32), ref, "f32", "q4 col")
 
 
-@pytest.mark.parametrize("B", [1, 8, 32])
+@pytest.mark.parametrize("B", [1, 8, 13, 24, 32])
 def test_q4_swiglu_and_row(B):
     _print_case(B=B)
     D, F, P = 512, 1024, 4
