@@ -548,28 +548,41 @@ def calib_copy(mib: int, steps: int):
 
 
 def time_graph(wl: Workload, K: int, W: int):
-    """The same steps captured once per rotated weight copy into HIP graphs
-    and replayed K times (launch overhead and inter-kernel gaps of the host
-    path removed).  None if capture is not possible for the workload."""
+    """The same steps replayed from HIP graphs: one graph per rotated weight
+    copy holding a single step, and one holding S consecutive steps (cycling
+    the copies), S = 8 rounded to whole rotations.  K steps = K // S replays
+    of the long graph plus K % S single-step replays; host launch overhead
+    and most inter-kernel gaps of the eager path are gone.  None if capture is
+    not possible for the workload."""
     import torch
+    S = wl.rotate * max(1, 8 // wl.rotate)
     try:
-        graphs = []
         cap = torch.cuda.Stream()
+        singles = []
         for r in range(wl.rotate):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=cap):
                 wl.step(r)
-            graphs.append(g)
+            singles.append(g)
+        block = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(block, stream=cap):
+            for i in range(S):
+                wl.step(i)
     except Exception as e:  # capture unsupported for this workload
         log(f"[bench] graph capture failed: {e}")
         return None
-    for i in range(W):
-        graphs[i % len(graphs)].replay()
+
+    def run(n):
+        for _ in range(n // S):
+            block.replay()
+        for i in range(n % S):
+            singles[i % len(singles)].replay()
+
+    run(W)
     torch.cuda.synchronize()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record()
-    for i in range(K):
-        graphs[i % len(graphs)].replay()
+    run(K)
     e.record()
     torch.cuda.synchronize()
     return s.elapsed_time(e) / K
