@@ -47,6 +47,27 @@ def test_decode_mlp_full():
     assert torch.equal(y, y2)
 
 
+def test_mxfp8_mlp_full():
+    """MX FP8 decode MLP (the layers bench.py times for it): B=16, D=4096,
+    F=14336, P=8, E4M3 codes with E8M0 scales per 32 inputs; every token."""
+    _case("MX FP8 decode MLP B=16 D=4096 F=14336 P=8")
+    B, D, F, P = 16, 4096, 14336, 8
+    X = synth.normal(90, (B, D), 1.0, "bf16")
+    ws = [synth.uniform(91 + i, shp, 1 / 64, "f32") for i, shp in enumerate([(F, D), (F, D), (D, F)])]
+    gc, gs = synth.quantize_mxfp8(np.concatenate([ws[0], ws[1]]))
+    dc, ds = synth.quantize_mxfp8(ws[2])
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev())
+    gu = sg.shard_mxfp8_linear(t(gc), t(gs), "all-to-sharded", segments=2, P=P)
+    dn = sg.shard_mxfp8_linear(t(dc), t(ds), "sharded-to-all", P=P)
+    h = sg.all_to_sharded(gu, to_dev(X, "bf16"), swiglu=True)
+    y = sg.sharded_to_all(dn, h)
+    Wgu, Wd = oracle.deq_mx8(gc, gs), oracle.deq_mx8(dc, ds)
+    Xd = oracle.decode(X, "bf16")
+    g, u = oracle.col(Xd, Wgu[:F], P=P), oracle.col(Xd, Wgu[F:], P=P)
+    assert_close(h, oracle.swiglu(g, u, "f64"), "bf16", "h")
+    assert_close(y, oracle.row(oracle.swiglu(g, u, "bf16"), Wd, P=P), "bf16", "y")
+
+
 def test_prefill_full_sampled():
     """B=4096, P=4: QKV (segments 3) + MLP on the full batch; 8 sampled tokens."""
     _case("prefill B=4096 D=4096 F=14336 P=4 + QKV")
