@@ -114,9 +114,8 @@ class DecodeMLP(Workload):
         self.gu = [sg.shard_linear(gu_w, "all-to-sharded", segments=2, P=P) for _ in range(self.rotate)]
         self.dn = [sg.shard_linear(dn_w, "sharded-to-all", P=P) for _ in range(self.rotate)]
         del gu_w, dn_w
-        self.h = torch.empty((P, B, F // P), dtype=torch.bfloat16, device="cuda")
         self.y = torch.empty((B, D), dtype=torch.bfloat16, device="cuda")
-        self.ws = sg.workspace(self.dn[0], B, "cuda")
+        self.ws = sg.mlp_workspace(self.gu[0], self.dn[0], B, "cuda")  # the down workspace, then the sharded h
         self.sg = sg
         w = 2 * (2 * F * D + D * F)  # weight bytes, read once
         a = 2 * (B * D + 2 * B * F + B * D)  # x in, h out and back in, y out
@@ -128,8 +127,7 @@ class DecodeMLP(Workload):
         k = i % self.rotate
         if ev:
             sg.time_next_launch(*ev)
-        sg.all_to_sharded(self.gu[k], self.x, swiglu=True, out=self.h)
-        sg.sharded_to_all(self.dn[k], self.h, out=self.y, ws=self.ws)
+        sg.mlp(self.gu[k], self.dn[k], self.x, out=self.y, ws=self.ws)
 
     def config(self):
         return {"workload": self.name, "tokens": self.B, "D": self.D, "F": self.F, "P": self.P,
@@ -469,8 +467,8 @@ class MxfpDecodeMLP(Workload):
         t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
         self.gu = [sg.shard_mxfp8_linear(t(gc), t(gs), "all-to-sharded", segments=2, P=P) for _ in range(self.rotate)]
         self.dn = [sg.shard_mxfp8_linear(t(dc), t(ds), "sharded-to-all", P=P) for _ in range(self.rotate)]
-        self.h = torch.empty((P, B, F // P), dtype=torch.bfloat16, device="cuda")
         self.y = torch.empty((B, D), dtype=torch.bfloat16, device="cuda")
+        self.ws = sg.mlp_workspace(self.gu[0], self.dn[0], B, "cuda")  # the down workspace, then the sharded h
         self.sg = sg
         codes = 2 * F * D + D * F
         w = codes + codes // 32  # E4M3 codes + E8M0 scales, read once
@@ -483,8 +481,7 @@ class MxfpDecodeMLP(Workload):
         k = i % self.rotate
         if ev:
             sg.time_next_launch(*ev)
-        sg.all_to_sharded(self.gu[k], self.x, swiglu=True, out=self.h)
-        sg.sharded_to_all(self.dn[k], self.h, out=self.y)
+        sg.mlp(self.gu[k], self.dn[k], self.x, out=self.y, ws=self.ws)
 
     def config(self):
         return {"workload": self.name, "tokens": self.B, "D": self.D, "F": self.F, "P": self.P,

@@ -166,6 +166,34 @@ sg_status sg_sharded_to_all_ex(const sg_layer* layer, const void* x_partial, int
                                int out_layout, sg_dtype y_dtype, void* workspace, size_t ws_bytes,
                                void* stream);
 
+/* Gated MLP forward, the chain of [MLX] 5.2-5.3: h_r = silu(x W_gate,r^T) *
+ * (x W_up,r^T) on every rank (all-to-sharded with the SwiGLU epilogue), then
+ * y = sum over r = 0..P-1 of h_r W_down,r^T (+ the down bias once), with the
+ * sharded h kept in the workspace instead of a caller array.  Results are
+ * bitwise those of sg_all_to_sharded(gate_up, ..., SG_EPI_SWIGLU, act dtype)
+ * followed by sg_sharded_to_all(down, ...).
+ *   gate_up  all-to-sharded layer, segments = 2 ([W_gate; W_up]), no bias.
+ *   down     sharded-to-all layer over the same P, in_dims = gate_up's
+ *            out_dims / 2, the same activation dtype.
+ *   x        (B, in_dims) of that dtype; y (B, out_dims of down) of y_dtype.
+ *   workspace device memory of at least sg_mlp_workspace(...) bytes, 16-byte
+ *            aligned, zero-filled before its first use: the down layer's
+ *            sg_sharded_to_all workspace first (its arrival counters, kept zero
+ *            by every call, at offset 0 for every B), then h (when both layers
+ *            run on the streaming kernel, stored fragment-major so that the
+ *            down layer reads each 16-token x 32-input operand as one
+ *            contiguous 1 KB).  The same workspace serves later calls of any B
+ *            it is large enough for; calls sharing it must not run concurrently.
+ * Errors: SG_ERR_INVALID_ARG for layers that do not form such a pair (the
+ * message says which rule fails), SG_ERR_WORKSPACE for a missing, small or
+ * misaligned workspace; B = 0 is a no-op. */
+sg_status sg_mlp(const sg_layer* gate_up, const sg_layer* down, const void* x, int64_t B, void* y,
+                 sg_dtype y_dtype, void* workspace, size_t ws_bytes, void* stream);
+
+/* Bytes of workspace sg_mlp needs for B tokens (0 for layers that do not form
+ * a gate|up, down pair or B <= 0). */
+size_t sg_mlp_workspace(const sg_layer* gate_up, const sg_layer* down, int64_t B);
+
 /* Bytes of workspace sg_sharded_to_all needs for B tokens (0 on bad input). */
 size_t sg_sharded_to_all_workspace(const sg_layer* layer, int64_t B);
 

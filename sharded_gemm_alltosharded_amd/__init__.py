@@ -12,6 +12,7 @@ kernels.  The entry points mirror include/shardgemm.h one to one:
     all_to_sharded             sg_all_to_sharded_ex (sg_all_to_sharded's layouts + a sharded input)
     sharded_to_all             sg_sharded_to_all_ex (+ sg_sharded_to_all_workspace; all-reduce or
                                reduce-scatter output)
+    mlp                        sg_mlp (+ sg_mlp_workspace): gate|up with SwiGLU, then down
     summa_matmul               sg_summa_matmul (+ sg_summa_workspace)
     Layer.info / Layer.shard   sg_layer_info / sg_layer_copy_shard
     time_next_launch           sg_time_next_launch (profiling)
@@ -74,6 +75,8 @@ def lib():
             "sg_all_to_sharded_ex": ([P, P, I, I64, P, I, I, I, P], I),
             "sg_sharded_to_all": ([P, P, I64, P, I, P, SZ, P], I),
             "sg_sharded_to_all_ex": ([P, P, I64, P, I, I, P, SZ, P], I),
+            "sg_mlp": ([P, P, P, I64, P, I, P, SZ, P], I),
+            "sg_mlp_workspace": ([P, P, I64], SZ),
             "sg_sharded_to_all_workspace": ([P, I64], SZ),
             "sg_summa_matmul": ([P, P, I, I64, I64, I64, I, P, I, I, P, SZ, P], I),
             "sg_summa_workspace": ([I, I64, I64, I], SZ),
@@ -270,6 +273,39 @@ def sharded_to_all(layer: Layer, x_partial: torch.Tensor, out_dtype=None, out: t
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().sg_sharded_to_all_ex(layer.handle, _ptr(x_partial), B, _ptr(out), OUT_SHARDED if scatter else OUT_FULL,
                                       _DT.get(out.dtype, -1), _ptr(ws), nbytes, _stream(x_partial.device)))
+    return out
+
+
+_mlp_workspaces: dict = {}
+
+
+def mlp_workspace(gate_up: Layer, down: Layer, B: int, device) -> torch.Tensor | None:
+    """A zero-filled workspace for mlp(), shared by calls on one device (None
+    when the layers do not form a gate|up, down pair: sg_mlp then says why)."""
+    need = int(lib().sg_mlp_workspace(gate_up.handle, down.handle, B))
+    if need == 0:
+        return None
+    key = torch.device(device)
+    ws = _mlp_workspaces.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.zeros(need, dtype=torch.uint8, device=key)
+        _mlp_workspaces[key] = ws
+    return ws
+
+
+def mlp(gate_up: Layer, down: Layer, x: torch.Tensor, out_dtype=None, out: torch.Tensor | None = None,
+        ws: torch.Tensor | None = None) -> torch.Tensor:
+    """(B, in) -> (B, out): down(silu(x W_gate^T) * (x W_up^T)) through sg_mlp,
+    the sharded h kept in the workspace."""
+    B = x.shape[0]
+    out_dtype = out_dtype or down.dtype
+    if out is None:
+        out = torch.empty((B, down.out_dims), dtype=out_dtype, device=x.device)
+    if ws is None:
+        ws = mlp_workspace(gate_up, down, B, x.device)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().sg_mlp(gate_up.handle, down.handle, _ptr(x), B, _ptr(out), _DT.get(out.dtype, -1), _ptr(ws),
+                        nbytes, _stream(x.device)))
     return out
 
 

@@ -215,6 +215,8 @@ Kind choose_row(const sg_layer* l, int64_t B) {
 }
 
 hipError_t run(const sg::Problem& p, Kind k, hipStream_t st) {
+    // fragment-major activations (the fused MLP's h) exist for the streaming kernel only
+    if ((p.xfrag || p.out_map == sg::OUT_FRAG) && k != K_SKINNY) return hipErrorInvalidValue;
     switch (k) {
     case K_TILE0: return sg::launch_tile(p, st, 0);
     case K_TILE1: return sg::launch_tile(p, st, 1);
@@ -627,6 +629,107 @@ sg_status sg_sharded_to_all_ex(const sg_layer* l, const void* x_partial, int64_t
 sg_status sg_sharded_to_all(const sg_layer* l, const void* x_partial, int64_t B, void* y, sg_dtype y_dtype,
                             void* workspace, size_t ws_bytes, void* stream) {
     return sg_sharded_to_all_ex(l, x_partial, B, y, SG_OUT_FULL, y_dtype, workspace, ws_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Fused gated MLP: gate|up all-to-sharded with SwiGLU, then the down
+// sharded-to-all, the sharded h kept in the caller's workspace.
+// ---------------------------------------------------------------------------
+namespace {
+
+const char* mlp_check(const sg_layer* gu, const sg_layer* dn) {
+    if (!gu || !dn) return "layer is NULL";
+    if (gu->mode != SG_ALL_TO_SHARDED || gu->segments != 2 || gu->bias)
+        return "the gate|up layer must be all-to-sharded with segments == 2 ([gate; up]) and no bias";
+    if (dn->mode != SG_SHARDED_TO_ALL) return "the down layer must be sharded-to-all";
+    if (gu->P != dn->P) return "the two layers must be sharded over the same P";
+    if (gu->out_dims / 2 != dn->in_dims) return "the down layer's input width must be half the gate|up output width";
+    if (gu->dtype != dn->dtype) return "the two layers must take the same activation dtype";
+    return nullptr;
+}
+
+size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+// bytes of h: P rank blocks of act_rows(B) x (F / P) activations
+size_t mlp_h_bytes(const sg_layer* gu, int64_t B) {
+    return align256((size_t)sg::act_rows(B) * (size_t)(gu->out_dims / 2) * dtype_size(gu->dtype));
+}
+
+}  // namespace
+
+// The down layer's workspace comes first and always spans at least its
+// arrival counters, so the counters sit at offset 0 for every B and h (which
+// needs no clearing) never overwrites them.
+static size_t mlp_down_bytes(const sg_layer* dn, int64_t B) {
+    return align256(std::max(sg_sharded_to_all_workspace(dn, B), sg::kPartialsOffset));
+}
+
+size_t sg_mlp_workspace(const sg_layer* gate_up, const sg_layer* down, int64_t B) {
+    if (mlp_check(gate_up, down) || B <= 0 || B > INT32_MAX) return 0;
+    return mlp_down_bytes(down, B) + mlp_h_bytes(gate_up, B);
+}
+
+sg_status sg_mlp(const sg_layer* gate_up, const sg_layer* down, const void* x, int64_t B, void* y, sg_dtype y_dtype,
+                 void* workspace, size_t ws_bytes, void* stream) {
+    g_err.clear();
+    if (const char* why = mlp_check(gate_up, down)) return fail(SG_ERR_INVALID_ARG, "%s", why);
+    if (B < 0 || B > INT32_MAX) return fail(SG_ERR_INVALID_ARG, "token count %lld out of range", (long long)B);
+    if (!dtype_ok(y_dtype)) return fail(SG_ERR_INVALID_ARG, "unknown output dtype %d", (int)y_dtype);
+    if (B == 0) return SG_OK;
+    if (!x || !y) return fail(SG_ERR_INVALID_ARG, "x and y must not be NULL");
+    const size_t db = mlp_down_bytes(down, B), need = db + mlp_h_bytes(gate_up, B);
+    if (!workspace || ws_bytes < need)
+        return fail(SG_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws_bytes, need);
+    if (!aligned16(workspace)) return fail(SG_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    void* h = (char*)workspace + db;
+    const sg_layer* gu = gate_up;
+    const sg_layer* dn = down;
+    // Both layers on the streaming kernel: h fragment-major, so that the down
+    // layer's activation loads are contiguous 1 KB reads (the row-major h of
+    // the separate calls costs each load 16 rows x 64 bytes).  Otherwise the
+    // two separate calls with a row-major h.
+    const bool fused = choose(gu, B, x, 1, 1) == K_SKINNY && choose_row(dn, B) == K_SKINNY && dn->wfrag &&
+                       aligned16(y) && aligned16(dn->w) && (dn->cols_r % 32) == 0;
+    if (!fused) {
+        sg_status st = sg_all_to_sharded_ex(gu, x, SG_IN_FULL, B, h, SG_OUT_SHARDED, SG_EPI_SWIGLU, gu->dtype, stream);
+        if (st != SG_OK) return st;
+        return sg_sharded_to_all_ex(dn, h, B, y, SG_OUT_FULL, y_dtype, workspace, db, stream);
+    }
+    sg::Problem p{};
+    p.A = x;
+    p.M = (int)B;
+    p.dtype = gu->dtype;
+    set_weights(p, gu);
+    p.lda = gu->in_dims;
+    p.Kseg = (int)gu->cols_r;
+    p.nseg = 1;
+    p.swiglu = 1;
+    p.N = (int)(gu->out_dims / 2);
+    p.floc = gu->rows_r / 2;
+    p.out = h;
+    p.out_dtype = gu->dtype;
+    p.out_map = sg::OUT_FRAG;
+    p.nloc = p.N / gu->P;
+    hipError_t e = run(p, K_SKINNY, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "mlp gate|up launch");
+    sg::Problem q{};
+    q.A = h;
+    q.xfrag = 1;
+    q.a_seg = sg::act_rows(B) * dn->cols_r;
+    q.M = (int)B;
+    q.Kseg = (int)dn->cols_r;
+    q.nseg = dn->P;
+    q.dtype = dn->dtype;
+    set_weights(q, dn);
+    q.N = (int)dn->out_dims;
+    q.out = y;
+    q.out_dtype = y_dtype;
+    q.out_map = sg::OUT_ROWMAJOR;
+    q.ldo = q.N;
+    q.bias = dn->bias;
+    e = run(q, K_SKINNY, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "mlp down launch");
+    return SG_OK;
 }
 
 // bytes of the transposed fragment-major copy of A the MFMA path reads

@@ -25,7 +25,7 @@ namespace sg {
 //    logical output column j (0 .. N-1, N = P * floc) pairs gate row and up row
 //    of rank j / floc, and the kernel stores silu(g) * u.
 // ---------------------------------------------------------------------------
-enum OutMap { OUT_ROWMAJOR = 0, OUT_SHARDED = 1 };
+enum OutMap { OUT_ROWMAJOR = 0, OUT_SHARDED = 1, OUT_FRAG = 2 };
 
 struct Problem {
     const void* A;
@@ -49,6 +49,7 @@ struct Problem {
     const uint8_t* ms;
     int64_t ms_seg;
     int qfrag;      // 4-bit codes / scales / biases stored fragment-major (q4 offsets)
+    int xfrag;      // A is a fragment-major sharded activation (act_frag_offset; streaming kernel only)
     int swiglu;     // fused gate/up pairs
     int64_t floc;   // rank width of the swiglu output (rows per gate block)
     // epilogue
@@ -56,7 +57,7 @@ struct Problem {
     int out_dtype;
     int out_map;    // OutMap
     int64_t ldo;    // OUT_ROWMAJOR row stride
-    int64_t nloc;   // OUT_SHARDED rank width: column n -> rank n / nloc
+    int64_t nloc;   // OUT_SHARDED / OUT_FRAG rank width: column n -> rank n / nloc
     const void* bias;  // per output column, dtype `dtype`; may be null
     int accumulate; // fp32 output only: out += result
     // cross-segment reduction through a workspace (split by segment)
@@ -73,6 +74,16 @@ struct Problem {
 // k step of a row block then reads 1 KB contiguous.
 __host__ __device__ inline int64_t frag_offset(int64_t row, int64_t k, int64_t nsteps) {
     return (((row >> 4) * nsteps + (k >> 5)) * 64 + (row & 15) + 16 * ((k >> 3) & 3)) * 8 + (k & 7);
+}
+
+// Fragment-major sharded activation (the h a fused MLP keeps between its two
+// layers): rank r's (act_rows(M), nloc) block at r * act_rows(M) * nloc, laid
+// out like a fragment-major weight with tokens as rows, so that the 16 tokens x
+// 32 inputs a streaming wave feeds one MFMA are one contiguous 1 KB.  Token
+// rows past M are padding (never stored, their results never kept).
+__host__ __device__ inline int64_t act_rows(int64_t M) { return (M + 15) / 16 * 16; }
+__host__ __device__ inline int64_t act_frag_offset(int64_t m, int64_t k, int64_t nsteps) {
+    return frag_offset(m, k, nsteps);
 }
 
 // E4M3 codes of a fragment-major MX FP8 layer: for each 16-row block and pair
@@ -243,6 +254,10 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 // output address of logical element (m, n)
 __device__ __forceinline__ int64_t out_index(const Problem& p, int m, int64_t n) {
+    if (p.out_map == OUT_FRAG) {
+        const int64_t r = n / p.nloc;
+        return r * act_rows(p.M) * p.nloc + act_frag_offset(m, n - r * p.nloc, p.nloc / 32);
+    }
     if (p.out_map == OUT_SHARDED) {
         int64_t r = n / p.nloc;
         return (r * p.M + m) * p.nloc + (n - r * p.nloc);

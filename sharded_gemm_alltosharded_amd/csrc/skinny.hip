@@ -99,14 +99,19 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Problem p) {
     const int wstep = FP8 ? 1024 : (p.wfrag ? 512 : 32);
     constexpr int KS = FP8 ? 64 : 32;  // k per step
     constexpr int XF = FP8 ? 2 : 1;    // activation fragments per step
+    // activations: row-major (lane's 16 bytes at m * lda + k), or fragment-major
+    // (act_frag_offset: the 16 tokens x 32 inputs of a step are one 1 KB, lane l
+    // at 8 l), elements per 32-wide k step xstep
     int64_t xoff[MT];
     bool xok[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         const int m = mt * 16 + (lane & 15);
         xok[mt] = m < p.M;
-        xoff[mt] = (int64_t)(xok[mt] ? m : 0) * p.lda + kq;
+        xoff[mt] = p.xfrag ? act_frag_offset(mt * 16 + (lane & 15), kq, p.Kseg / 32)
+                           : (int64_t)(xok[mt] ? m : 0) * p.lda + kq;
     }
+    const int64_t xstep = p.xfrag ? 512 : 32;
 
     const u32x4 zero = {0u, 0u, 0u, 0u};
     const int nsteps = (p.Kseg + KS - 1) / KS;
@@ -153,7 +158,7 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Problem p) {
                 for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                     for (int f = 0; f < XF; ++f)
-                        xv[buf][q][mt][f] = (ok && xok[mt]) ? *(const u32x4*)(Ab + xoff[mt] + k0 + 32 * f) : zero;
+                        xv[buf][q][mt][f] = (ok && xok[mt]) ? *(const u32x4*)(Ab + xoff[mt] + (int64_t)(k0 / 32 + f) * xstep) : zero;
             }
         };
         auto compute = [&](int buf) {

@@ -111,6 +111,9 @@ def test_forward_calls_validate_first(L):
     assert L.sg_layer_info(None, None, None, None, None, None, None, None) == sg.ERR_INVALID_ARG
     assert L.sg_layer_copy_shard(None, 0, 0, None, 0, None) == sg.ERR_INVALID_ARG
     L.sg_layer_free(None)  # ignored
+    assert L.sg_mlp(None, None, None, 4, None, sg.BF16, None, 0, None) == sg.ERR_INVALID_ARG
+    assert "NULL" in _err(L)
+    assert L.sg_mlp_workspace(None, None, 4) == 0
 
 
 def test_summa_rules(L):

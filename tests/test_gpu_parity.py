@@ -181,6 +181,67 @@ def test_mlp_chain_bf16():
     assert_close(y, ref, "bf16", "mlp")
 
 
+# sg_mlp: the same chain with h kept (fragment-major on the streaming path) in
+# the workspace.  The kernels and their arithmetic are those of the separate
+# calls, so the results must agree bit for bit; B = 40 takes the tile kernels
+# and the row-major h.
+MLP_CASES = [("bf16", 1, 512, 1024, 4), ("bf16", 16, 512, 1024, 8), ("f16", 20, 256, 512, 2),
+             ("bf16", 32, 512, 1024, 4), ("bf16", 7, 256, 768, 3), ("bf16", 40, 256, 512, 2)]
+
+
+@pytest.mark.parametrize("case", MLP_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_mlp_entry_point(case):
+    dtype, B, D, F, P = case
+    _print_case(dtype=dtype, B=B, D=D, F=F, P=P)
+    inp = synth.mlp_inputs(B, D, F, P, dtype, seed=31)
+    bd = synth.uniform(32, (D,), 0.5, dtype)
+    gu = sg.shard_linear(to_dev(np.concatenate([inp.Wg, inp.Wu]), dtype), "all-to-sharded", segments=2, P=P)
+    dn = sg.shard_linear(to_dev(inp.Wd, dtype), "sharded-to-all", P=P, bias=to_dev(bd, dtype))
+    x = to_dev(inp.X, dtype)
+    y = sg.mlp(gu, dn, x, out_dtype=torch.float32)
+    h = sg.all_to_sharded(gu, x, swiglu=True)
+    assert torch.equal(y, sg.sharded_to_all(dn, h, out_dtype=torch.float32))
+    assert torch.equal(y, sg.mlp(gu, dn, x, out_dtype=torch.float32))  # the workspace carries no state
+    g = oracle.col(inp.X, inp.Wg, P=P, dtype=dtype)
+    u = oracle.col(inp.X, inp.Wu, P=P, dtype=dtype)
+    ref = oracle.row(oracle.swiglu(g, u, dtype), inp.Wd, P=P, bias=bd, dtype=dtype)
+    assert_close(y, ref, "f32", "mlp")
+    y16 = sg.mlp(gu, dn, x)
+    assert torch.equal(y16, sg.sharded_to_all(dn, h))
+
+
+def test_mlp_entry_point_quantized():
+    """MX FP8 layers (streaming path, fragment-major h) and 4-bit layers (the
+    separate calls' path) against the separate calls, bitwise."""
+    B, D, F, P = 16, 512, 1024, 4
+    _print_case(B=B, D=D, F=F, P=P)
+    ws = [synth.uniform(33 + i, shp, 1 / np.sqrt(D), "f32") for i, shp in enumerate([(F, D), (F, D), (D, F)])]
+    X = to_dev(synth.normal(36, (B, D), 1.0, "bf16"), "bf16")
+    gu, _, _, _ = _mx_layer(np.concatenate([ws[0], ws[1]]), 0, P, S=2)
+    dn, _, _, _ = _mx_layer(ws[2], 1, P)
+    assert torch.equal(sg.mlp(gu, dn, X), sg.sharded_to_all(dn, sg.all_to_sharded(gu, X, swiglu=True)))
+    qgu, _ = _q4_layer(np.concatenate([ws[0], ws[1]]), 0, P, S=2)
+    qdn, _ = _q4_layer(ws[2], 1, P)
+    assert torch.equal(sg.mlp(qgu, qdn, X), sg.sharded_to_all(qdn, sg.all_to_sharded(qgu, X, swiglu=True)))
+
+
+def test_mlp_rejections():
+    D, F = 256, 512
+    w = to_dev(synth.uniform(37, (2 * F, D), 1 / 16, "bf16"), "bf16")
+    wd = to_dev(synth.uniform(38, (D, F), 1 / 16, "bf16"), "bf16")
+    gu = sg.shard_linear(w, "all-to-sharded", segments=2, P=2)
+    dn = sg.shard_linear(wd, "sharded-to-all", P=2)
+    x = to_dev(synth.normal(39, (4, D), 1.0, "bf16"), "bf16")
+    for a, b in [(dn, gu), (gu, sg.shard_linear(wd, "sharded-to-all", P=4)),
+                 (sg.shard_linear(w, "all-to-sharded", segments=1, P=2), dn)]:
+        with pytest.raises(sg.ShardGemmError):
+            sg.mlp(a, b, x)
+    need = sg.lib().sg_mlp_workspace(gu.handle, dn.handle, 4)
+    assert need > 0
+    with pytest.raises(sg.ShardGemmError, match="workspace"):
+        sg.mlp(gu, dn, x, ws=torch.zeros(need - 16, dtype=torch.uint8, device=dev()))
+
+
 def test_qkv_segments():
     """Fused [Wq; Wk; Wv] with segments = 3: rank r holds [Q_r; K_r; V_r]."""
     B, D, heads, hd, P = 64, 256, 8, 32, 4
