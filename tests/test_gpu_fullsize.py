@@ -45,6 +45,8 @@ def test_decode_mlp_full():
     # the fused rank sum is deterministic
     y2 = sg.sharded_to_all(dn, h)
     assert torch.equal(y, y2)
+    # the fused MLP entry point bench.py times: bit for bit the chain above
+    assert torch.equal(sg.mlp(gu, dn, x), y)
 
 
 def test_mxfp8_mlp_full():
@@ -66,6 +68,7 @@ def test_mxfp8_mlp_full():
     g, u = oracle.col(Xd, Wgu[:F], P=P), oracle.col(Xd, Wgu[F:], P=P)
     assert_close(h, oracle.swiglu(g, u, "f64"), "bf16", "h")
     assert_close(y, oracle.row(oracle.swiglu(g, u, "bf16"), Wd, P=P), "bf16", "y")
+    assert torch.equal(sg.mlp(gu, dn, to_dev(X, "bf16")), y)  # the entry point bench.py times
 
 
 def test_prefill_full_sampled():
