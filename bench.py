@@ -7,7 +7,8 @@ A step is one pass of the workload's whole sharded path over one batch of
 synthetic inputs already resident in HBM.  The default workload is the
 Llama-style gated MLP decode step (B=16 tokens, D=4096, F=14336, P=8 ranks on
 one GPU, bf16): gate/up all-to-sharded with the fused SwiGLU epilogue, then
-down sharded-to-all with the fused rank sum.  Other workloads:
+down sharded-to-all with the fused rank sum, through the fused MLP entry point
+(sg_mlp, the sharded h kept in its workspace).  Other workloads:
 
     3   prefill: B=4096, P=4, fused QKV column shard (segments=3) + the MLP
     4   4-bit affine MLP (group 64), B in {1, 8, 32} (--batch), P=4
