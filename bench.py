@@ -251,9 +251,8 @@ class Q4MLP(Workload):
         self.gu = [sg.shard_quantized_linear(*gt, D, "all-to-sharded", segments=2, P=P) for _ in range(self.rotate)]
         self.dn = [sg.shard_quantized_linear(*dt, F, "sharded-to-all", P=P) for _ in range(self.rotate)]
         del gt, dt
-        self.h = torch.empty((P, B, F // P), dtype=torch.bfloat16, device="cuda")
         self.y = torch.empty((B, D), dtype=torch.bfloat16, device="cuda")
-        self.ws = sg.workspace(self.dn[0], B, "cuda")
+        self.ws = sg.mlp_workspace(self.gu[0], self.dn[0], B, "cuda")  # the down workspace, then the sharded h
         self.sg = sg
         wbytes = lambda rows, cols: rows * cols // 2 + 2 * 2 * rows * (cols // 64)
         self.units = wbytes(2 * F, D) + wbytes(D, F) + 2 * (B * D + 2 * B * F + B * D)
@@ -264,8 +263,7 @@ class Q4MLP(Workload):
         k = i % self.rotate
         if ev:
             sg.time_next_launch(*ev)
-        sg.all_to_sharded(self.gu[k], self.x, swiglu=True, out=self.h)
-        sg.sharded_to_all(self.dn[k], self.h, out=self.y, ws=self.ws)
+        sg.mlp(self.gu[k], self.dn[k], self.x, out=self.y, ws=self.ws)
 
     def config(self):
         return {"workload": self.name, "tokens": self.B, "D": self.D, "F": self.F, "P": self.P,

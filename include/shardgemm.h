@@ -180,9 +180,9 @@ sg_status sg_sharded_to_all_ex(const sg_layer* layer, const void* x_partial, int
  *            aligned, zero-filled before its first use: the down layer's
  *            sg_sharded_to_all workspace first (its arrival counters, kept zero
  *            by every call, at offset 0 for every B), then h (when both layers
- *            run on the streaming kernel, stored fragment-major so that the
- *            down layer reads each 16-token x 32-input operand as one
- *            contiguous 1 KB).  The same workspace serves later calls of any B
+ *            run on a streaming kernel and B >= 8, stored fragment-major in
+ *            the down kernel's operand order so that it reads each 16-token
+ *            operand fragment as one contiguous 1 KB).  The same workspace serves later calls of any B
  *            it is large enough for; calls sharing it must not run concurrently.
  * Errors: SG_ERR_INVALID_ARG for layers that do not form such a pair (the
  * message says which rule fails), SG_ERR_WORKSPACE for a missing, small or

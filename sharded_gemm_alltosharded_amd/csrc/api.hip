@@ -215,8 +215,9 @@ Kind choose_row(const sg_layer* l, int64_t B) {
 }
 
 hipError_t run(const sg::Problem& p, Kind k, hipStream_t st) {
-    // fragment-major activations (the fused MLP's h) exist for the streaming kernel only
-    if ((p.xfrag || p.out_map == sg::OUT_FRAG) && k != K_SKINNY) return hipErrorInvalidValue;
+    // fragment-major activations (the fused MLP's h) exist for the streaming kernels only
+    if ((p.xfrag || p.out_map == sg::OUT_FRAG || p.out_map == sg::OUT_FRAG_Q4) && k != K_SKINNY && k != K_Q4)
+        return hipErrorInvalidValue;
     switch (k) {
     case K_TILE0: return sg::launch_tile(p, st, 0);
     case K_TILE1: return sg::launch_tile(p, st, 1);
@@ -684,13 +685,39 @@ sg_status sg_mlp(const sg_layer* gate_up, const sg_layer* down, const void* x, i
     void* h = (char*)workspace + db;
     const sg_layer* gu = gate_up;
     const sg_layer* dn = down;
-    // Both layers on the streaming kernel: h fragment-major, so that the down
-    // layer's activation loads are contiguous 1 KB reads (the row-major h of
-    // the separate calls costs each load 16 rows x 64 bytes).  Otherwise the
-    // two separate calls with a row-major h.
-    const bool fused = choose(gu, B, x, 1, 1) == K_SKINNY && choose_row(dn, B) == K_SKINNY && dn->wfrag &&
-                       aligned16(y) && aligned16(dn->w) && (dn->cols_r % 32) == 0;
-    if (!fused) {
+    // the down layer reading h fragment-major
+    sg::Problem q{};
+    q.A = h;
+    q.xfrag = 1;
+    q.a_seg = sg::act_rows(B) * dn->cols_r;
+    q.M = (int)B;
+    q.Kseg = (int)dn->cols_r;
+    q.nseg = dn->P;
+    q.dtype = dn->dtype;
+    set_weights(q, dn);
+    q.N = (int)dn->out_dims;
+    q.out = y;
+    q.out_dtype = y_dtype;
+    q.out_map = sg::OUT_ROWMAJOR;
+    q.ldo = q.N;
+    q.bias = dn->bias;
+    // Both layers on a streaming kernel and at least 8 tokens: h fragment-major
+    // in the order the down kernel reads (skinny.hip: act_frag_offset; 4-bit,
+    // the 16-row kernel: act_frag_offset_q4), so that its activation loads are
+    // contiguous 1 KB reads instead of 16 rows x 64 bytes (measured on the
+    // 4-bit down projection: 16.2 -> 13.7 us at 8 tokens, 33.0 -> 18.8 us at
+    // 32).  With fewer tokens a row-major load touches fewer cache lines than
+    // a 1 KB fragment (13.1 against 13.5 us at one token), so the two separate
+    // calls with a row-major h run instead, as for every other pair.
+    const Kind kg = choose(gu, B, x, 1, 1), kd = choose_row(dn, B);
+    const bool frag_pays = B >= 8;
+    int hmap = -1;
+    if (frag_pays && kg == K_SKINNY && kd == K_SKINNY && dn->wfrag && aligned16(y) && aligned16(dn->w) &&
+        dn->cols_r % 32 == 0)
+        hmap = sg::OUT_FRAG;
+    else if (frag_pays && kg == K_Q4 && kd == K_Q4 && sg::q4s_takes(q))
+        hmap = sg::OUT_FRAG_Q4;
+    if (hmap < 0) {
         sg_status st = sg_all_to_sharded_ex(gu, x, SG_IN_FULL, B, h, SG_OUT_SHARDED, SG_EPI_SWIGLU, gu->dtype, stream);
         if (st != SG_OK) return st;
         return sg_sharded_to_all_ex(dn, h, B, y, SG_OUT_FULL, y_dtype, workspace, db, stream);
@@ -708,26 +735,11 @@ sg_status sg_mlp(const sg_layer* gate_up, const sg_layer* down, const void* x, i
     p.floc = gu->rows_r / 2;
     p.out = h;
     p.out_dtype = gu->dtype;
-    p.out_map = sg::OUT_FRAG;
+    p.out_map = hmap;
     p.nloc = p.N / gu->P;
-    hipError_t e = run(p, K_SKINNY, (hipStream_t)stream);
+    hipError_t e = run(p, kg, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "mlp gate|up launch");
-    sg::Problem q{};
-    q.A = h;
-    q.xfrag = 1;
-    q.a_seg = sg::act_rows(B) * dn->cols_r;
-    q.M = (int)B;
-    q.Kseg = (int)dn->cols_r;
-    q.nseg = dn->P;
-    q.dtype = dn->dtype;
-    set_weights(q, dn);
-    q.N = (int)dn->out_dims;
-    q.out = y;
-    q.out_dtype = y_dtype;
-    q.out_map = sg::OUT_ROWMAJOR;
-    q.ldo = q.N;
-    q.bias = dn->bias;
-    e = run(q, K_SKINNY, (hipStream_t)stream);
+    e = run(q, kd, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "mlp down launch");
     return SG_OK;
 }

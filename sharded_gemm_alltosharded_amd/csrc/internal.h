@@ -25,7 +25,7 @@ namespace sg {
 //    logical output column j (0 .. N-1, N = P * floc) pairs gate row and up row
 //    of rank j / floc, and the kernel stores silu(g) * u.
 // ---------------------------------------------------------------------------
-enum OutMap { OUT_ROWMAJOR = 0, OUT_SHARDED = 1, OUT_FRAG = 2 };
+enum OutMap { OUT_ROWMAJOR = 0, OUT_SHARDED = 1, OUT_FRAG = 2, OUT_FRAG_Q4 = 3 };
 
 struct Problem {
     const void* A;
@@ -49,7 +49,8 @@ struct Problem {
     const uint8_t* ms;
     int64_t ms_seg;
     int qfrag;      // 4-bit codes / scales / biases stored fragment-major (q4 offsets)
-    int xfrag;      // A is a fragment-major sharded activation (act_frag_offset; streaming kernel only)
+    int xfrag;      // A is a fragment-major sharded activation in the reading kernel's order
+                    // (act_frag_offset for skinny.hip, act_frag_offset_q4 for q4s.hip)
     int swiglu;     // fused gate/up pairs
     int64_t floc;   // rank width of the swiglu output (rows per gate block)
     // epilogue
@@ -84,6 +85,14 @@ __host__ __device__ inline int64_t frag_offset(int64_t row, int64_t k, int64_t n
 __host__ __device__ inline int64_t act_rows(int64_t M) { return (M + 15) / 16 * 16; }
 __host__ __device__ inline int64_t act_frag_offset(int64_t m, int64_t k, int64_t nsteps) {
     return frag_offset(m, k, nsteps);
+}
+// The same for the 16-row 4-bit kernel's k order: inside a group of 64 inputs
+// the lane with chunk slot c feeds k = 16 c + 8 u + e to its MFMA step u, so
+// input k is stored at k' = 32 u + 8 c + e of the group (two 1 KB fragments
+// per 16 tokens and group, one per step).
+__host__ __device__ inline int64_t act_frag_offset_q4(int64_t m, int64_t k, int64_t nsteps) {
+    const int64_t kp = (k & ~(int64_t)63) | (((k >> 3) & 1) << 5) | (((k >> 4) & 3) << 3) | (k & 7);
+    return frag_offset(m, kp, nsteps);
 }
 
 // E4M3 codes of a fragment-major MX FP8 layer: for each 16-row block and pair
@@ -180,6 +189,7 @@ struct Q4Shape {
 SkinnyShape skinny_shape(int M, int N, int nseg, int swiglu);
 Q4Shape q4_shape(int M, int N, int nseg, int swiglu);
 SkinnyShape q4s_shape(int M, int N, int nseg, int swiglu);
+bool q4s_takes(const Problem& p);  // launch_q4 runs p on the 16-row kernel (q4s.hip)
 constexpr size_t kMaxStreamLds = 64 * 1024;
 int tile_count(int M, int N, int variant);
 inline size_t split_workspace_bytes(SplitLayout s) { return kPartialsOffset + s.floats * sizeof(float); }
@@ -254,9 +264,10 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 // output address of logical element (m, n)
 __device__ __forceinline__ int64_t out_index(const Problem& p, int m, int64_t n) {
-    if (p.out_map == OUT_FRAG) {
-        const int64_t r = n / p.nloc;
-        return r * act_rows(p.M) * p.nloc + act_frag_offset(m, n - r * p.nloc, p.nloc / 32);
+    if (p.out_map == OUT_FRAG || p.out_map == OUT_FRAG_Q4) {
+        const int64_t r = n / p.nloc, c = n - r * p.nloc;
+        return r * act_rows(p.M) * p.nloc +
+               (p.out_map == OUT_FRAG ? act_frag_offset(m, c, p.nloc / 32) : act_frag_offset_q4(m, c, p.nloc / 32));
     }
     if (p.out_map == OUT_SHARDED) {
         int64_t r = n / p.nloc;

@@ -293,6 +293,10 @@ static hipError_t launch_f(const Problem& p, hipStream_t s, const Q4Shape& sh) {
     }
 }
 
+bool q4s_takes(const Problem& p) {
+    return !p.swiglu && p.M <= 32 && p.Kseg % 256 == 0 && q4s_shape(p.M, p.N, p.nseg, 0).lds <= kMaxStreamLds;
+}
+
 hipError_t launch_q4(const Problem& p, hipStream_t s) {
     if (p.M == 0 || p.N == 0) return hipSuccess;
     if (!p.qfrag) return hipErrorInvalidValue;  // the streaming kernel reads the fragment layout
@@ -300,8 +304,8 @@ hipError_t launch_q4(const Problem& p, hipStream_t s) {
     // many ranks) run on 16-row blocks (q4s.hip), which give twice the
     // workgroups; measured on the 4-bit MLP shapes, the gate|up layer is faster
     // on 32-row blocks and the down layer on 16-row blocks.
-    if (!p.swiglu && p.M <= 32 && p.Kseg % 256 == 0 && q4s_shape(p.M, p.N, p.nseg, 0).lds <= kMaxStreamLds)
-        return launch_q4s(p, s);
+    if (q4s_takes(p)) return launch_q4s(p, s);
+    if (p.xfrag) return hipErrorInvalidValue;  // fragment-major activations: the 16-row kernel only
     const Q4Shape sh = q4_shape(p.M, p.N, p.nseg, p.swiglu);
     return p.dtype == SG_F16 ? launch_f<true>(p, s, sh) : launch_f<false>(p, s, sh);
 }

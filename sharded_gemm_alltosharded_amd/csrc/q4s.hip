@@ -97,8 +97,11 @@ __global__ __launch_bounds__(NW * 64) void q4s_kernel(Problem p) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         const int t = mt * 16 + (lane & 15);
-        xoff[mt] = (int64_t)(t < p.M ? t : 0) * p.lda + 16 * c;  // group g at + 64 g
+        // row-major: group g at + 64 g (steps u = 0, 1 at + 0, + 8); fragment-major
+        // (act_frag_offset_q4): group g at + 1024 g (steps at + 0, + 512)
+        xoff[mt] = p.xfrag ? act_frag_offset_q4(t, 16 * c, p.Kseg / 32) : (int64_t)(t < p.M ? t : 0) * p.lda + 16 * c;
     }
+    const int64_t xg = p.xfrag ? 1024 : 64, xu = p.xfrag ? 512 : 8;  // elements per group, per step
     const u32x4 ones = F16 ? u32x4{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u}
                            : u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
 
@@ -135,8 +138,8 @@ __global__ __launch_bounds__(NW * 64) void q4s_kernel(Problem p) {
                 f32x4 xs[MT];
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
-                    xf[mt][0] = *(const u32x4*)(Ab + xoff[mt] + g * 64);
-                    xf[mt][1] = *(const u32x4*)(Ab + xoff[mt] + g * 64 + 8);
+                    xf[mt][0] = *(const u32x4*)(Ab + xoff[mt] + g * xg);
+                    xf[mt][1] = *(const u32x4*)(Ab + xoff[mt] + g * xg + xu);
                     xs[mt] = mfma16<F16>(xf[mt][0], ones, f32x4{0.f, 0.f, 0.f, 0.f});
                     xs[mt] = mfma16<F16>(xf[mt][1], ones, xs[mt]);
                 }

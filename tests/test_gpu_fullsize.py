@@ -124,6 +124,7 @@ def test_q4_mlp_full(q4_weights, B):
     g, u = oracle.col(Xs, W["gate"], P=P), oracle.col(Xs, W["up"], P=P)
     assert_close(h[:, idx, :], oracle.swiglu(g, u, "f64"), "bf16", "h")
     assert_close(y[idx], oracle.row(oracle.swiglu(g, u, "bf16"), W["down"], P=P), "bf16", "y")
+    assert torch.equal(sg.mlp(gu, dn, to_dev(X, "bf16")), y)  # the entry point bench.py times
 
 
 @pytest.mark.parametrize("fused", [True, False])

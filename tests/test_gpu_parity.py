@@ -210,10 +210,11 @@ def test_mlp_entry_point(case):
     assert torch.equal(y16, sg.sharded_to_all(dn, h))
 
 
-def test_mlp_entry_point_quantized():
-    """MX FP8 layers (streaming path, fragment-major h) and 4-bit layers (the
-    separate calls' path) against the separate calls, bitwise."""
-    B, D, F, P = 16, 512, 1024, 4
+@pytest.mark.parametrize("B", [1, 8, 16, 32])
+def test_mlp_entry_point_quantized(B):
+    """MX FP8 and 4-bit layers (streaming kernels, h fragment-major in each
+    down kernel's k order) against the separate calls, bitwise."""
+    D, F, P = 512, 1024, 4
     _print_case(B=B, D=D, F=F, P=P)
     ws = [synth.uniform(33 + i, shp, 1 / np.sqrt(D), "f32") for i, shp in enumerate([(F, D), (F, D), (D, F)])]
     X = to_dev(synth.normal(36, (B, D), 1.0, "bf16"), "bf16")
