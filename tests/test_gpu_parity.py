@@ -226,6 +226,25 @@ def test_mlp_entry_point_quantized(B):
     assert torch.equal(sg.mlp(qgu, qdn, X), sg.sharded_to_all(qdn, sg.all_to_sharded(qgu, X, swiglu=True)))
 
 
+def test_mlp_shared_workspace_across_sizes():
+    """One workspace for calls of different B: the fallback path at B = 40
+    (its down layer splits by rank through the arrival counters at offset 0)
+    and the fragment-major path at B = 16 alternate; every call matches the
+    separate calls bit for bit."""
+    D, F, P = 256, 512, 2
+    inp = synth.mlp_inputs(40, D, F, P, "bf16", seed=40)
+    gu = sg.shard_linear(to_dev(np.concatenate([inp.Wg, inp.Wu]), "bf16"), "all-to-sharded", segments=2, P=P)
+    dn = sg.shard_linear(to_dev(inp.Wd, "bf16"), "sharded-to-all", P=P)
+    need = max(sg.lib().sg_mlp_workspace(gu.handle, dn.handle, b) for b in (16, 40))
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev())
+    for B in (40, 16, 40, 16, 40):
+        _print_case(B=B)
+        x = to_dev(inp.X[:B], "bf16")
+        y = sg.mlp(gu, dn, x, out_dtype=torch.float32, ws=ws)
+        ref = sg.sharded_to_all(dn, sg.all_to_sharded(gu, x, swiglu=True), out_dtype=torch.float32)
+        assert torch.equal(y, ref), B
+
+
 def test_mlp_rejections():
     D, F = 256, 512
     w = to_dev(synth.uniform(37, (2 * F, D), 1 / 16, "bf16"), "bf16")
