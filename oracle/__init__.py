@@ -19,6 +19,10 @@ deq4        4-bit affine dequantisation                             hand-packed 
 deq_mx8     MX FP8 dequantisation (E4M3 x E8M0 per 32)              closed forms, hand bytes
 summa       q-step block accumulation Y_ij += X_it A_tj             brute force, q-independence
 mlp         col(gate), col(up) -> swiglu -> row(down)               composition of the above
+col_bwd     VJP of all_to_sharded: dx = all_sum of dY_r W_r, dW_r   finite differences of col,
+            = dY_r^T X                                              unsharded identity
+row_bwd     VJP of sharded_to_all: dX_r = dY W_r, dW_r = dY^T X_r   finite differences of row,
+                                                                    unsharded identity
 all_gather  input shards (P, B, k) -> (B, P k), rank order          index arrays, brute force
 reduce_     summed (B, n) result -> (P, B, n/P), rank r's columns   index arrays, brute force
  scatter
@@ -236,6 +240,36 @@ def mlp(X, Wg, Wu, Wd, P, round_dtype="bf16", dtype=None) -> np.ndarray:
     Y = np.empty((B, D), dtype=np.float64)
     _check(lib().or_mlp(_p(X), B, D, F, _p(Wg), _p(Wu), _p(Wd), P, _DT[round_dtype], _p(Y)), "mlp")
     return Y
+
+
+def col_bwd(X, W, dY, P, S=1, dtype=None):
+    """Vector-Jacobian product of the all-to-sharded layer Y_r = X W_r^T (MLX
+    tensor-parallel guide, section 2.1 and the sum_gradients wrapper of
+    section 2.1/6): the input X is used by every rank, so its gradient is the
+    all_sum over ranks of dY_r W_r (summed here in rank order, in fp64); rank
+    r's weight gradient is dY_r^T X.  dY: (P, B, out/P) in the layer's output
+    layout.  Returns (dx (B, in), dW (P, out/P, in)); dW[r] is laid out as
+    slice_(W, 0, S, P, r).  A matmul is the library step here."""
+    X, W, dY = _f64(X, dtype), _f64(W, dtype), _f64(dY, dtype)
+    Ws = [slice_(W, 0, S, P, r) for r in range(P)]
+    dx = np.zeros((X.shape[0], W.shape[1]))
+    for r in range(P):
+        dx = dx + dY[r] @ Ws[r]
+    dW = np.stack([dY[r].T @ X for r in range(P)])
+    return dx, dW
+
+
+def row_bwd(Xs, W, dY, P, dtype=None):
+    """Vector-Jacobian product of the sharded-to-all layer Y = sum_r Xs_r W_r^T
+    (+ b) (MLX guide, section 2.2): the gradient reaching every rank is the
+    full dY, so rank r's input gradient is dY W_r (no communication: it stays
+    sharded like Xs) and its weight gradient dY^T Xs_r.  Xs: (P, B, in/P),
+    dY: (B, out).  Returns (dXs (P, B, in/P), dW (P, out, in/P))."""
+    Xs, W, dY = _f64(Xs, dtype), _f64(W, dtype), _f64(dY, dtype)
+    Ws = [slice_(W, 1, 1, P, r) for r in range(P)]
+    dXs = np.stack([dY @ Ws[r] for r in range(P)])
+    dW = np.stack([dY.T @ Xs[r] for r in range(P)])
+    return dXs, dW
 
 
 def all_gather(Xs) -> np.ndarray:

@@ -436,3 +436,70 @@ def test_deq_mx8_then_linear_matches_bruteforce():
     ref = bf_linear(_fr(X), Wf)
     for r in range(2):
         np.testing.assert_array_equal(got[r], np.array([row[2 * r:2 * r + 2] for row in ref], dtype=np.float64))
+
+
+# ---------------------------------------------------------------------------
+# Backward ("MLX 张量并行实战指南" sections 2.1-2.2: sum_gradients; the VJPs of
+# the two layers).  Pinned to the forward oracle by central finite differences
+# of the linear loss L = sum(G * Y): the layers are linear in X and in W, so
+# the difference quotient equals the gradient up to rounding.
+# ---------------------------------------------------------------------------
+def _fd(f, A, h=0.5):
+    g = np.zeros_like(A)
+    for idx in np.ndindex(*A.shape):
+        Ap, Am = A.copy(), A.copy()
+        Ap[idx] += h
+        Am[idx] -= h
+        g[idx] = (f(Ap) - f(Am)) / (2 * h)
+    return g
+
+
+@pytest.mark.parametrize("S,P", [(1, 2), (2, 2), (1, 3), (1, 1)])
+def test_col_bwd_finite_differences(S, P):
+    rng = np.random.default_rng(50 + S + 10 * P)
+    B, inn, out = 3, 5, 12
+    X, W = rng.standard_normal((B, inn)), rng.standard_normal((out, inn))
+    G = rng.standard_normal((P, B, out // P))
+    loss_x = lambda Xv: float(np.sum(G * oracle.col(Xv, W, P=P, S=S)))
+    loss_w = lambda Wv: float(np.sum(G * oracle.col(X, Wv, P=P, S=S)))
+    dx, dW = oracle.col_bwd(X, W, G, P=P, S=S)
+    np.testing.assert_allclose(dx, _fd(loss_x, X), rtol=1e-10, atol=1e-10)
+    gW = _fd(loss_w, W)
+    for r in range(P):
+        np.testing.assert_allclose(dW[r], oracle.slice_(gW, 0, S, P, r), rtol=1e-10, atol=1e-10)
+
+
+def test_col_bwd_unsharded_identity():
+    """The all_sum of the rank gradients is the unsharded gradient dY W."""
+    rng = np.random.default_rng(60)
+    B, inn, out, P = 4, 8, 16, 4
+    X, W, dYf = rng.standard_normal((B, inn)), rng.standard_normal((out, inn)), rng.standard_normal((B, out))
+    G = dYf.reshape(B, P, out // P).transpose(1, 0, 2)  # rank r holds columns [r out/P, (r+1) out/P)
+    dx, dW = oracle.col_bwd(X, W, G, P=P)
+    np.testing.assert_allclose(dx, dYf @ W, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(np.concatenate(list(dW)), dYf.T @ X, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("P", [1, 2, 4])
+def test_row_bwd_finite_differences(P):
+    rng = np.random.default_rng(70 + P)
+    B, inn, out = 3, 8, 5
+    Xs, W = rng.standard_normal((P, B, inn // P)), rng.standard_normal((out, inn))
+    G = rng.standard_normal((B, out))
+    loss_x = lambda Xv: float(np.sum(G * oracle.row(Xv, W, P=P)))
+    loss_w = lambda Wv: float(np.sum(G * oracle.row(Xs, Wv, P=P)))
+    dXs, dW = oracle.row_bwd(Xs, W, G, P=P)
+    np.testing.assert_allclose(dXs, _fd(loss_x, Xs), rtol=1e-10, atol=1e-10)
+    gW = _fd(loss_w, W)
+    for r in range(P):
+        np.testing.assert_allclose(dW[r], oracle.slice_(gW, 1, 1, P, r), rtol=1e-10, atol=1e-10)
+
+
+def test_row_bwd_unsharded_identity():
+    rng = np.random.default_rng(80)
+    B, inn, out, P = 4, 12, 6, 3
+    X, W, dY = rng.standard_normal((B, inn)), rng.standard_normal((out, inn)), rng.standard_normal((B, out))
+    Xs = X.reshape(B, P, inn // P).transpose(1, 0, 2)
+    dXs, dW = oracle.row_bwd(Xs, W, dY, P=P)
+    np.testing.assert_allclose(np.concatenate(list(dXs), axis=1), dY @ W, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(np.concatenate(list(dW), axis=1), dY.T @ X, rtol=1e-12, atol=1e-12)
