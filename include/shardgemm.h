@@ -194,6 +194,32 @@ sg_status sg_mlp(const sg_layer* gate_up, const sg_layer* down, const void* x, i
  * a gate|up, down pair or B <= 0). */
 size_t sg_mlp_workspace(const sg_layer* gate_up, const sg_layer* down, int64_t B);
 
+/* Backward of an all-to-sharded layer: the vector-Jacobian product of [MLX]
+ * 2.1 with its sum_gradients wrapper.  The input x is shared by every rank,
+ * so its gradient is the all_sum of the rank gradients, summed here on chip in
+ * rank order:
+ *   dx (B, in_dims) of dx_dtype = sum over r = 0..P-1 of dy[r] W_r;
+ *   dw (P, out_dims/P, in_dims) of dw_dtype, dw[r] = dy[r]^T x, laid out like
+ *      rank r's shard (the rows sg_layer_copy_shard returns, segments rule).
+ *   x  (B, in_dims) of the layer's dtype (needed for dw only; may be NULL
+ *      otherwise); dy (P, B, out_dims/P) of the layer's dtype, the layout of
+ *      the forward's sharded output.
+ * dx or dw may be NULL (not both).  Dense layers only (SG_ERR_UNSUPPORTED for
+ * 4-bit and MX FP8 layers); no bias gradient.  fp32 accumulation; the rank sum
+ * is deterministic.  B = 0 is a no-op. */
+sg_status sg_all_to_sharded_backward(const sg_layer* layer, const void* x, const void* dy, int64_t B, void* dx,
+                                     sg_dtype dx_dtype, void* dw, sg_dtype dw_dtype, void* stream);
+
+/* Backward of a sharded-to-all layer ([MLX] 2.2): every rank receives the
+ * full gradient dy (B, out_dims) of the summed output, so
+ *   dx_partial (P, B, in_dims/P) of dx_dtype, slice r = dy W_r (stays sharded,
+ *      no reduction);
+ *   dw (P, out_dims, in_dims/P) of dw_dtype, dw[r] = dy^T x_partial[r].
+ *   x_partial (P, B, in_dims/P) of the layer's dtype (for dw only).
+ * Everything else as sg_all_to_sharded_backward. */
+sg_status sg_sharded_to_all_backward(const sg_layer* layer, const void* x_partial, const void* dy, int64_t B,
+                                     void* dx_partial, sg_dtype dx_dtype, void* dw, sg_dtype dw_dtype, void* stream);
+
 /* Bytes of workspace sg_sharded_to_all needs for B tokens (0 on bad input). */
 size_t sg_sharded_to_all_workspace(const sg_layer* layer, int64_t B);
 

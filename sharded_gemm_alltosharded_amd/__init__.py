@@ -13,6 +13,8 @@ kernels.  The entry points mirror include/shardgemm.h one to one:
     sharded_to_all             sg_sharded_to_all_ex (+ sg_sharded_to_all_workspace; all-reduce or
                                reduce-scatter output)
     mlp                        sg_mlp (+ sg_mlp_workspace): gate|up with SwiGLU, then down
+    all_to_sharded_backward    sg_all_to_sharded_backward (dx = rank-order all_sum, dw)
+    sharded_to_all_backward    sg_sharded_to_all_backward (sharded dx, dw)
     summa_matmul               sg_summa_matmul (+ sg_summa_workspace)
     Layer.info / Layer.shard   sg_layer_info / sg_layer_copy_shard
     time_next_launch           sg_time_next_launch (profiling)
@@ -75,6 +77,8 @@ def lib():
             "sg_all_to_sharded_ex": ([P, P, I, I64, P, I, I, I, P], I),
             "sg_sharded_to_all": ([P, P, I64, P, I, P, SZ, P], I),
             "sg_sharded_to_all_ex": ([P, P, I64, P, I, I, P, SZ, P], I),
+            "sg_all_to_sharded_backward": ([P, P, P, I64, P, I, P, I, P], I),
+            "sg_sharded_to_all_backward": ([P, P, P, I64, P, I, P, I, P], I),
             "sg_mlp": ([P, P, P, I64, P, I, P, SZ, P], I),
             "sg_mlp_workspace": ([P, P, I64], SZ),
             "sg_sharded_to_all_workspace": ([P, I64], SZ),
@@ -307,6 +311,37 @@ def mlp(gate_up: Layer, down: Layer, x: torch.Tensor, out_dtype=None, out: torch
     _check(lib().sg_mlp(gate_up.handle, down.handle, _ptr(x), B, _ptr(out), _DT.get(out.dtype, -1), _ptr(ws),
                         nbytes, _stream(x.device)))
     return out
+
+
+def all_to_sharded_backward(layer: Layer, x: torch.Tensor | None, dy: torch.Tensor, need_dx: bool = True,
+                            need_dw: bool = True, dx_dtype=None, dw_dtype=torch.float32):
+    """Backward of an all-to-sharded layer (sg_all_to_sharded_backward): dy
+    (P, B, out/P) -> (dx (B, in) = the rank-order all_sum of dy[r] W_r,
+    dw (P, out/P, in), dw[r] = dy[r]^T x); either may be skipped (None)."""
+    B = dy.shape[1]
+    dx = torch.empty((B, layer.in_dims), dtype=dx_dtype or layer.dtype, device=dy.device) if need_dx else None
+    dw = torch.empty((layer.P, layer.out_dims // layer.P, layer.in_dims), dtype=dw_dtype,
+                     device=dy.device) if need_dw else None
+    _check(lib().sg_all_to_sharded_backward(layer.handle, _ptr(x), _ptr(dy), B, _ptr(dx),
+                                            _DT.get(dx.dtype if dx is not None else layer.dtype, -1), _ptr(dw),
+                                            _DT.get(dw_dtype, -1), _stream(dy.device)))
+    return dx, dw
+
+
+def sharded_to_all_backward(layer: Layer, x_partial: torch.Tensor | None, dy: torch.Tensor, need_dx: bool = True,
+                            need_dw: bool = True, dx_dtype=None, dw_dtype=torch.float32):
+    """Backward of a sharded-to-all layer (sg_sharded_to_all_backward): dy
+    (B, out) -> (dx_partial (P, B, in/P), slice r = dy W_r; dw (P, out, in/P),
+    dw[r] = dy^T x_partial[r]); either may be skipped (None)."""
+    B = dy.shape[0]
+    dx = torch.empty((layer.P, B, layer.in_dims // layer.P), dtype=dx_dtype or layer.dtype,
+                     device=dy.device) if need_dx else None
+    dw = torch.empty((layer.P, layer.out_dims, layer.in_dims // layer.P), dtype=dw_dtype,
+                     device=dy.device) if need_dw else None
+    _check(lib().sg_sharded_to_all_backward(layer.handle, _ptr(x_partial), _ptr(dy), B, _ptr(dx),
+                                            _DT.get(dx.dtype if dx is not None else layer.dtype, -1), _ptr(dw),
+                                            _DT.get(dw_dtype, -1), _stream(dy.device)))
+    return dx, dw
 
 
 def summa_workspace(dtype: torch.dtype, K: int, N: int, q: int) -> int:

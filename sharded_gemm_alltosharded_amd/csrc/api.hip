@@ -744,6 +744,129 @@ sg_status sg_mlp(const sg_layer* gate_up, const sg_layer* down, const void* x, i
     return SG_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Backward (vector-Jacobian products) of the two sharded layers
+// ---------------------------------------------------------------------------
+namespace {
+
+const char* bwd_check(const sg_layer* l, int mode, int64_t B, sg_dtype dx_dtype, sg_dtype dw_dtype) {
+    if (!l) return "layer is NULL";
+    if (l->mode != mode)
+        return mode == SG_ALL_TO_SHARDED ? "layer is sharded-to-all; use sg_sharded_to_all_backward"
+                                         : "layer is all-to-sharded; use sg_all_to_sharded_backward";
+    if (B < 0 || B > INT32_MAX) return "token count out of range";
+    if (!dtype_ok(dx_dtype) || !dtype_ok(dw_dtype)) return "unknown gradient dtype";
+    return nullptr;
+}
+
+}  // namespace
+
+sg_status sg_all_to_sharded_backward(const sg_layer* l, const void* x, const void* dy, int64_t B, void* dx,
+                                     sg_dtype dx_dtype, void* dw, sg_dtype dw_dtype, void* stream) {
+    g_err.clear();
+    if (const char* why = bwd_check(l, SG_ALL_TO_SHARDED, B, dx_dtype, dw_dtype)) return fail(SG_ERR_INVALID_ARG, "%s", why);
+    if (l->quantized) return fail(SG_ERR_UNSUPPORTED, "the backward is implemented for dense layers only");
+    if (!dx && !dw) return fail(SG_ERR_INVALID_ARG, "neither dx nor dw requested");
+    if (B == 0) return SG_OK;
+    if (!dy) return fail(SG_ERR_INVALID_ARG, "dy must not be NULL");
+    if (dw && !x) return fail(SG_ERR_INVALID_ARG, "dw needs the forward input x");
+    hipStream_t st = (hipStream_t)stream;
+    if (dx) {
+        // the sum_gradients all_sum: dx = sum_r dY_r W_r, ranks in order
+        sg::BwdDx p{};
+        p.A = dy;
+        p.lda = l->rows_r;
+        p.a_seg = B * l->rows_r;
+        p.W = l->w;
+        p.ldw = l->cols_r;
+        p.w_seg = l->rows_r * l->cols_r;
+        p.wsteps = l->cols_r / 32;
+        p.wfrag = l->wfrag;
+        p.dtype = l->dtype;
+        p.M = (int)B;
+        p.N = (int)l->cols_r;
+        p.K = (int)l->rows_r;
+        p.nseg = l->P;
+        p.reduce = 1;
+        p.out = dx;
+        p.out_dtype = dx_dtype;
+        hipError_t e = sg::launch_bwd_dx(p, st);
+        if (e != hipSuccess) return hip_fail(e, "all_to_sharded backward dx");
+    }
+    if (dw) {
+        sg::BwdDw q{};
+        q.G = dy;
+        q.ldg = l->rows_r;
+        q.g_seg = B * l->rows_r;
+        q.X = x;
+        q.ldx = l->cols_r;
+        q.x_seg = 0;
+        q.dtype = l->dtype;
+        q.M = (int)B;
+        q.R = (int)l->rows_r;
+        q.C = (int)l->cols_r;
+        q.nseg = l->P;
+        q.out = dw;
+        q.out_dtype = dw_dtype;
+        hipError_t e = sg::launch_bwd_dw(q, st);
+        if (e != hipSuccess) return hip_fail(e, "all_to_sharded backward dw");
+    }
+    return SG_OK;
+}
+
+sg_status sg_sharded_to_all_backward(const sg_layer* l, const void* x_partial, const void* dy, int64_t B,
+                                     void* dx_partial, sg_dtype dx_dtype, void* dw, sg_dtype dw_dtype, void* stream) {
+    g_err.clear();
+    if (const char* why = bwd_check(l, SG_SHARDED_TO_ALL, B, dx_dtype, dw_dtype)) return fail(SG_ERR_INVALID_ARG, "%s", why);
+    if (l->quantized) return fail(SG_ERR_UNSUPPORTED, "the backward is implemented for dense layers only");
+    if (!dx_partial && !dw) return fail(SG_ERR_INVALID_ARG, "neither dx nor dw requested");
+    if (B == 0) return SG_OK;
+    if (!dy) return fail(SG_ERR_INVALID_ARG, "dy must not be NULL");
+    if (dw && !x_partial) return fail(SG_ERR_INVALID_ARG, "dw needs the forward input x_partial");
+    hipStream_t st = (hipStream_t)stream;
+    if (dx_partial) {
+        // every rank receives the full dY: dX_r = dY W_r, no reduction
+        sg::BwdDx p{};
+        p.A = dy;
+        p.lda = l->rows_r;
+        p.a_seg = 0;
+        p.W = l->w;
+        p.ldw = l->cols_r;
+        p.w_seg = l->rows_r * l->cols_r;
+        p.wsteps = l->cols_r / 32;
+        p.wfrag = l->wfrag;
+        p.dtype = l->dtype;
+        p.M = (int)B;
+        p.N = (int)l->cols_r;
+        p.K = (int)l->rows_r;
+        p.nseg = l->P;
+        p.reduce = 0;
+        p.out = dx_partial;
+        p.out_dtype = dx_dtype;
+        hipError_t e = sg::launch_bwd_dx(p, st);
+        if (e != hipSuccess) return hip_fail(e, "sharded_to_all backward dx");
+    }
+    if (dw) {
+        sg::BwdDw q{};
+        q.G = dy;
+        q.ldg = l->rows_r;
+        q.g_seg = 0;
+        q.X = x_partial;
+        q.ldx = l->cols_r;
+        q.x_seg = B * l->cols_r;
+        q.dtype = l->dtype;
+        q.M = (int)B;
+        q.R = (int)l->rows_r;
+        q.C = (int)l->cols_r;
+        q.nseg = l->P;
+        q.out = dw;
+        q.out_dtype = dw_dtype;
+        hipError_t e = sg::launch_bwd_dw(q, st);
+        if (e != hipSuccess) return hip_fail(e, "sharded_to_all backward dw");
+    }
+    return SG_OK;
+}
+
 // bytes of the transposed fragment-major copy of A the MFMA path reads
 static size_t summa_ws_bytes(sg_dtype dtype, int64_t K, int64_t N, int q) {
     if (dtype != SG_BF16 && dtype != SG_F16) return 0;

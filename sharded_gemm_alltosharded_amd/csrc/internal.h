@@ -190,6 +190,31 @@ SkinnyShape skinny_shape(int M, int N, int nseg, int swiglu);
 Q4Shape q4_shape(int M, int N, int nseg, int swiglu);
 SkinnyShape q4s_shape(int M, int N, int nseg, int swiglu);
 bool q4s_takes(const Problem& p);  // launch_q4 runs p on the 16-row kernel (q4s.hip)
+
+// Backward products (backward.hip).  BwdDx: out[m][n] (reduce: summed over the
+// nseg ranks in order) or out[s][m][n] = sum_k A_s[m][k] W_s[k][n], W_s rank
+// s's stored (rows, cols) shard read as its (K, N) operand.  BwdDw:
+// out[s][o][i] = sum_m G_s[m][o] X_s[m][i].
+struct BwdDx {
+    const void* A;
+    int64_t lda, a_seg;
+    const void* W;
+    int64_t ldw, w_seg, wsteps;
+    int wfrag, dtype, M, N, K, nseg, reduce;
+    void* out;
+    int out_dtype;
+};
+struct BwdDw {
+    const void* G;
+    int64_t ldg, g_seg;
+    const void* X;
+    int64_t ldx, x_seg;
+    int dtype, M, R, C, nseg;
+    void* out;
+    int out_dtype;
+};
+hipError_t launch_bwd_dx(const BwdDx& p, hipStream_t s);
+hipError_t launch_bwd_dw(const BwdDw& p, hipStream_t s);
 constexpr size_t kMaxStreamLds = 64 * 1024;
 int tile_count(int M, int N, int variant);
 inline size_t split_workspace_bytes(SplitLayout s) { return kPartialsOffset + s.floats * sizeof(float); }

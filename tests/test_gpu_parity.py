@@ -685,3 +685,59 @@ def test_mx_rejections():
     with pytest.raises(sg.ShardGemmError) as e:
         sg.shard_mxfp8_linear(codes, scales, "all-to-sharded", P=2, act_dtype=torch.float16)
     assert e.value.code == sg.ERR_UNSUPPORTED
+
+
+# ---------------------------------------------------------------------------
+# backward (sum_gradients VJP of the all-to-sharded layer; the sharded-to-all VJP)
+# ---------------------------------------------------------------------------
+BWD_CASES = [("bf16", 8, 256, 512, 1, 4), ("bf16", 5, 96, 72, 1, 2), ("f16", 3, 128, 256, 2, 2),
+             ("f32", 4, 64, 96, 1, 3), ("bf16", 1, 512, 128, 1, 1)]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_all_to_sharded_backward(case):
+    dtype, B, inn, out, S, P = case
+    _print_case(dtype=dtype, B=B, inn=inn, out=out, S=S, P=P)
+    W = synth.uniform(90, (out, inn), inn ** -0.5, dtype)
+    X = synth.normal(91, (B, inn), 1.0, dtype)
+    G = synth.normal(92, (P, B, out // P), 1.0, dtype)
+    layer = sg.shard_linear(to_dev(W, dtype), "all-to-sharded", segments=S, P=P)
+    dx, dw = sg.all_to_sharded_backward(layer, to_dev(X, dtype), to_dev(G, dtype), dx_dtype=torch.float32)
+    rdx, rdw = oracle.col_bwd(X, W, G, P=P, S=S, dtype=dtype)
+    assert_close(dx, rdx, "f32", "dx")
+    assert_close(dw, rdw, "f32", "dw")
+    dx2, _ = sg.all_to_sharded_backward(layer, None, to_dev(G, dtype), need_dw=False, dx_dtype=torch.float32)
+    assert torch.equal(dx, dx2)  # the rank-order sum is deterministic
+    if dtype != "f32":
+        dx16, _ = sg.all_to_sharded_backward(layer, None, to_dev(G, dtype), need_dw=False)
+        assert_close(dx16, rdx, dtype, "dx 16-bit")
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_sharded_to_all_backward(case):
+    dtype, B, inn, out, S, P = case
+    if S != 1:
+        pytest.skip("sharded-to-all layers take one segment here")
+    inn, out = out, inn  # a down-projection shape: in = the wide side
+    _print_case(dtype=dtype, B=B, inn=inn, out=out, P=P)
+    W = synth.uniform(93, (out, inn), inn ** -0.5, dtype)
+    Xs = synth.normal(94, (P, B, inn // P), 1.0, dtype)
+    G = synth.normal(95, (B, out), 1.0, dtype)
+    layer = sg.shard_linear(to_dev(W, dtype), "sharded-to-all", P=P)
+    dxs, dw = sg.sharded_to_all_backward(layer, to_dev(Xs, dtype), to_dev(G, dtype), dx_dtype=torch.float32)
+    rdxs, rdw = oracle.row_bwd(Xs, W, G, P=P, dtype=dtype)
+    assert_close(dxs, rdxs, "f32", "dx_partial")
+    assert_close(dw, rdw, "f32", "dw")
+
+
+def test_backward_rejections():
+    w = to_dev(synth.uniform(96, (64, 64), 1 / 8, "bf16"), "bf16")
+    col = sg.shard_linear(w, "all-to-sharded", P=2)
+    row = sg.shard_linear(w, "sharded-to-all", P=2)
+    dy = torch.zeros((2, 4, 32), dtype=torch.bfloat16, device=dev())
+    with pytest.raises(sg.ShardGemmError):
+        sg.all_to_sharded_backward(row, None, dy, need_dw=False)  # wrong mode
+    with pytest.raises(sg.ShardGemmError, match="forward input"):
+        sg.all_to_sharded_backward(col, None, dy)  # dw without x
+    with pytest.raises(sg.ShardGemmError):
+        sg.sharded_to_all_backward(col, None, torch.zeros((4, 64), dtype=torch.bfloat16, device=dev()), need_dw=False)
