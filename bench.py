@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Throughput of the sharded-GEMM hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2|3|4|5a|5b|6|1]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2|3|4|5a|5b|6|7|1]
 
 A step is one pass of the workload's whole sharded path over one batch of
 synthetic inputs already resident in HBM.  The default workload is the
@@ -16,6 +16,8 @@ down sharded-to-all with the fused rank sum, through the fused MLP entry point
     5b  vocabulary-parallel head, fp16, 32 x 12288 . (50272 x 12288)^T, P=8
     6   the decode MLP of the default workload with MX FP8 weights (E4M3 codes,
         one E8M0 scale per 32 inputs)
+    7   backward of the decode MLP's two sharded layers (input and weight
+        gradients, the input-gradient all_sum fused)
     1   the fp32 worked example + the D=64 MLP (launch-bound, for completeness)
 
 Prints ONE JSON line on stdout; progress goes to stderr.  Weight copies are
@@ -48,7 +50,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--config", default="2", choices=["1", "2", "3", "4", "5a", "5b", "6"])
+    ap.add_argument("--config", default="2", choices=["1", "2", "3", "4", "5a", "5b", "6", "7"])
     ap.add_argument("--batch", type=int, default=1, help="tokens for the 4-bit workload (1, 8 or 32)")
     ap.add_argument("--summa", default="fused", choices=["fused", "steps"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -503,10 +505,77 @@ class MxfpDecodeMLP(Workload):
             f"dequantisation of all weights ({t_dec:.2f} s); step-equivalent {t_step:.2f} s")
 
 
+class BackwardMLP(Workload):
+    """Backward of the decode MLP's two sharded layers (B=16, D=4096, F=14336,
+    P=8, bf16; fp32 weight gradients): the sharded-to-all down layer (dh_r =
+    dY W_down,r and dW_down,r = dY^T h_r) and the all-to-sharded gate|up layer
+    (dx = the rank-order all_sum of dG_r W_gu,r, and dW_gu,r = dG_r^T x), with
+    synthetic upstream gradients dY and dG (the SwiGLU derivative between them
+    is elementwise and not part of the sharded path)."""
+    B, D, F, P = 16, 4096, 14336, 8
+    name = "llama-mlp-backward"
+    metric = "sharded-MLP backward GB/s (% HBM peak)"
+    steps, warmup = 20, 3
+    dominant = "bwd_dw_kernel (gate|up weight gradient, fp32)"
+    dominant_src = ("backward.hip", "internal.h")
+
+    def setup(self):
+        import numpy as np
+        import torch
+        import sharded_gemm_alltosharded_amd as sg
+        import synth
+        B, D, F, P = self.B, self.D, self.F, self.P
+        self.inp = inp = synth.mlp_inputs(B, D, F, P, synth.BF16, seed=0)
+        self.x = _dev_tensor(inp.X, "bf16")
+        self.gu = sg.shard_linear(_dev_tensor(np.concatenate([inp.Wg, inp.Wu]), "bf16"), "all-to-sharded",
+                                  segments=2, P=P)
+        self.dn = sg.shard_linear(_dev_tensor(inp.Wd, "bf16"), "sharded-to-all", P=P)
+        self.hs = _dev_tensor(synth.normal(100, (P, B, F // P), 1.0, synth.BF16), "bf16")
+        self.dy = _dev_tensor(synth.normal(101, (B, D), 1.0, synth.BF16), "bf16")
+        self.dg = _dev_tensor(synth.normal(102, (P, B, 2 * F // P), 1.0, synth.BF16), "bf16")
+        self.sg = sg
+        self.f32 = torch.float32
+        w = 2 * (2 * F * D + D * F)              # weights read once by the input-gradient products
+        g = 4 * (2 * F * D + D * F)              # fp32 weight gradients written once
+        a = 2 * (B * D + B * F + 2 * B * F + B * D + B * F)  # x, h, dG, dY in; dh out (bf16)
+        self.units = w + g + a + 4 * B * D       # + dx (fp32)
+        self.dom_units = 4 * (2 * F * D) + 2 * (B * D + 2 * B * F)
+
+    def step(self, i, ev=None):
+        sg = self.sg
+        sg.sharded_to_all_backward(self.dn, self.hs, self.dy, dx_dtype=None)
+        sg.all_to_sharded_backward(self.gu, None, self.dg, need_dw=False, dx_dtype=self.f32)
+        if ev:
+            sg.time_next_launch(*ev)
+        sg.all_to_sharded_backward(self.gu, self.x, self.dg, need_dx=False)
+
+    def config(self):
+        return {"workload": self.name, "tokens": self.B, "D": self.D, "F": self.F, "P": self.P,
+                "weight_gradients": "fp32"}
+
+    def cpu_baseline(self):
+        import numpy as np
+        import oracle
+        import synth
+        inp = self.inp
+        t0 = time.perf_counter()
+        X = oracle.decode(inp.X, "bf16")
+        Wgu = oracle.decode(np.concatenate([inp.Wg, inp.Wu]), "bf16")
+        Wd = oracle.decode(inp.Wd, "bf16")
+        hs = oracle.decode(synth.normal(100, (self.P, self.B, self.F // self.P), 1.0, synth.BF16), "bf16")
+        dy = oracle.decode(synth.normal(101, (self.B, self.D), 1.0, synth.BF16), "bf16")
+        dg = oracle.decode(synth.normal(102, (self.P, self.B, 2 * self.F // self.P), 1.0, synth.BF16), "bf16")
+        oracle.row_bwd(hs, Wd, dy, P=self.P)
+        oracle.col_bwd(X, Wgu, dg, P=self.P, S=2)
+        t_step = time.perf_counter() - t0
+        return self.units / t_step / 1e9, t_step, (
+            f"oracle backward of both layers on the whole step, weight decode included ({t_step:.1f} s)")
+
+
 def make(args) -> Workload:
     return {"1": lambda: Tiny(), "2": lambda: DecodeMLP(), "3": lambda: PrefillMLP(),
             "4": lambda: Q4MLP(args.batch), "5a": lambda: Summa(args.summa == "fused"),
-            "5b": lambda: VocabHead(), "6": lambda: MxfpDecodeMLP()}[args.config]()
+            "5b": lambda: VocabHead(), "6": lambda: MxfpDecodeMLP(), "7": lambda: BackwardMLP()}[args.config]()
 
 
 # ---------------------------------------------------------------------------

@@ -788,6 +788,7 @@ sg_status sg_all_to_sharded_backward(const sg_layer* l, const void* x, const voi
         p.K = (int)l->rows_r;
         p.nseg = l->P;
         p.reduce = 1;
+        p.stacked = 1;
         p.out = dx;
         p.out_dtype = dx_dtype;
         hipError_t e = sg::launch_bwd_dx(p, st);

@@ -16,7 +16,17 @@
 
 namespace sg {
 
+// operand element as fp32, the dtype fixed at compile time (no per-load branch,
+// so the unrolled loops keep several loads in flight)
+template <int DT>
+__device__ __forceinline__ float ld(const void* p, int64_t i) {
+    if constexpr (DT == SG_F32) return ((const float*)p)[i];
+    else if constexpr (DT == SG_BF16) return __uint_as_float((uint32_t)((const uint16_t*)p)[i] << 16);
+    else return (float)((const _Float16*)p)[i];
+}
+
 // out[m][n] (reduce) or out[s][m][n] = sum_k A_s[m][k] W_s[k][n]
+template <int DT, bool WFRAG>
 __global__ __launch_bounds__(256) void bwd_dx_kernel(BwdDx p) {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t plane = (int64_t)p.M * p.N;
@@ -28,11 +38,16 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(BwdDx p) {
     const int s0 = p.reduce ? 0 : so, s1 = p.reduce ? p.nseg : so + 1;
     float tot = 0.f;
     for (int s = s0; s < s1; ++s) {  // ranks in order: the all_sum
-        const int64_t ab = s * p.a_seg + (int64_t)m * p.lda, wb = s * p.w_seg;
+        // all-to-sharded ranks are stacked rows of one matrix (a fragment-major
+        // layout spans the stack, rank s's row k being row s K + k);
+        // sharded-to-all ranks are separate matrices w_seg apart
+        const int64_t ab = s * p.a_seg + (int64_t)m * p.lda;
+        const int64_t r0 = p.stacked ? (int64_t)s * p.K : 0, wb = p.stacked ? 0 : s * p.w_seg;
         float part = 0.f;
+#pragma unroll 8
         for (int k = 0; k < p.K; ++k) {
-            const int64_t wi = wb + (p.wfrag ? frag_offset(k, n, p.wsteps) : (int64_t)k * p.ldw + n);
-            part = fmaf(load_as_f32(p.A, p.dtype, ab + k), load_as_f32(p.W, p.dtype, wi), part);
+            const int64_t wi = wb + (WFRAG ? frag_offset(r0 + k, n, p.wsteps) : (r0 + k) * p.ldw + n);
+            part = fmaf(ld<DT>(p.A, ab + k), ld<DT>(p.W, wi), part);
         }
         tot += part;
     }
@@ -40,6 +55,7 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(BwdDx p) {
 }
 
 // out[s][o][i] = sum_m G_s[m][o] X_s[m][i]
+template <int DT>
 __global__ __launch_bounds__(256) void bwd_dw_kernel(BwdDw p) {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t plane = (int64_t)p.R * p.C;
@@ -49,22 +65,35 @@ __global__ __launch_bounds__(256) void bwd_dw_kernel(BwdDw p) {
     const int64_t o = rem / p.C, i = rem - o * p.C;
     const int64_t gb = s * p.g_seg + o, xb = s * p.x_seg + i;
     float acc = 0.f;
-    for (int m = 0; m < p.M; ++m)
-        acc = fmaf(load_as_f32(p.G, p.dtype, gb + (int64_t)m * p.ldg), load_as_f32(p.X, p.dtype, xb + (int64_t)m * p.ldx), acc);
+#pragma unroll 8
+    for (int m = 0; m < p.M; ++m) acc = fmaf(ld<DT>(p.G, gb + (int64_t)m * p.ldg), ld<DT>(p.X, xb + (int64_t)m * p.ldx), acc);
     store_from_f32(p.out, p.out_dtype, idx, acc);
 }
 
 hipError_t launch_bwd_dx(const BwdDx& p, hipStream_t s) {
     const int64_t total = (p.reduce ? 1 : p.nseg) * (int64_t)p.M * p.N;
     if (total == 0) return hipSuccess;
-    launch(bwd_dx_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, p);
+    const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+    if (p.dtype == SG_F32) {
+        if (p.wfrag) return hipErrorInvalidValue;  // fp32 layers are stored row-major
+        launch(bwd_dx_kernel<SG_F32, false>, grid, block, 0, s, p);
+    } else if (p.dtype == SG_BF16) {
+        if (p.wfrag) launch(bwd_dx_kernel<SG_BF16, true>, grid, block, 0, s, p);
+        else launch(bwd_dx_kernel<SG_BF16, false>, grid, block, 0, s, p);
+    } else {
+        if (p.wfrag) launch(bwd_dx_kernel<SG_F16, true>, grid, block, 0, s, p);
+        else launch(bwd_dx_kernel<SG_F16, false>, grid, block, 0, s, p);
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_bwd_dw(const BwdDw& p, hipStream_t s) {
     const int64_t total = p.nseg * (int64_t)p.R * p.C;
     if (total == 0) return hipSuccess;
-    launch(bwd_dw_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, p);
+    const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+    if (p.dtype == SG_F32) launch(bwd_dw_kernel<SG_F32>, grid, block, 0, s, p);
+    else if (p.dtype == SG_BF16) launch(bwd_dw_kernel<SG_BF16>, grid, block, 0, s, p);
+    else launch(bwd_dw_kernel<SG_F16>, grid, block, 0, s, p);
     return hipGetLastError();
 }
 

@@ -201,6 +201,7 @@ struct BwdDx {
     const void* W;
     int64_t ldw, w_seg, wsteps;
     int wfrag, dtype, M, N, K, nseg, reduce;
+    int stacked;  // ranks are stacked rows of one matrix (all-to-sharded), else w_seg apart
     void* out;
     int out_dtype;
 };

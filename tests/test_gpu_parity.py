@@ -691,7 +691,8 @@ def test_mx_rejections():
 # backward (sum_gradients VJP of the all-to-sharded layer; the sharded-to-all VJP)
 # ---------------------------------------------------------------------------
 BWD_CASES = [("bf16", 8, 256, 512, 1, 4), ("bf16", 5, 96, 72, 1, 2), ("f16", 3, 128, 256, 2, 2),
-             ("f32", 4, 64, 96, 1, 3), ("bf16", 1, 512, 128, 1, 1)]
+             ("f32", 4, 64, 96, 1, 3), ("bf16", 1, 512, 128, 1, 1),
+             ("bf16", 4, 64, 48, 1, 2)]  # 24 rows per rank: the fragment-major stack crosses rank boundaries
 
 
 @pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "-".join(map(str, c)))
