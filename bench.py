@@ -516,7 +516,7 @@ class BackwardMLP(Workload):
     name = "llama-mlp-backward"
     metric = "sharded-MLP backward GB/s (% HBM peak)"
     steps, warmup = 20, 3
-    dominant = "bwd_dw_kernel (gate|up weight gradient, fp32)"
+    dominant = "bwd_dxt_kernel (gate|up input gradient with the fused all_sum)"
     dominant_src = ("backward.hip", "internal.h")
 
     def setup(self):
@@ -539,14 +539,14 @@ class BackwardMLP(Workload):
         g = 4 * (2 * F * D + D * F)              # fp32 weight gradients written once
         a = 2 * (B * D + B * F + 2 * B * F + B * D + B * F)  # x, h, dG, dY in; dh out (bf16)
         self.units = w + g + a + 4 * B * D       # + dx (fp32)
-        self.dom_units = 4 * (2 * F * D) + 2 * (B * D + 2 * B * F)
+        self.dom_units = 2 * (2 * F * D) + 2 * (2 * B * F) + 4 * B * D  # W_gu, dG in; dx (fp32) out
 
     def step(self, i, ev=None):
         sg = self.sg
         sg.sharded_to_all_backward(self.dn, self.hs, self.dy, dx_dtype=None)
-        sg.all_to_sharded_backward(self.gu, None, self.dg, need_dw=False, dx_dtype=self.f32)
         if ev:
             sg.time_next_launch(*ev)
+        sg.all_to_sharded_backward(self.gu, None, self.dg, need_dw=False, dx_dtype=self.f32)
         sg.all_to_sharded_backward(self.gu, self.x, self.dg, need_dx=False)
 
     def config(self):

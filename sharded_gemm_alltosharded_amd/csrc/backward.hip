@@ -54,6 +54,62 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(BwdDx p) {
     store_from_f32(p.out, p.out_dtype, idx, tot);
 }
 
+// The same product, token-blocked: a workgroup of 16 waves owns 64 output
+// columns n (one per lane) and 16 tokens; each thread keeps the 16 tokens'
+// sums for its column, so every weight element is loaded once for all of
+// them.  The 16 waves split each rank's K range; a wave stages its 64 x 16
+// chunk of A in its own LDS buffer and reads it back as broadcasts.  The wave
+// partials are added in wave order after the one workgroup barrier, which every
+// thread reaches (no early exit).  grid: (N / 64, M / 16, reduce ? 1 : nseg).
+template <int DT, bool WFRAG>
+__global__ __launch_bounds__(1024) void bwd_dxt_kernel(BwdDx p) {
+    constexpr int NWV = 16, TB = 16, CH = 64;
+    __shared__ float stage[NWV][CH][TB];      // per wave: A chunk, [k][token]
+    __shared__ float red[NWV][TB][64];        // per wave: partial sums, [token][lane]
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t n = (int64_t)blockIdx.x * 64 + lane;
+    const int64_t nc = n < p.N ? n : p.N - 1;  // clamped column for loads
+    const int m0 = blockIdx.y * TB;
+    const int so = blockIdx.z;
+    const int s0 = p.reduce ? 0 : so, s1 = p.reduce ? p.nseg : so + 1;
+    const int kp = (p.K + NWV - 1) / NWV, ks = min(p.K, wave * kp), ke = min(p.K, ks + kp);
+    float acc[TB];
+#pragma unroll
+    for (int t = 0; t < TB; ++t) acc[t] = 0.f;
+    for (int s = s0; s < s1; ++s) {  // ranks in order
+        const int64_t r0 = p.stacked ? (int64_t)s * p.K : 0, wb = p.stacked ? 0 : s * p.w_seg;
+        for (int c = ks; c < ke; c += CH) {
+            // stage A[s][m0 + t][c + lane] (zero past ke or past M)
+            const int k = c + lane;
+#pragma unroll
+            for (int t = 0; t < TB; ++t) {
+                const bool ok = k < ke && m0 + t < p.M;
+                stage[wave][lane][t] = ok ? ld<DT>(p.A, s * p.a_seg + (int64_t)(m0 + t) * p.lda + k) : 0.f;
+            }
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's stores are in LDS
+            __builtin_amdgcn_wave_barrier();
+            const int len = min(CH, ke - c);
+            for (int kk = 0; kk < len; ++kk) {
+                const int64_t kr = r0 + c + kk;
+                const float w = ld<DT>(p.W, wb + (WFRAG ? frag_offset(kr, nc, p.wsteps) : kr * p.ldw + nc));
+#pragma unroll
+                for (int t = 0; t < TB; ++t) acc[t] = fmaf(stage[wave][kk][t], w, acc[t]);
+            }
+            __builtin_amdgcn_s_waitcnt(0xc07f);
+            __builtin_amdgcn_wave_barrier();  // every lane has read the chunk before it is overwritten
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < TB; ++t) red[wave][t][lane] = acc[t];
+    __syncthreads();
+    // thread (wave, lane): token m0 + wave, column n -- the wave partials in order
+    float v = 0.f;
+    for (int w = 0; w < NWV; ++w) v += red[w][wave][lane];
+    const int m = m0 + wave;
+    if (m < p.M && n < p.N) store_from_f32(p.out, p.out_dtype, ((int64_t)so * p.M + m) * p.N + n, v);
+}
+
 // out[s][o][i] = sum_m G_s[m][o] X_s[m][i]
 template <int DT>
 __global__ __launch_bounds__(256) void bwd_dw_kernel(BwdDw p) {
@@ -73,17 +129,14 @@ __global__ __launch_bounds__(256) void bwd_dw_kernel(BwdDw p) {
 hipError_t launch_bwd_dx(const BwdDx& p, hipStream_t s) {
     const int64_t total = (p.reduce ? 1 : p.nseg) * (int64_t)p.M * p.N;
     if (total == 0) return hipSuccess;
-    const dim3 grid((unsigned)((total + 255) / 256)), block(256);
-    if (p.dtype == SG_F32) {
-        if (p.wfrag) return hipErrorInvalidValue;  // fp32 layers are stored row-major
-        launch(bwd_dx_kernel<SG_F32, false>, grid, block, 0, s, p);
-    } else if (p.dtype == SG_BF16) {
-        if (p.wfrag) launch(bwd_dx_kernel<SG_BF16, true>, grid, block, 0, s, p);
-        else launch(bwd_dx_kernel<SG_BF16, false>, grid, block, 0, s, p);
-    } else {
-        if (p.wfrag) launch(bwd_dx_kernel<SG_F16, true>, grid, block, 0, s, p);
-        else launch(bwd_dx_kernel<SG_F16, false>, grid, block, 0, s, p);
-    }
+    if (p.dtype == SG_F32 && p.wfrag) return hipErrorInvalidValue;  // fp32 layers are stored row-major
+    const dim3 tgrid((unsigned)((p.N + 63) / 64), (unsigned)((p.M + 15) / 16), (unsigned)(p.reduce ? 1 : p.nseg));
+    const dim3 tblock(1024);
+    if (p.dtype == SG_F32) launch(bwd_dxt_kernel<SG_F32, false>, tgrid, tblock, 0, s, p);
+    else if (p.dtype == SG_BF16 && p.wfrag) launch(bwd_dxt_kernel<SG_BF16, true>, tgrid, tblock, 0, s, p);
+    else if (p.dtype == SG_BF16) launch(bwd_dxt_kernel<SG_BF16, false>, tgrid, tblock, 0, s, p);
+    else if (p.wfrag) launch(bwd_dxt_kernel<SG_F16, true>, tgrid, tblock, 0, s, p);
+    else launch(bwd_dxt_kernel<SG_F16, false>, tgrid, tblock, 0, s, p);
     return hipGetLastError();
 }
 
