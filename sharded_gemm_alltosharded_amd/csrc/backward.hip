@@ -8,10 +8,12 @@
 //  * sharded-to-all, Y = sum_r X_r W_r^T:  dX_r = dY W_r (stays sharded, no
 //    reduction), dW_r = dY^T X_r.
 //
-// First implementation: one thread per output element with fp32 accumulation
-// (the products are not yet on the matrix cores).  The weight is read in the
-// layout the layer stores (fragment-major or row-major), element W_r[k][n] of
-// rank r's (rows_r, cols_r) shard.
+// fp32 accumulation on the vector units (the products are not on the matrix
+// cores yet): the input gradient token-blocked with the K range split over the
+// waves of a workgroup, the weight gradient one thread per element (its
+// reduction runs over the B tokens only).  The weight is read in the layout the
+// layer stores (fragment-major or row-major), element W_r[k][n] of rank r's
+// (rows_r, cols_r) shard.
 #include "internal.h"
 
 namespace sg {
@@ -25,50 +27,24 @@ __device__ __forceinline__ float ld(const void* p, int64_t i) {
     else return (float)((const _Float16*)p)[i];
 }
 
-// out[m][n] (reduce) or out[s][m][n] = sum_k A_s[m][k] W_s[k][n]
-template <int DT, bool WFRAG>
-__global__ __launch_bounds__(256) void bwd_dx_kernel(BwdDx p) {
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t plane = (int64_t)p.M * p.N;
-    if (idx >= (p.reduce ? 1 : p.nseg) * plane) return;
-    const int so = (int)(idx / plane);
-    const int64_t rem = idx - so * plane;
-    const int m = (int)(rem / p.N);
-    const int64_t n = rem - (int64_t)m * p.N;
-    const int s0 = p.reduce ? 0 : so, s1 = p.reduce ? p.nseg : so + 1;
-    float tot = 0.f;
-    for (int s = s0; s < s1; ++s) {  // ranks in order: the all_sum
-        // all-to-sharded ranks are stacked rows of one matrix (a fragment-major
-        // layout spans the stack, rank s's row k being row s K + k);
-        // sharded-to-all ranks are separate matrices w_seg apart
-        const int64_t ab = s * p.a_seg + (int64_t)m * p.lda;
-        const int64_t r0 = p.stacked ? (int64_t)s * p.K : 0, wb = p.stacked ? 0 : s * p.w_seg;
-        float part = 0.f;
-#pragma unroll 8
-        for (int k = 0; k < p.K; ++k) {
-            const int64_t wi = wb + (WFRAG ? frag_offset(r0 + k, n, p.wsteps) : (r0 + k) * p.ldw + n);
-            part = fmaf(ld<DT>(p.A, ab + k), ld<DT>(p.W, wi), part);
-        }
-        tot += part;
-    }
-    store_from_f32(p.out, p.out_dtype, idx, tot);
-}
-
-// The same product, token-blocked: a workgroup of 16 waves owns 64 output
-// columns n (one per lane) and 16 tokens; each thread keeps the 16 tokens'
-// sums for its column, so every weight element is loaded once for all of
-// them.  The 16 waves split each rank's K range; a wave stages its 64 x 16
-// chunk of A in its own LDS buffer and reads it back as broadcasts.  The wave
-// partials are added in wave order after the one workgroup barrier, which every
-// thread reaches (no early exit).  grid: (N / 64, M / 16, reduce ? 1 : nseg).
-template <int DT, bool WFRAG>
+// out[m][n] (reduce: the ranks summed in order) or out[s][m][n] =
+// sum_k A_s[m][k] W_s[k][n], token-blocked: a workgroup of 16 waves owns CW output
+// columns n and 16 tokens.  Lane l takes column l % CW and every (64 / CW)-th
+// k of each staged chunk starting at l / CW, keeping the 16 tokens' sums for
+// its column, so every weight element is loaded once for all of them.  The 16
+// waves split each rank's K range; a wave stages its 64 x 16 chunk of A in its
+// own LDS buffer and reads it back as broadcasts.  The partials (waves, then
+// lane groups) are added in a fixed order after the one workgroup barrier,
+// which every thread reaches (no early exit).  CW < 64 gives narrow outputs
+// enough workgroups.  grid: (N / CW, M / 16, reduce ? 1 : nseg).
+template <int DT, bool WFRAG, int CW>
 __global__ __launch_bounds__(1024) void bwd_dxt_kernel(BwdDx p) {
-    constexpr int NWV = 16, TB = 16, CH = 64;
+    constexpr int NWV = 16, TB = 16, CH = 64, SUB = 64 / CW;
     __shared__ float stage[NWV][CH][TB];      // per wave: A chunk, [k][token]
     __shared__ float red[NWV][TB][64];        // per wave: partial sums, [token][lane]
-    const int lane = threadIdx.x & 63;
+    const int lane = threadIdx.x & 63, col = lane % CW, sub = lane / CW;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t n = (int64_t)blockIdx.x * 64 + lane;
+    const int64_t n = (int64_t)blockIdx.x * CW + col;
     const int64_t nc = n < p.N ? n : p.N - 1;  // clamped column for loads
     const int m0 = blockIdx.y * TB;
     const int so = blockIdx.z;
@@ -90,7 +66,7 @@ __global__ __launch_bounds__(1024) void bwd_dxt_kernel(BwdDx p) {
             __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's stores are in LDS
             __builtin_amdgcn_wave_barrier();
             const int len = min(CH, ke - c);
-            for (int kk = 0; kk < len; ++kk) {
+            for (int kk = sub; kk < len; kk += SUB) {
                 const int64_t kr = r0 + c + kk;
                 const float w = ld<DT>(p.W, wb + (WFRAG ? frag_offset(kr, nc, p.wsteps) : kr * p.ldw + nc));
 #pragma unroll
@@ -103,11 +79,28 @@ __global__ __launch_bounds__(1024) void bwd_dxt_kernel(BwdDx p) {
 #pragma unroll
     for (int t = 0; t < TB; ++t) red[wave][t][lane] = acc[t];
     __syncthreads();
-    // thread (wave, lane): token m0 + wave, column n -- the wave partials in order
-    float v = 0.f;
-    for (int w = 0; w < NWV; ++w) v += red[w][wave][lane];
-    const int m = m0 + wave;
-    if (m < p.M && n < p.N) store_from_f32(p.out, p.out_dtype, ((int64_t)so * p.M + m) * p.N + n, v);
+    // thread (wave, lane < CW): token m0 + wave, column n -- partials in order
+    if (lane < CW) {
+        float v = 0.f;
+        for (int w = 0; w < NWV; ++w)
+            for (int g = 0; g < SUB; ++g) v += red[w][wave][g * CW + col];
+        const int m = m0 + wave;
+        if (m < p.M && n < p.N) store_from_f32(p.out, p.out_dtype, ((int64_t)so * p.M + m) * p.N + n, v);
+    }
+}
+
+template <int DT, bool WFRAG>
+static void launch_dxt(const BwdDx& p, hipStream_t s) {
+    const unsigned gy = (unsigned)((p.M + 15) / 16), gz = (unsigned)(p.reduce ? 1 : p.nseg);
+    const dim3 block(1024);
+    // the widest column group that still gives every CU a workgroup
+    const int64_t per = (int64_t)gy * gz;
+    if ((p.N + 63) / 64 * per >= 256)
+        launch(bwd_dxt_kernel<DT, WFRAG, 64>, dim3((unsigned)((p.N + 63) / 64), gy, gz), block, 0, s, p);
+    else if ((p.N + 31) / 32 * per >= 256)
+        launch(bwd_dxt_kernel<DT, WFRAG, 32>, dim3((unsigned)((p.N + 31) / 32), gy, gz), block, 0, s, p);
+    else
+        launch(bwd_dxt_kernel<DT, WFRAG, 16>, dim3((unsigned)((p.N + 15) / 16), gy, gz), block, 0, s, p);
 }
 
 // out[s][o][i] = sum_m G_s[m][o] X_s[m][i]
@@ -130,13 +123,11 @@ hipError_t launch_bwd_dx(const BwdDx& p, hipStream_t s) {
     const int64_t total = (p.reduce ? 1 : p.nseg) * (int64_t)p.M * p.N;
     if (total == 0) return hipSuccess;
     if (p.dtype == SG_F32 && p.wfrag) return hipErrorInvalidValue;  // fp32 layers are stored row-major
-    const dim3 tgrid((unsigned)((p.N + 63) / 64), (unsigned)((p.M + 15) / 16), (unsigned)(p.reduce ? 1 : p.nseg));
-    const dim3 tblock(1024);
-    if (p.dtype == SG_F32) launch(bwd_dxt_kernel<SG_F32, false>, tgrid, tblock, 0, s, p);
-    else if (p.dtype == SG_BF16 && p.wfrag) launch(bwd_dxt_kernel<SG_BF16, true>, tgrid, tblock, 0, s, p);
-    else if (p.dtype == SG_BF16) launch(bwd_dxt_kernel<SG_BF16, false>, tgrid, tblock, 0, s, p);
-    else if (p.wfrag) launch(bwd_dxt_kernel<SG_F16, true>, tgrid, tblock, 0, s, p);
-    else launch(bwd_dxt_kernel<SG_F16, false>, tgrid, tblock, 0, s, p);
+    if (p.dtype == SG_F32) launch_dxt<SG_F32, false>(p, s);
+    else if (p.dtype == SG_BF16 && p.wfrag) launch_dxt<SG_BF16, true>(p, s);
+    else if (p.dtype == SG_BF16) launch_dxt<SG_BF16, false>(p, s);
+    else if (p.wfrag) launch_dxt<SG_F16, true>(p, s);
+    else launch_dxt<SG_F16, false>(p, s);
     return hipGetLastError();
 }
 
