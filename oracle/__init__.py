@@ -23,6 +23,8 @@ col_bwd     VJP of all_to_sharded: dx = all_sum of dY_r W_r, dW_r   finite diffe
             = dY_r^T X                                              unsharded identity
 row_bwd     VJP of sharded_to_all: dX_r = dY W_r, dW_r = dY^T X_r   finite differences of row,
                                                                     unsharded identity
+summa_abt   SUMMA backward dX = dY A^T in q steps (Matmul_ABT_2D)  finite differences of summa
+summa_atb   SUMMA backward dA = X^T dY in q steps (Matmul_ATB_2D)  finite differences of summa
 all_gather  input shards (P, B, k) -> (B, P k), rank order          index arrays, brute force
 reduce_     summed (B, n) result -> (P, B, n/P), rank r's columns   index arrays, brute force
  scatter
@@ -270,6 +272,37 @@ def row_bwd(Xs, W, dY, P, dtype=None):
     dXs = np.stack([dY @ Ws[r] for r in range(P)])
     dW = np.stack([dY.T @ Xs[r] for r in range(P)])
     return dXs, dW
+
+
+def summa_abt(dY, A, q, dtype=None) -> np.ndarray:
+    """Backward of Y = X A for X: dX = dY A^T, accumulated over the q blocks
+    of the shared inner dimension N in order t = 0..q-1 (ColossalAI 2D SUMMA
+    page, its Matmul_ABT_2D): dX_ik += dY_it A_kt^T.  dY (M, N), A (K, N)."""
+    dY, A = _f64(dY, dtype), _f64(A, dtype)
+    M, N = dY.shape
+    K = A.shape[0]
+    if q < 1 or N % q:
+        raise OracleError(3, "summa_abt")
+    b = N // q
+    dX = np.zeros((M, K))
+    for t in range(q):
+        dX = dX + dY[:, t * b:(t + 1) * b] @ A[:, t * b:(t + 1) * b].T
+    return dX
+
+
+def summa_atb(X, dY, q, dtype=None) -> np.ndarray:
+    """Backward of Y = X A for A: dA = X^T dY over the q blocks of the token
+    dimension M in order (the page's Matmul_ATB_2D): dA_kj += X_tk^T dY_tj.
+    X (M, K), dY (M, N)."""
+    X, dY = _f64(X, dtype), _f64(dY, dtype)
+    M = X.shape[0]
+    if q < 1 or M % q:
+        raise OracleError(3, "summa_atb")
+    b = M // q
+    dA = np.zeros((X.shape[1], dY.shape[1]))
+    for t in range(q):
+        dA = dA + X[t * b:(t + 1) * b].T @ dY[t * b:(t + 1) * b]
+    return dA
 
 
 def all_gather(Xs) -> np.ndarray:

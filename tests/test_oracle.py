@@ -503,3 +503,16 @@ def test_row_bwd_unsharded_identity():
     dXs, dW = oracle.row_bwd(Xs, W, dY, P=P)
     np.testing.assert_allclose(np.concatenate(list(dXs), axis=1), dY @ W, rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(np.concatenate(list(dW), axis=1), dY.T @ X, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("q", [1, 2, 3])
+def test_summa_backward_finite_differences(q):
+    """Matmul_ABT_2D / Matmul_ATB_2D of the SUMMA page: the gradients of
+    L = sum(G * summa(X, A, q)) with respect to X and A."""
+    rng = np.random.default_rng(90 + q)
+    M, K, N = 3 * q, 2 * q, 4 * q
+    X, A, G = rng.standard_normal((M, K)), rng.standard_normal((K, N)), rng.standard_normal((M, N))
+    np.testing.assert_allclose(oracle.summa_abt(G, A, q),
+                               _fd(lambda Xv: float(np.sum(G * oracle.summa(Xv, A, q))), X), rtol=1e-10, atol=1e-10)
+    np.testing.assert_allclose(oracle.summa_atb(X, G, q),
+                               _fd(lambda Av: float(np.sum(G * oracle.summa(X, Av, q))), A), rtol=1e-10, atol=1e-10)
