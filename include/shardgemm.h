@@ -220,6 +220,17 @@ sg_status sg_all_to_sharded_backward(const sg_layer* layer, const void* x, const
 sg_status sg_sharded_to_all_backward(const sg_layer* layer, const void* x_partial, const void* dy, int64_t B,
                                      void* dx_partial, sg_dtype dx_dtype, void* dw, sg_dtype dw_dtype, void* stream);
 
+/* SUMMA backward ([SUMMA] Matmul_ABT_2D and Matmul_ATB_2D, the gradients of
+ * Y = X A): with the inner dimension of each product cut into the q SUMMA step
+ * blocks, summed in step order t = 0..q-1,
+ *   dX (M, K) fp32 = dY A^T   (dX_ik = sum_t dY_it A_kt^T),
+ *   dA (K, N) fp32 = X^T dY   (dA_kj = sum_t X_tk^T dY_tj).
+ *   X (M, K), A (K, N), dY (M, N): row-major, of dtype.  dX or dA may be NULL
+ *   (not both); each output is overwritten.
+ * Errors as sg_summa_matmul (q must divide M, K and N). */
+sg_status sg_summa_backward(const void* X, const void* A, const void* dY, sg_dtype dtype, int64_t M, int64_t K,
+                            int64_t N, int q, float* dX, float* dA, void* stream);
+
 /* Bytes of workspace sg_sharded_to_all needs for B tokens (0 on bad input). */
 size_t sg_sharded_to_all_workspace(const sg_layer* layer, int64_t B);
 

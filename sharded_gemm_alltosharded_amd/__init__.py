@@ -16,6 +16,7 @@ kernels.  The entry points mirror include/shardgemm.h one to one:
     all_to_sharded_backward    sg_all_to_sharded_backward (dx = rank-order all_sum, dw)
     sharded_to_all_backward    sg_sharded_to_all_backward (sharded dx, dw)
     summa_matmul               sg_summa_matmul (+ sg_summa_workspace)
+    summa_backward             sg_summa_backward (Matmul_ABT_2D / Matmul_ATB_2D)
     Layer.info / Layer.shard   sg_layer_info / sg_layer_copy_shard
     time_next_launch           sg_time_next_launch (profiling)
 
@@ -79,6 +80,7 @@ def lib():
             "sg_sharded_to_all_ex": ([P, P, I64, P, I, I, P, SZ, P], I),
             "sg_all_to_sharded_backward": ([P, P, P, I64, P, I, P, I, P], I),
             "sg_sharded_to_all_backward": ([P, P, P, I64, P, I, P, I, P], I),
+            "sg_summa_backward": ([P, P, P, I, I64, I64, I64, I, P, P, P], I),
             "sg_mlp": ([P, P, P, I64, P, I, P, SZ, P], I),
             "sg_mlp_workspace": ([P, P, I64], SZ),
             "sg_sharded_to_all_workspace": ([P, I64], SZ),
@@ -342,6 +344,19 @@ def sharded_to_all_backward(layer: Layer, x_partial: torch.Tensor | None, dy: to
                                             _DT.get(dx.dtype if dx is not None else layer.dtype, -1), _ptr(dw),
                                             _DT.get(dw_dtype, -1), _stream(dy.device)))
     return dx, dw
+
+
+def summa_backward(X: torch.Tensor, A: torch.Tensor, dY: torch.Tensor, q: int, need_dx: bool = True,
+                   need_da: bool = True):
+    """Gradients of Y = X A in q SUMMA steps (sg_summa_backward): dX = dY A^T
+    (M, K) and dA = X^T dY (K, N), both fp32; either may be skipped (None)."""
+    M, K = X.shape
+    N = A.shape[1]
+    dX = torch.empty((M, K), dtype=torch.float32, device=dY.device) if need_dx else None
+    dA = torch.empty((K, N), dtype=torch.float32, device=dY.device) if need_da else None
+    _check(lib().sg_summa_backward(_ptr(X), _ptr(A), _ptr(dY), _DT.get(X.dtype, -1), M, K, N, q, _ptr(dX), _ptr(dA),
+                                   _stream(dY.device)))
+    return dX, dA
 
 
 def summa_workspace(dtype: torch.dtype, K: int, N: int, q: int) -> int:

@@ -868,6 +868,65 @@ sg_status sg_sharded_to_all_backward(const sg_layer* l, const void* x_partial, c
     return SG_OK;
 }
 
+// SUMMA backward ([SUMMA] Matmul_ABT_2D / Matmul_ATB_2D): dX = dY A^T with the
+// inner dimension N cut into the q step blocks (the K segments of the matrix-
+// core kernels, summed in step order), dA = X^T dY (the weight-gradient kernel).
+sg_status sg_summa_backward(const void* X, const void* A, const void* dY, sg_dtype dtype, int64_t M, int64_t K,
+                            int64_t N, int q, float* dX, float* dA, void* stream) {
+    g_err.clear();
+    if (!dtype_ok(dtype)) return fail(SG_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+    if (M < 0 || K < 0 || N < 0 || M > INT32_MAX || K > INT32_MAX || N > INT32_MAX)
+        return fail(SG_ERR_INVALID_ARG, "matrix sizes out of range");
+    if (q < 1) return fail(SG_ERR_NOT_DIVISIBLE, "the processor grid must be q x q with q >= 1 (got q = %d)", q);
+    if (M % q || K % q || N % q)
+        return fail(SG_ERR_NOT_DIVISIBLE, "M, K, N (%lld, %lld, %lld) must be divisible by q = %d",
+                    (long long)M, (long long)K, (long long)N, q);
+    if (!dX && !dA) return fail(SG_ERR_INVALID_ARG, "neither dX nor dA requested");
+    if (M == 0 || K == 0 || N == 0) return SG_OK;
+    if (!dY || (dX && !A) || (dA && !X)) return fail(SG_ERR_INVALID_ARG, "dY, and A for dX / X for dA, must not be NULL");
+    hipStream_t hs = (hipStream_t)stream;
+    if (dX) {
+        const int64_t bn = N / q;
+        sg::Problem p{};
+        p.A = dY;
+        p.lda = N;
+        p.a_seg = bn;  // step t: columns [t bn, (t+1) bn) of dY and of A
+        p.W = A;
+        p.ldw = N;
+        p.w_seg = bn;
+        p.M = (int)M;
+        p.N = (int)K;
+        p.Kseg = (int)bn;
+        p.nseg = q;
+        p.dtype = dtype;
+        p.out = dX;
+        p.out_dtype = SG_F32;
+        p.out_map = sg::OUT_ROWMAJOR;
+        p.ldo = K;
+        const bool mfma = dtype != SG_F32 && bn % 8 == 0 && N % 8 == 0 && aligned16(dY) && aligned16(A) && aligned16(dX);
+        const Kind k = !mfma ? K_GENERIC : (M >= 512 ? K_TILE0 : K_TILE1);
+        hipError_t e = run(p, k, hs);
+        if (e != hipSuccess) return hip_fail(e, "summa backward dX");
+    }
+    if (dA) {
+        sg::BwdDw w{};
+        w.G = X;  // dA[k][n] = sum_m X[m][k] dY[m][n]
+        w.ldg = K;
+        w.X = dY;
+        w.ldx = N;
+        w.dtype = dtype;
+        w.M = (int)M;
+        w.R = (int)K;
+        w.C = (int)N;
+        w.nseg = 1;
+        w.out = dA;
+        w.out_dtype = SG_F32;
+        hipError_t e = sg::launch_bwd_dw(w, hs);
+        if (e != hipSuccess) return hip_fail(e, "summa backward dA");
+    }
+    return SG_OK;
+}
+
 // bytes of the transposed fragment-major copy of A the MFMA path reads
 static size_t summa_ws_bytes(sg_dtype dtype, int64_t K, int64_t N, int q) {
     if (dtype != SG_BF16 && dtype != SG_F16) return 0;

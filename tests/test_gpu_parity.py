@@ -742,3 +742,22 @@ def test_backward_rejections():
         sg.all_to_sharded_backward(col, None, dy)  # dw without x
     with pytest.raises(sg.ShardGemmError):
         sg.sharded_to_all_backward(col, None, torch.zeros((4, 64), dtype=torch.bfloat16, device=dev()), need_dw=False)
+
+
+SUMMA_BWD_CASES = [("bf16", 256, 128, 512, 4), ("bf16", 64, 96, 48, 2), ("f16", 512, 256, 256, 1),
+                   ("f32", 24, 12, 18, 3), ("bf16", 48, 66, 30, 3)]
+
+
+@pytest.mark.parametrize("case", SUMMA_BWD_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_summa_backward(case):
+    """Matmul_ABT_2D / Matmul_ATB_2D: dX = dY A^T and dA = X^T dY in q steps."""
+    dtype, M, K, N, q = case
+    _print_case(dtype=dtype, M=M, K=K, N=N, q=q)
+    X = synth.normal(110, (M, K), K ** -0.25, dtype)
+    A = synth.normal(111, (K, N), K ** -0.25, dtype)
+    G = synth.normal(112, (M, N), 1.0, dtype)
+    dX, dA = sg.summa_backward(to_dev(X, dtype), to_dev(A, dtype), to_dev(G, dtype), q)
+    assert_close(dX, oracle.summa_abt(G, A, q, dtype=dtype), "f32", "dX")
+    assert_close(dA, oracle.summa_atb(X, G, q, dtype=dtype), "f32", "dA")
+    with pytest.raises(sg.ShardGemmError):
+        sg.summa_backward(to_dev(X, dtype), to_dev(A, dtype), to_dev(G, dtype), q + 5)
