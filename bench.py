@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Throughput of the sharded-GEMM hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2|3|4|5a|5b|6|7|1]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2|3|4|5a|5b|5c|6|7|1]
 
 A step is one pass of the workload's whole sharded path over one batch of
 synthetic inputs already resident in HBM.  The default workload is the
@@ -14,6 +14,7 @@ down sharded-to-all with the fused rank sum, through the fused MLP entry point
     4   4-bit affine MLP (group 64), B in {1, 8, 32} (--batch), P=4
     5a  SUMMA Y = X A, 8192^3 bf16, q=4 (--summa fused|steps)
     5b  vocabulary-parallel head, fp16, 32 x 12288 . (50272 x 12288)^T, P=8
+    5c  SUMMA backward at 8192^3, q=4: dX = dY A^T and dA = X^T dY
     6   the decode MLP of the default workload with MX FP8 weights (E4M3 codes,
         one E8M0 scale per 32 inputs)
     7   backward of the decode MLP's two sharded layers (input and weight
@@ -50,7 +51,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--config", default="2", choices=["1", "2", "3", "4", "5a", "5b", "6", "7"])
+    ap.add_argument("--config", default="2", choices=["1", "2", "3", "4", "5a", "5b", "5c", "6", "7"])
     ap.add_argument("--batch", type=int, default=1, help="tokens for the 4-bit workload (1, 8 or 32)")
     ap.add_argument("--summa", default="fused", choices=["fused", "steps"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -345,6 +346,54 @@ class Summa(Workload):
             f"({t_dec:.2f} s); step-equivalent {t_step:.0f} s")
 
 
+class SummaBackward(Workload):
+    """Backward of the SUMMA product Y = X A at 8192^3, q = 4, bf16 in, fp32
+    out: dX = dY A^T (Matmul_ABT_2D, matrix-core tile kernels with the q steps
+    as K segments) and dA = X^T dY (Matmul_ATB_2D, vector units)."""
+    n, q = 8192, 4
+    name = "summa-8192-q4-backward"
+    metric = "SUMMA backward TFLOP/s (% MFMA peak)"
+    unit = "TFLOP/s"
+    bound = "mfma"
+    steps, warmup = 3, 1
+    dominant = "bwd_dw_kernel (dA = X^T dY on the vector units)"
+    dominant_src = ("backward.hip", "internal.h")
+
+    def setup(self):
+        import sharded_gemm_alltosharded_amd as sg
+        import synth
+        self.Xh, self.Ah = synth.summa_inputs(self.n, seed=30)
+        self.Gh = synth.normal(113, (self.n, self.n), 1.0, synth.BF16)
+        self.X, self.A, self.G = (_dev_tensor(a, "bf16") for a in (self.Xh, self.Ah, self.Gh))
+        self.sg = sg
+        self.units = 2 * 2 * self.n ** 3
+        self.dom_units = 2 * self.n ** 3
+
+    def step(self, i, ev=None):
+        self.sg.summa_backward(self.X, self.A, self.G, self.q, need_da=False)
+        if ev:
+            self.sg.time_next_launch(*ev)
+        self.sg.summa_backward(self.X, self.A, self.G, self.q, need_dx=False)
+
+    def config(self):
+        return {"workload": self.name, "M": self.n, "K": self.n, "N": self.n, "q": self.q, "grads": "fp32"}
+
+    def cpu_baseline(self):
+        import oracle
+        t0 = time.perf_counter()
+        X, A, G = (oracle.decode(a, "bf16") for a in (self.Xh, self.Ah, self.Gh))
+        t_dec = time.perf_counter() - t0
+        S = 8
+        t0 = time.perf_counter()
+        oracle.summa_abt(G[:S], A, 4 if S % 4 == 0 else 1)
+        oracle.summa_atb(X[:S], G[:S], 4 if S % 4 == 0 else 1)
+        t_cmp = time.perf_counter() - t0
+        t_step = t_dec + t_cmp * self.n / S
+        return self.units / t_step / 1e12, t_step, (
+            f"oracle dX and dA on {S} of {self.n} token rows ({t_cmp:.2f} s) scaled x{self.n // S}, plus decode "
+            f"({t_dec:.2f} s); step-equivalent {t_step:.0f} s")
+
+
 class VocabHead(Workload):
     """Vocabulary-parallel head: X (32, 12288) fp16, W (50272, 12288) fp16, P = 8."""
     B, Hd, V, P = 32, 12288, 50272, 8
@@ -575,7 +624,8 @@ class BackwardMLP(Workload):
 def make(args) -> Workload:
     return {"1": lambda: Tiny(), "2": lambda: DecodeMLP(), "3": lambda: PrefillMLP(),
             "4": lambda: Q4MLP(args.batch), "5a": lambda: Summa(args.summa == "fused"),
-            "5b": lambda: VocabHead(), "6": lambda: MxfpDecodeMLP(), "7": lambda: BackwardMLP()}[args.config]()
+            "5b": lambda: VocabHead(), "6": lambda: MxfpDecodeMLP(), "7": lambda: BackwardMLP(),
+            "5c": lambda: SummaBackward()}[args.config]()
 
 
 # ---------------------------------------------------------------------------
