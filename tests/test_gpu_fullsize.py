@@ -155,3 +155,25 @@ def test_vocab_head_full_sampled():
     sharded = sg.all_to_sharded(layer, to_dev(Xh, "f16"))
     for r in (0, 7):
         assert torch.equal(sharded[r], logits[:, r * (V // P):(r + 1) * (V // P)])
+
+
+def test_mlp_backward_full():
+    """The backward bench.py times (--config 7): decode MLP shapes, B=16,
+    D=4096, F=14336, P=8, bf16 in, fp32 weight gradients; every output."""
+    _case("MLP backward B=16 D=4096 F=14336 P=8")
+    B, D, F, P = 16, 4096, 14336, 8
+    inp = synth.mlp_inputs(B, D, F, P, "bf16", seed=0)
+    Wgu = np.concatenate([inp.Wg, inp.Wu])
+    gu = sg.shard_linear(to_dev(Wgu, "bf16"), "all-to-sharded", segments=2, P=P)
+    dn = sg.shard_linear(to_dev(inp.Wd, "bf16"), "sharded-to-all", P=P)
+    hs = synth.normal(100, (P, B, F // P), 1.0, "bf16")
+    dy = synth.normal(101, (B, D), 1.0, "bf16")
+    dg = synth.normal(102, (P, B, 2 * F // P), 1.0, "bf16")
+    dh, dWd = sg.sharded_to_all_backward(dn, to_dev(hs, "bf16"), to_dev(dy, "bf16"), dx_dtype=torch.float32)
+    rdh, rdWd = oracle.row_bwd(hs, inp.Wd, dy, P=P, dtype="bf16")
+    assert_close(dh, rdh, "f32", "dh")
+    assert_close(dWd, rdWd, "f32", "dW_down")
+    dx, dWgu = sg.all_to_sharded_backward(gu, to_dev(inp.X, "bf16"), to_dev(dg, "bf16"), dx_dtype=torch.float32)
+    rdx, rdWgu = oracle.col_bwd(inp.X, Wgu, dg, P=P, S=2, dtype="bf16")
+    assert_close(dx, rdx, "f32", "dx")
+    assert_close(dWgu, rdWgu, "f32", "dW_gate_up")
