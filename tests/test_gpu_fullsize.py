@@ -139,6 +139,22 @@ def test_summa_full_sampled(fused):
     assert_close(Y[idx], ref, "f32", "summa")
 
 
+def test_summa_backward_full_sampled():
+    """SUMMA backward as bench.py times it (--config 5c): 8192^3, q = 4;
+    sampled rows of dX = dY A^T and of dA = X^T dY (rows k of dA need all of
+    X's column k)."""
+    _case("SUMMA backward 8192 q=4")
+    n, q = 8192, 4
+    Xh, Ah = synth.summa_inputs(n, seed=30)
+    Gh = synth.normal(113, (n, n), 1.0, "bf16")
+    dX, dA = sg.summa_backward(to_dev(Xh, "bf16"), to_dev(Ah, "bf16"), to_dev(Gh, "bf16"), q)
+    idx = np.array([0, 2047, 2048, 4000, 4096, 6143, 6144, 8191])
+    A, G = oracle.decode(Ah, "bf16"), oracle.decode(Gh, "bf16")
+    assert_close(dX[idx], oracle.summa_abt(G[idx], A, q), "f32", "dX")
+    Xc = oracle.decode(np.ascontiguousarray(Xh[:, idx]), "bf16")
+    assert_close(dA[idx], oracle.summa_atb(Xc, G, q), "f32", "dA")
+
+
 def test_vocab_head_full_sampled():
     """fp16 vocabulary head, 32 x 12288 against 50272 x 12288, P = 8 ranks of
     6284 rows, gathered logits: 3 sampled tokens, every vocabulary entry."""
