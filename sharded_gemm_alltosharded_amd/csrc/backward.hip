@@ -119,6 +119,43 @@ __global__ __launch_bounds__(256) void bwd_dw_kernel(BwdDw p) {
     store_from_f32(p.out, p.out_dtype, idx, acc);
 }
 
+// out[s][o][i .. i+3]: four adjacent outputs per thread share each G load and
+// read X four elements (8 or 16 bytes) at a time; C % 4 == 0 and 16-bit or fp32
+// rows aligned to 4 elements
+template <int DT>
+__global__ __launch_bounds__(256) void bwd_dw4_kernel(BwdDw p) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t C4 = p.C / 4, plane = (int64_t)p.R * C4;
+    if (idx >= p.nseg * plane) return;
+    const int s = (int)(idx / plane);
+    const int64_t rem = idx - s * plane;
+    const int64_t o = rem / C4, i = (rem - o * C4) * 4;
+    const int64_t gb = s * p.g_seg + o, xb = s * p.x_seg + i;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int m = 0; m < p.M; ++m) {
+        const float g = ld<DT>(p.G, gb + (int64_t)m * p.ldg);
+        const int64_t xi = xb + (int64_t)m * p.ldx;
+        float x[4];
+        if constexpr (DT == SG_F32) {
+            const float4 v = *(const float4*)((const float*)p.X + xi);
+            x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+        } else {
+            const uint2 v = *(const uint2*)((const uint16_t*)p.X + xi);
+            const uint16_t h[4] = {(uint16_t)(v.x & 0xFFFFu), (uint16_t)(v.x >> 16), (uint16_t)(v.y & 0xFFFFu),
+                                   (uint16_t)(v.y >> 16)};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                x[e] = DT == SG_BF16 ? __uint_as_float((uint32_t)h[e] << 16) : (float)__builtin_bit_cast(_Float16, h[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = fmaf(g, x[e], acc[e]);
+    }
+    const int64_t oi = (int64_t)s * p.R * p.C + o * p.C + i;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) store_from_f32(p.out, p.out_dtype, oi + e, acc[e]);
+}
+
 hipError_t launch_bwd_dx(const BwdDx& p, hipStream_t s) {
     const int64_t total = (p.reduce ? 1 : p.nseg) * (int64_t)p.M * p.N;
     if (total == 0) return hipSuccess;
@@ -134,6 +171,15 @@ hipError_t launch_bwd_dx(const BwdDx& p, hipStream_t s) {
 hipError_t launch_bwd_dw(const BwdDw& p, hipStream_t s) {
     const int64_t total = p.nseg * (int64_t)p.R * p.C;
     if (total == 0) return hipSuccess;
+    const int esz = p.dtype == SG_F32 ? 4 : 2;
+    const bool vec = p.C % 4 == 0 && p.ldx % 4 == 0 && p.x_seg % 4 == 0 && ((uintptr_t)p.X % (4 * esz)) == 0;
+    if (vec) {
+        const dim3 grid((unsigned)((total / 4 + 255) / 256)), block(256);
+        if (p.dtype == SG_F32) launch(bwd_dw4_kernel<SG_F32>, grid, block, 0, s, p);
+        else if (p.dtype == SG_BF16) launch(bwd_dw4_kernel<SG_BF16>, grid, block, 0, s, p);
+        else launch(bwd_dw4_kernel<SG_F16>, grid, block, 0, s, p);
+        return hipGetLastError();
+    }
     const dim3 grid((unsigned)((total + 255) / 256)), block(256);
     if (p.dtype == SG_F32) launch(bwd_dw_kernel<SG_F32>, grid, block, 0, s, p);
     else if (p.dtype == SG_BF16) launch(bwd_dw_kernel<SG_BF16>, grid, block, 0, s, p);
