@@ -356,7 +356,7 @@ class SummaBackward(Workload):
     unit = "TFLOP/s"
     bound = "mfma"
     steps, warmup = 3, 1
-    dominant = "bwd_dw_kernel (dA = X^T dY on the vector units)"
+    dominant = "bwd_dw4_kernel (dA = X^T dY on the vector units)"
     dominant_src = ("backward.hip", "internal.h")
 
     def setup(self):
