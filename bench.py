@@ -731,25 +731,31 @@ def main():
         wl.step(i)
     torch.cuda.synchronize()
 
-    # The dominant kernel's start / end events are armed on every `every`-th
-    # timed step only: arming costs a few microseconds of launch overhead, and
-    # sampling keeps that out of the step time.
-    every = max(1, K // 25)
+    # The timed loop launches nothing but the steps themselves.  The dominant
+    # kernel's own start / end events (armed through sg_time_next_launch, which
+    # records them from inside that launch) are taken afterwards, in a
+    # separate pass of the same steps, so that arming them never adds to the
+    # step time.
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    evs = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for i in range(0, K, every)}
-    for a, b in evs.values():  # create the events before the timed region
-        a.record()
-        b.record()
     torch.cuda.synchronize()
     start.record()
     for i in range(K):
-        wl.step(i, evs.get(i))
+        wl.step(i)
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / K
-    dom_ms = sum(a.elapsed_time(b) for a, b in evs.values()) / len(evs)
-    log(f"[bench] {ms * 1e3:.1f} us/step; dominant kernel {dom_ms * 1e3:.1f} us (its own start/end events)")
+    n_samp = max(8, min(25, K))
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_samp)]
+    for a, b in evs:  # create the events before they are armed
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    for i in range(n_samp):
+        wl.step(K + i, evs[i])
+    torch.cuda.synchronize()
+    dom_ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+    log(f"[bench] {ms * 1e3:.1f} us/step; dominant kernel {dom_ms * 1e3:.1f} us (its own start/end events, "
+        f"{n_samp} sampled steps after the timed ones)")
 
     graph_ms = None
     if not args.no_graph:

@@ -70,8 +70,9 @@ typedef struct sg_layer sg_layer; /* opaque, owned by the library */
  *            every segment, in segment order ([MLX] 3.2).
  *   P        number of ranks (P >= 1; P == 1 is the unsharded layer).
  * Errors: SG_ERR_NOT_DIVISIBLE when the split dimension is not divisible by
- * segments, or dim/segments not by P ([MLX] 2.1 and 6: "Cannot shard the
- * output of size .. across .. devices").  *out receives the new layer. */
+ * segments, or dim/segments not by P ([MLX] 2.1 and 6: a layer whose output
+ * width does not split evenly over the devices is rejected; the message
+ * names the size and the device count).  *out receives the new layer. */
 sg_status sg_shard_linear(const void* weight, sg_dtype dtype, int64_t out_dims, int64_t in_dims,
                           const void* bias, int mode, int segments, int P, void* stream,
                           sg_layer** out);

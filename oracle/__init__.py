@@ -86,6 +86,10 @@ def lib():
             "or_deqmx8": [P, P, I64, I64, I, P],
             "or_summa": [P, P, I64, I64, I64, I, P],
             "or_mlp": [P, I64, I64, I64, P, P, P, I, I, P],
+            "or_col_bwd": [P, I64, I64, P, I64, P, I, I, P, P],
+            "or_row_bwd": [P, I64, I64, P, I64, P, I, P, P],
+            "or_summa_abt": [P, P, I64, I64, I64, I, P],
+            "or_summa_atb": [P, P, I64, I64, I64, I, P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -246,18 +250,21 @@ def mlp(X, Wg, Wu, Wd, P, round_dtype="bf16", dtype=None) -> np.ndarray:
 
 def col_bwd(X, W, dY, P, S=1, dtype=None):
     """Vector-Jacobian product of the all-to-sharded layer Y_r = X W_r^T (MLX
-    tensor-parallel guide, section 2.1 and the sum_gradients wrapper of
-    section 2.1/6): the input X is used by every rank, so its gradient is the
-    all_sum over ranks of dY_r W_r (summed here in rank order, in fp64); rank
-    r's weight gradient is dY_r^T X.  dY: (P, B, out/P) in the layer's output
-    layout.  Returns (dx (B, in), dW (P, out/P, in)); dW[r] is laid out as
-    slice_(W, 0, S, P, r).  A matmul is the library step here."""
+    tensor-parallel guide, section 2.1 and its sum_gradients wrapper): the
+    input X is used by every rank, so its gradient is the all_sum over ranks
+    of dY_r W_r (each rank's product formed whole, then summed in rank order);
+    rank r's weight gradient is dY_r^T X.  dY: (P, B, out/P) in the layer's
+    output layout.  Returns (dx (B, in), dW (P, out/P, in)); dW[r] is laid out
+    as slice_(W, 0, S, P, r).  Plain fp64 loops (oracle.c or_col_bwd)."""
     X, W, dY = _f64(X, dtype), _f64(W, dtype), _f64(dY, dtype)
-    Ws = [slice_(W, 0, S, P, r) for r in range(P)]
-    dx = np.zeros((X.shape[0], W.shape[1]))
-    for r in range(P):
-        dx = dx + dY[r] @ Ws[r]
-    dW = np.stack([dY[r].T @ X for r in range(P)])
+    B, inn = X.shape
+    out = W.shape[0]
+    if out % S or (out // S) % P:
+        raise OracleError(3, "col_bwd")
+    dY = np.ascontiguousarray(dY).reshape(P, B, out // P)
+    dx = np.empty((B, inn))
+    dW = np.empty((P, out // P, inn))
+    _check(lib().or_col_bwd(_p(X), B, inn, _p(W), out, _p(dY), S, P, _p(dx), _p(dW)), "col_bwd")
     return dx, dW
 
 
@@ -266,42 +273,46 @@ def row_bwd(Xs, W, dY, P, dtype=None):
     (+ b) (MLX guide, section 2.2): the gradient reaching every rank is the
     full dY, so rank r's input gradient is dY W_r (no communication: it stays
     sharded like Xs) and its weight gradient dY^T Xs_r.  Xs: (P, B, in/P),
-    dY: (B, out).  Returns (dXs (P, B, in/P), dW (P, out, in/P))."""
+    dY: (B, out).  Returns (dXs (P, B, in/P), dW (P, out, in/P)).  Plain fp64
+    loops (oracle.c or_row_bwd)."""
     Xs, W, dY = _f64(Xs, dtype), _f64(W, dtype), _f64(dY, dtype)
-    Ws = [slice_(W, 1, 1, P, r) for r in range(P)]
-    dXs = np.stack([dY @ Ws[r] for r in range(P)])
-    dW = np.stack([dY.T @ Xs[r] for r in range(P)])
+    out, inn = W.shape
+    if inn % P:
+        raise OracleError(3, "row_bwd")
+    B = dY.shape[0]
+    Xs = np.ascontiguousarray(Xs).reshape(P, B, inn // P)
+    dXs = np.empty((P, B, inn // P))
+    dW = np.empty((P, out, inn // P))
+    _check(lib().or_row_bwd(_p(Xs), B, inn, _p(W), out, _p(dY), P, _p(dXs), _p(dW)), "row_bwd")
     return dXs, dW
 
 
 def summa_abt(dY, A, q, dtype=None) -> np.ndarray:
     """Backward of Y = X A for X: dX = dY A^T, accumulated over the q blocks
     of the shared inner dimension N in order t = 0..q-1 (ColossalAI 2D SUMMA
-    page, its Matmul_ABT_2D): dX_ik += dY_it A_kt^T.  dY (M, N), A (K, N)."""
+    page, its Matmul_ABT_2D): dX_ik += dY_it A_kt^T.  dY (M, N), A (K, N).
+    Plain fp64 loops (oracle.c or_summa_abt)."""
     dY, A = _f64(dY, dtype), _f64(A, dtype)
     M, N = dY.shape
     K = A.shape[0]
-    if q < 1 or N % q:
-        raise OracleError(3, "summa_abt")
-    b = N // q
-    dX = np.zeros((M, K))
-    for t in range(q):
-        dX = dX + dY[:, t * b:(t + 1) * b] @ A[:, t * b:(t + 1) * b].T
+    if A.shape[1] != N:
+        raise OracleError(1, "summa_abt")
+    dX = np.empty((M, K))
+    _check(lib().or_summa_abt(_p(dY), _p(A), M, K, N, q, _p(dX)), "summa_abt")
     return dX
 
 
 def summa_atb(X, dY, q, dtype=None) -> np.ndarray:
     """Backward of Y = X A for A: dA = X^T dY over the q blocks of the token
     dimension M in order (the page's Matmul_ATB_2D): dA_kj += X_tk^T dY_tj.
-    X (M, K), dY (M, N)."""
+    X (M, K), dY (M, N).  Plain fp64 loops (oracle.c or_summa_atb)."""
     X, dY = _f64(X, dtype), _f64(dY, dtype)
-    M = X.shape[0]
-    if q < 1 or M % q:
-        raise OracleError(3, "summa_atb")
-    b = M // q
-    dA = np.zeros((X.shape[1], dY.shape[1]))
-    for t in range(q):
-        dA = dA + X[t * b:(t + 1) * b].T @ dY[t * b:(t + 1) * b]
+    M, K = X.shape
+    N = dY.shape[1]
+    if dY.shape[0] != M:
+        raise OracleError(1, "summa_atb")
+    dA = np.empty((K, N))
+    _check(lib().or_summa_atb(_p(X), _p(dY), M, K, N, q, _p(dA)), "summa_atb")
     return dA
 
 

@@ -343,6 +343,142 @@ int or_mlp(const double* X, int64_t B, int64_t D, int64_t F, const double* Wg,
     return rc;
 }
 
+/* ------------------------------------------------------------------ */
+/* Backward of the two sharded layers ([MLX] 2.1 with its sum_gradients */
+/* wrapper, and 2.2): the vector-Jacobian products of O2 and O4.        */
+/* ------------------------------------------------------------------ */
+/* All-to-sharded: Y_r = X W_r^T with X shared by every rank, so the input
+ * gradient is the all_sum over ranks of dY_r W_r (each rank's product formed
+ * whole, then added in rank order r = 0 .. P-1, as or_row sums partials), and
+ * rank r's weight gradient is dY_r^T X, laid out like slice(W, rows, S, P, r).
+ *   X (B, in), W (out, in), dY (P, B, out/P); dx (B, in) and dW (P, out/P, in)
+ *   may each be NULL. */
+int or_col_bwd(const double* X, int64_t B, int64_t in, const double* W, int64_t out, const double* dY, int S,
+               int P, double* dx, double* dW) {
+    if (!W || !dY || B < 0 || in < 1 || out < 1 || S < 1 || P < 1 || (!dx && !dW) || (dW && !X))
+        return OR_INVALID;
+    if (out % S || (out / S) % P) return OR_NOT_DIVISIBLE;
+    int64_t nloc = out / P;
+    double* Wr = (double*)malloc(sizeof(double) * (size_t)(nloc * in));
+    double* Zr = (double*)malloc(sizeof(double) * (size_t)(B * in + 1));
+    if (!Wr || !Zr) { free(Wr); free(Zr); return OR_INVALID; }
+    if (dx)
+        for (int64_t i = 0; i < B * in; ++i) dx[i] = 0.0;
+    for (int r = 0; r < P; ++r) {
+        const double* G = dY + (int64_t)r * B * nloc;
+        if (dx) {
+            or_slice(W, sizeof(double), out, in, 0, S, P, r, Wr);
+#pragma omp parallel for collapse(2) schedule(static)
+            for (int64_t i = 0; i < B; ++i)
+                for (int64_t k = 0; k < in; ++k) {
+                    double acc = 0.0;
+                    for (int64_t j = 0; j < nloc; ++j) acc += G[i * nloc + j] * Wr[j * in + k];
+                    Zr[i * in + k] = acc;
+                }
+            for (int64_t i = 0; i < B * in; ++i) dx[i] += Zr[i]; /* all_sum, rank order */
+        }
+        if (dW) {
+            double* D = dW + (int64_t)r * nloc * in;
+#pragma omp parallel for collapse(2) schedule(static)
+            for (int64_t j = 0; j < nloc; ++j)
+                for (int64_t k = 0; k < in; ++k) {
+                    double acc = 0.0;
+                    for (int64_t i = 0; i < B; ++i) acc += G[i * nloc + j] * X[i * in + k];
+                    D[j * in + k] = acc;
+                }
+        }
+    }
+    free(Wr);
+    free(Zr);
+    return OR_OK;
+}
+
+/* Sharded-to-all: Y = sum_r Xs_r W_r^T (+ b); the gradient of the summed
+ * output reaches every rank whole, so rank r's input gradient dY W_r stays
+ * sharded (no reduction) and its weight gradient is dY^T Xs_r, laid out like
+ * slice(W, columns, 1, P, r).
+ *   Xs (P, B, in/P), W (out, in), dY (B, out); dXs (P, B, in/P) and
+ *   dW (P, out, in/P) may each be NULL. */
+int or_row_bwd(const double* Xs, int64_t B, int64_t in, const double* W, int64_t out, const double* dY, int P,
+               double* dXs, double* dW) {
+    if (!W || !dY || B < 0 || in < 1 || out < 1 || P < 1 || (!dXs && !dW) || (dW && !Xs)) return OR_INVALID;
+    if (in % P) return OR_NOT_DIVISIBLE;
+    int64_t kloc = in / P;
+    double* Wr = (double*)malloc(sizeof(double) * (size_t)(out * kloc));
+    if (!Wr) return OR_INVALID;
+    for (int r = 0; r < P; ++r) {
+        if (dXs) {
+            or_slice(W, sizeof(double), out, in, 1, 1, P, r, Wr);
+            double* D = dXs + (int64_t)r * B * kloc;
+#pragma omp parallel for collapse(2) schedule(static)
+            for (int64_t i = 0; i < B; ++i)
+                for (int64_t k = 0; k < kloc; ++k) {
+                    double acc = 0.0;
+                    for (int64_t o = 0; o < out; ++o) acc += dY[i * out + o] * Wr[o * kloc + k];
+                    D[i * kloc + k] = acc;
+                }
+        }
+        if (dW) {
+            const double* Xr = Xs + (int64_t)r * B * kloc;
+            double* D = dW + (int64_t)r * out * kloc;
+#pragma omp parallel for collapse(2) schedule(static)
+            for (int64_t o = 0; o < out; ++o)
+                for (int64_t k = 0; k < kloc; ++k) {
+                    double acc = 0.0;
+                    for (int64_t i = 0; i < B; ++i) acc += dY[i * out + o] * Xr[i * kloc + k];
+                    D[o * kloc + k] = acc;
+                }
+        }
+    }
+    free(Wr);
+    return OR_OK;
+}
+
+/* SUMMA backward ([SUMMA] Matmul_ABT_2D): for Y = X A, dX = dY A^T with the
+ * shared dimension N cut into the q step blocks; for every output, the
+ * block products are added in step order t = 0 .. q-1:
+ *   dX[i][k] = sum_t sum_{c in block t} dY[i][c] A[k][c].
+ *   dY (M, N), A (K, N), dX (M, K). */
+int or_summa_abt(const double* dY, const double* A, int64_t M, int64_t K, int64_t N, int q, double* dX) {
+    if (!dY || !A || !dX || M < 0 || K < 0 || N < 0 || q < 1) return OR_INVALID;
+    if (N % q) return OR_NOT_DIVISIBLE;
+    int64_t bn = N / q;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t k = 0; k < K; ++k) {
+            double sum = 0.0;
+            for (int t = 0; t < q; ++t) {
+                double acc = 0.0;
+                for (int64_t c = t * bn; c < (t + 1) * bn; ++c) acc += dY[i * N + c] * A[k * N + c];
+                sum += acc;
+            }
+            dX[i * K + k] = sum;
+        }
+    return OR_OK;
+}
+
+/* SUMMA backward ([SUMMA] Matmul_ATB_2D): dA = X^T dY with the token
+ * dimension M cut into the q step blocks, added in step order:
+ *   dA[k][j] = sum_t sum_{m in block t} X[m][k] dY[m][j].
+ *   X (M, K), dY (M, N), dA (K, N). */
+int or_summa_atb(const double* X, const double* dY, int64_t M, int64_t K, int64_t N, int q, double* dA) {
+    if (!X || !dY || !dA || M < 0 || K < 0 || N < 0 || q < 1) return OR_INVALID;
+    if (M % q) return OR_NOT_DIVISIBLE;
+    int64_t bm = M / q;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t j = 0; j < N; ++j) {
+            double sum = 0.0;
+            for (int t = 0; t < q; ++t) {
+                double acc = 0.0;
+                for (int64_t m = t * bm; m < (t + 1) * bm; ++m) acc += X[m * K + k] * dY[m * N + j];
+                sum += acc;
+            }
+            dA[k * N + j] = sum;
+        }
+    return OR_OK;
+}
+
 /* Number of threads the parallel loops use (1 without OpenMP). */
 int or_threads(void) {
 #ifdef _OPENMP

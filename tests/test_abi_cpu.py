@@ -62,8 +62,11 @@ def test_input_not_divisible(L):
 
 def test_segments_rules(L):
     assert _shard(L, 10, 4, sg.ALL_TO_SHARDED, 3, 1)[0] == sg.ERR_NOT_DIVISIBLE  # 10 % 3
+    assert "output of size 10 into 3 segments" in _err(L)
     assert _shard(L, 12, 4, sg.ALL_TO_SHARDED, 2, 4)[0] == sg.ERR_NOT_DIVISIBLE  # (12/2) % 4
-    assert "segments" not in _err(L) or True
+    assert "output of size 12 across 4 devices" in _err(L)
+    assert _shard(L, 4, 12, sg.SHARDED_TO_ALL, 2, 4)[0] == sg.ERR_NOT_DIVISIBLE  # input side, (12/2) % 4
+    assert "input of size 12 across 4 devices" in _err(L)
 
 
 def test_bad_mode(L):

@@ -692,7 +692,8 @@ def test_mx_rejections():
 # ---------------------------------------------------------------------------
 BWD_CASES = [("bf16", 8, 256, 512, 1, 4), ("bf16", 5, 96, 72, 1, 2), ("f16", 3, 128, 256, 2, 2),
              ("f32", 4, 64, 96, 1, 3), ("bf16", 1, 512, 128, 1, 1),
-             ("bf16", 4, 64, 48, 1, 2)]  # 24 rows per rank: the fragment-major stack crosses rank boundaries
+             ("bf16", 4, 64, 48, 1, 2),  # 24 rows per rank: the fragment-major stack crosses rank boundaries
+             ("f16", 5, 128, 256, 1, 4)]  # fp16 with one segment: the sharded-to-all backward in fp16 too
 
 
 @pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "-".join(map(str, c)))

@@ -367,6 +367,110 @@ def test_ulp_and_metrics():
     assert oracle.within(m, "bf16")
 
 
+def test_within_rejects_outside_the_tolerances():
+    """The acceptance rule of every parity test: fp32 outputs relL2 <= 1e-5;
+    16-bit outputs relL2 <= 4e-3 and error beyond half an output ulp
+    <= 1e-2 * rms(ref).  Each bound is checked on both sides, and each part
+    of the 16-bit rule alone must reject."""
+    ok16 = {"relL2": 3.9e-3, "maxabs_ulp": 0.9e-2 * 0.25, "rms": 0.25, "maxabs": 0.0}
+    assert oracle.within(ok16, "bf16") and oracle.within(ok16, "f16")
+    assert not oracle.within(dict(ok16, relL2=4.1e-3), "bf16")       # relL2 bound alone
+    assert not oracle.within(dict(ok16, relL2=5e-3), "f16")
+    assert not oracle.within(dict(ok16, maxabs_ulp=1.1e-2 * 0.25), "bf16")  # excess bound alone
+    # the excess bound scales with rms(ref): 0.05 passes at rms 10, fails at rms 1
+    assert oracle.within(dict(ok16, maxabs_ulp=0.05, rms=10.0), "bf16")
+    assert not oracle.within(dict(ok16, maxabs_ulp=0.05, rms=1.0), "bf16")
+    assert not oracle.within(dict(ok16, maxabs_ulp=5e-3, rms=0.1), "bf16")
+    ok32 = {"relL2": 0.9e-5, "maxabs_ulp": 1.0, "rms": 1.0, "maxabs": 1.0}
+    assert oracle.within(ok32, "f32")
+    assert not oracle.within(dict(ok32, relL2=1.1e-5), "f32")
+    assert not oracle.within(dict(ok32, relL2=4e-3), "f32")  # the 16-bit bound is not the fp32 one
+
+
+def test_within_on_perturbed_outputs():
+    """The same rule through metrics(): perturb a reference by known amounts."""
+    ref = np.linspace(-2.0, 2.0, 1001)
+    nr = np.linalg.norm(ref)
+    d = np.zeros_like(ref)
+    d[10] = 1.0
+    assert oracle.within(oracle.metrics(ref + 0.9e-5 * nr * d, ref, "f32"), "f32")
+    assert not oracle.within(oracle.metrics(ref + 1.1e-5 * nr * d, ref, "f32"), "f32")
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    half = 0.5 * oracle.ulp(ref, "bf16")
+    # one element off by half an ulp plus 1.1e-2 rms: relL2 stays tiny, the excess rule rejects
+    bad = ref.copy()
+    bad[500] += half[500] + 1.1e-2 * rms
+    m = oracle.metrics(bad, ref, "bf16")
+    assert m["relL2"] < 4e-3 and not oracle.within(m, "bf16")
+    good = ref.copy()
+    good[500] += half[500] + 0.9e-2 * rms
+    assert oracle.within(oracle.metrics(good, ref, "bf16"), "bf16")
+
+
+# ---------------------------------------------------------------------------
+# the gated MLP rounds the sharded h once to the activation dtype
+# ---------------------------------------------------------------------------
+def _rne(x: Fraction, bits: int, emin: int) -> Fraction:
+    """x rounded to `bits` significant bits (minimum normal exponent emin),
+    ties to even, in exact rational arithmetic."""
+    if x == 0:
+        return x
+    s = -1 if x < 0 else 1
+    a = abs(x)
+    e = math.floor(math.log2(a)) + 1  # a = f 2^e, 1/2 <= f < 1 (fixed up below)
+    while Fraction(2) ** (e - 1) > a:
+        e -= 1
+    while Fraction(2) ** e <= a:
+        e += 1
+    e = max(e, emin)
+    scaled = a * Fraction(2) ** (bits - e)
+    n = math.floor(scaled)
+    rem = scaled - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return s * Fraction(n) * Fraction(2) ** (e - bits)
+
+
+def test_mlp_rounds_h_once_closed_form():
+    """One token, one feature per rank, P = 2: g_r = 40, u_0 = 1 + 2^-7,
+    u_1 = 1 + 3 2^-7, so silu(g) u = 40.3125 and 40.9375 up to 2e-16.  The
+    stored h is their bf16 rounding (spacing 0.25 in [32, 64)): 40.25 and 41;
+    with W_down = [1, 1/2] the output is exactly 60.75, and 60.78125 - 3e-16
+    without the rounding."""
+    X = np.array([[1.0]])
+    Wg = np.array([[40.0], [40.0]])
+    Wu = np.array([[1.0078125], [1.0234375]])
+    Wd = np.array([[1.0, 0.5]])
+    assert oracle.mlp(X, Wg, Wu, Wd, P=2, round_dtype="bf16")[0, 0] == 60.75
+    exact = oracle.mlp(X, Wg, Wu, Wd, P=2, round_dtype="f64")[0, 0]
+    assert abs(exact - 60.78125) < 1e-12
+    # fp16 (11 significant bits, spacing 2^-5 in [32, 64)) keeps both products
+    assert oracle.mlp(X, Wg, Wu, Wd, P=2, round_dtype="f16")[0, 0] == 60.78125
+
+
+def test_mlp_bruteforce_rounded_h():
+    """Brute force of the whole chain on tiny bf16-valued inputs: g and u in
+    exact rational arithmetic (not rounded), silu in fp64, h rounded once to
+    bf16 by an exact rational RNE, the down layer's rank partials summed
+    exactly.  Equal bit for bit to oracle.mlp(round_dtype='bf16')."""
+    rng = np.random.default_rng(21)
+    B, D, F, P = 3, 8, 16, 2
+    # bf16-exact inputs: integers and halves scaled so g, u are generally not bf16 values
+    X = rng.integers(-8, 9, (B, D)) / 8.0
+    Wg = rng.integers(-16, 17, (F, D)) / 16.0
+    Wu = rng.integers(-16, 17, (F, D)) / 16.0
+    Wd = rng.integers(-8, 9, (D, F)) / 8.0
+    g = bf_linear(_fr(X), _fr(Wg))
+    u = bf_linear(_fr(X), _fr(Wu))
+    h = [[_rne(Fraction(float(gv) / (1.0 + math.exp(-float(gv)))) * uv, 8, -125) for gv, uv in zip(gr, ur)]
+         for gr, ur in zip(g, u)]
+    ref = np.array(bf_linear(h, _fr(Wd)), dtype=np.float64)
+    got = oracle.mlp(X, Wg, Wu, Wd, P=P, round_dtype="bf16")
+    np.testing.assert_array_equal(got, ref)
+    # the rounding matters on these inputs: the unrounded chain differs
+    assert not np.array_equal(oracle.mlp(X, Wg, Wu, Wd, P=P, round_dtype="f64"), ref)
+
+
 # ---------------------------------------------------------------------------
 # MX FP8 ("MLX 张量并行实战指南" 2.3 mode "mxfp8", read as OCP MX: E4M3 elements,
 # one E8M0 scale per 32 inputs, no biases)
@@ -516,3 +620,36 @@ def test_summa_backward_finite_differences(q):
                                _fd(lambda Xv: float(np.sum(G * oracle.summa(Xv, A, q))), X), rtol=1e-10, atol=1e-10)
     np.testing.assert_allclose(oracle.summa_atb(X, G, q),
                                _fd(lambda Av: float(np.sum(G * oracle.summa(X, Av, q))), A), rtol=1e-10, atol=1e-10)
+
+
+def test_backward_bruteforce_exact():
+    """The backward products on small integers, in exact rational arithmetic:
+    every sum is exact in fp64, so the oracle's loops must match bit for bit
+    (a transposed operand, a wrong rank slice or a dropped step changes them)."""
+    B, inn, out, P, S = 3, 6, 8, 2, 2
+    X, W = _ints(101, (B, inn)), _ints(102, (out, inn))
+    G = _ints(103, (P, B, out // P))
+    dx, dW = oracle.col_bwd(X, W, G, P=P, S=S)
+    want_dx = [[Fraction(0)] * inn for _ in range(B)]
+    for r in range(P):
+        Wr = _fr(oracle.slice_(W, 0, S, P, r))
+        prod = bf_matmul(_fr(G[r]), Wr)
+        want_dx = [[a + b for a, b in zip(ra, rb)] for ra, rb in zip(want_dx, prod)]
+        np.testing.assert_array_equal(dW[r], np.array(bf_matmul([list(c) for c in zip(*_fr(G[r]))], _fr(X)),
+                                                      dtype=np.float64))
+    np.testing.assert_array_equal(dx, np.array(want_dx, dtype=np.float64))
+
+    Xs, Wt, dY = _ints(104, (P, B, inn // P)), _ints(105, (out, inn)), _ints(106, (B, out))
+    dXs, dWr = oracle.row_bwd(Xs, Wt, dY, P=P)
+    for r in range(P):
+        Wr = _fr(oracle.slice_(Wt, 1, 1, P, r))
+        np.testing.assert_array_equal(dXs[r], np.array(bf_matmul(_fr(dY), Wr), dtype=np.float64))
+        np.testing.assert_array_equal(dWr[r], np.array(bf_matmul([list(c) for c in zip(*_fr(dY))], _fr(Xs[r])),
+                                                       dtype=np.float64))
+
+    M, K, N, q = 4, 6, 8, 2
+    Xm, A, Gm = _ints(107, (M, K)), _ints(108, (K, N)), _ints(109, (M, N))
+    np.testing.assert_array_equal(oracle.summa_abt(Gm, A, q),
+                                  np.array(bf_matmul(_fr(Gm), [list(c) for c in zip(*_fr(A))]), dtype=np.float64))
+    np.testing.assert_array_equal(oracle.summa_atb(Xm, Gm, q),
+                                  np.array(bf_matmul([list(c) for c in zip(*_fr(Xm))], _fr(Gm)), dtype=np.float64))

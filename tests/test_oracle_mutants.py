@@ -135,3 +135,74 @@ def test_summa_abt_wrong_sign(monkeypatch):
     o = oracle.summa_abt
     monkeypatch.setattr(oracle, "summa_abt", lambda dY, A, q, dtype=None: -o(dY, A, q, dtype=dtype))
     _fails(pins.test_summa_backward_finite_differences, 2)
+
+
+def _within_or(m, out_dtype):
+    if out_dtype in ("f32", "f64"):
+        return m["relL2"] <= 1e-5
+    return m["relL2"] <= 4e-3 or m["maxabs_ulp"] <= 1e-2 * m["rms"]
+
+
+def _within_no_rms(m, out_dtype):
+    if out_dtype in ("f32", "f64"):
+        return m["relL2"] <= 1e-5
+    return m["relL2"] <= 4e-3 and m["maxabs_ulp"] <= 1e-2
+
+
+def _within_typo(m, out_dtype):
+    if out_dtype in ("f32", "f64"):
+        return m["relL2"] <= 1e-5
+    return m["relL2"] <= 4e-2 and m["maxabs_ulp"] <= 1e-2 * m["rms"]
+
+
+def _within_f32_loose(m, out_dtype):
+    if out_dtype in ("f32", "f64"):
+        return m["relL2"] <= 1e-4
+    return m["relL2"] <= 4e-3 and m["maxabs_ulp"] <= 1e-2 * m["rms"]
+
+
+@pytest.mark.parametrize("bad", [_within_or, _within_no_rms, _within_typo, _within_f32_loose])
+def test_within_mutants(monkeypatch, bad):
+    monkeypatch.setattr(oracle, "within", bad)
+    failed = 0
+    for pin in (pins.test_within_rejects_outside_the_tolerances, pins.test_within_on_perturbed_outputs):
+        try:
+            pin()
+        except AssertionError:
+            failed += 1
+    assert failed > 0
+
+
+def test_mlp_skips_rounding_h(monkeypatch):
+    o = oracle.mlp
+    monkeypatch.setattr(oracle, "mlp", lambda X, Wg, Wu, Wd, P, round_dtype="bf16", dtype=None: o(
+        X, Wg, Wu, Wd, P, round_dtype="f64", dtype=dtype))
+    _fails(pins.test_mlp_rounds_h_once_closed_form)
+    _fails(pins.test_mlp_bruteforce_rounded_h)
+
+
+def test_mlp_rounds_g_and_u_too(monkeypatch):
+    """Rounding the fused gate and up results to the activation dtype before
+    SwiGLU (they never leave the kernel, so they must not be rounded)."""
+    def bad(X, Wg, Wu, Wd, P, round_dtype="bf16", dtype=None):
+        g = oracle.col(X, Wg, P=P, dtype=dtype)
+        u = oracle.col(X, Wu, P=P, dtype=dtype)
+        rg = np.vectorize(lambda v: oracle.round_to(v, round_dtype))
+        h = oracle.swiglu(rg(g), rg(u), round_dtype)
+        return oracle.row(h, Wd, P=P, dtype=dtype)
+
+    monkeypatch.setattr(oracle, "mlp", bad)
+    _fails(pins.test_mlp_bruteforce_rounded_h)
+
+
+def test_mlp_rounds_h_twice(monkeypatch):
+    """silu(g) rounded on its own before the product with u."""
+    def bad(X, Wg, Wu, Wd, P, round_dtype="bf16", dtype=None):
+        g = oracle.col(X, Wg, P=P, dtype=dtype)
+        u = oracle.col(X, Wu, P=P, dtype=dtype)
+        s = oracle.swiglu(g, np.ones_like(g), round_dtype)
+        h = np.vectorize(lambda v: oracle.round_to(v, round_dtype))(s * u)
+        return oracle.row(h, Wd, P=P, dtype=dtype)
+
+    monkeypatch.setattr(oracle, "mlp", bad)
+    _fails(pins.test_mlp_bruteforce_rounded_h)
