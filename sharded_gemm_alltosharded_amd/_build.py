@@ -28,14 +28,27 @@ def _objdir():
     return d
 
 
-def build_library(verbose: bool = False) -> str:
-    """Compile every source (in parallel) and link the shared library."""
+HEADERS = [os.path.join(CSRC, "internal.h"), os.path.join(os.path.dirname(HERE), "include", "shardgemm.h")]
+
+
+def _stale(src: str, obj: str) -> bool:
+    if not os.path.exists(obj):
+        return True
+    t = os.path.getmtime(obj)
+    return any(os.path.getmtime(f) > t for f in [src, *HEADERS])
+
+
+def build_library(verbose: bool = False, incremental: bool = False) -> str:
+    """Compile every source (in parallel) and link the shared library;
+    incremental=True recompiles only sources newer than their objects."""
     objdir = _objdir()
     procs = []
     objs = []
     for src in SOURCES:
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
         objs.append(obj)
+        if incremental and not _stale(os.path.join(CSRC, src), obj):
+            continue
         cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
     failed = []
@@ -57,4 +70,4 @@ def build_library(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build_library(verbose=True))
+    print(build_library(verbose=True, incremental="--incremental" in sys.argv))
