@@ -195,6 +195,20 @@ sg_status sg_mlp(const sg_layer* gate_up, const sg_layer* down, const void* x, i
  * a gate|up, down pair or B <= 0). */
 size_t sg_mlp_workspace(const sg_layer* gate_up, const sg_layer* down, int64_t B);
 
+/* sg_mlp for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * kernels and bitwise the same results as sg_mlp, with the workspace taken
+ * from a fixed scratch array of SG_MLP_STATIC_SCRATCH_BYTES (16 MiB) that the
+ * library holds on every device it runs on until the process ends.  The
+ * caller passes x and y as for sg_mlp; nothing is allocated or freed.
+ * Errors: as sg_mlp, and SG_ERR_WORKSPACE when sg_mlp_workspace(gate_up,
+ * down, B) exceeds the scratch (about 570 tokens for a 14336-wide bf16 h).
+ * All calls on one device share its scratch, so calls that overlap on one
+ * GPU (other streams or threads) race: the caller serialises them. */
+#define SG_MLP_STATIC_SCRATCH_BYTES (16u << 20)
+sg_status sg_mlp_static(const sg_layer* gate_up, const sg_layer* down, const void* x, int64_t B, void* y,
+                        sg_dtype y_dtype, void* stream);
+
 /* Backward of an all-to-sharded layer: the vector-Jacobian product of [MLX]
  * 2.1 with its sum_gradients wrapper.  The input x is shared by every rank,
  * so its gradient is the all_sum of the rank gradients, summed here on chip in

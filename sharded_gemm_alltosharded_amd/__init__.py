@@ -83,6 +83,7 @@ def lib():
             "sg_summa_backward": ([P, P, P, I, I64, I64, I64, I, P, P, P], I),
             "sg_mlp": ([P, P, P, I64, P, I, P, SZ, P], I),
             "sg_mlp_workspace": ([P, P, I64], SZ),
+            "sg_mlp_static": ([P, P, P, I64, P, I, P], I),
             "sg_sharded_to_all_workspace": ([P, I64], SZ),
             "sg_summa_matmul": ([P, P, I, I64, I64, I64, I, P, I, I, P, SZ, P], I),
             "sg_summa_workspace": ([I, I64, I64, I], SZ),
@@ -312,6 +313,18 @@ def mlp(gate_up: Layer, down: Layer, x: torch.Tensor, out_dtype=None, out: torch
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().sg_mlp(gate_up.handle, down.handle, _ptr(x), B, _ptr(out), _DT.get(out.dtype, -1), _ptr(ws),
                         nbytes, _stream(x.device)))
+    return out
+
+
+MLP_STATIC_SCRATCH_BYTES = 16 << 20  # SG_MLP_STATIC_SCRATCH_BYTES
+
+
+def mlp_static(gate_up: Layer, down: Layer, x: torch.Tensor, out: torch.Tensor) -> torch.Tensor:
+    """sg_mlp_static: mlp() without a workspace, for callers that cannot
+    allocate (the library's per-device static scratch holds h).  The caller
+    passes the output; this wrapper allocates nothing."""
+    _check(lib().sg_mlp_static(gate_up.handle, down.handle, _ptr(x), x.shape[0], _ptr(out), _DT.get(out.dtype, -1),
+                               _stream(x.device)))
     return out
 
 

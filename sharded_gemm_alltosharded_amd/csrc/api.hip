@@ -4,6 +4,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 
 #include "internal.h"
@@ -670,18 +671,10 @@ size_t sg_mlp_workspace(const sg_layer* gate_up, const sg_layer* down, int64_t B
     return mlp_down_bytes(down, B) + mlp_h_bytes(gate_up, B);
 }
 
-sg_status sg_mlp(const sg_layer* gate_up, const sg_layer* down, const void* x, int64_t B, void* y, sg_dtype y_dtype,
-                 void* workspace, size_t ws_bytes, void* stream) {
-    g_err.clear();
-    if (const char* why = mlp_check(gate_up, down)) return fail(SG_ERR_INVALID_ARG, "%s", why);
-    if (B < 0 || B > INT32_MAX) return fail(SG_ERR_INVALID_ARG, "token count %lld out of range", (long long)B);
-    if (!dtype_ok(y_dtype)) return fail(SG_ERR_INVALID_ARG, "unknown output dtype %d", (int)y_dtype);
-    if (B == 0) return SG_OK;
-    if (!x || !y) return fail(SG_ERR_INVALID_ARG, "x and y must not be NULL");
-    const size_t db = mlp_down_bytes(down, B), need = db + mlp_h_bytes(gate_up, B);
-    if (!workspace || ws_bytes < need)
-        return fail(SG_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws_bytes, need);
-    if (!aligned16(workspace)) return fail(SG_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+// the launches of sg_mlp on a checked workspace of at least sg_mlp_workspace bytes
+static sg_status mlp_run(const sg_layer* gate_up, const sg_layer* down, const void* x, int64_t B, void* y,
+                         sg_dtype y_dtype, void* workspace, void* stream) {
+    const size_t db = mlp_down_bytes(down, B);
     void* h = (char*)workspace + db;
     const sg_layer* gu = gate_up;
     const sg_layer* dn = down;
@@ -742,6 +735,100 @@ sg_status sg_mlp(const sg_layer* gate_up, const sg_layer* down, const void* x, i
     e = run(q, kd, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "mlp down launch");
     return SG_OK;
+}
+
+// argument checks shared by sg_mlp and sg_mlp_static; *done is set for B == 0
+static sg_status mlp_args(const sg_layer* gate_up, const sg_layer* down, const void* x, int64_t B, const void* y,
+                          sg_dtype y_dtype, bool* done) {
+    *done = false;
+    if (const char* why = mlp_check(gate_up, down)) return fail(SG_ERR_INVALID_ARG, "%s", why);
+    if (B < 0 || B > INT32_MAX) return fail(SG_ERR_INVALID_ARG, "token count %lld out of range", (long long)B);
+    if (!dtype_ok(y_dtype)) return fail(SG_ERR_INVALID_ARG, "unknown output dtype %d", (int)y_dtype);
+    if (B == 0) {
+        *done = true;
+        return SG_OK;
+    }
+    if (!x || !y) return fail(SG_ERR_INVALID_ARG, "x and y must not be NULL");
+    return SG_OK;
+}
+
+sg_status sg_mlp(const sg_layer* gate_up, const sg_layer* down, const void* x, int64_t B, void* y, sg_dtype y_dtype,
+                 void* workspace, size_t ws_bytes, void* stream) {
+    g_err.clear();
+    bool done = false;
+    sg_status st = mlp_args(gate_up, down, x, B, y, y_dtype, &done);
+    if (st != SG_OK || done) return st;
+    const size_t need = sg_mlp_workspace(gate_up, down, B);
+    if (!workspace || ws_bytes < need)
+        return fail(SG_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws_bytes, need);
+    if (!aligned16(workspace)) return fail(SG_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    return mlp_run(gate_up, down, x, B, y, y_dtype, workspace, stream);
+}
+
+// ---------------------------------------------------------------------------
+// sg_mlp without a workspace argument: a fixed scratch array per device.
+// In host code `mlp_scratch` names a host-side stand-in, not the device
+// array: every use goes through the device address hipGetSymbolAddress
+// returns, looked up once per device (with that device current) and kept.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char mlp_scratch[SG_MLP_STATIC_SCRATCH_BYTES];
+
+__global__ void zero_words_kernel(unsigned* p, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// the device address of the current device's scratch; on a device's first
+// call its arrival counters are cleared with a fill kernel on `st` (the
+// array starts zeroed and every call leaves them zero; the fill makes that
+// independent of the loader)
+sg_status scratch_for_current_device(hipStream_t st, void** out) {
+    int dev = -1;
+    HIP_TRY(hipGetDevice(&dev), "device query");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(SG_ERR_UNSUPPORTED, "device %d is beyond the %d devices the static scratch tracks", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(mlp_scratch)), "scratch address");
+        const int words = (int)(sg::kPartialsOffset / sizeof(unsigned));
+        hipLaunchKernelGGL(zero_words_kernel, dim3((words + 255) / 256), dim3(256), 0, st, (unsigned*)p, words);
+        HIP_TRY(hipGetLastError(), "scratch clear");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return SG_OK;
+}
+}  // namespace
+
+sg_status sg_mlp_static(const sg_layer* gate_up, const sg_layer* down, const void* x, int64_t B, void* y,
+                        sg_dtype y_dtype, void* stream) {
+    g_err.clear();
+    bool done = false;
+    sg_status st = mlp_args(gate_up, down, x, B, y, y_dtype, &done);
+    if (st != SG_OK || done) return st;
+    const size_t need = sg_mlp_workspace(gate_up, down, B);
+    if (need > (size_t)SG_MLP_STATIC_SCRATCH_BYTES)
+        return fail(SG_ERR_WORKSPACE,
+                    "sg_mlp_static: %lld tokens need %zu bytes of workspace, the static scratch holds %zu; "
+                    "use sg_mlp with a caller workspace", (long long)B, need, (size_t)SG_MLP_STATIC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    st = scratch_for_current_device((hipStream_t)stream, &ws);
+    if (st != SG_OK) return st;
+    if (sg_sharded_to_all_workspace(down, B) > 0) {
+        // the down layer splits by rank and counts arrivals in the scratch:
+        // start them from zero whatever an earlier call left
+        const int words = (int)(sg::kPartialsOffset / sizeof(unsigned));
+        hipLaunchKernelGGL(zero_words_kernel, dim3((words + 255) / 256), dim3(256), 0, (hipStream_t)stream,
+                           (unsigned*)ws, words);
+        HIP_TRY(hipGetLastError(), "scratch clear");
+    }
+    return mlp_run(gate_up, down, x, B, y, y_dtype, ws, stream);
 }
 
 // ---------------------------------------------------------------------------
