@@ -349,15 +349,16 @@ class Summa(Workload):
 class SummaBackward(Workload):
     """Backward of the SUMMA product Y = X A at 8192^3, q = 4, bf16 in, fp32
     out: dX = dY A^T (Matmul_ABT_2D, matrix-core tile kernels with the q steps
-    as K segments) and dA = X^T dY (Matmul_ATB_2D, vector units)."""
+    as K segments) and dA = X^T dY (Matmul_ATB_2D, the same kernels over X^T
+    and dY's transposed step blocks in a workspace)."""
     n, q = 8192, 4
     name = "summa-8192-q4-backward"
     metric = "SUMMA backward TFLOP/s (% MFMA peak)"
     unit = "TFLOP/s"
     bound = "mfma"
-    steps, warmup = 3, 1
-    dominant = "bwd_dw4_kernel (dA = X^T dY on the vector units)"
-    dominant_src = ("backward.hip", "internal.h")
+    steps, warmup = 10, 2
+    dominant = "tile_pp_kernel 256x256 (dA = X^T dY over the transposed copies, q steps in registers)"
+    dominant_src = ("tile_dma.hip", "internal.h")
 
     def setup(self):
         import sharded_gemm_alltosharded_amd as sg
@@ -365,6 +366,9 @@ class SummaBackward(Workload):
         self.Xh, self.Ah = synth.summa_inputs(self.n, seed=30)
         self.Gh = synth.normal(113, (self.n, self.n), 1.0, synth.BF16)
         self.X, self.A, self.G = (_dev_tensor(a, "bf16") for a in (self.Xh, self.Ah, self.Gh))
+        import torch
+        n = sg.lib().sg_summa_backward_workspace(sg.BF16, self.n, self.n, self.n, self.q)
+        self.ws = torch.empty(n, dtype=torch.uint8, device="cuda")  # X^T and dY's transposed step blocks
         self.sg = sg
         self.units = 2 * 2 * self.n ** 3
         self.dom_units = 2 * self.n ** 3
@@ -373,7 +377,7 @@ class SummaBackward(Workload):
         self.sg.summa_backward(self.X, self.A, self.G, self.q, need_da=False)
         if ev:
             self.sg.time_next_launch(*ev)
-        self.sg.summa_backward(self.X, self.A, self.G, self.q, need_dx=False)
+        self.sg.summa_backward(self.X, self.A, self.G, self.q, need_dx=False, ws=self.ws)
 
     def config(self):
         return {"workload": self.name, "M": self.n, "K": self.n, "N": self.n, "q": self.q, "grads": "fp32"}
@@ -565,7 +569,7 @@ class BackwardMLP(Workload):
     name = "llama-mlp-backward"
     metric = "sharded-MLP backward GB/s (% HBM peak)"
     steps, warmup = 20, 3
-    dominant = "bwd_dxt_kernel (gate|up input gradient with the fused all_sum)"
+    dominant = "dw_small_kernel (gate|up weight gradient, fp32, streaming writes)"
     dominant_src = ("backward.hip", "internal.h")
 
     def setup(self):
@@ -582,21 +586,23 @@ class BackwardMLP(Workload):
         self.hs = _dev_tensor(synth.normal(100, (P, B, F // P), 1.0, synth.BF16), "bf16")
         self.dy = _dev_tensor(synth.normal(101, (B, D), 1.0, synth.BF16), "bf16")
         self.dg = _dev_tensor(synth.normal(102, (P, B, 2 * F // P), 1.0, synth.BF16), "bf16")
+        n = max(sg.lib().sg_layer_backward_workspace(l.handle, B) for l in (self.gu, self.dn))
+        self.ws = torch.empty(n, dtype=torch.uint8, device="cuda")  # transposed operands of the weight gradients
         self.sg = sg
         self.f32 = torch.float32
         w = 2 * (2 * F * D + D * F)              # weights read once by the input-gradient products
         g = 4 * (2 * F * D + D * F)              # fp32 weight gradients written once
         a = 2 * (B * D + B * F + 2 * B * F + B * D + B * F)  # x, h, dG, dY in; dh out (bf16)
         self.units = w + g + a + 4 * B * D       # + dx (fp32)
-        self.dom_units = 2 * (2 * F * D) + 2 * (2 * B * F) + 4 * B * D  # W_gu, dG in; dx (fp32) out
+        self.dom_units = 4 * (2 * F * D) + 2 * (2 * B * F + B * D)  # dW_gu (fp32) out; dG, x in
 
     def step(self, i, ev=None):
         sg = self.sg
-        sg.sharded_to_all_backward(self.dn, self.hs, self.dy, dx_dtype=None)
+        sg.sharded_to_all_backward(self.dn, self.hs, self.dy, dx_dtype=None, ws=self.ws)
+        sg.all_to_sharded_backward(self.gu, None, self.dg, need_dw=False, dx_dtype=self.f32)
         if ev:
             sg.time_next_launch(*ev)
-        sg.all_to_sharded_backward(self.gu, None, self.dg, need_dw=False, dx_dtype=self.f32)
-        sg.all_to_sharded_backward(self.gu, self.x, self.dg, need_dx=False)
+        sg.all_to_sharded_backward(self.gu, self.x, self.dg, need_dx=False, ws=self.ws)
 
     def config(self):
         return {"workload": self.name, "tokens": self.B, "D": self.D, "F": self.F, "P": self.P,

@@ -219,11 +219,26 @@ sg_status sg_mlp_static(const sg_layer* gate_up, const sg_layer* down, const voi
  *   x  (B, in_dims) of the layer's dtype (needed for dw only; may be NULL
  *      otherwise); dy (P, B, out_dims/P) of the layer's dtype, the layout of
  *      the forward's sharded output.
+ *   workspace device scratch of at least sg_layer_backward_workspace(layer, B)
+ *      bytes, 16-byte aligned, or NULL.  dw runs on the matrix cores: up to
+ *      128 tokens reading dy and x in place (no workspace), beyond that over
+ *      x and dy transposed into the workspace (tokens padded to a multiple of
+ *      32), or on the vector units when no workspace is given.  No
+ *      initialisation needed; calls that share a workspace must not overlap.
+ *      SG_ERR_WORKSPACE when a needed workspace is given too small or
+ *      misaligned.
+ * dx runs on the forward kernels over a transposed copy of the rank shards
+ * that the layer builds on the first backward call that reads it (16-bit
+ * layers whose out_dims/P is a multiple of 32 and in_dims of 16; the same
+ * bytes as the weights again, held until sg_layer_free; that first call
+ * allocates and synchronises the stream).  Backward calls on one layer must not
+ * run concurrently with its first one.
  * dx or dw may be NULL (not both).  Dense layers only (SG_ERR_UNSUPPORTED for
  * 4-bit and MX FP8 layers); no bias gradient.  fp32 accumulation; the rank sum
  * is deterministic.  B = 0 is a no-op. */
 sg_status sg_all_to_sharded_backward(const sg_layer* layer, const void* x, const void* dy, int64_t B, void* dx,
-                                     sg_dtype dx_dtype, void* dw, sg_dtype dw_dtype, void* stream);
+                                     sg_dtype dx_dtype, void* dw, sg_dtype dw_dtype, void* workspace,
+                                     size_t ws_bytes, void* stream);
 
 /* Backward of a sharded-to-all layer ([MLX] 2.2): every rank receives the
  * full gradient dy (B, out_dims) of the summed output, so
@@ -231,9 +246,18 @@ sg_status sg_all_to_sharded_backward(const sg_layer* layer, const void* x, const
  *      no reduction);
  *   dw (P, out_dims, in_dims/P) of dw_dtype, dw[r] = dy^T x_partial[r].
  *   x_partial (P, B, in_dims/P) of the layer's dtype (for dw only).
- * Everything else as sg_all_to_sharded_backward. */
+ * The transposed shard copy needs out_dims % 32 == 0 and (in_dims/P) % 16 == 0.
+ * Everything else, the workspace included, as sg_all_to_sharded_backward. */
 sg_status sg_sharded_to_all_backward(const sg_layer* layer, const void* x_partial, const void* dy, int64_t B,
-                                     void* dx_partial, sg_dtype dx_dtype, void* dw, sg_dtype dw_dtype, void* stream);
+                                     void* dx_partial, sg_dtype dx_dtype, void* dw, sg_dtype dw_dtype,
+                                     void* workspace, size_t ws_bytes, void* stream);
+
+/* Bytes of workspace the matrix-core weight gradient of either backward needs
+ * for B tokens ((out_dims + in_dims) x B rounded up to 32, 16-bit); 0 when it
+ * needs none (at most 128 tokens), when the layer's gradients run on the
+ * vector units only (fp32, quantized, or shapes whose transposes do not
+ * tile), or on bad input. */
+size_t sg_layer_backward_workspace(const sg_layer* layer, int64_t B);
 
 /* SUMMA backward ([SUMMA] Matmul_ABT_2D and Matmul_ATB_2D, the gradients of
  * Y = X A): with the inner dimension of each product cut into the q SUMMA step
@@ -242,9 +266,19 @@ sg_status sg_sharded_to_all_backward(const sg_layer* layer, const void* x_partia
  *   dA (K, N) fp32 = X^T dY   (dA_kj = sum_t X_tk^T dY_tj).
  *   X (M, K), A (K, N), dY (M, N): row-major, of dtype.  dX or dA may be NULL
  *   (not both); each output is overwritten.
- * Errors as sg_summa_matmul (q must divide M, K and N). */
+ *   workspace device scratch of at least sg_summa_backward_workspace(...)
+ *   bytes, 16-byte aligned, or NULL: with it dA runs on the matrix cores over
+ *   X^T and the transposed step blocks of dY written into it; without it on
+ *   the vector units.  dX always runs on the matrix cores (16-bit dtypes).
+ * Errors as sg_summa_matmul (q must divide M, K and N); SG_ERR_WORKSPACE for a
+ * workspace below the size the query gives. */
 sg_status sg_summa_backward(const void* X, const void* A, const void* dY, sg_dtype dtype, int64_t M, int64_t K,
-                            int64_t N, int q, float* dX, float* dA, void* stream);
+                            int64_t N, int q, float* dX, float* dA, void* workspace, size_t ws_bytes, void* stream);
+
+/* Bytes of workspace sg_summa_backward's matrix-core dA needs ((K + N) M
+ * 16-bit elements): 0 unless dtype is 16-bit, (M/q) % 32 == 0, N % 16 == 0 and
+ * K % 8 == 0. */
+size_t sg_summa_backward_workspace(sg_dtype dtype, int64_t M, int64_t K, int64_t N, int q);
 
 /* Bytes of workspace sg_sharded_to_all needs for B tokens (0 on bad input). */
 size_t sg_sharded_to_all_workspace(const sg_layer* layer, int64_t B);

@@ -78,9 +78,11 @@ def lib():
             "sg_all_to_sharded_ex": ([P, P, I, I64, P, I, I, I, P], I),
             "sg_sharded_to_all": ([P, P, I64, P, I, P, SZ, P], I),
             "sg_sharded_to_all_ex": ([P, P, I64, P, I, I, P, SZ, P], I),
-            "sg_all_to_sharded_backward": ([P, P, P, I64, P, I, P, I, P], I),
-            "sg_sharded_to_all_backward": ([P, P, P, I64, P, I, P, I, P], I),
-            "sg_summa_backward": ([P, P, P, I, I64, I64, I64, I, P, P, P], I),
+            "sg_all_to_sharded_backward": ([P, P, P, I64, P, I, P, I, P, SZ, P], I),
+            "sg_sharded_to_all_backward": ([P, P, P, I64, P, I, P, I, P, SZ, P], I),
+            "sg_layer_backward_workspace": ([P, I64], SZ),
+            "sg_summa_backward": ([P, P, P, I, I64, I64, I64, I, P, P, P, SZ, P], I),
+            "sg_summa_backward_workspace": ([I, I64, I64, I64, I], SZ),
             "sg_mlp": ([P, P, P, I64, P, I, P, SZ, P], I),
             "sg_mlp_workspace": ([P, P, I64], SZ),
             "sg_mlp_static": ([P, P, P, I64, P, I, P], I),
@@ -328,8 +330,18 @@ def mlp_static(gate_up: Layer, down: Layer, x: torch.Tensor, out: torch.Tensor) 
     return out
 
 
+def _bwd_ws(layer: Layer, B: int, ws, device):
+    """The weight-gradient workspace: "auto" takes sg_layer_backward_workspace
+    bytes from torch's caching allocator (stream-ordered), None runs the
+    weight gradient on the vector units, or a uint8 device tensor."""
+    if isinstance(ws, str):
+        n = int(lib().sg_layer_backward_workspace(layer.handle, B))
+        ws = torch.empty(n, dtype=torch.uint8, device=device) if n else None
+    return ws, (0 if ws is None else ws.numel() * ws.element_size())
+
+
 def all_to_sharded_backward(layer: Layer, x: torch.Tensor | None, dy: torch.Tensor, need_dx: bool = True,
-                            need_dw: bool = True, dx_dtype=None, dw_dtype=torch.float32):
+                            need_dw: bool = True, dx_dtype=None, dw_dtype=torch.float32, ws="auto"):
     """Backward of an all-to-sharded layer (sg_all_to_sharded_backward): dy
     (P, B, out/P) -> (dx (B, in) = the rank-order all_sum of dy[r] W_r,
     dw (P, out/P, in), dw[r] = dy[r]^T x); either may be skipped (None)."""
@@ -337,14 +349,15 @@ def all_to_sharded_backward(layer: Layer, x: torch.Tensor | None, dy: torch.Tens
     dx = torch.empty((B, layer.in_dims), dtype=dx_dtype or layer.dtype, device=dy.device) if need_dx else None
     dw = torch.empty((layer.P, layer.out_dims // layer.P, layer.in_dims), dtype=dw_dtype,
                      device=dy.device) if need_dw else None
+    ws, nbytes = _bwd_ws(layer, B, ws if need_dw else None, dy.device)
     _check(lib().sg_all_to_sharded_backward(layer.handle, _ptr(x), _ptr(dy), B, _ptr(dx),
                                             _DT.get(dx.dtype if dx is not None else layer.dtype, -1), _ptr(dw),
-                                            _DT.get(dw_dtype, -1), _stream(dy.device)))
+                                            _DT.get(dw_dtype, -1), _ptr(ws), nbytes, _stream(dy.device)))
     return dx, dw
 
 
 def sharded_to_all_backward(layer: Layer, x_partial: torch.Tensor | None, dy: torch.Tensor, need_dx: bool = True,
-                            need_dw: bool = True, dx_dtype=None, dw_dtype=torch.float32):
+                            need_dw: bool = True, dx_dtype=None, dw_dtype=torch.float32, ws="auto"):
     """Backward of a sharded-to-all layer (sg_sharded_to_all_backward): dy
     (B, out) -> (dx_partial (P, B, in/P), slice r = dy W_r; dw (P, out, in/P),
     dw[r] = dy^T x_partial[r]); either may be skipped (None)."""
@@ -353,22 +366,29 @@ def sharded_to_all_backward(layer: Layer, x_partial: torch.Tensor | None, dy: to
                      device=dy.device) if need_dx else None
     dw = torch.empty((layer.P, layer.out_dims, layer.in_dims // layer.P), dtype=dw_dtype,
                      device=dy.device) if need_dw else None
+    ws, nbytes = _bwd_ws(layer, B, ws if need_dw else None, dy.device)
     _check(lib().sg_sharded_to_all_backward(layer.handle, _ptr(x_partial), _ptr(dy), B, _ptr(dx),
                                             _DT.get(dx.dtype if dx is not None else layer.dtype, -1), _ptr(dw),
-                                            _DT.get(dw_dtype, -1), _stream(dy.device)))
+                                            _DT.get(dw_dtype, -1), _ptr(ws), nbytes, _stream(dy.device)))
     return dx, dw
 
 
 def summa_backward(X: torch.Tensor, A: torch.Tensor, dY: torch.Tensor, q: int, need_dx: bool = True,
-                   need_da: bool = True):
+                   need_da: bool = True, ws="auto"):
     """Gradients of Y = X A in q SUMMA steps (sg_summa_backward): dX = dY A^T
-    (M, K) and dA = X^T dY (K, N), both fp32; either may be skipped (None)."""
+    (M, K) and dA = X^T dY (K, N), both fp32; either may be skipped (None).
+    ws: "auto" (sg_summa_backward_workspace bytes from torch's allocator), None
+    (dA on the vector units) or a uint8 device tensor."""
     M, K = X.shape
     N = A.shape[1]
     dX = torch.empty((M, K), dtype=torch.float32, device=dY.device) if need_dx else None
     dA = torch.empty((K, N), dtype=torch.float32, device=dY.device) if need_da else None
+    if isinstance(ws, str):
+        n = int(lib().sg_summa_backward_workspace(_DT.get(X.dtype, -1), M, K, N, q)) if need_da else 0
+        ws = torch.empty(n, dtype=torch.uint8, device=dY.device) if n else None
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().sg_summa_backward(_ptr(X), _ptr(A), _ptr(dY), _DT.get(X.dtype, -1), M, K, N, q, _ptr(dX), _ptr(dA),
-                                   _stream(dY.device)))
+                                   _ptr(ws), nbytes, _stream(dY.device)))
     return dX, dA
 
 

@@ -23,6 +23,11 @@ struct sg_layer {
     int mx;                  // MX FP8 layer: w holds E4M3 code bytes (dense layouts, wfrag), ms its scales
     uint8_t* ms;             // MX FP8 E8M0 scales: P x rows_r x cols_r/32 (sg::mx_scale_offset when wfrag)
     int device;
+    // dense 16-bit layers: the rank shards transposed, fragment-major (built by
+    // the first backward call that reads them): all-to-sharded, P matrices
+    // W_r^T (cols_r, rows_r); sharded-to-all, the stack of W_r^T, (in, out)
+    void* wt;
+    std::mutex wt_mu;
 };
 
 namespace sg {
@@ -113,6 +118,7 @@ void free_layer(sg_layer* l) {
     if (l->qb) (void)hipFree(l->qb);
     if (l->ms) (void)hipFree(l->ms);
     if (l->bias) (void)hipFree(l->bias);
+    if (l->wt) (void)hipFree(l->wt);
     delete l;
 }
 
@@ -833,6 +839,18 @@ sg_status sg_mlp_static(const sg_layer* gate_up, const sg_layer* down, const voi
 
 // ---------------------------------------------------------------------------
 // Backward (vector-Jacobian products) of the two sharded layers
+//
+// Input gradients run on the forward kernels: dx of an all-to-sharded layer,
+// sum_r dY_r W_r, is a sharded-to-all product with the rank shards
+// transposed (the rank-order sum fused as in the forward), and dX_r = dY W_r
+// of a sharded-to-all layer is an all-to-sharded product with the stack of
+// W_r^T and a sharded output.  The transposed shards are a second,
+// fragment-major copy of the layer's weights, built once by the first
+// backward call that needs it.  Weight gradients (a contraction over the
+// tokens) and SUMMA's dA = X^T dY run on the matrix-core tile kernels with
+// both operands transposed into the caller's workspace (tokens zero-padded to
+// a multiple of 32).  Shapes or dtypes those kernels do not take, or a call
+// without a workspace, run on the vector-unit kernels of backward.hip.
 // ---------------------------------------------------------------------------
 namespace {
 
@@ -846,42 +864,210 @@ const char* bwd_check(const sg_layer* l, int mode, int64_t B, sg_dtype dx_dtype,
     return nullptr;
 }
 
+int64_t pad32(int64_t n) { return (n + 31) / 32 * 32; }
+
+// the transposed-shard copy: 16-bit dense layers whose transposes tile into
+// 16-row x 32-k fragments (rows_r is the k of the transposed product)
+bool wt_ok(const sg_layer* l) {
+    return !l->quantized && !l->mx && l->dtype != SG_F32 && l->rows_r % 32 == 0 && l->cols_r % 16 == 0;
+}
+
+sg_status ensure_wt(const sg_layer* lc, hipStream_t st) {
+    sg_layer* l = const_cast<sg_layer*>(lc);  // the copy is a cache of the layer's own weights
+    std::lock_guard<std::mutex> lock(l->wt_mu);
+    if (l->wt) return SG_OK;
+    const size_t bytes = (size_t)(l->P * l->rows_r * l->cols_r) * dtype_size(l->dtype);
+    void* rowmajor = l->w;
+    void* tmp = nullptr;
+    void* wt = nullptr;
+    hipError_t e = hipSuccess;
+    if (l->wfrag) {
+        e = hipMalloc(&tmp, bytes);
+        const int mats = l->mode == SG_ALL_TO_SHARDED ? 1 : l->P;
+        const int64_t rows = l->mode == SG_ALL_TO_SHARDED ? l->out_dims : l->rows_r;
+        if (e == hipSuccess) e = sg::frag_transform(tmp, l->w, mats, rows, l->cols_r, 0, st);
+        rowmajor = tmp;
+    }
+    if (e == hipSuccess) e = hipMalloc(&wt, bytes);
+    // rank r's (rows_r, cols_r) shard -> rows r cols_r .. of the stack, k = its rows
+    if (e == hipSuccess) e = sg::t_frag(wt, rowmajor, l->P, l->rows_r, l->cols_r, l->rows_r, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (tmp) (void)hipFree(tmp);
+    if (e != hipSuccess) {
+        if (wt) (void)hipFree(wt);
+        return hip_fail(e, "transposed shard copy");
+    }
+    l->wt = wt;
+    return SG_OK;
+}
+
+// kernel family for a product of M tokens against N stacked output rows,
+// nseg K segments of Kseg, on fragment-major 16-bit weights (no split)
+Kind choose_bwd(int64_t M, int64_t N, int nseg, int swiglu = 0) {
+    if (M <= 32 && sg::skinny_shape((int)M, (int)N, nseg, swiglu).lds <= sg::kMaxStreamLds) return K_SKINNY;
+    return M >= 512 ? K_TILE0 : K_TILE1;
+}
+
+// weight-gradient workspace: A = the upstream gradient transposed (out, Bp)
+// row-major, then W = the input transposed, (in, Bp) fragment-major
+size_t dw_ws_bytes(const sg_layer* l, int64_t B) {
+    return align256((size_t)(l->out_dims * pad32(B)) * 2) + align256((size_t)(l->in_dims * pad32(B)) * 2);
+}
+bool dw_mfma_ok(const sg_layer* l) {
+    if (l->quantized || l->mx || l->dtype == SG_F32) return false;
+    return l->mode == SG_ALL_TO_SHARDED ? (l->in_dims % 16 == 0 && l->rows_r % 8 == 0)
+                                        : (l->cols_r % 16 == 0 && l->out_dims % 8 == 0);
+}
+
+// dW with few tokens: bound by its output writes, on the small-K kernel that
+// reads the caller's row-major dy and x directly (no workspace)
+bool dw_small_ok(const sg_layer* l, int64_t B) {
+    if (l->quantized || l->mx || l->dtype == SG_F32 || (B + 15) / 16 * 16 > sg::kDwSmallMaxTokens) return false;
+    return l->mode == SG_ALL_TO_SHARDED ? (l->rows_r % 8 == 0 && l->in_dims % 8 == 0)
+                                        : (l->out_dims % 8 == 0 && l->cols_r % 8 == 0);
+}
+
+sg_status dw_small(const sg_layer* l, const void* x, const void* dy, int64_t B, void* dw, sg_dtype dw_dtype,
+                   hipStream_t st) {
+    sg::BwdDwSmall p{};
+    const bool a2s = l->mode == SG_ALL_TO_SHARDED;
+    p.G = dy;  // a2s: (P, B, out/P), rank blocks of out/P rows; s2a: (B, out)
+    p.gl = a2s ? l->rows_r : l->out_dims;
+    p.g_seg = a2s ? B * l->rows_r : 0;
+    p.ldg = a2s ? l->rows_r : l->out_dims;
+    p.X = x;  // a2s: (B, in); s2a: (P, B, in/P), rank blocks of in/P columns
+    p.xl = a2s ? l->in_dims : l->cols_r;
+    p.x_seg = a2s ? 0 : B * l->cols_r;
+    p.ldx = a2s ? l->in_dims : l->cols_r;
+    p.dtype = l->dtype;
+    p.O = (int)l->out_dims;
+    p.I = (int)l->in_dims;
+    p.B = (int)B;
+    p.Bp = (int)((B + 15) / 16 * 16);
+    p.out = dw;
+    p.out_dtype = dw_dtype;
+    p.nloc = a2s ? 0 : l->cols_r;  // a2s: (P, out/P, in) is the row-major (out, in)
+    hipError_t e = sg::launch_dw_small(p, st);
+    if (e != hipSuccess) return hip_fail(e, "weight-gradient launch");
+    return SG_OK;
+}
+
+// dW by the tile kernels: M = out rows (all ranks), N = in, K = Bp tokens
+sg_status dw_mfma(const sg_layer* l, const void* x, const void* dy, int64_t B, void* dw, sg_dtype dw_dtype,
+                  void* workspace, hipStream_t st) {
+    const int64_t Bp = pad32(B);
+    void* wa = workspace;
+    void* ww = (char*)workspace + align256((size_t)(l->out_dims * Bp) * 2);
+    hipError_t e;
+    if (l->mode == SG_ALL_TO_SHARDED) {
+        e = sg::transpose16(wa, dy, l->P, B, l->rows_r, Bp, st);            // (P, out/P, Bp) = (out, Bp)
+        if (e == hipSuccess) e = sg::t_frag(ww, x, 1, B, l->in_dims, Bp, st);  // X^T, (in, Bp)
+    } else {
+        e = sg::transpose16(wa, dy, 1, B, l->out_dims, Bp, st);               // dY^T, (out, Bp)
+        if (e == hipSuccess) e = sg::t_frag(ww, x, l->P, B, l->cols_r, Bp, st);  // X_r^T stacked, (in, Bp)
+    }
+    if (e != hipSuccess) return hip_fail(e, "weight-gradient operand transform");
+    sg::Problem p{};
+    p.A = wa;
+    p.lda = Bp;
+    p.M = (int)l->out_dims;
+    p.Kseg = (int)Bp;
+    p.nseg = 1;
+    p.dtype = l->dtype;
+    p.W = ww;
+    p.ldw = Bp;
+    p.wfrag = 1;
+    p.wsteps = Bp / 32;
+    p.N = (int)l->in_dims;
+    p.out = dw;
+    p.out_dtype = dw_dtype;
+    if (l->mode == SG_ALL_TO_SHARDED) {
+        p.out_map = sg::OUT_ROWMAJOR;  // (P, out/P, in) is the stacked (out, in)
+        p.ldo = l->in_dims;
+    } else {
+        p.out_map = sg::OUT_SHARDED;  // column n -> rank n / (in/P): (P, out, in/P)
+        p.nloc = l->cols_r;
+    }
+    e = run(p, p.M >= 512 ? K_TILE0 : K_TILE1, st);
+    if (e != hipSuccess) return hip_fail(e, "weight-gradient launch");
+    return SG_OK;
+}
+
 }  // namespace
 
+size_t sg_layer_backward_workspace(const sg_layer* l, int64_t B) {
+    if (!l || B <= 0 || B > INT32_MAX || !dw_mfma_ok(l) || dw_small_ok(l, B)) return 0;
+    return dw_ws_bytes(l, B);
+}
+
 sg_status sg_all_to_sharded_backward(const sg_layer* l, const void* x, const void* dy, int64_t B, void* dx,
-                                     sg_dtype dx_dtype, void* dw, sg_dtype dw_dtype, void* stream) {
+                                     sg_dtype dx_dtype, void* dw, sg_dtype dw_dtype, void* workspace, size_t ws_bytes,
+                                     void* stream) {
     g_err.clear();
     if (const char* why = bwd_check(l, SG_ALL_TO_SHARDED, B, dx_dtype, dw_dtype)) return fail(SG_ERR_INVALID_ARG, "%s", why);
-    if (l->quantized) return fail(SG_ERR_UNSUPPORTED, "the backward is implemented for dense layers only");
+    if (l->quantized || l->mx) return fail(SG_ERR_UNSUPPORTED, "the backward is implemented for dense layers only");
     if (!dx && !dw) return fail(SG_ERR_INVALID_ARG, "neither dx nor dw requested");
     if (B == 0) return SG_OK;
     if (!dy) return fail(SG_ERR_INVALID_ARG, "dy must not be NULL");
     if (dw && !x) return fail(SG_ERR_INVALID_ARG, "dw needs the forward input x");
+    const bool small = dw_small_ok(l, B);
+    const bool ws_ok = !small && workspace && aligned16(workspace) && dw_mfma_ok(l) && ws_bytes >= dw_ws_bytes(l, B);
+    if (dw && workspace && !small && !ws_ok && dw_mfma_ok(l))
+        return fail(SG_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed (16-byte aligned)", ws_bytes,
+                    dw_ws_bytes(l, B));
     hipStream_t st = (hipStream_t)stream;
     if (dx) {
-        // the sum_gradients all_sum: dx = sum_r dY_r W_r, ranks in order
-        sg::BwdDx p{};
-        p.A = dy;
-        p.lda = l->rows_r;
-        p.a_seg = B * l->rows_r;
-        p.W = l->w;
-        p.ldw = l->cols_r;
-        p.w_seg = l->rows_r * l->cols_r;
-        p.wsteps = l->cols_r / 32;
-        p.wfrag = l->wfrag;
-        p.dtype = l->dtype;
-        p.M = (int)B;
-        p.N = (int)l->cols_r;
-        p.K = (int)l->rows_r;
-        p.nseg = l->P;
-        p.reduce = 1;
-        p.stacked = 1;
-        p.out = dx;
-        p.out_dtype = dx_dtype;
-        hipError_t e = sg::launch_bwd_dx(p, st);
-        if (e != hipSuccess) return hip_fail(e, "all_to_sharded backward dx");
+        if (wt_ok(l) && aligned16(dy) && aligned16(dx)) {
+            // the sum_gradients all_sum: dx = sum_r dY_r W_r, a sharded-to-all
+            // product on the transposed shards, ranks summed in order
+            sg_status s2 = ensure_wt(l, st);
+            if (s2 != SG_OK) return s2;
+            sg::Problem p{};
+            p.A = dy;
+            p.lda = l->rows_r;
+            p.a_seg = B * l->rows_r;
+            p.M = (int)B;
+            p.Kseg = (int)l->rows_r;
+            p.nseg = l->P;
+            p.dtype = l->dtype;
+            p.W = l->wt;
+            p.ldw = l->rows_r;
+            p.w_seg = l->cols_r * l->rows_r;
+            p.wfrag = 1;
+            p.wsteps = l->rows_r / 32;
+            p.N = (int)l->cols_r;
+            p.out = dx;
+            p.out_dtype = dx_dtype;
+            p.out_map = sg::OUT_ROWMAJOR;
+            p.ldo = l->cols_r;
+            hipError_t e = run(p, choose_bwd(B, l->cols_r, l->P), st);
+            if (e != hipSuccess) return hip_fail(e, "all_to_sharded backward dx");
+        } else {
+            sg::BwdDx p{};
+            p.A = dy;
+            p.lda = l->rows_r;
+            p.a_seg = B * l->rows_r;
+            p.W = l->w;
+            p.ldw = l->cols_r;
+            p.w_seg = l->rows_r * l->cols_r;
+            p.wsteps = l->cols_r / 32;
+            p.wfrag = l->wfrag;
+            p.dtype = l->dtype;
+            p.M = (int)B;
+            p.N = (int)l->cols_r;
+            p.K = (int)l->rows_r;
+            p.nseg = l->P;
+            p.reduce = 1;
+            p.stacked = 1;
+            p.out = dx;
+            p.out_dtype = dx_dtype;
+            hipError_t e = sg::launch_bwd_dx(p, st);
+            if (e != hipSuccess) return hip_fail(e, "all_to_sharded backward dx");
+        }
     }
     if (dw) {
+        if (small && aligned16(x) && aligned16(dy)) return dw_small(l, x, dy, B, dw, dw_dtype, st);
+        if (ws_ok && aligned16(x) && aligned16(dy) && aligned16(dw)) return dw_mfma(l, x, dy, B, dw, dw_dtype, workspace, st);
         sg::BwdDw q{};
         q.G = dy;
         q.ldg = l->rows_r;
@@ -903,38 +1089,71 @@ sg_status sg_all_to_sharded_backward(const sg_layer* l, const void* x, const voi
 }
 
 sg_status sg_sharded_to_all_backward(const sg_layer* l, const void* x_partial, const void* dy, int64_t B,
-                                     void* dx_partial, sg_dtype dx_dtype, void* dw, sg_dtype dw_dtype, void* stream) {
+                                     void* dx_partial, sg_dtype dx_dtype, void* dw, sg_dtype dw_dtype, void* workspace,
+                                     size_t ws_bytes, void* stream) {
     g_err.clear();
     if (const char* why = bwd_check(l, SG_SHARDED_TO_ALL, B, dx_dtype, dw_dtype)) return fail(SG_ERR_INVALID_ARG, "%s", why);
-    if (l->quantized) return fail(SG_ERR_UNSUPPORTED, "the backward is implemented for dense layers only");
+    if (l->quantized || l->mx) return fail(SG_ERR_UNSUPPORTED, "the backward is implemented for dense layers only");
     if (!dx_partial && !dw) return fail(SG_ERR_INVALID_ARG, "neither dx nor dw requested");
     if (B == 0) return SG_OK;
     if (!dy) return fail(SG_ERR_INVALID_ARG, "dy must not be NULL");
     if (dw && !x_partial) return fail(SG_ERR_INVALID_ARG, "dw needs the forward input x_partial");
+    const bool small = dw_small_ok(l, B);
+    const bool ws_ok = !small && workspace && aligned16(workspace) && dw_mfma_ok(l) && ws_bytes >= dw_ws_bytes(l, B);
+    if (dw && workspace && !small && !ws_ok && dw_mfma_ok(l))
+        return fail(SG_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed (16-byte aligned)", ws_bytes,
+                    dw_ws_bytes(l, B));
     hipStream_t st = (hipStream_t)stream;
     if (dx_partial) {
-        // every rank receives the full dY: dX_r = dY W_r, no reduction
-        sg::BwdDx p{};
-        p.A = dy;
-        p.lda = l->rows_r;
-        p.a_seg = 0;
-        p.W = l->w;
-        p.ldw = l->cols_r;
-        p.w_seg = l->rows_r * l->cols_r;
-        p.wsteps = l->cols_r / 32;
-        p.wfrag = l->wfrag;
-        p.dtype = l->dtype;
-        p.M = (int)B;
-        p.N = (int)l->cols_r;
-        p.K = (int)l->rows_r;
-        p.nseg = l->P;
-        p.reduce = 0;
-        p.out = dx_partial;
-        p.out_dtype = dx_dtype;
-        hipError_t e = sg::launch_bwd_dx(p, st);
-        if (e != hipSuccess) return hip_fail(e, "sharded_to_all backward dx");
+        if (wt_ok(l) && aligned16(dy) && aligned16(dx_partial)) {
+            // every rank receives the full dY: dX_r = dY W_r, an all-to-sharded
+            // product on the stacked W_r^T with a sharded output
+            sg_status s2 = ensure_wt(l, st);
+            if (s2 != SG_OK) return s2;
+            sg::Problem p{};
+            p.A = dy;
+            p.lda = l->out_dims;
+            p.M = (int)B;
+            p.Kseg = (int)l->out_dims;
+            p.nseg = 1;
+            p.dtype = l->dtype;
+            p.W = l->wt;
+            p.ldw = l->out_dims;
+            p.wfrag = 1;
+            p.wsteps = l->out_dims / 32;
+            p.N = (int)l->in_dims;
+            p.out = dx_partial;
+            p.out_dtype = dx_dtype;
+            p.out_map = sg::OUT_SHARDED;
+            p.nloc = l->cols_r;
+            hipError_t e = run(p, choose_bwd(B, l->in_dims, 1), st);
+            if (e != hipSuccess) return hip_fail(e, "sharded_to_all backward dx");
+        } else {
+            sg::BwdDx p{};
+            p.A = dy;
+            p.lda = l->rows_r;
+            p.a_seg = 0;
+            p.W = l->w;
+            p.ldw = l->cols_r;
+            p.w_seg = l->rows_r * l->cols_r;
+            p.wsteps = l->cols_r / 32;
+            p.wfrag = l->wfrag;
+            p.dtype = l->dtype;
+            p.M = (int)B;
+            p.N = (int)l->cols_r;
+            p.K = (int)l->rows_r;
+            p.nseg = l->P;
+            p.reduce = 0;
+            p.out = dx_partial;
+            p.out_dtype = dx_dtype;
+            hipError_t e = sg::launch_bwd_dx(p, st);
+            if (e != hipSuccess) return hip_fail(e, "sharded_to_all backward dx");
+        }
     }
     if (dw) {
+        if (small && aligned16(x_partial) && aligned16(dy)) return dw_small(l, x_partial, dy, B, dw, dw_dtype, st);
+        if (ws_ok && aligned16(x_partial) && aligned16(dy) && aligned16(dw))
+            return dw_mfma(l, x_partial, dy, B, dw, dw_dtype, workspace, st);
         sg::BwdDw q{};
         q.G = dy;
         q.ldg = l->rows_r;
@@ -955,11 +1174,28 @@ sg_status sg_sharded_to_all_backward(const sg_layer* l, const void* x_partial, c
     return SG_OK;
 }
 
+// SUMMA backward workspace: X^T (K, M) row-major, then dY's q step blocks
+// transposed, dY_t^T (N, M/q), fragment-major
+static bool summa_bwd_mfma_ok(sg_dtype dtype, int64_t M, int64_t K, int64_t N, int q) {
+    return (dtype == SG_BF16 || dtype == SG_F16) && q >= 1 && M % q == 0 && (M / q) % 32 == 0 && N % 16 == 0 &&
+           K % 8 == 0;
+}
+static size_t summa_bwd_ws(int64_t M, int64_t K, int64_t N) {
+    return align256((size_t)(K * M) * 2) + align256((size_t)(N * M) * 2);
+}
+
+size_t sg_summa_backward_workspace(sg_dtype dtype, int64_t M, int64_t K, int64_t N, int q) {
+    if (M <= 0 || K <= 0 || N <= 0 || M > INT32_MAX || K > INT32_MAX || N > INT32_MAX) return 0;
+    return summa_bwd_mfma_ok(dtype, M, K, N, q) ? summa_bwd_ws(M, K, N) : 0;
+}
+
 // SUMMA backward ([SUMMA] Matmul_ABT_2D / Matmul_ATB_2D): dX = dY A^T with the
 // inner dimension N cut into the q step blocks (the K segments of the matrix-
-// core kernels, summed in step order), dA = X^T dY (the weight-gradient kernel).
+// core kernels, summed in step order); dA = X^T dY with the tokens M cut into
+// the q step blocks, on the same kernels over the workspace's transposed
+// copies (else the vector-unit weight-gradient kernel).
 sg_status sg_summa_backward(const void* X, const void* A, const void* dY, sg_dtype dtype, int64_t M, int64_t K,
-                            int64_t N, int q, float* dX, float* dA, void* stream) {
+                            int64_t N, int q, float* dX, float* dA, void* workspace, size_t ws_bytes, void* stream) {
     g_err.clear();
     if (!dtype_ok(dtype)) return fail(SG_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
     if (M < 0 || K < 0 || N < 0 || M > INT32_MAX || K > INT32_MAX || N > INT32_MAX)
@@ -969,6 +1205,10 @@ sg_status sg_summa_backward(const void* X, const void* A, const void* dY, sg_dty
         return fail(SG_ERR_NOT_DIVISIBLE, "M, K, N (%lld, %lld, %lld) must be divisible by q = %d",
                     (long long)M, (long long)K, (long long)N, q);
     if (!dX && !dA) return fail(SG_ERR_INVALID_ARG, "neither dX nor dA requested");
+    const bool mm = summa_bwd_mfma_ok(dtype, M, K, N, q);
+    if (workspace && mm && ws_bytes < summa_bwd_ws(M, K, N))
+        return fail(SG_ERR_WORKSPACE, "SUMMA backward workspace of %zu bytes, %zu needed", ws_bytes,
+                    summa_bwd_ws(M, K, N));
     if (M == 0 || K == 0 || N == 0) return SG_OK;
     if (!dY || (dX && !A) || (dA && !X)) return fail(SG_ERR_INVALID_ARG, "dY, and A for dX / X for dA, must not be NULL");
     hipStream_t hs = (hipStream_t)stream;
@@ -996,6 +1236,35 @@ sg_status sg_summa_backward(const void* X, const void* A, const void* dY, sg_dty
         if (e != hipSuccess) return hip_fail(e, "summa backward dX");
     }
     if (dA) {
+        if (mm && workspace && aligned16(workspace) && aligned16(X) && aligned16(dY) && aligned16(dA)) {
+            const int64_t bm = M / q;
+            void* xt = workspace;
+            void* gt = (char*)workspace + align256((size_t)(K * M) * 2);
+            hipError_t e = sg::transpose16(xt, X, 1, M, K, M, hs);     // X^T, (K, M)
+            if (e == hipSuccess) e = sg::t_frag(gt, dY, q, bm, N, bm, hs);  // dY_t^T, q x (N, M/q)
+            if (e != hipSuccess) return hip_fail(e, "summa backward operand transform");
+            sg::Problem p{};
+            p.A = xt;
+            p.lda = M;
+            p.a_seg = bm;  // step t: columns [t bm, (t+1) bm) of X^T
+            p.M = (int)K;
+            p.Kseg = (int)bm;
+            p.nseg = q;
+            p.dtype = dtype;
+            p.W = gt;
+            p.ldw = bm;
+            p.w_seg = N * bm;
+            p.wfrag = 1;
+            p.wsteps = bm / 32;
+            p.N = (int)N;
+            p.out = dA;
+            p.out_dtype = SG_F32;
+            p.out_map = sg::OUT_ROWMAJOR;
+            p.ldo = N;
+            e = run(p, K >= 512 ? K_TILE0 : K_TILE1, hs);
+            if (e != hipSuccess) return hip_fail(e, "summa backward dA");
+            return SG_OK;
+        }
         sg::BwdDw w{};
         w.G = X;  // dA[k][n] = sum_m X[m][k] dY[m][n]
         w.ldg = K;

@@ -156,6 +156,129 @@ __global__ __launch_bounds__(256) void bwd_dw4_kernel(BwdDw p) {
     for (int e = 0; e < 4; ++e) store_from_f32(p.out, p.out_dtype, oi + e, acc[e]);
 }
 
+// Weight gradient with few tokens on the matrix cores, reading the caller's
+// row-major upstream gradient and layer input directly:
+//     out[o][i] = sum_b G(b, o) X(b, i),
+// G(b, o) = G[(o / gl) g_seg + b ldg + o % gl] and X(b, i) likewise (the rank
+// blocks of a sharded operand), out (O, I) row-major or, with nloc > 0, the
+// sharded (I / nloc, O, nloc).  A workgroup (4 waves) owns 128 o x 128 i: it
+// stages both operands' 128 x Bp slices in LDS transposed (token-contiguous,
+// tokens past B zero; 16-byte global reads of 8 consecutive o or i), then each
+// wave runs v_mfma_f32_32x32x16 on 64 x 64 outputs with the rows o as the row
+// operand and the inputs i as the column operand.  Each accumulator register
+// then holds 32 consecutive i of one row across lanes 0-31 (and of the row 4
+// further down across lanes 32-63), so every store writes two contiguous
+// 128-byte row pieces -- the kernel is bound by these fp32 writes.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+template <bool F16>
+__device__ __forceinline__ f32x16_t mfma32x16(u32x4_t a, u32x4_t b, f32x16_t c) {
+    if constexpr (F16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                      0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                       c, 0, 0, 0);
+}
+
+// stage rows [r0, r0 + 128) of the transposed operand T(row, b) = S(b, row)
+// into lds[row - r0][b], b < Bp (zero past B and past rows)
+__device__ __forceinline__ void stage_t(uint16_t* lds, int ldl, const uint16_t* S, int64_t gl, int64_t seg,
+                                        int64_t ld, int r0, int rows, int B, int Bp) {
+    const int chunks = 16 * Bp;  // (b, 8-row chunk) pairs
+    for (int c = threadIdx.x; c < chunks; c += blockDim.x) {
+        const int b = c >> 4, rr = (c & 15) * 8;
+        const int row = r0 + rr;
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (b < B && row < rows) {
+            const int64_t g = row / gl;
+            v = *(const u32x4_t*)(S + g * seg + (int64_t)b * ld + (row - g * gl));
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            lds[(rr + 2 * e) * ldl + b] = (uint16_t)(v[e] & 0xFFFFu);
+            lds[(rr + 2 * e + 1) * ldl + b] = (uint16_t)(v[e] >> 16);
+        }
+    }
+}
+
+template <bool F16>
+__global__ __launch_bounds__(256) void dw_small_kernel(BwdDwSmall p) {
+    extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+    const int ldl = p.Bp + 8;  // LDS row: Bp tokens + 16 bytes of padding
+    uint16_t* sA = smem;
+    uint16_t* sB = smem + 128 * ldl;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int ob = blockIdx.y * 128, ib = blockIdx.x * 128;
+    stage_t(sA, ldl, (const uint16_t*)p.G, p.gl, p.g_seg, p.ldg, ob, p.O, p.B, p.Bp);
+    stage_t(sB, ldl, (const uint16_t*)p.X, p.xl, p.x_seg, p.ldx, ib, p.I, p.B, p.Bp);
+    __syncthreads();
+    const int wo = (wave >> 1) * 64, wi = (wave & 1) * 64;
+    const int r = lane & 31, kh = (lane >> 5) * 8;
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[x][y][e] = 0.f;
+    for (int k = 0; k < p.Bp; k += 16) {
+        u32x4_t a[2], b[2];
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+            a[x] = *(const u32x4_t*)(sA + (wo + x * 32 + r) * ldl + k + kh);
+            b[x] = *(const u32x4_t*)(sB + (wi + x * 32 + r) * ldl + k + kh);
+        }
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int y = 0; y < 2; ++y) acc[x][y] = mfma32x16<F16>(a[x], b[y], acc[x][y]);
+    }
+    // lane l of a 32 x 32 block: column l & 31, rows 8 j + 4 (l >> 5) + e
+    static_for<0, 2>([&](auto xc) {
+        constexpr int x = decltype(xc)::value;
+        static_for<0, 2>([&](auto yc) {
+            constexpr int y = decltype(yc)::value;
+            const int i = ib + wi + y * 32 + (lane & 31);
+            if (i >= p.I) return;
+            int64_t col = i, base = 0, ld = p.I;
+            if (p.nloc > 0) {
+                const int64_t rk = i / p.nloc;
+                col = i - rk * p.nloc;
+                base = rk * (int64_t)p.O * p.nloc;
+                ld = p.nloc;
+            }
+            static_for<0, 16>([&](auto ec) {
+                constexpr int e = decltype(ec)::value;
+                const int o = ob + wo + x * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                if (o >= p.O) return;
+                const int64_t at = base + (int64_t)o * ld + col;
+                // written once, never read back here: streaming stores (measured ~10%
+                // faster on the decode-MLP gradients than cached ones)
+                if (p.out_dtype == SG_F32) __builtin_nontemporal_store(acc[x][y][e], (float*)p.out + at);
+                else store_from_f32(p.out, p.out_dtype, at, acc[x][y][e]);
+            });
+        });
+    });
+}
+
+size_t dw_small_lds(int Bp) { return (size_t)2 * 128 * (Bp + 8) * sizeof(uint16_t); }
+
+hipError_t launch_dw_small(const BwdDwSmall& p, hipStream_t s) {
+    if (p.O == 0 || p.I == 0 || p.B == 0) return hipSuccess;
+    if (p.Bp % 16 || p.Bp < p.B || p.Bp > kDwSmallMaxTokens || (p.dtype != SG_BF16 && p.dtype != SG_F16) || p.gl % 8 ||
+        p.xl % 8 || p.ldg % 8 || p.ldx % 8 || p.g_seg % 8 || p.x_seg % 8 || p.O % 8 || p.I % 8)
+        return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((p.I + 127) / 128), (unsigned)((p.O + 127) / 128)), block(256);
+    const size_t lds = dw_small_lds(p.Bp);
+    if (p.dtype == SG_F16) launch(dw_small_kernel<true>, grid, block, lds, s, p);
+    else launch(dw_small_kernel<false>, grid, block, lds, s, p);
+    return hipGetLastError();
+}
+
 hipError_t launch_bwd_dx(const BwdDx& p, hipStream_t s) {
     const int64_t total = (p.reduce ? 1 : p.nseg) * (int64_t)p.M * p.N;
     if (total == 0) return hipSuccess;

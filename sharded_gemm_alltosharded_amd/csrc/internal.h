@@ -154,6 +154,12 @@ hipError_t launch_q4s(const Problem& p, hipStream_t s);  // 16-row blocks, M <= 
 hipError_t frag_transform(void* dst, const void* src, int P, int64_t rows, int64_t K, int forward, hipStream_t s);
 // SUMMA's A (K, N) -> q fragment-major blocks of A_t^T (N, K / q); N % 16 == 0, (K / q) % 32 == 0
 hipError_t nn_to_frag(void* dst, const void* A, int64_t K, int64_t N, int q, hipStream_t s);
+// P row-major (R, C) 16-bit matrices -> P row-major (C, Rp) transposes, columns
+// R .. Rp-1 zero; C % 8 == 0, Rp % 8 == 0
+hipError_t transpose16(void* dst, const void* src, int P, int64_t R, int64_t C, int64_t Rp, hipStream_t s);
+// P row-major (R, C) 16-bit matrices -> their transposes stacked as one
+// fragment-major (P C, Rp) matrix, k >= R zero; C % 16 == 0, Rp % 32 == 0
+hipError_t t_frag(void* dst, const void* src, int P, int64_t R, int64_t C, int64_t Rp, hipStream_t s);
 // MX FP8: P stacked (rows, K) code bytes and (rows, K/32) scales <-> fragment-major
 // (either pair of pointers may be null); rows % 16 == 0, K % 128 == 0
 hipError_t mx_transform(uint8_t* dst_codes, const uint8_t* src_codes, uint8_t* dst_scales,
@@ -214,6 +220,22 @@ struct BwdDw {
     void* out;
     int out_dtype;
 };
+// Weight gradient with few tokens (backward.hip): out[o][i] = sum_b G(b, o) X(b, i)
+// with G(b, o) = G[(o / gl) g_seg + b ldg + o % gl], X likewise; out (O, I)
+// row-major, or (I / nloc, O, nloc) when nloc > 0.  Bp = B rounded up to 16,
+// at most kDwSmallMaxTokens; gl, xl, ldg, ldx, g_seg, x_seg multiples of 8.
+constexpr int kDwSmallMaxTokens = 128;
+struct BwdDwSmall {
+    const void* G;
+    int64_t gl, g_seg, ldg;
+    const void* X;
+    int64_t xl, x_seg, ldx;
+    int dtype, O, I, B, Bp;
+    void* out;
+    int out_dtype;
+    int64_t nloc;
+};
+hipError_t launch_dw_small(const BwdDwSmall& p, hipStream_t s);
 hipError_t launch_bwd_dx(const BwdDx& p, hipStream_t s);
 hipError_t launch_bwd_dw(const BwdDw& p, hipStream_t s);
 constexpr size_t kMaxStreamLds = 64 * 1024;

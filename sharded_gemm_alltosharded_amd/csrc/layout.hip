@@ -110,6 +110,85 @@ hipError_t nn_to_frag(void* dst, const void* A, int64_t K, int64_t N, int q, hip
     return hipGetLastError();
 }
 
+// P row-major (R, C) 16-bit matrices -> P row-major (C, Rp) transposes, the
+// columns R .. Rp-1 of each zero-filled (a padded contraction dimension adds
+// nothing).  One workgroup per 64 x 64 tile: 16-byte row reads into LDS, then
+// each thread gathers 8 values of one output row and writes them as 16
+// contiguous bytes.  Needs C % 8 == 0 and Rp % 8 == 0.
+__global__ __launch_bounds__(256) void transpose16_kernel(const uint16_t* src, uint16_t* dst, int64_t R, int64_t C,
+                                                          int64_t Rp) {
+    __shared__ uint16_t tile[64][64 + 2];
+    const int tid = threadIdx.x;
+    const int64_t c0 = (int64_t)blockIdx.x * 64, r0 = (int64_t)blockIdx.y * 64;
+    const uint16_t* S = src + (int64_t)blockIdx.z * R * C;
+    uint16_t* D = dst + (int64_t)blockIdx.z * C * Rp;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int r = (tid >> 3) + 32 * i, c = (tid & 7) * 8;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (r0 + r < R && c0 + c < C) v = *(const u32x4*)(S + (r0 + r) * C + c0 + c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            tile[r][c + 2 * e] = (uint16_t)(v[e] & 0xFFFFu);
+            tile[r][c + 2 * e + 1] = (uint16_t)(v[e] >> 16);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int c = (tid >> 3) + 32 * i, r = (tid & 7) * 8;
+        if (c0 + c >= C || r0 + r >= Rp) continue;
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = tile[r + 2 * e][c] | ((uint32_t)tile[r + 2 * e + 1][c] << 16);
+        *(u32x4*)(D + (c0 + c) * Rp + r0 + r) = u32x4{w[0], w[1], w[2], w[3]};
+    }
+}
+
+hipError_t transpose16(void* dst, const void* src, int P, int64_t R, int64_t C, int64_t Rp, hipStream_t s) {
+    if (P == 0 || C == 0 || Rp == 0) return hipSuccess;
+    if (C % 8 || Rp % 8 || Rp < R) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(transpose16_kernel, dim3((unsigned)((C + 63) / 64), (unsigned)((Rp + 63) / 64), (unsigned)P),
+                       dim3(256), 0, s, (const uint16_t*)src, (uint16_t*)dst, R, C, Rp);
+    return hipGetLastError();
+}
+
+// P row-major (R, C) 16-bit matrices -> one fragment-major matrix of P C rows
+// and Rp k: element (p C + c, r) = src[p][r][c], zero for r >= R (the
+// transposes stacked, as the MFMA kernels read a weight operand).  Same tile
+// scheme as nn_frag_kernel.  Needs C % 16 == 0 and Rp % 32 == 0.
+__global__ __launch_bounds__(256) void t_frag_kernel(const uint16_t* src, uint16_t* dst, int64_t R, int64_t C,
+                                                     int64_t Rp) {
+    __shared__ __attribute__((aligned(16))) uint16_t tile[32][64 + 8];
+    const int tid = threadIdx.x;
+    const int64_t n0 = (int64_t)blockIdx.x * 64, k0 = (int64_t)blockIdx.y * 32;
+    const int64_t mat = blockIdx.z;
+    const uint16_t* S = src + mat * R * C;
+    {
+        const int r = tid >> 3, c = tid & 7;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (k0 + r < R && n0 + c * 8 < C) v = *(const u32x4*)(S + (k0 + r) * C + n0 + c * 8);
+        *(u32x4*)&tile[r][c * 8] = v;
+    }
+    __syncthreads();
+    const int b = tid >> 6, l = tid & 63;
+    if (n0 + b * 16 >= C) return;
+    const int n = b * 16 + (l & 15), kq = 8 * (l >> 4);
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = tile[kq + 2 * i][n] | ((uint32_t)tile[kq + 2 * i + 1][n] << 16);
+    const int64_t row = mat * C + n0 + b * 16;  // first row of this 16-row block in the stack
+    *(u32x4*)(dst + frag_offset(row + (l & 15), k0 + kq, Rp / 32)) = u32x4{w[0], w[1], w[2], w[3]};
+}
+
+hipError_t t_frag(void* dst, const void* src, int P, int64_t R, int64_t C, int64_t Rp, hipStream_t s) {
+    if (P == 0 || C == 0 || Rp == 0) return hipSuccess;
+    if (C % 16 || Rp % 32 || Rp < R) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(t_frag_kernel, dim3((unsigned)((C + 63) / 64), (unsigned)(Rp / 32), (unsigned)P), dim3(256), 0,
+                       s, (const uint16_t*)src, (uint16_t*)dst, R, C, Rp);
+    return hipGetLastError();
+}
+
 // MX FP8 layers: P stacked (rows, K) byte matrices of E4M3 codes <-> the
 // fragment-major byte layout (mx_code_offset), and their (rows, K/32) E8M0
 // scales <-> mx_scale_offset.  One thread per 8 codes / per scale.

@@ -14,6 +14,7 @@ import synth
 from gpu_util import assert_close, bits, dev, to_dev, to_np
 
 pytestmark = pytest.mark.gpu
+DT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
 
 
 @pytest.fixture(autouse=True, scope="module")
@@ -693,18 +694,23 @@ def test_mx_rejections():
 BWD_CASES = [("bf16", 8, 256, 512, 1, 4), ("bf16", 5, 96, 72, 1, 2), ("f16", 3, 128, 256, 2, 2),
              ("f32", 4, 64, 96, 1, 3), ("bf16", 1, 512, 128, 1, 1),
              ("bf16", 4, 64, 48, 1, 2),  # 24 rows per rank: the fragment-major stack crosses rank boundaries
-             ("f16", 5, 128, 256, 1, 4)]  # fp16 with one segment: the sharded-to-all backward in fp16 too
+             ("f16", 5, 128, 256, 1, 4),  # fp16 with one segment: the sharded-to-all backward in fp16 too
+             ("bf16", 40, 256, 512, 1, 4),  # input gradients on the 128 x 128 tile kernel, 64 padded tokens
+             ("bf16", 520, 256, 512, 2, 2)]  # the 256 x 256 tile kernels, 544 padded tokens
+# ws: "auto" = weight gradients on the matrix cores over the transposed
+# operands in a workspace; None = the vector-unit weight-gradient kernel
 
 
+@pytest.mark.parametrize("ws", ["auto", None])
 @pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "-".join(map(str, c)))
-def test_all_to_sharded_backward(case):
+def test_all_to_sharded_backward(case, ws):
     dtype, B, inn, out, S, P = case
-    _print_case(dtype=dtype, B=B, inn=inn, out=out, S=S, P=P)
+    _print_case(dtype=dtype, B=B, inn=inn, out=out, S=S, P=P, ws=ws)
     W = synth.uniform(90, (out, inn), inn ** -0.5, dtype)
     X = synth.normal(91, (B, inn), 1.0, dtype)
     G = synth.normal(92, (P, B, out // P), 1.0, dtype)
     layer = sg.shard_linear(to_dev(W, dtype), "all-to-sharded", segments=S, P=P)
-    dx, dw = sg.all_to_sharded_backward(layer, to_dev(X, dtype), to_dev(G, dtype), dx_dtype=torch.float32)
+    dx, dw = sg.all_to_sharded_backward(layer, to_dev(X, dtype), to_dev(G, dtype), dx_dtype=torch.float32, ws=ws)
     rdx, rdw = oracle.col_bwd(X, W, G, P=P, S=S, dtype=dtype)
     assert_close(dx, rdx, "f32", "dx")
     assert_close(dw, rdw, "f32", "dw")
@@ -715,19 +721,24 @@ def test_all_to_sharded_backward(case):
         assert_close(dx16, rdx, dtype, "dx 16-bit")
 
 
+@pytest.mark.parametrize("ws", ["auto", None])
 @pytest.mark.parametrize("case", [c for c in BWD_CASES if c[4] == 1], ids=lambda c: "-".join(map(str, c)))
-def test_sharded_to_all_backward(case):
+def test_sharded_to_all_backward(case, ws):
     dtype, B, inn, out, S, P = case  # one segment: the down-projection layers these cases stand for
     inn, out = out, inn  # a down-projection shape: in = the wide side
-    _print_case(dtype=dtype, B=B, inn=inn, out=out, P=P)
+    _print_case(dtype=dtype, B=B, inn=inn, out=out, P=P, ws=ws)
     W = synth.uniform(93, (out, inn), inn ** -0.5, dtype)
     Xs = synth.normal(94, (P, B, inn // P), 1.0, dtype)
     G = synth.normal(95, (B, out), 1.0, dtype)
     layer = sg.shard_linear(to_dev(W, dtype), "sharded-to-all", P=P)
-    dxs, dw = sg.sharded_to_all_backward(layer, to_dev(Xs, dtype), to_dev(G, dtype), dx_dtype=torch.float32)
+    dxs, dw = sg.sharded_to_all_backward(layer, to_dev(Xs, dtype), to_dev(G, dtype), dx_dtype=torch.float32, ws=ws)
     rdxs, rdw = oracle.row_bwd(Xs, W, G, P=P, dtype=dtype)
     assert_close(dxs, rdxs, "f32", "dx_partial")
     assert_close(dw, rdw, "f32", "dw")
+    if dtype != "f32":
+        dxs16, dw16 = sg.sharded_to_all_backward(layer, to_dev(Xs, dtype), to_dev(G, dtype), dw_dtype=DT[dtype], ws=ws)
+        assert_close(dxs16, rdxs, dtype, "dx_partial 16-bit")
+        assert_close(dw16, rdw, dtype, "dw 16-bit")
 
 
 def test_backward_rejections():
@@ -741,21 +752,30 @@ def test_backward_rejections():
         sg.all_to_sharded_backward(col, None, dy)  # dw without x
     with pytest.raises(sg.ShardGemmError):
         sg.sharded_to_all_backward(col, None, torch.zeros((4, 64), dtype=torch.bfloat16, device=dev()), need_dw=False)
+    assert sg.lib().sg_layer_backward_workspace(col.handle, 4) == 0  # few tokens: dw reads dy and x in place
+    x = torch.zeros((200, 64), dtype=torch.bfloat16, device=dev())
+    dy2 = torch.zeros((2, 200, 32), dtype=torch.bfloat16, device=dev())
+    need = sg.lib().sg_layer_backward_workspace(col.handle, 200)
+    assert need > 0
+    with pytest.raises(sg.ShardGemmError, match="workspace"):
+        sg.all_to_sharded_backward(col, x, dy2, ws=torch.zeros(need - 256, dtype=torch.uint8, device=dev()))
 
 
 SUMMA_BWD_CASES = [("bf16", 256, 128, 512, 4), ("bf16", 64, 96, 48, 2), ("f16", 512, 256, 256, 1),
-                   ("f32", 24, 12, 18, 3), ("bf16", 48, 66, 30, 3)]
+                   ("f32", 24, 12, 18, 3), ("bf16", 48, 66, 30, 3),
+                   ("bf16", 128, 768, 272, 2)]  # dA on the 256 x 256 tile kernel, a ragged N tile
 
 
+@pytest.mark.parametrize("ws", ["auto", None])
 @pytest.mark.parametrize("case", SUMMA_BWD_CASES, ids=lambda c: "-".join(map(str, c)))
-def test_summa_backward(case):
+def test_summa_backward(case, ws):
     """Matmul_ABT_2D / Matmul_ATB_2D: dX = dY A^T and dA = X^T dY in q steps."""
     dtype, M, K, N, q = case
-    _print_case(dtype=dtype, M=M, K=K, N=N, q=q)
+    _print_case(dtype=dtype, M=M, K=K, N=N, q=q, ws=ws)
     X = synth.normal(110, (M, K), K ** -0.25, dtype)
     A = synth.normal(111, (K, N), K ** -0.25, dtype)
     G = synth.normal(112, (M, N), 1.0, dtype)
-    dX, dA = sg.summa_backward(to_dev(X, dtype), to_dev(A, dtype), to_dev(G, dtype), q)
+    dX, dA = sg.summa_backward(to_dev(X, dtype), to_dev(A, dtype), to_dev(G, dtype), q, ws=ws)
     assert_close(dX, oracle.summa_abt(G, A, q, dtype=dtype), "f32", "dX")
     assert_close(dA, oracle.summa_atb(X, G, q, dtype=dtype), "f32", "dA")
     with pytest.raises(sg.ShardGemmError):
