@@ -87,6 +87,9 @@ sg_status sg_shard_linear(const void* weight, sg_dtype dtype, int64_t out_dims, 
  *   act      activation dtype of the layer (SG_BF16 or SG_F16).
  *   bias     (out_dims) of `act`, or NULL (the layer bias, as for sg_shard_linear).
  * Only group_size 64 and bits 4 are implemented (else SG_ERR_UNSUPPORTED).
+ * Up to 32 tokens run on the streaming kernels, more on a matrix-core tile
+ * kernel (both when out_dims % 32 == 0 and the rank's in_dims % 256 == 0, the
+ * fragment-major code layout); other shapes take the generic kernel.
  * Sharded-to-all needs (in_dims/segments/P) % group_size == 0 so that no
  * quantization group straddles two ranks (SG_ERR_NOT_DIVISIBLE). */
 sg_status sg_shard_quantized_linear(const uint32_t* wq, const uint16_t* scales,
@@ -106,7 +109,8 @@ sg_status sg_shard_quantized_linear(const uint32_t* wq, const uint16_t* scales,
  * block would straddle two ranks ((in_dims/segments/P) % 32).  Up to 32 tokens
  * run on the streaming kernel (codes converted to bf16 in registers) when the
  * shards tile into 16-row blocks and in/P (sharded-to-all) or in is a multiple
- * of 128; other calls take the generic kernel.  sg_layer_copy_shard returns
+ * of 128; more tokens on the matrix-core tile kernels (codes converted to bf16
+ * as they are staged); other calls take the generic kernel.  sg_layer_copy_shard returns
  * codes (what 0) and scales (what 2); sg_layer_info reports quantized = 2. */
 sg_status sg_shard_mxfp8_linear(const uint8_t* codes, const uint8_t* scales, int64_t out_dims,
                                 int64_t in_dims, sg_dtype act, const void* bias, int mode, int segments,
@@ -133,9 +137,11 @@ sg_status sg_all_to_sharded(const sg_layer* layer, const void* x, int64_t B, voi
  *              SG_IN_SHARDED: x (P, B, in_dims/P), slice r holding columns
  *              [r in/P, (r+1) in/P) of the activation; every rank all-gathers it
  *              before its matmul (Case 2), which here is the K loop walking the P
- *              slices in order.  Dense layers only (SG_ERR_UNSUPPORTED for 4-bit
- *              layers, and for fragment-stored weights when (in_dims/P) % 32 != 0);
- *              SG_ERR_NOT_DIVISIBLE when P does not divide in_dims.
+ *              slices in order.  Dense and 4-bit layers: SG_ERR_UNSUPPORTED for
+ *              MX FP8 layers, for fragment-stored dense weights when
+ *              (in_dims/P) % 32 != 0, and for 4-bit layers when (in_dims/P) is
+ *              not a multiple of 256 (fragment-stored codes) or 64 (row-major
+ *              codes); SG_ERR_NOT_DIVISIBLE when P does not divide in_dims.
  *   out_layout SG_OUT_SHARDED: y (P, B, n_out/P) (gather = 0 of sg_all_to_sharded);
  *              SG_OUT_FULL: y (B, n_out), the rank-order all-gather (gather = 1).
  * Everything else as sg_all_to_sharded. */

@@ -9,7 +9,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libshardgemm.so")
-SOURCES = ["api.hip", "generic.hip", "tile.hip", "skinny.hip", "q4.hip", "q4s.hip", "layout.hip", "tile_dma.hip", "backward.hip"]
+SOURCES = ["api.hip", "generic.hip", "tile.hip", "skinny.hip", "q4.hip", "q4s.hip", "layout.hip", "tile_dma.hip", "backward.hip", "q4tile.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

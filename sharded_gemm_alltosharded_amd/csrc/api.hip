@@ -140,7 +140,7 @@ sg_status common_checks(int mode, int segments, int P, int64_t out_dims, int64_t
 // ---------------------------------------------------------------------------
 // kernel choice
 // ---------------------------------------------------------------------------
-enum Kind { K_GENERIC, K_TILE0, K_TILE1, K_SKINNY, K_Q4 };
+enum Kind { K_GENERIC, K_TILE0, K_TILE1, K_SKINNY, K_Q4, K_Q4TILE };
 
 int num_cus() {
     static int cus = -1;
@@ -172,17 +172,23 @@ bool q4_fits(const sg_layer* l, int64_t B, int swiglu) {
     return sg::q4_shape((int)B, n, nseg, swiglu).lds <= sg::kMaxStreamLds;
 }
 
-// MX FP8 layers: the streaming kernel when the codes are fragment-major,
-// else the generic kernel (the tile kernels take 16-bit weights only)
+// MX FP8 layers: the streaming kernel for few tokens when the codes are
+// fragment-major; more tokens on the tile kernels (codes converted to bf16 in
+// the loader), inputs with 16-byte rows; else the generic kernel
 Kind choose_mx(const sg_layer* l, int64_t B, const void* x, int swiglu, int nseg) {
     const bool ok = B <= 32 && l->wfrag && (l->cols_r / 32) % 4 == 0 && aligned16(x) && aligned16(l->w);
-    return ok && skinny_fits(l, B, swiglu, nseg) ? K_SKINNY : K_GENERIC;
+    if (ok && skinny_fits(l, B, swiglu, nseg)) return K_SKINNY;
+    if (B > 32 && aligned16(x) && l->cols_r % 8 == 0) return B >= 512 ? K_TILE0 : K_TILE1;
+    return K_GENERIC;
 }
 
 Kind choose(const sg_layer* l, int64_t B, const void* x, int swiglu = 0, int nseg = 1) {
     if (l->mx) return choose_mx(l, B, x, swiglu, nseg);
-    if (l->quantized)
-        return (B <= 32 && l->qfrag && aligned16(x) && q4_fits(l, B, swiglu)) ? K_Q4 : K_GENERIC;
+    if (l->quantized) {
+        if (!l->qfrag || !aligned16(x)) return K_GENERIC;
+        // few tokens: the streaming kernels; more: the 4-bit tile kernel
+        return (B <= 32 && nseg == 1 && q4_fits(l, B, swiglu)) ? K_Q4 : K_Q4TILE;
+    }
     if (!mfma_ok(l, x)) return K_GENERIC;
     if (B <= 32 && skinny_fits(l, B, swiglu, nseg)) return K_SKINNY;
     return B >= 512 ? K_TILE0 : K_TILE1;
@@ -215,7 +221,7 @@ sg::SplitLayout split_layout(const sg_layer* l, Kind k, int64_t B) {
 // is checked separately; misaligned pointers fall back to the generic path)
 Kind choose_row(const sg_layer* l, int64_t B) {
     if (l->mx) return choose_mx(l, B, l->w, 0, l->P);
-    if (l->quantized) return B <= 32 && l->qfrag && q4_fits(l, B, 0) ? K_Q4 : K_GENERIC;
+    if (l->quantized) return !l->qfrag ? K_GENERIC : (B <= 32 && q4_fits(l, B, 0) ? K_Q4 : K_Q4TILE);
     if (l->dtype == SG_F32 || l->cols_r % 8) return K_GENERIC;
     if (B <= 32 && skinny_fits(l, B, 0, l->P)) return K_SKINNY;
     return B >= 512 ? K_TILE0 : K_TILE1;
@@ -225,11 +231,13 @@ hipError_t run(const sg::Problem& p, Kind k, hipStream_t st) {
     // fragment-major activations (the fused MLP's h) exist for the streaming kernels only
     if ((p.xfrag || p.out_map == sg::OUT_FRAG || p.out_map == sg::OUT_FRAG_Q4) && k != K_SKINNY && k != K_Q4)
         return hipErrorInvalidValue;
+    if (k == K_Q4TILE && !sg::q4_tile_fits(p)) k = K_GENERIC;
     switch (k) {
     case K_TILE0: return sg::launch_tile(p, st, 0);
     case K_TILE1: return sg::launch_tile(p, st, 1);
     case K_SKINNY: return sg::launch_skinny(p, st);
     case K_Q4: return sg::launch_q4(p, st);
+    case K_Q4TILE: return sg::launch_q4_tile(p, st);
     default: return sg::launch_generic(p, st);
     }
 }
@@ -524,8 +532,12 @@ sg_status sg_all_to_sharded_ex(const sg_layer* l, const void* x, int in_layout, 
         if (l->in_dims % l->P)
             return fail(SG_ERR_NOT_DIVISIBLE, "Cannot shard the input of size %lld across %d devices.",
                         (long long)l->in_dims, l->P);
-        if (l->quantized || l->mx)
-            return fail(SG_ERR_UNSUPPORTED, "a sharded input is implemented for dense layers only");
+        if (l->mx) return fail(SG_ERR_UNSUPPORTED, "a sharded input is implemented for dense and 4-bit layers");
+        // 4-bit: no quantization group (in the stored layout, no run of four)
+        // may straddle two input shards
+        if (l->quantized && (l->in_dims / l->P) % (l->qfrag ? 256 : 64))
+            return fail(SG_ERR_UNSUPPORTED, "a sharded input on a 4-bit layer needs in_dims / P to be a multiple of %d",
+                        l->qfrag ? 256 : 64);
         if (l->wfrag && (l->in_dims / l->P) % 32)
             return fail(SG_ERR_UNSUPPORTED, "a sharded input needs in_dims / P to be a multiple of 32 (got %lld)",
                         (long long)(l->in_dims / l->P));
@@ -546,6 +558,10 @@ sg_status sg_all_to_sharded_ex(const sg_layer* l, const void* x, int in_layout, 
         p.Kseg = (int)kr;
         p.nseg = l->P;
         p.w_seg = l->wfrag ? kr * 16 : kr;  // next k range of every weight row
+        if (l->quantized) {  // shard s starts kr / 64 groups further along each row
+            p.q_seg = l->qfrag ? 4 * kr : kr / 8;
+            p.g_seg = l->qfrag ? kr / 2 : kr / 64;
+        }
     } else {
         p.lda = l->in_dims;
         p.Kseg = (int)l->cols_r;

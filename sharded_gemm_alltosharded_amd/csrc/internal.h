@@ -150,6 +150,8 @@ hipError_t launch_tile(const Problem& p, hipStream_t s, int variant);
 hipError_t launch_skinny(const Problem& p, hipStream_t s);
 hipError_t launch_q4(const Problem& p, hipStream_t s);
 hipError_t launch_q4s(const Problem& p, hipStream_t s);  // 16-row blocks, M <= 32, Kseg % 256 == 0
+hipError_t launch_q4_tile(const Problem& p, hipStream_t s);  // 4-bit, many tokens (q4tile.hip)
+bool q4_tile_fits(const Problem& p);
 // P stacked (rows, K) 16-bit matrices: row-major -> fragment-major (forward) or back
 hipError_t frag_transform(void* dst, const void* src, int P, int64_t rows, int64_t K, int forward, hipStream_t s);
 // SUMMA's A (K, N) -> q fragment-major blocks of A_t^T (N, K / q); N % 16 == 0, (K / q) % 32 == 0
@@ -294,6 +296,20 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
 __device__ __forceinline__ float e8m0_to_f32(uint32_t x) {
     if (x == 255u) return __builtin_nanf("");
     return x ? __uint_as_float(x << 23) : __uint_as_float(0x00400000u);  // 2^-127 is subnormal
+}
+
+// eight E4M3 codes (two words) times the E8M0 scale 2^(x - 127) -> eight bf16
+// (four words, k order) with v_cvt_scalef32_pk_bf16_fp8; exact: an E4M3 value
+// has 4 significant bits and the scale is a power of two
+__device__ __forceinline__ uint32_t __attribute__((ext_vector_type(4)))
+mx8_to_bf16(uint32_t __attribute__((ext_vector_type(2))) c, uint32_t scale_byte) {
+    const float sc = scale_byte ? __uint_as_float(scale_byte << 23) : __uint_as_float(0x00400000u);
+    uint32_t __attribute__((ext_vector_type(4))) r;
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[0], sc, false));
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[0], sc, true));
+    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[1], sc, false));
+    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[1], sc, true));
+    return r;
 }
 
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }

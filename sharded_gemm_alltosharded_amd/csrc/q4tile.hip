@@ -1,0 +1,258 @@
+// 4-bit affine tile GEMM for many tokens (M > 32): the quantized
+// all-to-sharded / sharded-to-all layers of "MLX 张量并行实战指南" sections 2.3
+// and 6 (group_size 64, bits 4, affine) when the streaming kernels' token limit
+// is passed.  Same factored arithmetic as q4.hip, exact in the codes: per
+// quantization group g of weight row n,
+//     sum_k w[n,k] x[t,k] = s[n,g] * sum_k (C + q[n,k]) x[t,k] + (b[n,g] - C s[n,g]) * sum_k x[t,k],
+// the first sum and sum_k x[t,k] on the matrix cores, the affine terms in
+// fp32 once per group.
+//
+// Workgroup: 4 waves (2 x 2) on 128 tokens x 128 weight rows (SwiGLU: 64
+// gate rows and the 64 matching up rows, 64 outputs), one k tile per
+// quantization group (64 inputs).  v_mfma_f32_32x32x16 with the tokens as the
+// row operand and the weight rows as the column operand gives each lane one
+// weight row per 32-row block, so each lane needs one (scale, bias) per group.
+// The lane's four MFMA steps of a group use input chunks 4h + u (h = lane / 32,
+// u = 0..3): its 16 bytes of the group's fragment-major codes (q4_word_offset)
+// arrive straight from global memory (one coalesced 1 KB per 32-row block),
+// and the matching activation chunks come from LDS (register-staged, double
+// buffered, 16-byte chunks XOR-swizzled by (row ^ row >> 3) & 7).  The group
+// sum of the activations is one more MFMA per step against an all-ones
+// operand, in the accumulator's own layout.  Ranks of a sharded-to-all layer
+// are the K segments of the loop, summed in order in registers.
+#include "internal.h"
+
+namespace sg {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+namespace {
+
+template <bool F16>
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+    if constexpr (F16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                      0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                       0, 0, 0);
+}
+
+// eight codes (stored in q4_nibble_pos order) -> eight (C + q) 16-bit numbers
+template <bool F16>
+__device__ __forceinline__ u32x4 unpack8(uint32_t w) {
+    constexpr uint32_t magic = F16 ? 0x64006400u : 0x43004300u;
+    u32x4 r;
+    r[0] = (w & 0x000F000Fu) | magic;
+    r[1] = ((w >> 4) & 0x000F000Fu) | magic;
+    r[2] = ((w >> 8) & 0x000F000Fu) | magic;
+    r[3] = ((w >> 12) & 0x000F000Fu) | magic;
+    return r;
+}
+
+__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+
+}  // namespace
+
+template <bool F16, bool SWIGLU>
+__global__ __launch_bounds__(256) void q4_tile_kernel(Problem p, int tiles_m, int tiles_n) {
+    constexpr int BM = 128, BN = 128, BK = 64;
+    constexpr int NOUT = SWIGLU ? BN / 2 : BN;  // logical columns per tile
+    constexpr float C = F16 ? 1024.f : 128.f;
+    __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * BK];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wave_m = wave >> 1, wave_n = wave & 1;
+    const int tile = xcd_remap(blockIdx.x, tiles_m * tiles_n);
+    constexpr int GM = 4;  // tile rows per group of the raster (shared weight panels)
+    const int grp = tile / (GM * tiles_n), first_m = grp * GM, gsz = min(GM, tiles_m - first_m);
+    const int tin = tile - grp * GM * tiles_n;
+    const int m0 = (first_m + tin % gsz) * BM;
+    const int64_t n0 = (int64_t)(tin / gsz) * NOUT;
+    const int G = p.Kseg / 64;  // groups per segment
+    const int ngroups = G * p.nseg;
+
+    // activation loader: thread -> rows lrow + 32 i, 16-byte chunk lch
+    const int lrow = tid >> 3, lch = tid & 7;
+    int64_t aoff[4];
+    bool aok[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int m = m0 + lrow + 32 * i;
+        aok[i] = m < p.M;
+        aoff[i] = (int64_t)(aok[i] ? m : 0) * p.lda + lch * 8;
+    }
+    // this lane's weight row in each of the wave's two 32-row blocks
+    const int h = lane >> 5;
+    int64_t qoff[2], goff[2];
+    bool nok[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+        int64_t row;
+        if constexpr (SWIGLU) {
+            const int64_t j = n0 + wave_n * 32 + (lane & 31);  // nb 0: gate row, 1: up row of output j
+            nok[nb] = j < p.N;
+            row = weight_row(p, nok[nb] ? j : 0, nb);
+        } else {
+            const int64_t n = n0 + wave_n * 64 + nb * 32 + (lane & 31);
+            nok[nb] = n < p.N;
+            row = nok[nb] ? n : 0;
+        }
+        // the stored layout spans ldg groups per row (a segment may be part of it)
+        qoff[nb] = q4_word_offset(row, 4 * h, p.ldg);  // group g at + 256 g (u32)
+        goff[nb] = q4_group_offset(row, 0, p.ldg);     // group g at + 128 (g / 4) + g % 4 (halves)
+    }
+
+    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+    u32x4 ra[4];
+    auto gload = [&](int gi) {
+        const int s = gi / G, g = gi - s * G;
+        const uint16_t* Ab = (const uint16_t*)p.A + s * p.a_seg + g * 64;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ra[i] = aok[i] ? *(const u32x4*)(Ab + aoff[i]) : zero4;
+    };
+    auto sstore = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = lrow + 32 * i;
+            *(u32x4*)(&sA[buf][row * BK + ((lch ^ swz(row)) << 3)]) = ra[i];
+        }
+    };
+    // codes, scale and bias of group gi for the lane's two rows
+    u32x4 cw[2];
+    uint16_t sc16[2], bi16[2];
+    auto wload = [&](int gi) {
+        const int s = gi / G, g = gi - s * G;
+        const uint32_t* Qb = p.wq + s * p.q_seg;
+        const uint16_t* Sb = p.qs + s * p.g_seg;
+        const uint16_t* Bb = p.qb + s * p.g_seg;
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            cw[nb] = *(const u32x4*)(Qb + qoff[nb] + (int64_t)g * 256);
+            const int64_t go = goff[nb] + (int64_t)(g >> 2) * 128 + (g & 3);
+            sc16[nb] = Sb[go];
+            bi16[nb] = Bb[go];
+        }
+    };
+
+    f32x16 y[2][2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) y[nb][mb][r] = 0.f;
+    f32x16 zero16;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) zero16[r] = 0.f;
+    const u32x4 ones = F16 ? u32x4{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u}
+                           : u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    const int frow = lane & 31;
+
+    if (ngroups > 0) {
+        gload(0);
+        sstore(0);
+        wload(0);
+    }
+    __syncthreads();
+    for (int gi = 0; gi < ngroups; ++gi) {
+        const int buf = gi & 1;
+        const u32x4 cwc[2] = {cw[0], cw[1]};
+        const float sc[2] = {f16_to_f32(sc16[0]), f16_to_f32(sc16[1])};
+        const float bi[2] = {f16_to_f32(bi16[0]), f16_to_f32(bi16[1])};
+        if (gi + 1 < ngroups) {
+            gload(gi + 1);
+            wload(gi + 1);
+        }
+        // activation chunks 4h + u of the wave's two token blocks
+        const uint16_t* a = sA[buf];
+        u32x4 xf[2][4];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            const int row = wave_m * 64 + mb * 32 + frow;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) xf[mb][u] = *(const u32x4*)(a + row * BK + (((4 * h + u) ^ swz(row)) << 3));
+        }
+        f32x16 xs[2];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            xs[mb] = mfma32<F16>(xf[mb][0], ones, zero16);
+#pragma unroll
+            for (int u = 1; u < 4; ++u) xs[mb] = mfma32<F16>(xf[mb][u], ones, xs[mb]);
+        }
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            u32x4 wf[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) wf[u] = unpack8<F16>(cwc[nb][u]);
+            const float bp = fmaf(-C, sc[nb], bi[nb]);
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+                f32x16 acc = mfma32<F16>(xf[mb][0], wf[0], zero16);
+#pragma unroll
+                for (int u = 1; u < 4; ++u) acc = mfma32<F16>(xf[mb][u], wf[u], acc);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) y[nb][mb][r] = fmaf(sc[nb], acc[r], fmaf(bp, xs[mb][r], y[nb][mb][r]));
+            }
+        }
+        if (gi + 1 < ngroups) sstore(buf ^ 1);
+        __syncthreads();
+    }
+
+    // epilogue: lane l of a 32 x 32 block holds weight row l & 31 (column) and
+    // tokens 8 j + 4 (l >> 5) + e (rows)
+    static_for<0, 2>([&](auto mc) {
+        constexpr int mb = decltype(mc)::value;
+        static_for<0, 16>([&](auto rc) {
+            constexpr int r = decltype(rc)::value;
+            const int m = m0 + wave_m * 64 + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (m >= p.M) return;
+            if constexpr (SWIGLU) {
+                const int64_t n = n0 + wave_n * 32 + (lane & 31);
+                if (!nok[0]) return;
+                const float v = silu_f32(y[0][mb][r]) * y[1][mb][r];
+                store_from_f32(p.out, p.out_dtype, out_index(p, m, n), v);
+            } else {
+                static_for<0, 2>([&](auto nc) {
+                    constexpr int nb = decltype(nc)::value;
+                    const int64_t n = n0 + wave_n * 64 + nb * 32 + (lane & 31);
+                    if (!nok[nb]) return;
+                    float v = y[nb][mb][r];
+                    if (p.bias) v += load_as_f32(p.bias, p.dtype, n);
+                    const int64_t o = out_index(p, m, n);
+                    if (p.accumulate && p.out_dtype == SG_F32) v += ((const float*)p.out)[o];
+                    store_from_f32(p.out, p.out_dtype, o, v);
+                });
+            }
+        });
+    });
+}
+
+// fragment-major codes (rows % 32 == 0, groups per segment % 4 == 0), 16-byte
+// activation rows
+bool q4_tile_fits(const Problem& p) {
+    return p.qfrag && !p.xfrag && p.Kseg % 256 == 0 && p.lda % 8 == 0 && p.a_seg % 8 == 0 &&
+           (p.out_map == OUT_ROWMAJOR || p.out_map == OUT_SHARDED) && !p.split;
+}
+
+hipError_t launch_q4_tile(const Problem& p, hipStream_t s) {
+    if (p.M == 0 || p.N == 0) return hipSuccess;
+    if (!q4_tile_fits(p)) return hipErrorInvalidValue;
+    const int nout = p.swiglu ? 64 : 128;
+    const int tm = (p.M + 127) / 128, tn = (p.N + nout - 1) / nout;
+    const dim3 grid(tm * tn), block(256);
+    const bool f16 = p.dtype == SG_F16;
+    if (p.swiglu) {
+        if (f16) launch(q4_tile_kernel<true, true>, grid, block, 0, s, p, tm, tn);
+        else launch(q4_tile_kernel<false, true>, grid, block, 0, s, p, tm, tn);
+    } else {
+        if (f16) launch(q4_tile_kernel<true, false>, grid, block, 0, s, p, tm, tn);
+        else launch(q4_tile_kernel<false, false>, grid, block, 0, s, p, tm, tn);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace sg

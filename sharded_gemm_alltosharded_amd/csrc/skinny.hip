@@ -47,17 +47,8 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 
 // MX FP8 weights (FP8): a step covers two 32-wide k steps; the lane's 16 code
 // bytes of the pair are one load (mx_code_offset), its row's two E8M0 scales
-// two bytes of one word; v_cvt_scalef32_pk_bf16_fp8 turns each 8 codes into
-// the bf16 operand (exact: 4 significant bits times a power of two).
-__device__ __forceinline__ u32x4 mx8_to_bf16(u32x2 c, uint32_t scale_byte) {
-    const float sc = scale_byte ? __uint_as_float(scale_byte << 23) : __uint_as_float(0x00400000u);
-    u32x4 r;
-    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[0], sc, false));
-    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[0], sc, true));
-    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[1], sc, false));
-    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[1], sc, true));
-    return r;
-}
+// two bytes of one word; mx8_to_bf16 (internal.h) turns each 8 codes into the
+// bf16 operand.
 
 template <int MT, int RB, int NW, bool F16, bool SWIGLU, int U, bool FP8 = false>
 __global__ __launch_bounds__(NW * 64) void skinny_kernel(Problem p) {

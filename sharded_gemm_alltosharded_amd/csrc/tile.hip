@@ -105,8 +105,13 @@ __device__ __forceinline__ void store4(const Problem& p, int m, int64_t n, float
     }
 }
 
-template <int BM, int BN, bool F16, int WMODE, bool SPLIT>
+// FP8: MX FP8 weights (E4M3 codes, one E8M0 scale per 32 inputs of a row), each
+// 8-code chunk turned into the bf16 operand in registers before the LDS store
+// (exact: 4 significant bits times a power of two), so the MFMAs and the rest
+// of the pipeline are the dense ones.
+template <int BM, int BN, bool F16, int WMODE, bool SPLIT, bool FP8 = false>
 __global__ __launch_bounds__(256) void tile_kernel(Problem p, int tiles_m, int tiles_n) {
+    static_assert(!FP8 || (!F16 && WMODE != WM_NN), "MX FP8 weights: bf16 activations, (out, in) weights");
     constexpr int WTM = BM / 2, WTN = BN / 2;  // per-wave outputs
     constexpr int NBM = WTM / 32, NBN = WTN / 32;
     constexpr int CA = BM / 32, CB = BN / 32;  // 16-byte chunks per thread
@@ -149,6 +154,7 @@ __global__ __launch_bounds__(256) void tile_kernel(Problem p, int tiles_m, int t
         aoff[i] = (int64_t)(aok[i] ? m : 0) * p.lda + lch * 8;
     }
     int64_t woff[CB];
+    int64_t wrow[CB];  // FP8: the weight row of each chunk
     bool wok[CB];
     const int tkb = tid >> 5, tnb = tid & 31;  // transposing loader (NN)
     if constexpr (WMODE == WM_NN) {
@@ -169,6 +175,7 @@ __global__ __launch_bounds__(256) void tile_kernel(Problem p, int tiles_m, int t
                 row = wok[i] ? n : 0;
             }
             woff[i] = p.wfrag ? frag_offset(row, lch * 8, p.wsteps) : row * p.ldw + lch * 8;
+            wrow[i] = row;
         }
     }
     // advancing k by one 64-wide tile moves 64 elements (row-major) or two
@@ -195,6 +202,20 @@ __global__ __launch_bounds__(256) void tile_kernel(Problem p, int tiles_m, int t
             for (int e = 0; e < 8; ++e) {
                 const bool ok = wok[0] && (k0 + tkb * 8 + e < p.Kseg);
                 rb[e] = ok ? *(const u32x4*)(Wb + (int64_t)(k0 + e) * p.ldw + woff[0]) : zero;
+            }
+        } else if constexpr (FP8) {
+            const uint8_t* W8 = (const uint8_t*)p.W + s * p.w_seg;
+            const uint8_t* S8 = p.ms + s * p.ms_seg;
+            const int k = k0 + lch * 8;
+#pragma unroll
+            for (int i = 0; i < CB; ++i) {
+                if (wok[i] && kok) {
+                    const int64_t ci = p.wfrag ? mx_code_offset(wrow[i], k, p.wsteps) : wrow[i] * p.ldw + k;
+                    const int64_t si = p.wfrag ? mx_scale_offset(wrow[i], k >> 5, p.wsteps) : wrow[i] * (p.ldw >> 5) + (k >> 5);
+                    rb[i] = mx8_to_bf16(*(const u32x2*)(W8 + ci), S8[si]);
+                } else {
+                    rb[i] = zero;
+                }
             }
         } else {
 #pragma unroll
@@ -359,13 +380,20 @@ SplitLayout tile_split_layout(int M, int N, int nseg, int variant) {
     return {t * bm * bm * nseg, t};
 }
 
-template <int BM, int BN, bool F16, int WMODE, bool SPLIT>
+template <int BM, int BN, bool F16, int WMODE, bool SPLIT, bool FP8 = false>
 static hipError_t launch_one(const Problem& p, hipStream_t s) {
     const int nout = WMODE == WM_SWIGLU ? BN / 2 : BN;
     const int tm = (p.M + BM - 1) / BM, tn = (p.N + nout - 1) / nout;
     dim3 grid(tm * tn, SPLIT ? p.nseg : 1);
-    launch((tile_kernel<BM, BN, F16, WMODE, SPLIT>), grid, dim3(256), 0, s, p, tm, tn);
+    launch((tile_kernel<BM, BN, F16, WMODE, SPLIT, FP8>), grid, dim3(256), 0, s, p, tm, tn);
     return hipGetLastError();
+}
+
+template <int BM, int BN>
+static hipError_t launch_fp8(const Problem& p, hipStream_t s) {
+    if (p.dtype != SG_BF16 || p.nn) return hipErrorInvalidValue;
+    if (p.swiglu) return launch_one<BM, BN, false, WM_SWIGLU, false, true>(p, s);
+    return p.split ? launch_one<BM, BN, false, WM_NT, true, true>(p, s) : launch_one<BM, BN, false, WM_NT, false, true>(p, s);
 }
 
 template <int BM, int BN, bool F16>
@@ -384,6 +412,7 @@ hipError_t launch_tile(const Problem& p, hipStream_t s, int variant) {
     if (p.M == 0 || p.N == 0) return hipSuccess;
     // 256 x 256 weight tiles: the direct-to-LDS pipeline (tile_dma.hip)
     if (variant == 0 && tile_dma_fits(p)) return launch_tile_dma(p, s);
+    if (p.fp8) return variant == 0 ? launch_fp8<256, 256>(p, s) : launch_fp8<128, 128>(p, s);
     const bool f16 = p.dtype == SG_F16;
     if (variant == 0) return f16 ? launch_mode<256, 256, true>(p, s) : launch_mode<256, 256, false>(p, s);
     return f16 ? launch_mode<128, 128, true>(p, s) : launch_mode<128, 128, false>(p, s);

@@ -311,7 +311,8 @@ __global__ __launch_bounds__(512) void tile_pp_kernel(Problem p, int tiles_m, in
 }
 
 bool tile_dma_fits(const Problem& p) {
-    return !p.nn && !p.split && p.Kseg % 32 == 0 && a_extent(p) < (1LL << 31) && w_extent(p) < (1LL << 31);
+    return !p.nn && !p.split && !p.fp8 && !p.wq && p.Kseg % 32 == 0 && a_extent(p) < (1LL << 31) &&
+           w_extent(p) < (1LL << 31);
 }
 
 hipError_t launch_tile_dma(const Problem& p, hipStream_t s) {

@@ -289,7 +289,7 @@ def _q4_layer(w, mode, P, S=1):
     return layer, oracle.deq4(packed, s, b, 64)
 
 
-@pytest.mark.parametrize("B", [1, 8, 13, 32, 40])
+@pytest.mark.parametrize("B", [1, 8, 13, 32, 40, 100, 300])  # > 32 tokens: the 4-bit tile kernel
 def test_q4_all_to_sharded(B):
     _print_case(B=B)
     D, out, P = 512, 384, 4
@@ -299,7 +299,7 @@ def test_q4_all_to_sharded(B):
     assert_close(sg.all_to_sharded(layer, to_dev(X, "bf16"), out_dtype=torch.float32), ref, "f32", "q4 col")
 
 
-@pytest.mark.parametrize("B", [1, 8, 13, 24, 32])
+@pytest.mark.parametrize("B", [1, 8, 13, 24, 32, 48, 300])
 def test_q4_swiglu_and_row(B):
     _print_case(B=B)
     D, F, P = 512, 1024, 4
@@ -382,7 +382,7 @@ def test_integer_exact_summa():
             np.testing.assert_array_equal(to_np(y), oracle.summa(X, A, 4, dtype="bf16"))
 
 
-@pytest.mark.parametrize("B", [1, 8, 32])
+@pytest.mark.parametrize("B", [1, 8, 32, 64, 520])
 def test_integer_exact_q4(B):
     """Power-of-two scales, integer biases and integer activations: exact."""
     out, D, P = 128, 512, 2
@@ -513,6 +513,19 @@ def test_all_gather_input_row_major_weights():
     assert_close(y, oracle.col(oracle.all_gather(Xs), W, P=P, dtype="bf16"), "f32", "row-major gathered input")
 
 
+@pytest.mark.parametrize("B", [5, 60])
+def test_all_gather_input_q4(B):
+    """A 4-bit all-to-sharded layer fed its input as rank shards ([HSYM] Case
+    2): the 4-bit tile kernel walks the P input slices as K segments."""
+    _print_case(B=B)
+    D, out, P = 1024, 384, 4
+    layer, Wd = _q4_layer(synth.uniform(66, (out, D), 1 / np.sqrt(D), "f32"), 0, P)
+    Xs = synth.normal(67, (P, B, D // P), 1.0, "bf16")
+    ref = oracle.col(oracle.all_gather(Xs), Wd, P=P, dtype="bf16")
+    y = sg.all_to_sharded(layer, to_dev(Xs, "bf16"), x_sharded=True, out_dtype=torch.float32)
+    assert_close(y, ref, "f32", "q4 all-gather input")
+
+
 def test_all_gather_input_rejections():
     W = synth.uniform(53, (64, 96), 0.1, "bf16")
     layer = sg.shard_linear(to_dev(W, "bf16"), "all-to-sharded", P=2)  # in / P = 48: not 32-aligned
@@ -549,7 +562,7 @@ def test_reduce_scatter_output(B, P):
         assert torch.equal(y[r], yf[:, r * (out // P):(r + 1) * (out // P)])
 
 
-@pytest.mark.parametrize("B", [1, 8, 32])
+@pytest.mark.parametrize("B", [1, 8, 32, 100])
 def test_reduce_scatter_q4(B):
     _print_case(B=B)
     D, F, P = 512, 1024, 4
@@ -619,7 +632,7 @@ def test_slicing_mx_bit_exact(mode, out, inn, S, P):
         layer.shard(0, 3)  # no quantization biases
 
 
-@pytest.mark.parametrize("B", [1, 8, 16, 32, 40])
+@pytest.mark.parametrize("B", [1, 8, 16, 32, 40, 600])  # > 32 tokens: the tile kernels, codes converted in the loader
 def test_mx_all_to_sharded(B):
     _print_case(B=B)
     D, out, P = 512, 384, 4
@@ -630,7 +643,7 @@ def test_mx_all_to_sharded(B):
         assert_close(y, oracle.col(X, Wd, P=P, gather=gather, dtype="bf16"), "f32", "mx col")
 
 
-@pytest.mark.parametrize("B", [1, 16, 32])
+@pytest.mark.parametrize("B", [1, 16, 32, 48, 520])
 def test_mx_swiglu_and_row(B):
     _print_case(B=B)
     D, F, P = 512, 1024, 4
@@ -655,7 +668,7 @@ def test_mx_row_major_layout():
     assert_close(y, oracle.col(X, Wd, P=P, gather=True, dtype="bf16"), "f32", "mx row-major")
 
 
-@pytest.mark.parametrize("B", [1, 8, 32])
+@pytest.mark.parametrize("B", [1, 8, 32, 64, 520])
 def test_integer_exact_mx(B):
     """Integer-valued E4M3 codes at scale 2^0 and 2^1, integer activations: exact."""
     out, D, P = 128, 512, 2
