@@ -8,12 +8,17 @@
 //  * sharded-to-all, Y = sum_r X_r W_r^T:  dX_r = dY W_r (stays sharded, no
 //    reduction), dW_r = dY^T X_r.
 //
-// fp32 accumulation on the vector units (the products are not on the matrix
-// cores yet): the input gradient token-blocked with the K range split over the
-// waves of a workgroup, the weight gradient one thread per element (its
-// reduction runs over the B tokens only).  The weight is read in the layout the
-// layer stores (fragment-major or row-major), element W_r[k][n] of rank r's
-// (rows_r, cols_r) shard.
+// 16-bit layers whose shapes tile run their input gradients on the forward
+// matrix-core kernels over a transposed copy of the shards, and their weight
+// gradients on dw_small_kernel below (few tokens) or on the tile kernels over
+// transposed operands.  This file also holds the vector-unit kernels that
+// serve every other case (fp32 layers, unaligned shapes, many-token weight
+// gradients without a workspace), with fp32 accumulation: the input gradient
+// token-blocked with the K range split over the waves of a workgroup, the
+// weight gradient a few elements per thread (its reduction runs over the B
+// tokens only).  They read the weight in the layout the layer stores
+// (fragment-major or row-major), element W_r[k][n] of rank r's (rows_r,
+// cols_r) shard.
 #include "internal.h"
 
 namespace sg {
