@@ -8,8 +8,13 @@
 // 16-bit numbers c + q with c = 128 (bf16) or 1024 (fp16), so the MFMA forms
 // acc = sum (c + q) x = sum q x + c * xs, and the epilogue of the group adds
 //     s * acc + (b - c * s) * xs,
-// where xs = sum_k x[t,k] comes from one more MFMA of the token fragments
-// against an all-ones operand (same register layout as acc, no shuffles).
+// where xs = sum_k x[t,k] comes from one more MFMA, of an all-ones operand
+// against the token fragments.  The scale term is one FMA per accumulator per
+// group; the bias term sum_g (b - c s)[n,g] xs[t,g] is itself a small product
+// over the groups, run on the fp32 MFMA (v_mfma_f32_32x32x2f32) per pair of
+// groups straight into the same accumulators, which halves the vector-unit
+// work of a group (the kernel is issue-bound on the vector unit, not on HBM)
+// once there are more than 8 tokens.
 //
 // MFMA v_mfma_f32_32x32x16: the tokens are the row operand (32 token slots),
 // 32 weight rows the column operand, so each lane owns one weight row and
@@ -46,16 +51,23 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// eight codes (stored in q4_nibble_pos order) -> eight (c + q) 16-bit numbers
-template <bool F16>
-__device__ __forceinline__ u32x4 unpack8(uint32_t w) {
-    constexpr uint32_t magic = F16 ? 0x64006400u : 0x43004300u;
+// eight codes (stored in q4_nibble_pos order) -> eight (c + q) 16-bit numbers.
+// mask = 0x000F000F and magic = the 16-bit pattern of c in both halves, held in
+// registers so that each and-or is one v_and_or_b32 (gfx9's three-operand
+// instructions take no literal constants).
+__device__ __forceinline__ u32x4 unpack8(uint32_t w, uint32_t mask, uint32_t magic) {
     u32x4 r;
-    r[0] = (w & 0x000F000Fu) | magic;
-    r[1] = ((w >> 4) & 0x000F000Fu) | magic;
-    r[2] = ((w >> 8) & 0x000F000Fu) | magic;
-    r[3] = ((w >> 12) & 0x000F000Fu) | magic;
+    r[0] = (w & mask) | magic;
+    r[1] = ((w >> 4) & mask) | magic;
+    r[2] = ((w >> 8) & mask) | magic;
+    r[3] = ((w >> 12) & mask) | magic;
     return r;
+}
+
+// the fp32 MFMA of the bias term: D (32 x 32) += A (32 x 2) B (2 x 32), lane l
+// holding A[l & 31][l >> 5] and B[l >> 5][l & 31]
+__device__ __forceinline__ f32x16 mfma32_f32(float a, float b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
 template <int TB, int RB, int NW, bool F16, bool SWIGLU, bool PF, bool XH>
@@ -64,6 +76,10 @@ __global__ __launch_bounds__(NW * 64) void q4_kernel(Problem p) {
     constexpr int NR = 4 * TB;                            // token registers in use
     constexpr int SLOT = RB * NR * 64;                    // floats per unit slot
     constexpr float C = F16 ? 1024.f : 128.f;
+    // the bias term on the fp32 MFMA (MB) once the tokens fill most of the
+    // accumulators; with up to 8 tokens its two FMAs per group touch only 4 of
+    // them, and the MFMA's 16 live accumulators would cost registers instead
+    constexpr bool MB = TB >= 2;
     static_assert(!SWIGLU || RB % 2 == 0, "gate/up blocks come in pairs");
     extern __shared__ float slots[];
 
@@ -92,12 +108,22 @@ __global__ __launch_bounds__(NW * 64) void q4_kernel(Problem p) {
         qoff[rb] = q4_word_offset(row, 4 * h, G);  // group g at + 256 g
         goff[rb] = q4_group_offset(row, 0, G);     // run r at + 128 r
     }
+    // Rows past N and tokens past M read row / token 0 (never stored).  With MB
+    // the loads take no branch; without, they are skipped and read as zero
+    // (measured faster with up to 8 tokens, whose registers are nearly full).
     const int t = lane & 31;
-    const bool xok = t < p.M;
-    const int64_t xoff = (int64_t)(xok ? t : 0) * p.lda + h * 32;
+    const bool xok = MB || t < p.M;
+    const int64_t xoff = (int64_t)(t < p.M ? t : 0) * p.lda + h * 32;
     const u32x4 ones = F16 ? u32x4{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u}
                            : u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
     const u32x4 zero = {0u, 0u, 0u, 0u};
+    const f32x16 fzero = {};
+    uint32_t mask = 0x000F000Fu, magic = F16 ? 0x64006400u : 0x43004300u;
+    if constexpr (MB) {
+        asm("s_mov_b32 %0, 0x000f000f" : "=s"(mask));
+        asm("v_mov_b32 %0, %1" : "=v"(magic) : "i"(F16 ? 0x64006400 : 0x43004300));
+    }
+    const int hs = 16 * h;  // this lane's half of a scale word: group 2p + h of pair p
 
     for (int u = wave; u < units; u += NW) {
         const int s = u / J, j = u % J;
@@ -107,22 +133,20 @@ __global__ __launch_bounds__(NW * 64) void q4_kernel(Problem p) {
         const uint16_t* Ab = (const uint16_t*)p.A + s * p.a_seg + xoff;
         f32x16 y[RB];
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) y[rb][r] = 0.f;
+        for (int rb = 0; rb < RB; ++rb) y[rb] = fzero;
         // codes, scales and biases of a run of 4 groups; with PF the next run's
         // are in flight while this one is computed (register double buffer)
         constexpr int NB = PF ? 2 : 1;
         u32x4 wv[NB][4][RB];
         u32x2 sv[NB][RB], bv[NB][RB];
         auto load = [&](int buf, int run) {
+            const uint32_t* qr = Qb + (int64_t)run * 1024;
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
                 for (int gi = 0; gi < 4; ++gi)
-                    wv[buf][gi][rb] = wok[rb] ? __builtin_nontemporal_load(
-                                                    (const u32x4*)(Qb + qoff[rb] + (int64_t)(run * 4 + gi) * 256))
-                                              : zero;
+                    wv[buf][gi][rb] = (MB || wok[rb]) ? __builtin_nontemporal_load((const u32x4*)(qr + qoff[rb] + gi * 256))
+                                                      : zero;
                 sv[buf][rb] = *(const u32x2*)(Sb + goff[rb] + (int64_t)run * 128);
                 bv[buf][rb] = *(const u32x2*)(Bb + goff[rb] + (int64_t)run * 128);
             }
@@ -138,30 +162,45 @@ __global__ __launch_bounds__(NW * 64) void q4_kernel(Problem p) {
 #pragma unroll
                     for (int q = 0; q < 4; ++q) xr[gi][q] = xok ? *(const u32x4*)(Ab + (g0 + gi) * 64 + q * 8) : zero;
             }
+            float xa = 0.f;  // A operand of the pair's bias MFMA: xs[token t][group 2p + h]
 #pragma unroll
             for (int gi = 0; gi < 4; ++gi) {
                 u32x4 xf[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
                     xf[q] = XH ? xr[XH ? gi : 0][q] : (xok ? *(const u32x4*)(Ab + (g0 + gi) * 64 + q * 8) : zero);
-                f32x16 xs;
+                // MB: ones (A) x tokens (B), every register of lane l holds xs of
+                // token l & 31; else tokens (A) x ones (B), xs in acc's layout
+                f32x16 xs = fzero;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) xs[r] = 0.f;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) xs = mfma32<F16>(xf[q], ones, xs);
+                for (int q = 0; q < 4; ++q) xs = MB ? mfma32<F16>(ones, xf[q], xs) : mfma32<F16>(xf[q], ones, xs);
+                if constexpr (MB) xa = (gi & 1) ? (h ? xs[0] : xa) : xs[0];
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb) {
-                    f32x16 acc;
+                    f32x16 acc = fzero;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) acc = mfma32<F16>(xf[q], unpack8<F16>(wv[buf][gi][rb][q]), acc);
-                    const uint32_t sw = sv[buf][rb][gi >> 1], bw = bv[buf][rb][gi >> 1];
+                    for (int q = 0; q < 4; ++q) acc = mfma32<F16>(xf[q], unpack8(wv[buf][gi][rb][q], mask, magic), acc);
+                    const uint32_t sw = sv[buf][rb][gi >> 1];
                     const float sc = f16_to_f32((uint16_t)((gi & 1) ? (sw >> 16) : (sw & 0xFFFFu)));
-                    const float bi = f16_to_f32((uint16_t)((gi & 1) ? (bw >> 16) : (bw & 0xFFFFu)));
-                    const float bp = fmaf(-C, sc, bi);
+                    if constexpr (MB) {
 #pragma unroll
-                    for (int r = 0; r < NR; ++r) y[rb][r] = fmaf(sc, acc[r], fmaf(bp, xs[r], y[rb][r]));
+                        for (int r = 0; r < NR; ++r) y[rb][r] = fmaf(sc, acc[r], y[rb][r]);
+                    } else {
+                        const uint32_t bw = bv[buf][rb][gi >> 1];
+                        const float bi = f16_to_f32((uint16_t)((gi & 1) ? (bw >> 16) : (bw & 0xFFFFu)));
+                        const float bp = fmaf(-C, sc, bi);
+#pragma unroll
+                        for (int r = 0; r < NR; ++r) y[rb][r] = fmaf(sc, acc[r], fmaf(bp, xs[r], y[rb][r]));
+                    }
+                }
+                if (MB && (gi & 1)) {
+                    // bias term of groups gi - 1, gi: lane (row, h) supplies (b - c s) of group gi - 1 + h
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb) {
+                        const float sc = f16_to_f32((uint16_t)(sv[buf][rb][gi >> 1] >> hs));
+                        const float bi = f16_to_f32((uint16_t)(bv[buf][rb][gi >> 1] >> hs));
+                        y[rb] = mfma32_f32(xa, fmaf(-C, sc, bi), y[rb]);
+                    }
                 }
             }
         };
@@ -219,11 +258,11 @@ __global__ __launch_bounds__(NW * 64) void q4_kernel(Problem p) {
 
 // Shape choice: RB row blocks of 32 per wave (a gate/up pair for SwiGLU; more
 // share each activation fragment), about 1500 waves on the chip, LDS slots
-// within kMaxStreamLds.  Eight waves per workgroup whenever the slots allow:
-// at four the larger token counts compile to one wave per SIMD (their
-// registers fill the file) and a run's loads are not hidden -- measured 40.4
-// against 31.9 us for the 32-token gate|up layer.  Four row blocks only up to
-// 8 tokens (beyond that the token registers make them spill).
+// within kMaxStreamLds.  Up to 8 tokens eight waves per workgroup; beyond,
+// where the bias term runs on the MFMA and the kernel needs ~165 registers,
+// four (measured on the gate|up layer of the decode MLP: 16 tokens 23.7 ->
+// 21.7 us with the activations hoisted, 32 tokens 29.9 -> 28.2 us).  Four row
+// blocks only up to 8 tokens (beyond that the token registers make them spill).
 Q4Shape q4_shape(int M, int N, int nseg, int swiglu) {
     Q4Shape sh;
     sh.TB = (M + 7) / 8;
@@ -238,7 +277,7 @@ Q4Shape q4_shape(int M, int N, int nseg, int swiglu) {
         if (swiglu && rb < 2) break;
         if (rb == 4 && sh.TB > 1) continue;
         const int64_t wgs = (rows + rb * 32 - 1) / (rb * 32);
-        const int nw = lds_of(rb, 8) <= kMaxStreamLds ? 8 : 4;
+        const int nw = (sh.TB == 1 && lds_of(rb, 8) <= kMaxStreamLds) ? 8 : 4;
         if ((wgs * nw >= 1536 && lds_of(rb, nw) <= kMaxStreamLds) || rb == (swiglu ? 2 : 1)) {
             sh.RB = rb;
             sh.NW = nw;
@@ -267,9 +306,9 @@ hipError_t launch_q4_variant(const Problem& p, hipStream_t s, size_t lds) {
 
 template <int TB, int RB, bool F16>
 static hipError_t launch_rb(const Problem& p, hipStream_t s, const Q4Shape& sh) {
-    // up to 8 tokens the run's activation fragments are hoisted (measured
+    // up to 16 tokens the run's activation fragments are hoisted (measured
     // faster); beyond that their registers cost more than the latency saved
-    constexpr bool XH = TB == 1;
+    constexpr bool XH = TB <= 2;
     return sh.NW == 4 ? launch_q4_variant<TB, RB, 4, F16, false, XH>(p, s, sh.lds)
                       : launch_q4_variant<TB, RB, 8, F16, false, XH>(p, s, sh.lds);
 }
