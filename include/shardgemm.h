@@ -286,7 +286,11 @@ sg_status sg_summa_backward(const void* X, const void* A, const void* dY, sg_dty
  * K % 8 == 0. */
 size_t sg_summa_backward_workspace(sg_dtype dtype, int64_t M, int64_t K, int64_t N, int q);
 
-/* Bytes of workspace sg_sharded_to_all needs for B tokens (0 on bad input). */
+/* Bytes of workspace sg_sharded_to_all needs for B tokens (0 on bad input, and
+ * when the call runs without one).  Non-zero when the output alone gives too
+ * few tiles to fill the chip (beyond 32 tokens, dense 16-bit and 4-bit
+ * layers): each rank's product is then a workgroup of its own, with partial
+ * tiles in the workspace summed in rank order by the last to arrive. */
 size_t sg_sharded_to_all_workspace(const sg_layer* layer, int64_t B);
 
 /* SUMMA on a q x q grid ([SUMMA], SUMMA section, equations (1), (2)).

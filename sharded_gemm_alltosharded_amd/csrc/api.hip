@@ -205,6 +205,7 @@ bool want_split(const sg_layer* l, Kind k, int64_t B) {
     switch (k) {
     case K_TILE0: return sg::tile_count((int)B, (int)l->out_dims, 0) * 2 <= cus;
     case K_TILE1: return sg::tile_count((int)B, (int)l->out_dims, 1) * 2 <= cus;
+    case K_Q4TILE: return sg::q4_tile_count((int)B, (int)l->out_dims) * 2 <= cus;
     default: return false;
     }
 }
@@ -213,6 +214,10 @@ sg::SplitLayout split_layout(const sg_layer* l, Kind k, int64_t B) {
     switch (k) {
     case K_TILE0: return sg::tile_split_layout((int)B, (int)l->out_dims, l->P, 0);
     case K_TILE1: return sg::tile_split_layout((int)B, (int)l->out_dims, l->P, 1);
+    case K_Q4TILE: {
+        const size_t t = (size_t)sg::q4_tile_count((int)B, (int)l->out_dims);
+        return {t * 128 * 128 * l->P, t};
+    }
     default: return {0, 0};
     }
 }

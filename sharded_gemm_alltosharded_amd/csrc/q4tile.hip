@@ -4,8 +4,10 @@
 // is passed.  Same factored arithmetic as q4.hip, exact in the codes: per
 // quantization group g of weight row n,
 //     sum_k w[n,k] x[t,k] = s[n,g] * sum_k (C + q[n,k]) x[t,k] + (b[n,g] - C s[n,g]) * sum_k x[t,k],
-// the first sum and sum_k x[t,k] on the matrix cores, the affine terms in
-// fp32 once per group.
+// the first sum and sum_k x[t,k] on the matrix cores; the scale term is one
+// fp32 FMA per accumulator per group, and the bias term
+// sum_g (b - C s)[n,g] xs[t,g], itself a product over the groups, runs on the
+// fp32 MFMA per pair of groups into the same accumulators.
 //
 // Workgroup: 4 waves (2 x 2) on 128 tokens x 128 weight rows (SwiGLU: 64
 // gate rows and the 64 matching up rows, 64 outputs), one k tile per
@@ -17,9 +19,11 @@
 // arrive straight from global memory (one coalesced 1 KB per 32-row block),
 // and the matching activation chunks come from LDS (register-staged, double
 // buffered, 16-byte chunks XOR-swizzled by (row ^ row >> 3) & 7).  The group
-// sum of the activations is one more MFMA per step against an all-ones
-// operand, in the accumulator's own layout.  Ranks of a sharded-to-all layer
-// are the K segments of the loop, summed in order in registers.
+// sum of the activations is one more MFMA per step, of an all-ones operand
+// against the token fragments.  Ranks of a sharded-to-all layer are the K
+// segments of the loop, summed in order in registers.  Two workgroups per CU
+// (two waves per SIMD) so that one wave's loads and barrier waits overlap the
+// other's matrix work.
 #include "internal.h"
 
 namespace sg {
@@ -27,6 +31,7 @@ namespace sg {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 namespace {
@@ -41,24 +46,29 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
                                                        0, 0, 0);
 }
 
-// eight codes (stored in q4_nibble_pos order) -> eight (C + q) 16-bit numbers
-template <bool F16>
-__device__ __forceinline__ u32x4 unpack8(uint32_t w) {
-    constexpr uint32_t magic = F16 ? 0x64006400u : 0x43004300u;
+// eight codes (stored in q4_nibble_pos order) -> eight (C + q) 16-bit numbers;
+// mask and magic in registers, so each and-or is one v_and_or_b32
+__device__ __forceinline__ u32x4 unpack8(uint32_t w, uint32_t mask, uint32_t magic) {
     u32x4 r;
-    r[0] = (w & 0x000F000Fu) | magic;
-    r[1] = ((w >> 4) & 0x000F000Fu) | magic;
-    r[2] = ((w >> 8) & 0x000F000Fu) | magic;
-    r[3] = ((w >> 12) & 0x000F000Fu) | magic;
+    r[0] = (w & mask) | magic;
+    r[1] = ((w >> 4) & mask) | magic;
+    r[2] = ((w >> 8) & mask) | magic;
+    r[3] = ((w >> 12) & mask) | magic;
     return r;
+}
+
+// fp32 MFMA: D (32 x 32) += A (32 x 2) B (2 x 32), lane l holding A[l & 31][l >> 5]
+// and B[l >> 5][l & 31]
+__device__ __forceinline__ f32x16 mfma32_f32(float a, float b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
 }  // namespace
 
-template <bool F16, bool SWIGLU>
-__global__ __launch_bounds__(256) void q4_tile_kernel(Problem p, int tiles_m, int tiles_n) {
+template <bool F16, bool SWIGLU, bool SPLIT>
+__global__ __launch_bounds__(256, 2) void q4_tile_kernel(Problem p, int tiles_m, int tiles_n) {
     constexpr int BM = 128, BN = 128, BK = 64;
     constexpr int NOUT = SWIGLU ? BN / 2 : BN;  // logical columns per tile
     constexpr float C = F16 ? 1024.f : 128.f;
@@ -73,17 +83,18 @@ __global__ __launch_bounds__(256) void q4_tile_kernel(Problem p, int tiles_m, in
     const int m0 = (first_m + tin % gsz) * BM;
     const int64_t n0 = (int64_t)(tin / gsz) * NOUT;
     const int G = p.Kseg / 64;  // groups per segment
-    const int ngroups = G * p.nseg;
+    // SPLIT: this workgroup takes segment blockIdx.y only (groups [g_lo, g_lo + G))
+    const int g_lo = SPLIT ? (int)blockIdx.y * G : 0;
+    const int ngroups = SPLIT ? G : G * p.nseg;
 
-    // activation loader: thread -> rows lrow + 32 i, 16-byte chunk lch
+    // activation loader: thread -> rows lrow + 32 i, 16-byte chunk lch; tokens
+    // past M read token 0 (no branch on the loads) and are never stored
     const int lrow = tid >> 3, lch = tid & 7;
     int64_t aoff[4];
-    bool aok[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int m = m0 + lrow + 32 * i;
-        aok[i] = m < p.M;
-        aoff[i] = (int64_t)(aok[i] ? m : 0) * p.lda + lch * 8;
+        aoff[i] = (int64_t)(m < p.M ? m : 0) * p.lda + lch * 8;
     }
     // this lane's weight row in each of the wave's two 32-row blocks
     const int h = lane >> 5;
@@ -106,13 +117,12 @@ __global__ __launch_bounds__(256) void q4_tile_kernel(Problem p, int tiles_m, in
         goff[nb] = q4_group_offset(row, 0, p.ldg);     // group g at + 128 (g / 4) + g % 4 (halves)
     }
 
-    const u32x4 zero4 = {0u, 0u, 0u, 0u};
     u32x4 ra[4];
-    auto gload = [&](int gi) {
-        const int s = gi / G, g = gi - s * G;
+    auto gload = [&](int gl) {
+        const int gi = g_lo + gl, s = gi / G, g = gi - s * G;
         const uint16_t* Ab = (const uint16_t*)p.A + s * p.a_seg + g * 64;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ra[i] = aok[i] ? *(const u32x4*)(Ab + aoff[i]) : zero4;
+        for (int i = 0; i < 4; ++i) ra[i] = *(const u32x4*)(Ab + aoff[i]);
     };
     auto sstore = [&](int buf) {
 #pragma unroll
@@ -124,8 +134,8 @@ __global__ __launch_bounds__(256) void q4_tile_kernel(Problem p, int tiles_m, in
     // codes, scale and bias of group gi for the lane's two rows
     u32x4 cw[2];
     uint16_t sc16[2], bi16[2];
-    auto wload = [&](int gi) {
-        const int s = gi / G, g = gi - s * G;
+    auto wload = [&](int gl) {
+        const int gi = g_lo + gl, s = gi / G, g = gi - s * G;
         const uint32_t* Qb = p.wq + s * p.q_seg;
         const uint16_t* Sb = p.qs + s * p.g_seg;
         const uint16_t* Bb = p.qb + s * p.g_seg;
@@ -139,17 +149,16 @@ __global__ __launch_bounds__(256) void q4_tile_kernel(Problem p, int tiles_m, in
     };
 
     f32x16 y[2][2];
+    const f32x16 zero16 = {};
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) y[nb][mb][r] = 0.f;
-    f32x16 zero16;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) zero16[r] = 0.f;
+        for (int mb = 0; mb < 2; ++mb) y[nb][mb] = zero16;
     const u32x4 ones = F16 ? u32x4{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u}
                            : u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    uint32_t mask, magic;
+    asm("s_mov_b32 %0, 0x000f000f" : "=s"(mask));
+    asm("v_mov_b32 %0, %1" : "=v"(magic) : "i"(F16 ? 0x64006400 : 0x43004300));
     const int frow = lane & 31;
 
     if (ngroups > 0) {
@@ -158,6 +167,10 @@ __global__ __launch_bounds__(256) void q4_tile_kernel(Problem p, int tiles_m, in
         wload(0);
     }
     __syncthreads();
+    // The bias term sum_g (b - C s)[n,g] xs[t,g] runs on the fp32 MFMA per pair
+    // of groups (its 2 k = the pair): lane (l & 31, h) supplies xs of token
+    // l & 31 and (b - C s) of its row, both of group 2 p + h.
+    float xa[2] = {0.f, 0.f}, bq[2] = {0.f, 0.f};
     for (int gi = 0; gi < ngroups; ++gi) {
         const int buf = gi & 1;
         const u32x4 cwc[2] = {cw[0], cw[1]};
@@ -176,30 +189,87 @@ __global__ __launch_bounds__(256) void q4_tile_kernel(Problem p, int tiles_m, in
 #pragma unroll
             for (int u = 0; u < 4; ++u) xf[mb][u] = *(const u32x4*)(a + row * BK + (((4 * h + u) ^ swz(row)) << 3));
         }
-        f32x16 xs[2];
+        // ones (A) x tokens (B): every register of lane l holds xs of token l & 31
+        const bool mine = (gi & 1) == h;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
-            xs[mb] = mfma32<F16>(xf[mb][0], ones, zero16);
+            f32x16 xs = zero16;
 #pragma unroll
-            for (int u = 1; u < 4; ++u) xs[mb] = mfma32<F16>(xf[mb][u], ones, xs[mb]);
+            for (int u = 0; u < 4; ++u) xs = mfma32<F16>(ones, xf[mb][u], xs);
+            xa[mb] = mine ? xs[0] : xa[mb];
         }
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
+            bq[nb] = mine ? fmaf(-C, sc[nb], bi[nb]) : bq[nb];
             u32x4 wf[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) wf[u] = unpack8<F16>(cwc[nb][u]);
-            const float bp = fmaf(-C, sc[nb], bi[nb]);
+            for (int u = 0; u < 4; ++u) wf[u] = unpack8(cwc[nb][u], mask, magic);
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb) {
-                f32x16 acc = mfma32<F16>(xf[mb][0], wf[0], zero16);
+                f32x16 acc = zero16;
 #pragma unroll
-                for (int u = 1; u < 4; ++u) acc = mfma32<F16>(xf[mb][u], wf[u], acc);
+                for (int u = 0; u < 4; ++u) acc = mfma32<F16>(xf[mb][u], wf[u], acc);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) y[nb][mb][r] = fmaf(sc[nb], acc[r], fmaf(bp, xs[mb][r], y[nb][mb][r]));
+                for (int r = 0; r < 16; ++r) y[nb][mb][r] = fmaf(sc[nb], acc[r], y[nb][mb][r]);
             }
+        }
+        // the pair's bias term once both groups are in (or the last, odd group:
+        // the lanes of the missing group then hold its xs = 0 contribution)
+        if ((gi & 1) || gi + 1 == ngroups) {
+            if (!(gi & 1)) {  // last group of an odd count: no partner group
+                if (h) { xa[0] = 0.f; xa[1] = 0.f; }
+            }
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb) y[nb][mb] = mfma32_f32(xa[mb], bq[nb], y[nb][mb]);
         }
         if (gi + 1 < ngroups) sstore(buf ^ 1);
         __syncthreads();
+    }
+
+    // cross-segment reduction (split by rank): every workgroup stores its
+    // partial tile; the last of a tile's nseg to arrive adds them in rank order
+    if constexpr (SPLIT) {
+        const int ntiles = tiles_m * tiles_n;
+        const int64_t slab = (int64_t)ntiles * BM * BN;  // floats per segment
+        f32x4* mine = (f32x4*)(p.ws + blockIdx.y * slab + (int64_t)tile * BM * BN);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    mine[((nb * 2 + mb) * 4 + q) * 256 + tid] =
+                        f32x4{y[nb][mb][4 * q], y[nb][mb][4 * q + 1], y[nb][mb][4 * q + 2], y[nb][mb][4 * q + 3]};
+        __threadfence();
+        __syncthreads();
+        __shared__ int last;
+        if (tid == 0) {
+            const unsigned prev = atomicAdd(&p.counters[tile], 1u);
+            last = prev == (unsigned)p.nseg - 1;
+            if (last) p.counters[tile] = 0u;  // ready for the next call
+        }
+        __syncthreads();
+        if (!last) return;
+        __threadfence();
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) y[nb][mb] = zero16;
+        for (int sr = 0; sr < p.nseg; ++sr) {  // rank order
+            const f32x4* src = (const f32x4*)(p.ws + sr * slab + (int64_t)tile * BM * BN);
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const f32x4 v = src[((nb * 2 + mb) * 4 + q) * 256 + tid];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) y[nb][mb][4 * q + e] += v[e];
+                    }
+        }
     }
 
     // epilogue: lane l of a 32 x 32 block holds weight row l & 31 (column) and
@@ -235,22 +305,27 @@ __global__ __launch_bounds__(256) void q4_tile_kernel(Problem p, int tiles_m, in
 // activation rows
 bool q4_tile_fits(const Problem& p) {
     return p.qfrag && !p.xfrag && p.Kseg % 256 == 0 && p.lda % 8 == 0 && p.a_seg % 8 == 0 &&
-           (p.out_map == OUT_ROWMAJOR || p.out_map == OUT_SHARDED) && !p.split;
+           (p.out_map == OUT_ROWMAJOR || p.out_map == OUT_SHARDED) && !(p.split && p.swiglu);
 }
+
+int q4_tile_count(int M, int N) { return ((M + 127) / 128) * ((N + 127) / 128); }
 
 hipError_t launch_q4_tile(const Problem& p, hipStream_t s) {
     if (p.M == 0 || p.N == 0) return hipSuccess;
     if (!q4_tile_fits(p)) return hipErrorInvalidValue;
     const int nout = p.swiglu ? 64 : 128;
     const int tm = (p.M + 127) / 128, tn = (p.N + nout - 1) / nout;
-    const dim3 grid(tm * tn), block(256);
+    const dim3 grid(tm * tn, p.split ? p.nseg : 1), block(256);
     const bool f16 = p.dtype == SG_F16;
     if (p.swiglu) {
-        if (f16) launch(q4_tile_kernel<true, true>, grid, block, 0, s, p, tm, tn);
-        else launch(q4_tile_kernel<false, true>, grid, block, 0, s, p, tm, tn);
+        if (f16) launch(q4_tile_kernel<true, true, false>, grid, block, 0, s, p, tm, tn);
+        else launch(q4_tile_kernel<false, true, false>, grid, block, 0, s, p, tm, tn);
+    } else if (p.split) {
+        if (f16) launch(q4_tile_kernel<true, false, true>, grid, block, 0, s, p, tm, tn);
+        else launch(q4_tile_kernel<false, false, true>, grid, block, 0, s, p, tm, tn);
     } else {
-        if (f16) launch(q4_tile_kernel<true, false>, grid, block, 0, s, p, tm, tn);
-        else launch(q4_tile_kernel<false, false>, grid, block, 0, s, p, tm, tn);
+        if (f16) launch(q4_tile_kernel<true, false, false>, grid, block, 0, s, p, tm, tn);
+        else launch(q4_tile_kernel<false, false, false>, grid, block, 0, s, p, tm, tn);
     }
     return hipGetLastError();
 }
