@@ -412,7 +412,9 @@ hipError_t launch_tile(const Problem& p, hipStream_t s, int variant) {
     if (p.M == 0 || p.N == 0) return hipSuccess;
     // 256 x 256 weight tiles: the direct-to-LDS pipeline (tile_dma.hip)
     if (variant == 0 && tile_dma_fits(p)) return launch_tile_dma(p, s);
-    if (p.fp8) return variant == 0 ? launch_fp8<256, 256>(p, s) : launch_fp8<128, 128>(p, s);
+    // MX FP8 weights: 128 x 128 tiles only (the 256 x 256 form with the FP8
+    // loader spills its registers)
+    if (p.fp8) return launch_fp8<128, 128>(p, s);
     const bool f16 = p.dtype == SG_F16;
     if (variant == 0) return f16 ? launch_mode<256, 256, true>(p, s) : launch_mode<256, 256, false>(p, s);
     return f16 ? launch_mode<128, 128, true>(p, s) : launch_mode<128, 128, false>(p, s);
