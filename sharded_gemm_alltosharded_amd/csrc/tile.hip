@@ -357,7 +357,7 @@ __global__ __launch_bounds__(256) void tile_kernel(Problem p, int tiles_m, int t
                     n = n0 + (blk32 >> 1) * 32 + 8 * blk + 4 * hi;
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        v[e] = silu_f32(acc[i][j][4 * blk + e]) * acc[i + 1][j][4 * blk + e];
+                        v[e] = silu_f32(acc[i][j][4 * blk + e]) * acc[i | 1][j][4 * blk + e];  // i even: i | 1 = i + 1
                 } else {
                     n = n0 + wave_n * WTN + i * 32 + 8 * blk + 4 * hi;
 #pragma unroll

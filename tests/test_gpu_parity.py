@@ -211,10 +211,12 @@ def test_mlp_entry_point(case):
     assert torch.equal(y16, sg.sharded_to_all(dn, h))
 
 
-@pytest.mark.parametrize("B", [1, 8, 16, 32])
+@pytest.mark.parametrize("B", [1, 8, 16, 32, 40, 200])
 def test_mlp_entry_point_quantized(B):
-    """MX FP8 and 4-bit layers (streaming kernels, h fragment-major in each
-    down kernel's k order) against the separate calls, bitwise."""
+    """MX FP8 and 4-bit layers against the separate calls, bitwise: up to 32
+    tokens the streaming kernels with h fragment-major in each down kernel's k
+    order, beyond that the tile kernels (the 4-bit down layer split by rank
+    through the fused call's workspace)."""
     D, F, P = 512, 1024, 4
     _print_case(B=B, D=D, F=F, P=P)
     ws = [synth.uniform(33 + i, shp, 1 / np.sqrt(D), "f32") for i, shp in enumerate([(F, D), (F, D), (D, F)])]
