@@ -6,15 +6,16 @@
 //     sum_k w[n,k] x[t,k] = s[n,g] * sum_k q[n,k] x[t,k] + b[n,g] * sum_k x[t,k]
 // The codes stay exact: a mask-and-or turns eight 4-bit codes into eight
 // 16-bit numbers c + q with c = 128 (bf16) or 1024 (fp16), so the MFMA forms
-// acc = sum (c + q) x = sum q x + c * xs, and the epilogue of the group adds
+// acc = sum (c + q) x = sum q x + c * xs per group, and the group adds
 //     s * acc + (b - c * s) * xs,
-// where xs = sum_k x[t,k] comes from one more MFMA, of an all-ones operand
-// against the token fragments.  The scale term is one FMA per accumulator per
-// group; the bias term sum_g (b - c s)[n,g] xs[t,g] is itself a small product
-// over the groups, run on the fp32 MFMA (v_mfma_f32_32x32x2f32) per pair of
-// groups straight into the same accumulators, which halves the vector-unit
-// work of a group (the kernel is issue-bound on the vector unit, not on HBM)
-// once there are more than 8 tokens.
+// where xs = sum_k x[t,k] comes from one more MFMA against an all-ones
+// operand.  With up to 8 tokens both terms are FMAs on the accumulators (xs in
+// their layout).  Beyond 8 tokens (MB) the scale term stays one FMA per
+// accumulator per group, while the bias term sum_g (b - c s)[n,g] xs[t,g] --
+// itself a small product over the groups -- runs on the fp32 MFMA
+// (v_mfma_f32_32x32x2f32) per pair of groups straight into the accumulators,
+// which halves the vector-unit work of a group (the kernel is issue-bound on
+// the vector unit, not on HBM).
 //
 // MFMA v_mfma_f32_32x32x16: the tokens are the row operand (32 token slots),
 // 32 weight rows the column operand, so each lane owns one weight row and
@@ -27,10 +28,10 @@
 // Workgroup = NW waves on RB blocks of 32 rows (gate/up pairs for SwiGLU)
 // across every rank; a wave takes one (rank, part) unit for all RB row blocks
 // (one activation fragment serves RB of them; codes are read once, with
-// non-temporal loads) and walks that rank's groups in
-// runs of 4 (scales and biases arrive 8 bytes at a time), runs j, j + J, ...  Unit partials land in LDS slots and are summed in
-// part order, then rank order -- the fused all_sum, as in the dense streaming
-// kernel -- with no cross-workgroup traffic.
+// non-temporal loads) and walks that rank's groups in runs of 4 (scales and
+// biases arrive 8 bytes at a time), runs j, j + J, ...  Unit partials land in
+// LDS slots and are summed in part order, then rank order -- the fused
+// all_sum, as in the dense streaming kernel -- with no cross-workgroup traffic.
 #include "internal.h"
 
 namespace sg {

@@ -21,7 +21,10 @@
 // buffered, 16-byte chunks XOR-swizzled by (row ^ row >> 3) & 7).  The group
 // sum of the activations is one more MFMA per step, of an all-ones operand
 // against the token fragments.  Ranks of a sharded-to-all layer are the K
-// segments of the loop, summed in order in registers.  Two workgroups per CU
+// segments of the loop, summed in order in registers, or (SPLIT, when the
+// output gives too few tiles to fill the chip) one workgroup per rank and
+// tile, the partial tiles stored in the caller's workspace and added in rank
+// order by the last of a tile's workgroups to arrive.  Two workgroups per CU
 // (two waves per SIMD) so that one wave's loads and barrier waits overlap the
 // other's matrix work.
 #include "internal.h"
