@@ -219,7 +219,7 @@ sg::SplitLayout split_layout(const sg_layer* l, Kind k, int64_t B) {
     case K_TILE1: return sg::tile_split_layout((int)B, (int)l->out_dims, l->P, 1);
     case K_Q4TILE: {
         const size_t t = (size_t)sg::q4_tile_count((int)B, (int)l->out_dims);
-        return {t * 128 * 128 * l->P, t};
+        return {t * (size_t)sg::q4_tile_rows((int)B) * 128 * l->P, t};
     }
     default: return {0, 0};
     }

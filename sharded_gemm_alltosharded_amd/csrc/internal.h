@@ -152,7 +152,8 @@ hipError_t launch_q4(const Problem& p, hipStream_t s);
 hipError_t launch_q4s(const Problem& p, hipStream_t s);  // 16-row blocks, M <= 32, Kseg % 256 == 0
 hipError_t launch_q4_tile(const Problem& p, hipStream_t s);  // 4-bit, many tokens (q4tile.hip)
 bool q4_tile_fits(const Problem& p);
-int q4_tile_count(int M, int N);  // 128 x 128 output tiles of the 4-bit tile kernel (no SwiGLU)
+int q4_tile_count(int M, int N);  // output tiles of the 4-bit tile kernel (no SwiGLU): q4_tile_rows(M) x 128
+int q4_tile_rows(int M);           // its token tile: 64 up to 64 tokens, else 128
 // P stacked (rows, K) 16-bit matrices: row-major -> fragment-major (forward) or back
 hipError_t frag_transform(void* dst, const void* src, int P, int64_t rows, int64_t K, int forward, hipStream_t s);
 // SUMMA's A (K, N) -> q fragment-major blocks of A_t^T (N, K / q); N % 16 == 0, (K / q) % 32 == 0

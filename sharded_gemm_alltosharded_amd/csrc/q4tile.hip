@@ -9,8 +9,8 @@
 // sum_g (b - C s)[n,g] xs[t,g], itself a product over the groups, runs on the
 // fp32 MFMA per pair of groups into the same accumulators.
 //
-// Workgroup: 4 waves (2 x 2) on 128 tokens x 128 weight rows (SwiGLU: 64
-// gate rows and the 64 matching up rows, 64 outputs), one k tile per
+// Workgroup: 4 waves (2 x 2) on 64 or 128 tokens x 128 weight rows (SwiGLU:
+// 64 gate rows and the 64 matching up rows, 64 outputs), one k tile per
 // quantization group (64 inputs).  v_mfma_f32_32x32x16 with the tokens as the
 // row operand and the weight rows as the column operand gives each lane one
 // weight row per 32-row block, so each lane needs one (scale, bias) per group.
@@ -70,9 +70,9 @@ __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
 }  // namespace
 
-template <bool F16, bool SWIGLU, bool SPLIT>
+template <bool F16, bool SWIGLU, bool SPLIT, int NMB>
 __global__ __launch_bounds__(256, 2) void q4_tile_kernel(Problem p, int tiles_m, int tiles_n) {
-    constexpr int BM = 128, BN = 128, BK = 64;
+    constexpr int BM = 64 * NMB, BN = 128, BK = 64;  // NMB 32-token blocks per wave
     constexpr int NOUT = SWIGLU ? BN / 2 : BN;  // logical columns per tile
     constexpr float C = F16 ? 1024.f : 128.f;
     __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * BK];
@@ -92,10 +92,11 @@ __global__ __launch_bounds__(256, 2) void q4_tile_kernel(Problem p, int tiles_m,
 
     // activation loader: thread -> rows lrow + 32 i, 16-byte chunk lch; tokens
     // past M read token 0 (no branch on the loads) and are never stored
+    constexpr int NLD = BM / 32;
     const int lrow = tid >> 3, lch = tid & 7;
-    int64_t aoff[4];
+    int64_t aoff[NLD];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NLD; ++i) {
         const int m = m0 + lrow + 32 * i;
         aoff[i] = (int64_t)(m < p.M ? m : 0) * p.lda + lch * 8;
     }
@@ -120,16 +121,16 @@ __global__ __launch_bounds__(256, 2) void q4_tile_kernel(Problem p, int tiles_m,
         goff[nb] = q4_group_offset(row, 0, p.ldg);     // group g at + 128 (g / 4) + g % 4 (halves)
     }
 
-    u32x4 ra[4];
+    u32x4 ra[NLD];
     auto gload = [&](int gl) {
         const int gi = g_lo + gl, s = gi / G, g = gi - s * G;
         const uint16_t* Ab = (const uint16_t*)p.A + s * p.a_seg + g * 64;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ra[i] = *(const u32x4*)(Ab + aoff[i]);
+        for (int i = 0; i < NLD; ++i) ra[i] = *(const u32x4*)(Ab + aoff[i]);
     };
     auto sstore = [&](int buf) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < NLD; ++i) {
             const int row = lrow + 32 * i;
             *(u32x4*)(&sA[buf][row * BK + ((lch ^ swz(row)) << 3)]) = ra[i];
         }
@@ -151,12 +152,12 @@ __global__ __launch_bounds__(256, 2) void q4_tile_kernel(Problem p, int tiles_m,
         }
     };
 
-    f32x16 y[2][2];
+    f32x16 y[2][NMB];
     const f32x16 zero16 = {};
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) y[nb][mb] = zero16;
+        for (int mb = 0; mb < NMB; ++mb) y[nb][mb] = zero16;
     const u32x4 ones = F16 ? u32x4{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u}
                            : u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
     uint32_t mask, magic;
@@ -173,7 +174,7 @@ __global__ __launch_bounds__(256, 2) void q4_tile_kernel(Problem p, int tiles_m,
     // The bias term sum_g (b - C s)[n,g] xs[t,g] runs on the fp32 MFMA per pair
     // of groups (its 2 k = the pair): lane (l & 31, h) supplies xs of token
     // l & 31 and (b - C s) of its row, both of group 2 p + h.
-    float xa[2] = {0.f, 0.f}, bq[2] = {0.f, 0.f};
+    float xa[NMB] = {}, bq[2] = {0.f, 0.f};
     for (int gi = 0; gi < ngroups; ++gi) {
         const int buf = gi & 1;
         const u32x4 cwc[2] = {cw[0], cw[1]};
@@ -185,17 +186,17 @@ __global__ __launch_bounds__(256, 2) void q4_tile_kernel(Problem p, int tiles_m,
         }
         // activation chunks 4h + u of the wave's two token blocks
         const uint16_t* a = sA[buf];
-        u32x4 xf[2][4];
+        u32x4 xf[NMB][4];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-            const int row = wave_m * 64 + mb * 32 + frow;
+        for (int mb = 0; mb < NMB; ++mb) {
+            const int row = wave_m * (32 * NMB) + mb * 32 + frow;
 #pragma unroll
             for (int u = 0; u < 4; ++u) xf[mb][u] = *(const u32x4*)(a + row * BK + (((4 * h + u) ^ swz(row)) << 3));
         }
         // ones (A) x tokens (B): every register of lane l holds xs of token l & 31
         const bool mine = (gi & 1) == h;
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
+        for (int mb = 0; mb < NMB; ++mb) {
             f32x16 xs = zero16;
 #pragma unroll
             for (int u = 0; u < 4; ++u) xs = mfma32<F16>(ones, xf[mb][u], xs);
@@ -208,7 +209,7 @@ __global__ __launch_bounds__(256, 2) void q4_tile_kernel(Problem p, int tiles_m,
 #pragma unroll
             for (int u = 0; u < 4; ++u) wf[u] = unpack8(cwc[nb][u], mask, magic);
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
+            for (int mb = 0; mb < NMB; ++mb) {
                 f32x16 acc = zero16;
 #pragma unroll
                 for (int u = 0; u < 4; ++u) acc = mfma32<F16>(xf[mb][u], wf[u], acc);
@@ -220,12 +221,15 @@ __global__ __launch_bounds__(256, 2) void q4_tile_kernel(Problem p, int tiles_m,
         // the lanes of the missing group then hold its xs = 0 contribution)
         if ((gi & 1) || gi + 1 == ngroups) {
             if (!(gi & 1)) {  // last group of an odd count: no partner group
-                if (h) { xa[0] = 0.f; xa[1] = 0.f; }
+                if (h) {
+#pragma unroll
+                    for (int mb = 0; mb < NMB; ++mb) xa[mb] = 0.f;
+                }
             }
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-                for (int mb = 0; mb < 2; ++mb) y[nb][mb] = mfma32_f32(xa[mb], bq[nb], y[nb][mb]);
+                for (int mb = 0; mb < NMB; ++mb) y[nb][mb] = mfma32_f32(xa[mb], bq[nb], y[nb][mb]);
         }
         if (gi + 1 < ngroups) sstore(buf ^ 1);
         __syncthreads();
@@ -240,10 +244,10 @@ __global__ __launch_bounds__(256, 2) void q4_tile_kernel(Problem p, int tiles_m,
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
+            for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    mine[((nb * 2 + mb) * 4 + q) * 256 + tid] =
+                    mine[((nb * NMB + mb) * 4 + q) * 256 + tid] =
                         f32x4{y[nb][mb][4 * q], y[nb][mb][4 * q + 1], y[nb][mb][4 * q + 2], y[nb][mb][4 * q + 3]};
         __threadfence();
         __syncthreads();
@@ -259,16 +263,16 @@ __global__ __launch_bounds__(256, 2) void q4_tile_kernel(Problem p, int tiles_m,
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) y[nb][mb] = zero16;
+            for (int mb = 0; mb < NMB; ++mb) y[nb][mb] = zero16;
         for (int sr = 0; sr < p.nseg; ++sr) {  // rank order
             const f32x4* src = (const f32x4*)(p.ws + sr * slab + (int64_t)tile * BM * BN);
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-                for (int mb = 0; mb < 2; ++mb)
+                for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const f32x4 v = src[((nb * 2 + mb) * 4 + q) * 256 + tid];
+                        const f32x4 v = src[((nb * NMB + mb) * 4 + q) * 256 + tid];
 #pragma unroll
                         for (int e = 0; e < 4; ++e) y[nb][mb][4 * q + e] += v[e];
                     }
@@ -277,11 +281,11 @@ __global__ __launch_bounds__(256, 2) void q4_tile_kernel(Problem p, int tiles_m,
 
     // epilogue: lane l of a 32 x 32 block holds weight row l & 31 (column) and
     // tokens 8 j + 4 (l >> 5) + e (rows)
-    static_for<0, 2>([&](auto mc) {
+    static_for<0, NMB>([&](auto mc) {
         constexpr int mb = decltype(mc)::value;
         static_for<0, 16>([&](auto rc) {
             constexpr int r = decltype(rc)::value;
-            const int m = m0 + wave_m * 64 + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+            const int m = m0 + wave_m * (32 * NMB) + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
             if (m >= p.M) return;
             if constexpr (SWIGLU) {
                 const int64_t n = n0 + wave_n * 32 + (lane & 31);
@@ -311,24 +315,46 @@ bool q4_tile_fits(const Problem& p) {
            (p.out_map == OUT_ROWMAJOR || p.out_map == OUT_SHARDED) && !(p.split && p.swiglu);
 }
 
-int q4_tile_count(int M, int N) { return ((M + 127) / 128) * ((N + 127) / 128); }
+// Token tile, 64 (one 32-token block per wave: half the accumulators, three
+// workgroups per CU) or 128, measured on the decode MLP shapes from 40 to 1024
+// tokens: the gate|up layer is faster on 64-token tiles up to 192 tokens
+// (128 tokens: 85 against 97 us); the down layer (4096 outputs) on 128-token
+// tiles split by rank from 65 to 256 tokens (256 tokens: 158 against 208 us)
+// and on 64-token tiles beyond, where they fill the chip without the split
+// (512 tokens: 184 against 269 us).
+static int q4_tile_bm(int M, bool swiglu) {
+    if (swiglu) return M <= 192 ? 64 : 128;
+    return (M > 64 && M <= 256) ? 128 : 64;
+}
+
+int q4_tile_count(int M, int N) {
+    const int bm = q4_tile_bm(M, false);
+    return ((M + bm - 1) / bm) * ((N + 127) / 128);
+}
+int q4_tile_rows(int M) { return q4_tile_bm(M, false); }
+
+template <bool F16, bool SWIGLU, bool SPLIT>
+static void launch_nmb(const Problem& p, hipStream_t s, dim3 grid, int tm, int tn) {
+    if (q4_tile_bm(p.M, SWIGLU) == 64) launch(q4_tile_kernel<F16, SWIGLU, SPLIT, 1>, grid, dim3(256), 0, s, p, tm, tn);
+    else launch(q4_tile_kernel<F16, SWIGLU, SPLIT, 2>, grid, dim3(256), 0, s, p, tm, tn);
+}
 
 hipError_t launch_q4_tile(const Problem& p, hipStream_t s) {
     if (p.M == 0 || p.N == 0) return hipSuccess;
     if (!q4_tile_fits(p)) return hipErrorInvalidValue;
-    const int nout = p.swiglu ? 64 : 128;
-    const int tm = (p.M + 127) / 128, tn = (p.N + nout - 1) / nout;
-    const dim3 grid(tm * tn, p.split ? p.nseg : 1), block(256);
+    const int nout = p.swiglu ? 64 : 128, bm = q4_tile_bm(p.M, p.swiglu);
+    const int tm = (p.M + bm - 1) / bm, tn = (p.N + nout - 1) / nout;
+    const dim3 grid(tm * tn, p.split ? p.nseg : 1);
     const bool f16 = p.dtype == SG_F16;
     if (p.swiglu) {
-        if (f16) launch(q4_tile_kernel<true, true, false>, grid, block, 0, s, p, tm, tn);
-        else launch(q4_tile_kernel<false, true, false>, grid, block, 0, s, p, tm, tn);
+        if (f16) launch_nmb<true, true, false>(p, s, grid, tm, tn);
+        else launch_nmb<false, true, false>(p, s, grid, tm, tn);
     } else if (p.split) {
-        if (f16) launch(q4_tile_kernel<true, false, true>, grid, block, 0, s, p, tm, tn);
-        else launch(q4_tile_kernel<false, false, true>, grid, block, 0, s, p, tm, tn);
+        if (f16) launch_nmb<true, false, true>(p, s, grid, tm, tn);
+        else launch_nmb<false, false, true>(p, s, grid, tm, tn);
     } else {
-        if (f16) launch(q4_tile_kernel<true, false, false>, grid, block, 0, s, p, tm, tn);
-        else launch(q4_tile_kernel<false, false, false>, grid, block, 0, s, p, tm, tn);
+        if (f16) launch_nmb<true, false, false>(p, s, grid, tm, tn);
+        else launch_nmb<false, false, false>(p, s, grid, tm, tn);
     }
     return hipGetLastError();
 }
