@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--config", default="2", choices=["1", "2", "3", "4", "5a", "5b", "5c", "6", "7"])
     ap.add_argument("--batch", type=int, default=1, help="tokens for the 4-bit workload (1, 8 or 32)")
     ap.add_argument("--summa", default="fused", choices=["fused", "steps"])
+    ap.add_argument("--rank-share", action="store_true",
+                    help="configs 2, 3, 4, 5b: only rank 0's share of the layers (P = 1, the per-GPU shapes "
+                         "of a deployment with one rank per GPU; the rank-order reduction across GPUs is not run)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay measurement")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MiB",
@@ -97,6 +100,18 @@ class Workload:
     # weights as in the step), for timing it in a back-to-back burst; None when
     # no call launches it alone (its own start/end events are used instead).
     dominant_call = None
+
+    # rank 0's share alone (--rank-share): what one GPU of a one-rank-per-GPU
+    # deployment computes locally; None where the workload has no such form
+    rank_share = None
+
+    def _share(self, copies_bytes):
+        """Shrink to P = 1 and rotate enough weight copies (>= 512 MB) that the
+        Infinity Cache cannot hold them; copies_bytes = one copy's weight bytes."""
+        self.share_of = self.P
+        self.P = 1
+        self.rotate = max(2, -(-(512 << 20) // copies_bytes))
+        self.name += "-rank-share"
 
 
 def _dev_tensor(a, dtype):
@@ -151,9 +166,16 @@ class DecodeMLP(Workload):
         # workspace; here row-major, the same kernel and weight stream)
         self.sg.all_to_sharded(self.gu[i % self.rotate], self.x, swiglu=True, out=self.hbuf)
 
+    def rank_share(self):
+        self.F //= self.P
+        self._share(2 * 3 * self.F * self.D)
+
     def config(self):
-        return {"workload": self.name, "tokens": self.B, "D": self.D, "F": self.F, "P": self.P,
-                "weight_copies_rotated": self.rotate}
+        c = {"workload": self.name, "tokens": self.B, "D": self.D, "F": self.F, "P": self.P,
+             "weight_copies_rotated": self.rotate}
+        if getattr(self, "share_of", None):
+            c["share_of_ranks"] = self.share_of
+        return c
 
     def cpu_baseline(self):
         import oracle
@@ -216,9 +238,17 @@ class PrefillMLP(Workload):
     def dominant_call(self, i):
         self.sg.all_to_sharded(self.gu, self.x, swiglu=True, out=self.h)
 
+    def rank_share(self):
+        self.F //= self.P
+        self.H //= self.P
+        self._share(2 * (3 * self.H * self.HD + 3 * self.F) * self.D)
+
     def config(self):
-        return {"workload": self.name, "tokens": self.B, "D": self.D, "F": self.F, "P": self.P,
-                "qkv": f"{self.H} heads x {self.HD}, segments=3"}
+        c = {"workload": self.name, "tokens": self.B, "D": self.D, "F": self.F, "P": self.P,
+             "qkv": f"{self.H} heads x {self.HD}, segments=3"}
+        if getattr(self, "share_of", None):
+            c["share_of_ranks"] = self.share_of
+        return c
 
     def cpu_baseline(self):
         import oracle
@@ -293,9 +323,16 @@ class Q4MLP(Workload):
     def dominant_call(self, i):
         self.sg.all_to_sharded(self.gu[i % self.rotate], self.x, swiglu=True, out=self.hbuf)
 
+    def rank_share(self):
+        self.F //= self.P
+        self._share(3 * self.F * self.D * 9 // 16)  # 4.5 bits per weight
+
     def config(self):
-        return {"workload": self.name, "tokens": self.B, "D": self.D, "F": self.F, "P": self.P,
-                "group_size": 64, "bits": 4, "weight_copies_rotated": self.rotate}
+        c = {"workload": self.name, "tokens": self.B, "D": self.D, "F": self.F, "P": self.P,
+             "group_size": 64, "bits": 4, "weight_copies_rotated": self.rotate}
+        if getattr(self, "share_of", None):
+            c["share_of_ranks"] = self.share_of
+        return c
 
     def cpu_baseline(self):
         import oracle
@@ -441,7 +478,7 @@ class VocabHead(Workload):
         self.x = _dev_tensor(self.Xh, "f16")
         wt = _dev_tensor(Wh, "f16")
         self.Wh = Wh
-        self.layer = sg.shard_linear(wt, "all-to-sharded", P=self.P)
+        self.layers = [sg.shard_linear(wt, "all-to-sharded", P=self.P) for _ in range(self.rotate)]
         del wt
         self.y = torch.empty((self.B, self.V), dtype=torch.float16, device="cuda")
         self.sg = sg
@@ -451,14 +488,21 @@ class VocabHead(Workload):
     def step(self, i, ev=None):
         if ev:
             self.sg.time_next_launch(*ev)
-        self.sg.all_to_sharded(self.layer, self.x, gather=True, out=self.y)
+        self.sg.all_to_sharded(self.layers[i % self.rotate], self.x, gather=True, out=self.y)
 
     def dominant_call(self, i):
-        self.sg.all_to_sharded(self.layer, self.x, gather=True, out=self.y)
+        self.sg.all_to_sharded(self.layers[i % self.rotate], self.x, gather=True, out=self.y)
+
+    def rank_share(self):
+        self.V //= self.P
+        self._share(2 * self.V * self.Hd)
 
     def config(self):
-        return {"workload": self.name, "tokens": self.B, "hidden": self.Hd, "vocab": self.V, "P": self.P,
-                "rows_per_rank": self.V // self.P}
+        c = {"workload": self.name, "tokens": self.B, "hidden": self.Hd, "vocab": self.V, "P": self.P,
+             "rows_per_rank": self.V // self.P}
+        if getattr(self, "share_of", None):
+            c["share_of_ranks"] = self.share_of
+        return c
 
     def cpu_baseline(self):
         import oracle
@@ -663,10 +707,15 @@ class BackwardMLP(Workload):
 
 
 def make(args) -> Workload:
-    return {"1": lambda: Tiny(), "2": lambda: DecodeMLP(), "3": lambda: PrefillMLP(),
-            "4": lambda: Q4MLP(args.batch), "5a": lambda: Summa(args.summa == "fused"),
-            "5b": lambda: VocabHead(), "6": lambda: MxfpDecodeMLP(), "7": lambda: BackwardMLP(),
-            "5c": lambda: SummaBackward()}[args.config]()
+    wl = {"1": lambda: Tiny(), "2": lambda: DecodeMLP(), "3": lambda: PrefillMLP(),
+          "4": lambda: Q4MLP(args.batch), "5a": lambda: Summa(args.summa == "fused"),
+          "5b": lambda: VocabHead(), "6": lambda: MxfpDecodeMLP(), "7": lambda: BackwardMLP(),
+          "5c": lambda: SummaBackward()}[args.config]()
+    if getattr(args, "rank_share", False):
+        if wl.rank_share is None:
+            raise SystemExit(f"--rank-share: config {args.config} has no per-rank form (configs 2, 3, 4, 5b)")
+        wl.rank_share()
+    return wl
 
 
 # ---------------------------------------------------------------------------

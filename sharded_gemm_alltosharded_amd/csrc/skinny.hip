@@ -227,8 +227,11 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(Problem p) {
 // Shape choice (from a sweep of RB, NW and U on the decode gate|up, down and
 // vocabulary-head shapes): as many row blocks per wave as still leave about
 // 1500 waves on the chip (each activation fragment then serves RB weight
-// fragments), the fewest waves per workgroup that reach that, at least one
-// wave per rank, and LDS slots within kMaxStreamLds.
+// fragments) and workgroups for at least three quarters of the 256 CUs, the
+// fewest waves per workgroup that reach that, at least one wave per rank, and
+// LDS slots within kMaxStreamLds.  (Without the workgroup floor, one rank's
+// share of the vocabulary head -- 6284 rows -- ran 99 workgroups of 8 waves:
+// 95.6 us, against 66.8 us on 197 of 4.)
 SkinnyShape skinny_shape(int M, int N, int nseg, int swiglu) {
     SkinnyShape sh;
     sh.MT = M <= 16 ? 1 : 2;
@@ -249,7 +252,7 @@ SkinnyShape skinny_shape(int M, int N, int nseg, int swiglu) {
         int nw = 2;
         while (nw < 8 && (wgs * nw < target || nw < nseg || lds_of(rb, nw) > kMaxStreamLds)) nw *= 2;
         while (nw > 2 && lds_of(rb, nw) > kMaxStreamLds) nw /= 2;
-        if ((wgs * nw >= target && lds_of(rb, nw) <= kMaxStreamLds) || rb == (swiglu ? 2 : 1)) {
+        if ((wgs * nw >= target && wgs >= 192 && lds_of(rb, nw) <= kMaxStreamLds) || rb == (swiglu ? 2 : 1)) {
             sh.RB = rb;
             sh.NW = nw;
             break;
