@@ -76,3 +76,32 @@ def test_mlp_static_rejects_beyond_the_scratch():
     yf = torch.empty((Bf, D), dtype=torch.float32, device=dev())
     sg.mlp_static(gu, dn, xf, yf)
     assert torch.equal(yf, sg.mlp(gu, dn, xf, out_dtype=torch.float32))
+
+
+def _q4(w, mode, P, S=1):
+    packed, s, b, _ = synth.quantize_q4(w, 64)
+    return sg.shard_quantized_linear(torch.from_numpy(packed.view(np.int32)).to(dev()),
+                                     torch.from_numpy(s.view(np.int16)).to(dev()),
+                                     torch.from_numpy(b.view(np.int16)).to(dev()), w.shape[1], mode,
+                                     segments=S, P=P)
+
+
+@pytest.mark.parametrize("Bs", [(100, 24), (24, 64)], ids=lambda b: "-".join(map(str, b)))
+def test_mlp_static_quantized(Bs):
+    """4-bit layers: the tile kernels (the down layer split by rank through the
+    scratch's counters and partial tiles) and the streaming kernels (h
+    fragment-major in the scratch), two calls in a row."""
+    D, F, P = 512, 1024, 4
+    print(f"case: q4 D={D} F={F} P={P} B={Bs}", flush=True)
+    ws = [synth.uniform(70 + i, shp, 1 / np.sqrt(D), "f32") for i, shp in enumerate([(F, D), (F, D), (D, F)])]
+    gu, dn = _q4(np.concatenate([ws[0], ws[1]]), 0, P, S=2), _q4(ws[2], 1, P)
+    X = synth.normal(73, (max(Bs), D), 1.0, "bf16")
+    for B in Bs:
+        x = to_dev(X[:B], "bf16")
+        y = torch.empty((B, D), dtype=torch.float32, device=dev())
+        before = torch.cuda.memory_allocated()
+        sg.mlp_static(gu, dn, x, y)
+        assert torch.cuda.memory_allocated() == before
+        ref = sg.mlp(gu, dn, x, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref), B
