@@ -208,7 +208,10 @@ bool want_split(const sg_layer* l, Kind k, int64_t B) {
     switch (k) {
     case K_TILE0: return sg::tile_count((int)B, (int)l->out_dims, 0) * 2 <= cus;
     case K_TILE1: return sg::tile_count((int)B, (int)l->out_dims, 1) * 2 <= cus;
-    case K_Q4TILE: return sg::q4_tile_count((int)B, (int)l->out_dims) * 2 <= cus;
+    // the 4-bit tile kernel splits only below a quarter tile per CU: above,
+    // the unsplit 64-token tiles win (down projection at 192 tokens 129 against
+    // 148 us)
+    case K_Q4TILE: return sg::q4_tile_count((int)B, (int)l->out_dims) * 4 <= cus;
     default: return false;
     }
 }

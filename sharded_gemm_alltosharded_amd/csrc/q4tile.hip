@@ -26,7 +26,9 @@
 // tile, the partial tiles stored in the caller's workspace and added in rank
 // order by the last of a tile's workgroups to arrive.  Two workgroups per CU
 // (two waves per SIMD) so that one wave's loads and barrier waits overlap the
-// other's matrix work.
+// other's matrix work.  q4_tile_dma_kernel below is the same tile with every
+// operand staged by direct-to-LDS loads several groups ahead; it runs whenever
+// its 32-bit buffer offsets reach every operand.
 #include "internal.h"
 
 namespace sg {
@@ -36,6 +38,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 namespace {
 
@@ -68,7 +71,117 @@ __device__ __forceinline__ f32x16 mfma32_f32(float a, float b, f32x16 c) {
 
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
+// direct-to-LDS loads (each lane's bytes land at the wave's LDS base + size x
+// lane) through buffer resources, and LDS reads issued as inline assembly so
+// that the compiler's wait insertion does not hold them behind the loads still
+// in flight (the caller waits for them with wait_lgkm, which ties the registers)
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, voff, soff, 0, 0);
+}
+__device__ __forceinline__ u32x4 lds16(const void* p) {
+    const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+    u32x4 r;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(a));
+    return r;
+}
+__device__ __forceinline__ u32x2 lds8(const void* p) {
+    const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+    u32x2 r;
+    asm volatile("ds_read_b64 %0, %1" : "=v"(r) : "v"(a));
+    return r;
+}
+// s_waitcnt vmcnt(N) (N <= 63), other counters untouched
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+__device__ __forceinline__ int swz8(int row) { return (row >> 1) & 7; }
+
 }  // namespace
+
+// Cross-segment reduction (split by rank: every workgroup stores its partial
+// tile, and the last of a tile's nseg to arrive adds them in rank order) and
+// the stores of a finished tile.
+template <bool SWIGLU, bool SPLIT, int NMB>
+__device__ __forceinline__ void q4_tile_finish(const Problem& p, f32x16 (&y)[2][NMB], int tiles_m, int tiles_n,
+                                               int tile, int m0, int64_t n0, int wave_m, int wave_n,
+                                               const bool (&nok)[2]) {
+    constexpr int BM = 64 * NMB, BN = 128;
+    const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
+    const f32x16 zero16 = {};
+    if constexpr (SPLIT) {
+        const int ntiles = tiles_m * tiles_n;
+        const int64_t slab = (int64_t)ntiles * BM * BN;  // floats per segment
+        f32x4* mine = (f32x4*)(p.ws + blockIdx.y * slab + (int64_t)tile * BM * BN);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    mine[((nb * NMB + mb) * 4 + q) * 256 + tid] =
+                        f32x4{y[nb][mb][4 * q], y[nb][mb][4 * q + 1], y[nb][mb][4 * q + 2], y[nb][mb][4 * q + 3]};
+        __threadfence();
+        __syncthreads();
+        __shared__ int last;
+        if (tid == 0) {
+            const unsigned prev = atomicAdd(&p.counters[tile], 1u);
+            last = prev == (unsigned)p.nseg - 1;
+            if (last) p.counters[tile] = 0u;  // ready for the next call
+        }
+        __syncthreads();
+        if (!last) return;
+        __threadfence();
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb) y[nb][mb] = zero16;
+        for (int sr = 0; sr < p.nseg; ++sr) {  // rank order
+            const f32x4* src = (const f32x4*)(p.ws + sr * slab + (int64_t)tile * BM * BN);
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const f32x4 v = src[((nb * NMB + mb) * 4 + q) * 256 + tid];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) y[nb][mb][4 * q + e] += v[e];
+                    }
+        }
+    }
+
+    // epilogue: lane l of a 32 x 32 block holds weight row l & 31 (column) and
+    // tokens 8 j + 4 (l >> 5) + e (rows)
+    static_for<0, NMB>([&](auto mc) {
+        constexpr int mb = decltype(mc)::value;
+        static_for<0, 16>([&](auto rc) {
+            constexpr int r = decltype(rc)::value;
+            const int m = m0 + wave_m * (32 * NMB) + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (m >= p.M) return;
+            if constexpr (SWIGLU) {
+                const int64_t n = n0 + wave_n * 32 + (lane & 31);
+                if (!nok[0]) return;
+                const float v = silu_f32(y[0][mb][r]) * y[1][mb][r];
+                store_from_f32(p.out, p.out_dtype, out_index(p, m, n), v);
+            } else {
+                static_for<0, 2>([&](auto nc) {
+                    constexpr int nb = decltype(nc)::value;
+                    const int64_t n = n0 + wave_n * 64 + nb * 32 + (lane & 31);
+                    if (!nok[nb]) return;
+                    float v = y[nb][mb][r];
+                    if (p.bias) v += load_as_f32(p.bias, p.dtype, n);
+                    const int64_t o = out_index(p, m, n);
+                    if (p.accumulate && p.out_dtype == SG_F32) v += ((const float*)p.out)[o];
+                    store_from_f32(p.out, p.out_dtype, o, v);
+                });
+            }
+        });
+    });
+}
 
 template <bool F16, bool SWIGLU, bool SPLIT, int NMB>
 __global__ __launch_bounds__(256, 2) void q4_tile_kernel(Problem p, int tiles_m, int tiles_n) {
@@ -235,77 +348,201 @@ __global__ __launch_bounds__(256, 2) void q4_tile_kernel(Problem p, int tiles_m,
         __syncthreads();
     }
 
-    // cross-segment reduction (split by rank): every workgroup stores its
-    // partial tile; the last of a tile's nseg to arrive adds them in rank order
-    if constexpr (SPLIT) {
-        const int ntiles = tiles_m * tiles_n;
-        const int64_t slab = (int64_t)ntiles * BM * BN;  // floats per segment
-        f32x4* mine = (f32x4*)(p.ws + blockIdx.y * slab + (int64_t)tile * BM * BN);
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-            for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    mine[((nb * NMB + mb) * 4 + q) * 256 + tid] =
-                        f32x4{y[nb][mb][4 * q], y[nb][mb][4 * q + 1], y[nb][mb][4 * q + 2], y[nb][mb][4 * q + 3]};
-        __threadfence();
-        __syncthreads();
-        __shared__ int last;
-        if (tid == 0) {
-            const unsigned prev = atomicAdd(&p.counters[tile], 1u);
-            last = prev == (unsigned)p.nseg - 1;
-            if (last) p.counters[tile] = 0u;  // ready for the next call
-        }
-        __syncthreads();
-        if (!last) return;
-        __threadfence();
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-            for (int mb = 0; mb < NMB; ++mb) y[nb][mb] = zero16;
-        for (int sr = 0; sr < p.nseg; ++sr) {  // rank order
-            const f32x4* src = (const f32x4*)(p.ws + sr * slab + (int64_t)tile * BM * BN);
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-                for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const f32x4 v = src[((nb * NMB + mb) * 4 + q) * 256 + tid];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) y[nb][mb][4 * q + e] += v[e];
-                    }
-        }
-    }
+    q4_tile_finish<SWIGLU, SPLIT, NMB>(p, y, tiles_m, tiles_n, tile, m0, n0, wave_m, wave_n, nok);
+}
 
-    // epilogue: lane l of a 32 x 32 block holds weight row l & 31 (column) and
-    // tokens 8 j + 4 (l >> 5) + e (rows)
-    static_for<0, NMB>([&](auto mc) {
-        constexpr int mb = decltype(mc)::value;
-        static_for<0, 16>([&](auto rc) {
-            constexpr int r = decltype(rc)::value;
-            const int m = m0 + wave_m * (32 * NMB) + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (m >= p.M) return;
-            if constexpr (SWIGLU) {
-                const int64_t n = n0 + wave_n * 32 + (lane & 31);
-                if (!nok[0]) return;
-                const float v = silu_f32(y[0][mb][r]) * y[1][mb][r];
-                store_from_f32(p.out, p.out_dtype, out_index(p, m, n), v);
-            } else {
-                static_for<0, 2>([&](auto nc) {
-                    constexpr int nb = decltype(nc)::value;
-                    const int64_t n = n0 + wave_n * 64 + nb * 32 + (lane & 31);
-                    if (!nok[nb]) return;
-                    float v = y[nb][mb][r];
-                    if (p.bias) v += load_as_f32(p.bias, p.dtype, n);
-                    const int64_t o = out_index(p, m, n);
-                    if (p.accumulate && p.out_dtype == SG_F32) v += ((const float*)p.out)[o];
-                    store_from_f32(p.out, p.out_dtype, o, v);
-                });
+// The same tile with its operands staged by direct-to-LDS loads in a ring of
+// NS group stages (activations BM x 64, the four 32-row blocks' 1 KB code
+// fragments), issued NS - 1 groups ahead, and each run's scales and biases
+// (2 x 4 blocks x 256 bytes) in two run buffers: the register-staged kernel
+// above prefetches one group ahead and waits on its code loads at every group.
+// Every wave issues the same loads in the same order (dummy loads of the last
+// group or run past the end), so the waits are compile-time counts.
+template <bool F16, bool SWIGLU, bool SPLIT, int NMB>
+__global__ __launch_bounds__(256, 2) void q4_tile_dma_kernel(Problem p, int tiles_m, int tiles_n) {
+    constexpr int BM = 64 * NMB, BN = 128;
+    constexpr int NOUT = SWIGLU ? BN / 2 : BN;
+    constexpr float C = F16 ? 1024.f : 128.f;
+    constexpr int NS = NMB == 1 ? 4 : 3;       // group stages
+    constexpr int SA = BM * 128, ST = SA + 4096;  // activation / stage bytes
+    constexpr int NA = BM / 32;                // activation loads per wave per group
+    constexpr int L = NA + 1;                  // loads per wave per group (+ codes)
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * ST + 2 * 2048];
+    uint8_t* const sscale = smem + NS * ST;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave_m = wave >> 1, wave_n = wave & 1, h = lane >> 5;
+    const int tile = xcd_remap(blockIdx.x, tiles_m * tiles_n);
+    constexpr int GM = 4;
+    const int grp = tile / (GM * tiles_n), first_m = grp * GM, gsz = min(GM, tiles_m - first_m);
+    const int tin = tile - grp * GM * tiles_n;
+    const int m0 = (first_m + tin % gsz) * BM;
+    const int64_t n0 = (int64_t)(tin / gsz) * NOUT;
+    const int G = p.Kseg / 64;
+    const int g_lo = SPLIT ? (int)blockIdx.y * G : 0;
+    const int ngroups = SPLIT ? G : G * p.nseg;  // a multiple of 4
+    const int nruns = ngroups / 4;
+
+    // rows of the wave's blocks (for the stores) and the block whose fragments
+    // and scales this wave loads: slot w = (w >> 1) wave_n, (w & 1) nb
+    bool nok[2];
+    int64_t bw;
+    {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            const int64_t j = SWIGLU ? n0 + wave_n * 32 + (lane & 31) : n0 + wave_n * 64 + nb * 32 + (lane & 31);
+            nok[nb] = j < p.N;
+        }
+        const int sn = wave >> 1, snb = wave & 1;
+        const int64_t j0 = SWIGLU ? n0 + sn * 32 : n0 + sn * 64 + snb * 32;
+        const int64_t jc = j0 < p.N ? j0 : 0;
+        bw = (SWIGLU ? weight_row(p, jc, snb) : jc) >> 5;
+    }
+    const int64_t rows = SWIGLU ? 2 * (int64_t)p.N : p.N;
+    const int64_t nblk = (rows + 31) / 32;
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)p.A, 0, (int)((((int64_t)p.nseg - 1) * p.a_seg + (int64_t)(p.M - 1) * p.lda + p.Kseg) * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)p.wq, 0, (int)((((int64_t)p.nseg - 1) * p.q_seg + nblk * p.ldg * 256) * 4), 0x00020000);
+    const int sext = (int)((((int64_t)p.nseg - 1) * p.g_seg + nblk * (p.ldg / 4) * 128) * 2);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)p.qs, 0, sext, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void*)p.qb, 0, sext, 0x00020000);
+
+    // per-lane byte offsets: activation load j covers tile rows (w + 4 j) 8 ..
+    // + 8, lane -> row lane >> 3, 16-byte chunk lane & 7 (stored at chunk
+    // (lane & 7) ^ swz8(row) of the row); the code fragment 1 KB, lane at 16
+    // lane; the scale run 256 bytes, lane at 4 lane
+    uint32_t aoffd[NA];
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
+        const int row = (wave + 4 * j) * 8 + (lane >> 3);
+        const int m = min(m0 + row, p.M - 1);
+        aoffd[j] = (uint32_t)(((int64_t)m * p.lda + (((lane & 7) ^ swz8(row)) << 3)) * 2);
+    }
+    const uint32_t coff = (uint32_t)(bw * p.ldg * 256 * 4 + lane * 16);
+    const uint32_t soffl = (uint32_t)(bw * (p.ldg / 4) * 128 * 2 + lane * 4);
+
+    // group gl's loads into stage gu % NS (gu = the unclamped slot index)
+    auto issue_group = [&](int gu) {
+        const int gl = min(gu, ngroups - 1), gi = g_lo + gl, s = gi / G, g = gi - s * G;
+        uint8_t* st = smem + (gu % NS) * ST;
+        const uint32_t as = (uint32_t)((s * p.a_seg + (int64_t)g * 64) * 2);
+#pragma unroll
+        for (int j = 0; j < NA; ++j) dma16(ra, aoffd[j], as, st + (wave + 4 * j) * 1024);
+        dma16(rq, coff, (uint32_t)((s * p.q_seg + (int64_t)g * 256) * 4), st + SA + wave * 1024);
+    };
+    auto issue_scales = [&](int ru) {
+        const int r = min(ru, nruns - 1), gi = g_lo + 4 * r, s = gi / G, g = gi - s * G;
+        uint8_t* b = sscale + (ru & 1) * 2048;
+        const uint32_t so = (uint32_t)((s * p.g_seg + (int64_t)(g >> 2) * 128) * 2);
+        dma4(rs, soffl, so, b + wave * 256);
+        dma4(rb, soffl, so, b + 1024 + wave * 256);
+    };
+
+    f32x16 y[2][NMB];
+    const f32x16 zero16 = {};
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) y[nb][mb] = zero16;
+    const u32x4 ones = F16 ? u32x4{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u}
+                           : u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    uint32_t mask, magic;
+    asm("s_mov_b32 %0, 0x000f000f" : "=s"(mask));
+    asm("v_mov_b32 %0, %1" : "=v"(magic) : "i"(F16 ? 0x64006400 : 0x43004300));
+    const int frow = lane & 31;
+
+    // prologue: groups 0 .. NS - 2 (each run's scales just before its first group)
+#pragma unroll
+    for (int u = 0; u < NS - 1; ++u) {
+        if (u % 4 == 0) issue_scales(u / 4);
+        issue_group(u);
+    }
+    float xa[NMB] = {}, bq[2] = {0.f, 0.f};
+    u32x2 sv[2], bv[2];
+    for (int base = 0; base < ngroups; base += 4) {
+        static_for<0, 4>([&](auto qc) {
+            constexpr int q = decltype(qc)::value;
+            const int gl = base + q;
+            // this wave's loads of group gl (and of its run's scales) have landed
+            // once at most the later groups' batches are outstanding
+            constexpr int extra = (NS == 4) ? ((q == 2 || q == 3) ? 2 : 0) : (q == 3 ? 2 : 0);
+            wait_vm<(NS - 2) * L + extra>();
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            // stage (gl - 1) % NS and the other run buffer are free: everyone
+            // finished reading them before this barrier
+            if ((gl + NS - 1) % 4 == 0) issue_scales((gl + NS - 1) / 4);
+            issue_group(gl + NS - 1);
+            const uint8_t* st = smem + (gl % NS) * ST;
+            u32x4 xf[NMB][4], cw[2];
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb) {
+                const int row = wave_m * (32 * NMB) + mb * 32 + frow;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) xf[mb][u] = lds16(st + row * 128 + (((4 * h + u) ^ swz8(row)) << 4));
+            }
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) cw[nb] = lds16(st + SA + (wave_n * 2 + nb) * 1024 + lane * 16);
+            if constexpr (q == 0) {
+                const uint8_t* b = sscale + ((gl >> 2) & 1) * 2048;
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb) {
+                    sv[nb] = lds8(b + (wave_n * 2 + nb) * 256 + frow * 8);
+                    bv[nb] = lds8(b + 1024 + (wave_n * 2 + nb) * 256 + frow * 8);
+                }
+                asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(sv[0]), "+v"(sv[1]), "+v"(bv[0]), "+v"(bv[1]));
+            }
+            if constexpr (NMB == 1)
+                asm volatile("s_waitcnt lgkmcnt(0)"
+                             : "+v"(xf[0][0]), "+v"(xf[0][1]), "+v"(xf[0][2]), "+v"(xf[0][3]), "+v"(cw[0]), "+v"(cw[1]));
+            else
+                asm volatile("s_waitcnt lgkmcnt(0)"
+                             : "+v"(xf[0][0]), "+v"(xf[0][1]), "+v"(xf[0][2]), "+v"(xf[0][3]),
+                               "+v"(xf[NMB - 1][0]), "+v"(xf[NMB - 1][1]), "+v"(xf[NMB - 1][2]), "+v"(xf[NMB - 1][3]),
+                               "+v"(cw[0]), "+v"(cw[1]));
+            float sc[2], bi[2];
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+                const uint32_t sw = sv[nb][q >> 1], bw2 = bv[nb][q >> 1];
+                sc[nb] = f16_to_f32((uint16_t)((q & 1) ? (sw >> 16) : (sw & 0xFFFFu)));
+                bi[nb] = f16_to_f32((uint16_t)((q & 1) ? (bw2 >> 16) : (bw2 & 0xFFFFu)));
+            }
+            // ones (A) x tokens (B): every register of lane l holds xs of token l & 31
+            const bool mine = (q & 1) == h;
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb) {
+                f32x16 xs = zero16;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) xs = mfma32<F16>(ones, xf[mb][u], xs);
+                xa[mb] = mine ? xs[0] : xa[mb];
+            }
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+                bq[nb] = mine ? fmaf(-C, sc[nb], bi[nb]) : bq[nb];
+                u32x4 wf[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) wf[u] = unpack8(cw[nb][u], mask, magic);
+#pragma unroll
+                for (int mb = 0; mb < NMB; ++mb) {
+                    f32x16 acc = zero16;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) acc = mfma32<F16>(xf[mb][u], wf[u], acc);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) y[nb][mb][r] = fmaf(sc[nb], acc[r], y[nb][mb][r]);
+                }
+            }
+            if constexpr (q & 1) {  // the pair's bias term
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                    for (int mb = 0; mb < NMB; ++mb) y[nb][mb] = mfma32_f32(xa[mb], bq[nb], y[nb][mb]);
             }
         });
-    });
+    }
+    // no load may still be writing this workgroup's LDS when it ends
+    wait_vm<0>();
+    q4_tile_finish<SWIGLU, SPLIT, NMB>(p, y, tiles_m, tiles_n, tile, m0, n0, wave_m, wave_n, nok);
 }
 
 // fragment-major codes (rows % 32 == 0, groups per segment % 4 == 0), 16-byte
@@ -316,16 +553,13 @@ bool q4_tile_fits(const Problem& p) {
 }
 
 // Token tile, 64 (one 32-token block per wave: half the accumulators, three
-// workgroups per CU) or 128, measured on the decode MLP shapes from 40 to 1024
-// tokens: the gate|up layer is faster on 64-token tiles up to 192 tokens
-// (128 tokens: 85 against 97 us); the down layer (4096 outputs) on 128-token
-// tiles split by rank from 65 to 256 tokens (256 tokens: 158 against 208 us)
-// and on 64-token tiles beyond, where they fill the chip without the split
-// (512 tokens: 184 against 269 us).
-static int q4_tile_bm(int M, bool swiglu) {
-    if (swiglu) return M <= 192 ? 64 : 128;
-    return (M > 64 && M <= 256) ? 128 : 64;
-}
+// workgroups per CU) or 128, measured with the direct-to-LDS kernel on the
+// decode MLP shapes from 40 to 512 tokens: 64-token tiles win or tie
+// everywhere (gate|up at 64 tokens 43 against 80 us, at 512 tokens 191
+// against 203 us; the down layer at 512 tokens 130 against 220 us); 128-token
+// tiles are kept beyond 512 tokens for the SwiGLU layer, where they halve the
+// weight re-reads.
+static int q4_tile_bm(int M, bool swiglu) { return (swiglu && M > 512) ? 128 : 64; }
 
 int q4_tile_count(int M, int N) {
     const int bm = q4_tile_bm(M, false);
@@ -333,10 +567,27 @@ int q4_tile_count(int M, int N) {
 }
 int q4_tile_rows(int M) { return q4_tile_bm(M, false); }
 
+// the direct-to-LDS form addresses every operand through 32-bit buffer
+// offsets, and reads a SwiGLU layer's gate and up rows as whole 32-row blocks
+static bool q4_tile_dma_fits(const Problem& p) {
+    if (p.swiglu && p.floc % 32) return false;
+    const int64_t rows = p.swiglu ? 2 * (int64_t)p.N : p.N, nblk = (rows + 31) / 32;
+    const int64_t a = (((int64_t)p.nseg - 1) * p.a_seg + (int64_t)(p.M - 1) * p.lda + p.Kseg) * 2;
+    const int64_t q = (((int64_t)p.nseg - 1) * p.q_seg + nblk * p.ldg * 256) * 4;
+    const int64_t g = (((int64_t)p.nseg - 1) * p.g_seg + nblk * (p.ldg / 4) * 128) * 2;
+    return a < (1LL << 31) && q < (1LL << 31) && g < (1LL << 31) && p.ldg % 4 == 0;
+}
+
 template <bool F16, bool SWIGLU, bool SPLIT>
 static void launch_nmb(const Problem& p, hipStream_t s, dim3 grid, int tm, int tn) {
-    if (q4_tile_bm(p.M, SWIGLU) == 64) launch(q4_tile_kernel<F16, SWIGLU, SPLIT, 1>, grid, dim3(256), 0, s, p, tm, tn);
-    else launch(q4_tile_kernel<F16, SWIGLU, SPLIT, 2>, grid, dim3(256), 0, s, p, tm, tn);
+    const bool nmb1 = q4_tile_bm(p.M, SWIGLU) == 64;
+    if (q4_tile_dma_fits(p)) {
+        if (nmb1) launch(q4_tile_dma_kernel<F16, SWIGLU, SPLIT, 1>, grid, dim3(256), 0, s, p, tm, tn);
+        else launch(q4_tile_dma_kernel<F16, SWIGLU, SPLIT, 2>, grid, dim3(256), 0, s, p, tm, tn);
+    } else {
+        if (nmb1) launch(q4_tile_kernel<F16, SWIGLU, SPLIT, 1>, grid, dim3(256), 0, s, p, tm, tn);
+        else launch(q4_tile_kernel<F16, SWIGLU, SPLIT, 2>, grid, dim3(256), 0, s, p, tm, tn);
+    }
 }
 
 hipError_t launch_q4_tile(const Problem& p, hipStream_t s) {
