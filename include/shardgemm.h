@@ -155,10 +155,9 @@ sg_status sg_all_to_sharded_ex(const sg_layer* layer, const void* x, int in_layo
  *   y        (B, out_dims) of y_dtype: sum over r = 0..P-1 of
  *            x_partial[r] W_r^T, then + bias once.
  *   workspace device scratch of at least sg_sharded_to_all_workspace(layer, B)
- *            bytes (NULL allowed when that is 0).  It must be zero-filled
- *            before its first use; every call leaves the arrival counters at
- *            its start zero again, so the same workspace serves later calls of
- *            any shape.  Calls that share a workspace must not run
+ *            bytes, 16-byte aligned (NULL allowed when that is 0); no
+ *            initial contents are needed, and the same workspace serves later
+ *            calls of any shape.  Calls that share a workspace must not run
  *            concurrently. */
 sg_status sg_sharded_to_all(const sg_layer* layer, const void* x_partial, int64_t B, void* y,
                             sg_dtype y_dtype, void* workspace, size_t ws_bytes, void* stream);
@@ -184,9 +183,8 @@ sg_status sg_sharded_to_all_ex(const sg_layer* layer, const void* x_partial, int
  *            out_dims / 2, the same activation dtype.
  *   x        (B, in_dims) of that dtype; y (B, out_dims of down) of y_dtype.
  *   workspace device memory of at least sg_mlp_workspace(...) bytes, 16-byte
- *            aligned, zero-filled before its first use: the down layer's
- *            sg_sharded_to_all workspace first (its arrival counters, kept zero
- *            by every call, at offset 0 for every B), then h (when both layers
+ *            aligned, no initial contents needed: the down layer's
+ *            sg_sharded_to_all workspace first, then h (when both layers
  *            run on a streaming kernel and B >= 8, stored fragment-major in
  *            the down kernel's operand order so that it reads each 16-token
  *            operand fragment as one contiguous 1 KB).  The same workspace serves later calls of any B
@@ -208,7 +206,9 @@ size_t sg_mlp_workspace(const sg_layer* gate_up, const sg_layer* down, int64_t B
  * library holds on every device it runs on until the process ends.  The
  * caller passes x and y as for sg_mlp; nothing is allocated or freed.
  * Errors: as sg_mlp, and SG_ERR_WORKSPACE when sg_mlp_workspace(gate_up,
- * down, B) exceeds the scratch (about 570 tokens for a 14336-wide bf16 h).
+ * down, B) exceeds the scratch (on 4096 x 14336 decode-MLP layers over 8
+ * ranks the scratch holds every token count up to 32 for bf16 layers, up to
+ * 64 for 4-bit ones: beyond, the down layer's rank split needs more).
  * All calls on one device share its scratch, so calls that overlap on one
  * GPU (other streams or threads) race: the caller serialises them. */
 #define SG_MLP_STATIC_SCRATCH_BYTES (16u << 20)
@@ -288,9 +288,10 @@ size_t sg_summa_backward_workspace(sg_dtype dtype, int64_t M, int64_t K, int64_t
 
 /* Bytes of workspace sg_sharded_to_all needs for B tokens (0 on bad input, and
  * when the call runs without one).  Non-zero when the output alone gives too
- * few tiles to fill the chip (beyond 32 tokens, dense 16-bit and 4-bit
- * layers): each rank's product is then a workgroup of its own, with partial
- * tiles in the workspace summed in rank order by the last to arrive. */
+ * few tiles to fill the chip (beyond 32 tokens, dense 16-bit, MX FP8 and
+ * 4-bit layers): groups of ranks are then workgroups of their own, their
+ * partial tiles stored in the workspace and summed in rank order by a second
+ * kernel. */
 size_t sg_sharded_to_all_workspace(const sg_layer* layer, int64_t B);
 
 /* SUMMA on a q x q grid ([SUMMA], SUMMA section, equations (1), (2)).

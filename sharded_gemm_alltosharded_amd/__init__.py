@@ -255,15 +255,14 @@ _workspaces: dict = {}
 
 
 def workspace(layer: Layer, B: int, device) -> torch.Tensor | None:
-    """A zero-filled workspace shared by calls on one device (the library
-    leaves it zero-filled after every call)."""
+    """A workspace shared by calls on one device (no initial contents needed)."""
     need = lib().sg_sharded_to_all_workspace(layer.handle, B)
     if need == 0:
         return None
     key = torch.device(device)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < need:
-        ws = torch.zeros(need, dtype=torch.uint8, device=key)
+        ws = torch.empty(need, dtype=torch.uint8, device=key)
         _workspaces[key] = ws
     return ws
 
@@ -289,7 +288,7 @@ _mlp_workspaces: dict = {}
 
 
 def mlp_workspace(gate_up: Layer, down: Layer, B: int, device) -> torch.Tensor | None:
-    """A zero-filled workspace for mlp(), shared by calls on one device (None
+    """A workspace for mlp(), shared by calls on one device (None
     when the layers do not form a gate|up, down pair: sg_mlp then says why)."""
     need = int(lib().sg_mlp_workspace(gate_up.handle, down.handle, B))
     if need == 0:
@@ -297,7 +296,7 @@ def mlp_workspace(gate_up: Layer, down: Layer, B: int, device) -> torch.Tensor |
     key = torch.device(device)
     ws = _mlp_workspaces.get(key)
     if ws is None or ws.numel() < need:
-        ws = torch.zeros(need, dtype=torch.uint8, device=key)
+        ws = torch.empty(need, dtype=torch.uint8, device=key)
         _mlp_workspaces[key] = ws
     return ws
 

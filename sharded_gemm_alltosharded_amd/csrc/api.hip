@@ -142,17 +142,7 @@ sg_status common_checks(int mode, int segments, int P, int64_t out_dims, int64_t
 // ---------------------------------------------------------------------------
 enum Kind { K_GENERIC, K_TILE0, K_TILE1, K_SKINNY, K_Q4, K_Q4TILE };
 
-int num_cus() {
-    static int cus = -1;
-    if (cus < 0) {
-        int dev = 0;
-        hipDeviceProp_t prop;
-        cus = (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess)
-                  ? prop.multiProcessorCount
-                  : 256;
-    }
-    return cus;
-}
+int num_cus() { return sg::device_cus(); }
 
 // dense operands: the MFMA paths need 16-byte rows
 bool mfma_ok(const sg_layer* l, const void* x) {
@@ -194,7 +184,9 @@ Kind choose(const sg_layer* l, int64_t B, const void* x, int swiglu = 0, int nse
     }
     if (!mfma_ok(l, x)) return K_GENERIC;
     if (B <= 32 && skinny_fits(l, B, swiglu, nseg)) return K_SKINNY;
-    return B >= 512 ? K_TILE0 : K_TILE1;
+    // up to 256 tokens the 128 x 128 tiles (more workgroups); beyond, the
+    // ping-pong kernel (decode-MLP gate|up at 384 tokens: 187 -> 122 us)
+    return B > 256 ? K_TILE0 : K_TILE1;
 }
 
 // Split sharded-to-all work by rank when the output alone gives too few
@@ -203,15 +195,14 @@ sg::SplitLayout split_layout(const sg_layer* l, Kind k, int64_t B);
 
 bool want_split(const sg_layer* l, Kind k, int64_t B) {
     if (l->P < 2) return false;
-    if (split_layout(l, k, B).counters > sg::kMaxCounters) return false;
     const int cus = num_cus();
     switch (k) {
     case K_TILE0: return sg::tile_count((int)B, (int)l->out_dims, 0) * 2 <= cus;
     case K_TILE1: return sg::tile_count((int)B, (int)l->out_dims, 1) * 2 <= cus;
-    // the 4-bit tile kernel splits only below a quarter tile per CU: above,
-    // the unsplit 64-token tiles win (down projection at 192 tokens 129 against
-    // 148 us)
-    case K_Q4TILE: return sg::q4_tile_count((int)B, (int)l->out_dims) * 4 <= cus;
+    // the 4-bit tile kernel (three workgroups per CU) splits up to one tile
+    // per CU (decode-MLP down projection: 126 -> 45 us at 192 tokens, 143 ->
+    // 101 us at 512)
+    case K_Q4TILE: return sg::q4_tile_count((int)B, (int)l->out_dims) <= cus;
     default: return false;
     }
 }
@@ -235,7 +226,10 @@ Kind choose_row(const sg_layer* l, int64_t B) {
     if (l->quantized) return !l->qfrag ? K_GENERIC : (B <= 32 && q4_fits(l, B, 0) ? K_Q4 : K_Q4TILE);
     if (l->dtype == SG_F32 || l->cols_r % 8) return K_GENERIC;
     if (B <= 32 && skinny_fits(l, B, 0, l->P)) return K_SKINNY;
-    return B >= 512 ? K_TILE0 : K_TILE1;
+    // the ping-pong kernel split into groups of ranks whenever the output
+    // gives too few tiles (decode-MLP down projection against the 128 x 128
+    // tiles: 93 -> 56 us at 64 tokens, 139 -> 69 us at 256)
+    return K_TILE0;
 }
 
 hipError_t run(const sg::Problem& p, Kind k, hipStream_t st) {
@@ -653,8 +647,7 @@ sg_status sg_sharded_to_all_ex(const sg_layer* l, const void* x_partial, int64_t
             return fail(SG_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws_bytes, bytes);
         if (!aligned16(workspace)) return fail(SG_ERR_WORKSPACE, "workspace must be 16-byte aligned");
         p.split = 1;
-        p.counters = (unsigned*)workspace;
-        p.ws = (float*)((char*)workspace + sg::kPartialsOffset);
+        p.ws = (float*)workspace;
     }
     hipError_t e = run(p, k, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "sharded_to_all launch");
@@ -692,12 +685,8 @@ size_t mlp_h_bytes(const sg_layer* gu, int64_t B) {
 
 }  // namespace
 
-// The down layer's workspace comes first and always spans at least its
-// arrival counters, so the counters sit at offset 0 for every B and h (which
-// needs no clearing) never overwrites them.
-static size_t mlp_down_bytes(const sg_layer* dn, int64_t B) {
-    return align256(std::max(sg_sharded_to_all_workspace(dn, B), sg::kPartialsOffset));
-}
+// The down layer's workspace (partial tiles when it splits by rank), then h.
+static size_t mlp_down_bytes(const sg_layer* dn, int64_t B) { return align256(sg_sharded_to_all_workspace(dn, B)); }
 
 size_t sg_mlp_workspace(const sg_layer* gate_up, const sg_layer* down, int64_t B) {
     if (mlp_check(gate_up, down) || B <= 0 || B > INT32_MAX) return 0;
@@ -806,21 +795,14 @@ sg_status sg_mlp(const sg_layer* gate_up, const sg_layer* down, const void* x, i
 // ---------------------------------------------------------------------------
 static __device__ __align__(256) unsigned char mlp_scratch[SG_MLP_STATIC_SCRATCH_BYTES];
 
-__global__ void zero_words_kernel(unsigned* p, int n) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) p[i] = 0u;
-}
-
 namespace {
 constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void* g_scratch_ptr[kMaxDevices];
 
-// the device address of the current device's scratch; on a device's first
-// call its arrival counters are cleared with a fill kernel on `st` (the
-// array starts zeroed and every call leaves them zero; the fill makes that
-// independent of the loader)
-sg_status scratch_for_current_device(hipStream_t st, void** out) {
+// the device address of the current device's scratch (nothing in it needs
+// clearing: every call writes what it reads)
+sg_status scratch_for_current_device(void** out) {
     int dev = -1;
     HIP_TRY(hipGetDevice(&dev), "device query");
     if (dev < 0 || dev >= kMaxDevices)
@@ -829,9 +811,6 @@ sg_status scratch_for_current_device(hipStream_t st, void** out) {
     if (!g_scratch_ptr[dev]) {
         void* p = nullptr;
         HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(mlp_scratch)), "scratch address");
-        const int words = (int)(sg::kPartialsOffset / sizeof(unsigned));
-        hipLaunchKernelGGL(zero_words_kernel, dim3((words + 255) / 256), dim3(256), 0, st, (unsigned*)p, words);
-        HIP_TRY(hipGetLastError(), "scratch clear");
         g_scratch_ptr[dev] = p;
     }
     *out = g_scratch_ptr[dev];
@@ -851,16 +830,8 @@ sg_status sg_mlp_static(const sg_layer* gate_up, const sg_layer* down, const voi
                     "sg_mlp_static: %lld tokens need %zu bytes of workspace, the static scratch holds %zu; "
                     "use sg_mlp with a caller workspace", (long long)B, need, (size_t)SG_MLP_STATIC_SCRATCH_BYTES);
     void* ws = nullptr;
-    st = scratch_for_current_device((hipStream_t)stream, &ws);
+    st = scratch_for_current_device(&ws);
     if (st != SG_OK) return st;
-    if (sg_sharded_to_all_workspace(down, B) > 0) {
-        // the down layer splits by rank and counts arrivals in the scratch:
-        // start them from zero whatever an earlier call left
-        const int words = (int)(sg::kPartialsOffset / sizeof(unsigned));
-        hipLaunchKernelGGL(zero_words_kernel, dim3((words + 255) / 256), dim3(256), 0, (hipStream_t)stream,
-                           (unsigned*)ws, words);
-        HIP_TRY(hipGetLastError(), "scratch clear");
-    }
     return mlp_run(gate_up, down, x, B, y, y_dtype, ws, stream);
 }
 

@@ -61,10 +61,11 @@ struct Problem {
     int64_t nloc;   // OUT_SHARDED / OUT_FRAG rank width: column n -> rank n / nloc
     const void* bias;  // per output column, dtype `dtype`; may be null
     int accumulate; // fp32 output only: out += result
-    // cross-segment reduction through a workspace (split by segment)
+    // cross-segment reduction through a workspace (split by segment): the
+    // product kernel stores one partial slab per group of segments, a second
+    // kernel adds them in order
     int split;
-    float* ws;          // nseg partial slabs
-    unsigned* counters; // one per output tile, zero between calls
+    float* ws;
 };
 
 // Fragment-major layout of a row-major (rows, K) weight, rows % 16 == 0 and
@@ -174,18 +175,24 @@ hipError_t q4_repack(uint32_t* w, int64_t n, int forward, hipStream_t s);
 hipError_t q4_transform(uint32_t* dst_w, const uint32_t* src_w, uint16_t* dst_g, const uint16_t* src_g, int P,
                         int64_t rows, int64_t K, int forward, hipStream_t s);
 
-// Workspace of the split-by-segment reduction: a fixed region of arrival
-// counters (one per output tile or row group) at the start, then `floats`
-// partial values (one slab per segment).  The counters sit at the same place
-// for every call, so the zeros one call leaves behind are the zeros the next
-// call (of any shape) starts from; the partial slabs need no clearing.
+// Workspace of the split-by-segment reduction: `floats` partial values (one
+// slab of `tiles` output tiles per group of segments), written before they
+// are read by every call, so it needs no clearing.
 struct SplitLayout {
     size_t floats;
-    size_t counters;
+    size_t tiles;
 };
-constexpr size_t kMaxCounters = 4096;
-constexpr size_t kPartialsOffset = kMaxCounters * sizeof(unsigned);
 SplitLayout tile_split_layout(int M, int N, int nseg, int variant);
+// compute units of the current device (queried once)
+int device_cus();
+// groups of consecutive segments the 256 x 256 tile kernel splits a
+// sharded-to-all product into: the fewest that divide nseg and give every
+// compute unit a workgroup
+int tile_pp_groups(int M, int N, int nseg);
+// second kernel of a split tile product: adds the groups' partial tiles in
+// order and stores them; layout 0: ping-pong 256 x 256 tiles, 1: register-
+// staged 128 x 128, 2: register-staged 256 x 256
+hipError_t launch_split_reduce(const Problem& p, int tiles_m, int tiles_n, int groups, int layout, hipStream_t s);
 
 // launch shapes of the streaming kernels (dynamic LDS bytes included)
 struct SkinnyShape {
@@ -244,7 +251,7 @@ hipError_t launch_bwd_dx(const BwdDx& p, hipStream_t s);
 hipError_t launch_bwd_dw(const BwdDw& p, hipStream_t s);
 constexpr size_t kMaxStreamLds = 64 * 1024;
 int tile_count(int M, int N, int variant);
-inline size_t split_workspace_bytes(SplitLayout s) { return kPartialsOffset + s.floats * sizeof(float); }
+inline size_t split_workspace_bytes(SplitLayout s) { return s.floats * sizeof(float); }
 
 // ---------------------------------------------------------------------------
 // device helpers

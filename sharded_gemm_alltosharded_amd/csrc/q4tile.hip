@@ -24,7 +24,7 @@
 // segments of the loop, summed in order in registers, or (SPLIT, when the
 // output gives too few tiles to fill the chip) one workgroup per rank and
 // tile, the partial tiles stored in the caller's workspace and added in rank
-// order by the last of a tile's workgroups to arrive.  Two workgroups per CU
+// order by a second kernel (q4_split_reduce_kernel).  Two workgroups per CU
 // (two waves per SIMD) so that one wave's loads and barrier waits overlap the
 // other's matrix work.  q4_tile_dma_kernel below is the same tile with every
 // operand staged by direct-to-LDS loads several groups ahead; it runs whenever
@@ -102,20 +102,18 @@ __device__ __forceinline__ int swz8(int row) { return (row >> 1) & 7; }
 
 }  // namespace
 
-// Cross-segment reduction (split by rank: every workgroup stores its partial
-// tile, and the last of a tile's nseg to arrive adds them in rank order) and
-// the stores of a finished tile.
+// The stores of a finished tile, or (split by rank) of its partial tile.
 template <bool SWIGLU, bool SPLIT, int NMB>
 __device__ __forceinline__ void q4_tile_finish(const Problem& p, f32x16 (&y)[2][NMB], int tiles_m, int tiles_n,
                                                int tile, int m0, int64_t n0, int wave_m, int wave_n,
                                                const bool (&nok)[2]) {
     constexpr int BM = 64 * NMB, BN = 128;
     const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
-    const f32x16 zero16 = {};
     if constexpr (SPLIT) {
-        const int ntiles = tiles_m * tiles_n;
-        const int64_t slab = (int64_t)ntiles * BM * BN;  // floats per segment
-        f32x4* mine = (f32x4*)(p.ws + blockIdx.y * slab + (int64_t)tile * BM * BN);
+        // this segment's partial tile: thread tid's float4 v = (nb NMB + mb) 4 + q
+        // (y[nb][mb][4q .. 4q + 3]) at float4 index v * 256 + tid of the tile's
+        // slab; q4_split_reduce_kernel adds the segments in rank order
+        f32x4* mine = (f32x4*)(p.ws + ((int64_t)blockIdx.y * tiles_m * tiles_n + tile) * (BM * BN));
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
@@ -124,34 +122,7 @@ __device__ __forceinline__ void q4_tile_finish(const Problem& p, f32x16 (&y)[2][
                 for (int q = 0; q < 4; ++q)
                     mine[((nb * NMB + mb) * 4 + q) * 256 + tid] =
                         f32x4{y[nb][mb][4 * q], y[nb][mb][4 * q + 1], y[nb][mb][4 * q + 2], y[nb][mb][4 * q + 3]};
-        __threadfence();
-        __syncthreads();
-        __shared__ int last;
-        if (tid == 0) {
-            const unsigned prev = atomicAdd(&p.counters[tile], 1u);
-            last = prev == (unsigned)p.nseg - 1;
-            if (last) p.counters[tile] = 0u;  // ready for the next call
-        }
-        __syncthreads();
-        if (!last) return;
-        __threadfence();
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-            for (int mb = 0; mb < NMB; ++mb) y[nb][mb] = zero16;
-        for (int sr = 0; sr < p.nseg; ++sr) {  // rank order
-            const f32x4* src = (const f32x4*)(p.ws + sr * slab + (int64_t)tile * BM * BN);
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-                for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const f32x4 v = src[((nb * NMB + mb) * 4 + q) * 256 + tid];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) y[nb][mb][4 * q + e] += v[e];
-                    }
-        }
+        return;
     }
 
     // epilogue: lane l of a 32 x 32 block holds weight row l & 31 (column) and
@@ -545,6 +516,55 @@ __global__ __launch_bounds__(256, 2) void q4_tile_dma_kernel(Problem p, int tile
     q4_tile_finish<SWIGLU, SPLIT, NMB>(p, y, tiles_m, tiles_n, tile, m0, n0, wave_m, wave_n, nok);
 }
 
+// Sum of a split product's partial tiles (no SwiGLU): workgroup (tile, y)
+// takes float4 indices RV y .. RV y + RV - 1 of every thread of the tile
+// kernels' partial layout, adds the segments' partials in rank order and
+// stores them with the bias.  A second kernel rather than the last workgroup
+// of a tile to arrive: the kernel boundary orders the partial stores before
+// the loads (an in-kernel handoff needs a device-scope release per
+// workgroup), and the sums are spread over every compute unit.
+template <int NMB, int RV>
+__global__ __launch_bounds__(256) void q4_split_reduce_kernel(Problem p, int tiles_m, int tiles_n) {
+    constexpr int BM = 64 * NMB, BN = 128;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
+    const int wave_m = wave >> 1, wave_n = wave & 1;
+    const int tile = blockIdx.x;
+    constexpr int GM = 4;  // the tile -> (m0, n0) map of the tile kernels
+    const int grp = tile / (GM * tiles_n), first_m = grp * GM, gsz = min(GM, tiles_m - first_m);
+    const int tin = tile - grp * GM * tiles_n;
+    const int m0 = (first_m + tin % gsz) * BM;
+    const int64_t n0 = (int64_t)(tin / gsz) * BN;
+    const int v0 = blockIdx.y * RV;
+    f32x4 sum[RV];
+#pragma unroll
+    for (int r = 0; r < RV; ++r) sum[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < p.nseg; ++g) {  // rank order
+        const f32x4* src = (const f32x4*)(p.ws + ((int64_t)g * tiles_m * tiles_n + tile) * (BM * BN));
+        f32x4 v[RV];
+#pragma unroll
+        for (int r = 0; r < RV; ++r) v[r] = src[(v0 + r) * 256 + tid];
+#pragma unroll
+        for (int r = 0; r < RV; ++r) sum[r] += v[r];
+    }
+#pragma unroll
+    for (int r = 0; r < RV; ++r) {
+        const int v = v0 + r, nb = v / (NMB * 4), mb = (v / 4) % NMB, q = v % 4;
+        const int64_t n = n0 + wave_n * 64 + nb * 32 + (lane & 31);
+        if (n >= p.N) continue;
+        const float bias = p.bias ? load_as_f32(p.bias, p.dtype, n) : 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int m = m0 + wave_m * (32 * NMB) + mb * 32 + 8 * q + 4 * h + e;
+            if (m >= p.M) continue;
+            float x = sum[r][e];
+            if (p.bias) x += bias;
+            const int64_t o = out_index(p, m, n);
+            if (p.accumulate && p.out_dtype == SG_F32) x += ((const float*)p.out)[o];
+            store_from_f32(p.out, p.out_dtype, o, x);
+        }
+    }
+}
+
 // fragment-major codes (rows % 32 == 0, groups per segment % 4 == 0), 16-byte
 // activation rows
 bool q4_tile_fits(const Problem& p) {
@@ -603,6 +623,11 @@ hipError_t launch_q4_tile(const Problem& p, hipStream_t s) {
     } else if (p.split) {
         if (f16) launch_nmb<true, false, true>(p, s, grid, tm, tn);
         else launch_nmb<false, false, true>(p, s, grid, tm, tn);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        constexpr int RV = 4;  // 8 float4 per thread (one 32-token block per wave)
+        if (bm != 64) return hipErrorInvalidValue;
+        launch(q4_split_reduce_kernel<1, RV>, dim3(tm * tn, 8 / RV), dim3(256), 0, s, p, tm, tn);
     } else {
         if (f16) launch_nmb<true, false, false>(p, s, grid, tm, tn);
         else launch_nmb<false, false, false>(p, s, grid, tm, tn);

@@ -137,8 +137,9 @@ __global__ __launch_bounds__(256) void tile_kernel(Problem p, int tiles_m, int t
     const int tm = first_m + tin % gsz, tn = tin / gsz;
     const int m0 = tm * BM;
     const int64_t n0 = (int64_t)tn * NOUT;
-    const int seg_lo = SPLIT ? blockIdx.y : 0;
-    const int seg_cnt = SPLIT ? 1 : p.nseg;
+    // split: workgroup (tile, y) takes group y of gridDim.y groups of consecutive segments
+    const int seg_cnt = SPLIT ? p.nseg / (int)gridDim.y : p.nseg;
+    const int seg_lo = SPLIT ? (int)blockIdx.y * seg_cnt : 0;
 
     const uint16_t* Ag = (const uint16_t*)p.A;
     const uint16_t* Wg = (const uint16_t*)p.W;
@@ -292,51 +293,22 @@ __global__ __launch_bounds__(256) void tile_kernel(Problem p, int tiles_m, int t
         __syncthreads();
     }
 
-    // ---- cross-segment reduction through the workspace
+    // ---- rank split: this segment's partial tile to the workspace (thread
+    // tid's float4 v = (i NBM + j) 4 + q at float4 index v * 256 + tid of the
+    // tile's slab); split_reduce_kernel adds the segments in rank order
     if constexpr (SPLIT) {
-        constexpr int NV = NBN * NBM * 4;  // float4 per thread
-        const int64_t slab = (int64_t)ntiles * 256 * NV * 4;  // floats per segment
-        f32x4* mine = (f32x4*)(p.ws + blockIdx.y * slab + (int64_t)tile * 256 * NV * 4);
+        f32x4* mine = (f32x4*)(p.ws + ((int64_t)blockIdx.y * ntiles + tile) * (BM * BN));
 #pragma unroll
         for (int i = 0; i < NBN; ++i)
 #pragma unroll
             for (int j = 0; j < NBM; ++j)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                               acc[i][j][4 * q + 3]};
+                    const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                     acc[i][j][4 * q + 3]};
                     mine[((i * NBM + j) * 4 + q) * 256 + tid] = v;
                 }
-        __threadfence();
-        __syncthreads();
-        __shared__ int last;
-        if (tid == 0) {
-            const unsigned prev = atomicAdd(&p.counters[tile], 1u);
-            last = prev == (unsigned)p.nseg - 1;
-            if (last) p.counters[tile] = 0u;  // ready for the next call
-        }
-        __syncthreads();
-        if (!last) return;
-        __threadfence();
-#pragma unroll
-        for (int i = 0; i < NBN; ++i)
-#pragma unroll
-            for (int j = 0; j < NBM; ++j)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-        for (int s = 0; s < p.nseg; ++s) {  // rank order
-            const f32x4* src = (const f32x4*)(p.ws + s * slab + (int64_t)tile * 256 * NV * 4);
-#pragma unroll
-            for (int i = 0; i < NBN; ++i)
-#pragma unroll
-                for (int j = 0; j < NBM; ++j)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const f32x4 v = src[((i * NBM + j) * 4 + q) * 256 + tid];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] += v[e];
-                    }
-        }
+        return;
     }
 
     // ---- epilogue
@@ -369,23 +341,124 @@ __global__ __launch_bounds__(256) void tile_kernel(Problem p, int tiles_m, int t
     });
 }
 
+// Sum of a split product's partial tiles (NT or NN weights, no SwiGLU):
+// partial g of tile t is the BM x BN floats at (g ntiles + t) BM BN of the
+// workspace, holding thread tid's float4 v (its accumulator acc[i][j][4q ..
+// 4q + 3], v = (i NBM + j) 4 + q) at float4 index v NT + tid.  Workgroup
+// (t, y) takes float4 indices RV y .. RV y + RV - 1 of every thread, adds the
+// groups' partials in group (rank) order and stores them through the
+// epilogue (bias, output layout and dtype).  A second kernel rather than the
+// last workgroup of a tile to arrive: the kernel boundary orders the partial
+// stores before the loads, where an in-kernel handoff needs a device-scope
+// release per workgroup, and the sum is spread over every compute unit.
+// MLOW: the product kernel's wave w covers rows (w mod 2) WTM (the ping-pong
+// kernel) rather than (w / 2) WTM.
+template <int BM, int BN, int WTM, int WTN, int NT, bool MLOW, int RV>
+__global__ __launch_bounds__(NT) void split_reduce_kernel(Problem p, int tiles_m, int tiles_n, int groups) {
+    constexpr int NBM = WTM / 32, NWN = BN / WTN;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wave_m = MLOW ? wave % (BM / WTM) : wave / NWN;
+    const int wave_n = MLOW ? wave / (BM / WTM) : wave % NWN;
+    const int hi = lane >> 5;
+    const int ntiles = tiles_m * tiles_n;
+    const int tile = blockIdx.x;
+    constexpr int GM = 4;  // the tile -> (m0, n0) map of the product kernels
+    const int gidx = tile / (GM * tiles_n);
+    const int first_m = gidx * GM;
+    const int gsz = min(GM, tiles_m - first_m);
+    const int tin = tile - gidx * GM * tiles_n;
+    const int m0 = (first_m + tin % gsz) * BM;
+    const int64_t n0 = (int64_t)(tin / gsz) * BN;
+
+    const int v0 = blockIdx.y * RV;
+    f32x4 sum[RV];
+#pragma unroll
+    for (int r = 0; r < RV; ++r) sum[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < groups; ++g) {  // rank order
+        const f32x4* src = (const f32x4*)(p.ws + ((int64_t)g * ntiles + tile) * (BM * BN));
+        f32x4 v[RV];
+#pragma unroll
+        for (int r = 0; r < RV; ++r) v[r] = src[(v0 + r) * NT + tid];
+#pragma unroll
+        for (int r = 0; r < RV; ++r) sum[r] += v[r];
+    }
+#pragma unroll
+    for (int r = 0; r < RV; ++r) {
+        const int v = v0 + r, i = v / (NBM * 4), j = (v / 4) % NBM, q = v % 4;
+        const int m = m0 + wave_m * WTM + j * 32 + (lane & 31);
+        if (m >= p.M) continue;
+        const int64_t n = n0 + wave_n * WTN + i * 32 + 8 * q + 4 * hi;
+        float o[4] = {sum[r][0], sum[r][1], sum[r][2], sum[r][3]};
+        store4(p, m, n, o);
+    }
+}
+
+hipError_t launch_split_reduce(const Problem& p, int tiles_m, int tiles_n, int groups, int layout, hipStream_t s) {
+    constexpr int RV = 4;
+    const int ntiles = tiles_m * tiles_n;
+    switch (layout) {
+    case 0:  // ping-pong 256 x 256, 8 waves of 128 x 64: 32 float4 per thread
+        launch((split_reduce_kernel<256, 256, 128, 64, 512, true, RV>), dim3(ntiles, 32 / RV), dim3(512), 0, s, p,
+               tiles_m, tiles_n, groups);
+        break;
+    case 1:  // register-staged 128 x 128, 4 waves of 64 x 64: 16 float4 per thread
+        launch((split_reduce_kernel<128, 128, 64, 64, 256, false, RV>), dim3(ntiles, 16 / RV), dim3(256), 0, s, p,
+               tiles_m, tiles_n, groups);
+        break;
+    default:  // register-staged 256 x 256, 4 waves of 128 x 128: 64 float4 per thread
+        launch((split_reduce_kernel<256, 256, 128, 128, 256, false, RV>), dim3(ntiles, 64 / RV), dim3(256), 0, s, p,
+               tiles_m, tiles_n, groups);
+        break;
+    }
+    return hipGetLastError();
+}
+
 // variant 0: 256 x 256 tiles; variant 1: 128 x 128 tiles
 int tile_count(int M, int N, int variant) {
     const int bm = variant == 0 ? 256 : 128;
     return ((M + bm - 1) / bm) * ((N + bm - 1) / bm);
 }
 
+int device_cus() {
+    static int cus = -1;
+    if (cus < 0) {
+        int dev = 0;
+        hipDeviceProp_t prop;
+        cus = (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess)
+                  ? prop.multiProcessorCount
+                  : 256;
+    }
+    return cus;
+}
+
+int tile_pp_groups(int M, int N, int nseg) {
+    const int tiles = tile_count(M, N, 0), cus = device_cus();
+    for (int d = 1; d < nseg; ++d)
+        if (nseg % d == 0 && tiles * d >= cus) return d;
+    return nseg;
+}
+
+// variant 0 splits into tile_pp_groups groups, variant 1 into nseg
 SplitLayout tile_split_layout(int M, int N, int nseg, int variant) {
     const size_t t = (size_t)tile_count(M, N, variant), bm = variant == 0 ? 256 : 128;
-    return {t * bm * bm * nseg, t};
+    const size_t groups = variant == 0 ? (size_t)tile_pp_groups(M, N, nseg) : (size_t)nseg;
+    return {t * bm * bm * groups, t};
 }
 
 template <int BM, int BN, bool F16, int WMODE, bool SPLIT, bool FP8 = false>
 static hipError_t launch_one(const Problem& p, hipStream_t s) {
     const int nout = WMODE == WM_SWIGLU ? BN / 2 : BN;
     const int tm = (p.M + BM - 1) / BM, tn = (p.N + nout - 1) / nout;
-    dim3 grid(tm * tn, SPLIT ? p.nseg : 1);
+    // the split groups tile_split_layout sizes the workspace for
+    const int groups = !SPLIT ? 1 : BM == 256 ? tile_pp_groups(p.M, p.N, p.nseg) : p.nseg;
+    dim3 grid(tm * tn, groups);
     launch((tile_kernel<BM, BN, F16, WMODE, SPLIT, FP8>), grid, dim3(256), 0, s, p, tm, tn);
+    if constexpr (SPLIT) {
+        static_assert(WMODE != WM_SWIGLU, "no split with SwiGLU");
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_split_reduce(p, tm, tn, groups, BM == 128 ? 1 : 2, s);
+    }
     return hipGetLastError();
 }
 
@@ -398,8 +471,8 @@ static hipError_t launch_fp8(const Problem& p, hipStream_t s) {
 
 template <int BM, int BN, bool F16>
 static hipError_t launch_mode(const Problem& p, hipStream_t s) {
-    if (p.nn) return p.split ? launch_one<BM, 256, F16, WM_NN, true>(p, s)
-                             : launch_one<BM, 256, F16, WM_NN, false>(p, s);
+    // transposed weights: no split (no caller splits them)
+    if (p.nn) return p.split ? hipErrorInvalidValue : launch_one<BM, 256, F16, WM_NN, false>(p, s);
     if (p.swiglu) return launch_one<BM, BN, F16, WM_SWIGLU, false>(p, s);
     return p.split ? launch_one<BM, BN, F16, WM_NT, true>(p, s)
                    : launch_one<BM, BN, F16, WM_NT, false>(p, s);

@@ -34,9 +34,21 @@
 // quarter and the swizzle gives each row >> 2 its own chunk, so the fragment
 // reads are conflict-free (swizzling by (r >> 1) & 3 measured at half rate).
 //
+// Rank split (sharded-to-all layers whose output gives too few tiles): the
+// segments form gridDim.y groups of consecutive ranks; workgroup (tile, y)
+// runs group y's k tiles and writes its fp32 partial tile to the caller's
+// workspace, and a second kernel (split_reduce_kernel, tile.hip) adds each
+// tile's partials in group (rank) order and stores the result.  The kernel boundary
+// orders the partials' stores before their loads; an in-kernel handoff (the
+// last workgroup of a tile to arrive sums the partials) needs a device-scope
+// release per workgroup, and with eight groups of 256 x 256 tiles the
+// releases and the one-workgroup sums cost more than the products (512
+// tokens x 4096 outputs x 8 ranks of 1792: 230 us in one kernel against
+// 90 us for the products alone).
+//
 // Rows past M or N read a clamped valid row (their outputs are never stored).
-// Requirements (tile_dma_fits): NT or SwiGLU weights, K a multiple of 32, no
-// split, operand extents below 2 GiB.
+// Requirements (tile_dma_fits): NT or SwiGLU weights (no split with SwiGLU), K
+// a multiple of 32, operand extents below 2 GiB.
 #include "internal.h"
 
 namespace sg {
@@ -146,7 +158,7 @@ __device__ __forceinline__ void store4(const Problem& p, int m, int64_t n, float
 //    its own loads of k tile t have landed (those of the two later k tiles may
 //    stay in flight); the barrier then publishes k tile t to all waves.
 //  * every wave passes the same 2 nkt + 2 barriers.
-template <bool F16, bool SWIGLU>
+template <bool F16, bool SWIGLU, bool SPLIT>
 __global__ __launch_bounds__(512) void tile_pp_kernel(Problem p, int tiles_m, int tiles_n) {
     constexpr int BM = 256, BN = 256, BK = 32, NW = 8, NS = 4;
     constexpr int WTM = 128, WTN = 64, NBM = WTM / 32, NBN = WTN / 32;
@@ -193,11 +205,13 @@ __global__ __launch_bounds__(512) void tile_pp_kernel(Problem p, int tiles_m, in
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)p.A, 0, (int)a_extent(p), 0x00020000);
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)p.W, 0, (int)w_extent(p), 0x00020000);
     const int ktiles_seg = p.Kseg / BK;
-    const int nkt = ktiles_seg * p.nseg;
+    const int gsegs = SPLIT ? p.nseg / (int)gridDim.y : p.nseg;  // segments of this workgroup
+    const int nkt = ktiles_seg * gsegs;
+    const int seg_lo = SPLIT ? (int)blockIdx.y * gsegs : 0;     // its first segment
 
     auto issue = [&](int kt) {
-        const int s = kt / ktiles_seg;
-        const int k0 = (kt - s * ktiles_seg) * BK;
+        const int s = seg_lo + kt / ktiles_seg;
+        const int k0 = (kt - (s - seg_lo) * ktiles_seg) * BK;
         const uint32_t sa = (uint32_t)((s * p.a_seg + k0) * 2);
         const uint32_t sw = (uint32_t)((s * p.w_seg + (int64_t)k0 * bk_step) * 2);
         uint16_t* a = sA + (kt % NS) * TILE;
@@ -278,6 +292,24 @@ __global__ __launch_bounds__(512) void tile_pp_kernel(Problem p, int tiles_m, in
     }
     if (group == 0) __builtin_amdgcn_s_barrier();
 
+    // ---- rank split: this group's partial tile to the workspace, thread tid's
+    // float4 v (accumulator acc[i][j][4q .. 4q + 3], v = (i NBM + j) 4 + q) at
+    // float4 index v * 512 + tid of the tile's slab
+    if constexpr (SPLIT) {
+        f32x4* mine = (f32x4*)(p.ws + ((int64_t)blockIdx.y * ntiles + tile) * (BM * BN));
+#pragma unroll
+        for (int i = 0; i < NBN; ++i)
+#pragma unroll
+            for (int j = 0; j < NBM; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                     acc[i][j][4 * q + 3]};
+                    mine[((i * NBM + j) * 4 + q) * 512 + tid] = v;
+                }
+        return;
+    }
+
     // epilogue: lane l of a 32 x 32 block holds column l & 31 (token) and rows
     // 8 blk + 4 (l >> 5) + e (weight rows) of the block
     const int hi = lane >> 5;
@@ -311,7 +343,7 @@ __global__ __launch_bounds__(512) void tile_pp_kernel(Problem p, int tiles_m, in
 }
 
 bool tile_dma_fits(const Problem& p) {
-    return !p.nn && !p.split && !p.fp8 && !p.wq && p.Kseg % 32 == 0 && a_extent(p) < (1LL << 31) &&
+    return !p.nn && !(p.split && p.swiglu) && !p.fp8 && !p.wq && p.Kseg % 32 == 0 && a_extent(p) < (1LL << 31) &&
            w_extent(p) < (1LL << 31);
 }
 
@@ -321,13 +353,20 @@ hipError_t launch_tile_dma(const Problem& p, hipStream_t s) {
     const int nout = p.swiglu ? 128 : 256;
     const int tm = (p.M + 255) / 256, tn = (p.N + nout - 1) / nout;
     const bool f16 = p.dtype == SG_F16;
-    const dim3 grid(tm * tn), block(512);
+    const int groups = p.split ? tile_pp_groups(p.M, p.N, p.nseg) : 1;
+    const dim3 grid(tm * tn, groups), block(512);
     if (p.swiglu) {
-        if (f16) launch(tile_pp_kernel<true, true>, grid, block, 0, s, p, tm, tn);
-        else launch(tile_pp_kernel<false, true>, grid, block, 0, s, p, tm, tn);
+        if (f16) launch(tile_pp_kernel<true, true, false>, grid, block, 0, s, p, tm, tn);
+        else launch(tile_pp_kernel<false, true, false>, grid, block, 0, s, p, tm, tn);
+    } else if (p.split) {
+        if (f16) launch(tile_pp_kernel<true, false, true>, grid, block, 0, s, p, tm, tn);
+        else launch(tile_pp_kernel<false, false, true>, grid, block, 0, s, p, tm, tn);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_split_reduce(p, tm, tn, groups, 0, s);
     } else {
-        if (f16) launch(tile_pp_kernel<true, false>, grid, block, 0, s, p, tm, tn);
-        else launch(tile_pp_kernel<false, false>, grid, block, 0, s, p, tm, tn);
+        if (f16) launch(tile_pp_kernel<true, false, false>, grid, block, 0, s, p, tm, tn);
+        else launch(tile_pp_kernel<false, false, false>, grid, block, 0, s, p, tm, tn);
     }
     return hipGetLastError();
 }

@@ -142,10 +142,13 @@ def test_swiglu_epilogue(case, gather):
 # ---------------------------------------------------------------------------
 ROW_CASES = [
     ("bf16", 1, 512, 96, 2), ("bf16", 16, 14336 // 4, 256, 8), ("f16", 29, 768, 200, 3), ("bf16", 8, 256, 64, 1),
-    ("bf16", 100, 512, 256, 4),    # tile 128, rank split (2 tiles)
-    ("bf16", 256, 128, 9216, 2),   # tile 128, no split (144 tiles)
-    ("f16", 600, 256, 512, 4),     # tile 256, rank split
-    ("bf16", 2304, 128, 4096, 2),  # tile 256, no split (144 tiles)
+    ("bf16", 100, 512, 256, 4),    # ping-pong tile, rank split (1 tile, 4 groups)
+    ("bf16", 256, 128, 9216, 2),   # ping-pong tile, split into 2 groups (36 tiles)
+    ("f16", 600, 256, 512, 4),     # ping-pong tile, rank split
+    ("bf16", 1000, 1024, 4096, 8),  # ping-pong tile, 64 tiles: split into 4 groups of 2 ranks (256 CUs)
+    ("f16", 1800, 256, 4096, 4),   # ping-pong tile, 128 tiles: split into 2 groups of 2 ranks (256 CUs)
+    ("bf16", 1100, 320, 4096, 8),  # rank width 40 (not a multiple of 32): register-staged 256 tile, 4 groups
+    ("bf16", 2304, 128, 4096, 2),  # ping-pong tile, no split (144 tiles)
     ("bf16", 7, 12, 9, 2),         # generic
 ]
 
@@ -231,7 +234,7 @@ def test_mlp_entry_point_quantized(B):
 
 def test_mlp_shared_workspace_across_sizes():
     """One workspace for calls of different B: the fallback path at B = 40
-    (its down layer splits by rank through the arrival counters at offset 0)
+    (its down layer splits by rank, partial tiles at the workspace's start)
     and the fragment-major path at B = 16 alternate; every call matches the
     separate calls bit for bit."""
     D, F, P = 256, 512, 2

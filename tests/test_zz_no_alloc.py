@@ -31,8 +31,8 @@ def _layers(B, D, F, P, dtype, seed):
 
 
 # (dtype, D, F, P, first B, second B): streaming kernels with the fragment-major
-# h; the fallback pair whose down layer splits by rank through the arrival
-# counters in the scratch; fp16
+# h; the fallback pair whose down layer splits by rank through partial tiles
+# in the scratch; fp16
 CASES = [("bf16", 512, 1024, 8, 16, 5), ("bf16", 256, 512, 2, 40, 16), ("f16", 256, 768, 3, 32, 8),
          ("bf16", 4096, 14336, 8, 16, 1)]
 
@@ -88,8 +88,8 @@ def _q4(w, mode, P, S=1):
 
 @pytest.mark.parametrize("Bs", [(100, 24), (24, 64)], ids=lambda b: "-".join(map(str, b)))
 def test_mlp_static_quantized(Bs):
-    """4-bit layers: the tile kernels (the down layer split by rank through the
-    scratch's counters and partial tiles) and the streaming kernels (h
+    """4-bit layers: the tile kernels (the down layer split by rank through
+    partial tiles in the scratch) and the streaming kernels (h
     fragment-major in the scratch), two calls in a row."""
     D, F, P = 512, 1024, 4
     print(f"case: q4 D={D} F={F} P={P} B={Bs}", flush=True)
