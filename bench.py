@@ -11,7 +11,8 @@ down sharded-to-all with the fused rank sum, through the fused MLP entry point
 (sg_mlp, the sharded h kept in its workspace).  Other workloads:
 
     3   prefill: B=4096, P=4, fused QKV column shard (segments=3) + the MLP
-    4   4-bit affine MLP (group 64), B in {1, 8, 32} (--batch), P=4
+    4   4-bit affine MLP (group 64), B in {1, 8, 32} (--batch; beyond 32 tokens the
+        4-bit tile kernel, its roofline on the matrix cores), P=4
     5a  SUMMA Y = X A, 8192^3 bf16, q=4 (--summa fused|steps)
     5b  vocabulary-parallel head, fp16, 32 x 12288 . (50272 x 12288)^T, P=8
     5c  SUMMA backward at 8192^3, q=4: dX = dY A^T and dA = X^T dY
@@ -53,7 +54,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--config", default="2", choices=["1", "2", "3", "4", "5a", "5b", "5c", "6", "7"])
-    ap.add_argument("--batch", type=int, default=1, help="tokens for the 4-bit workload (1, 8 or 32)")
+    ap.add_argument("--batch", type=int, default=1, help="tokens for the 4-bit workload (1, 8 or 32; more runs the 4-bit tile kernel)")
     ap.add_argument("--summa", default="fused", choices=["fused", "steps"])
     ap.add_argument("--rank-share", action="store_true",
                     help="configs 2, 3, 4, 5b: only rank 0's share of the layers (P = 1, the per-GPU shapes "
@@ -92,6 +93,7 @@ class Workload:
     steps, warmup = 200, 20
     dominant = ""          # kernel the roofline describes
     dominant_src = ()      # sources it is built from (traffic is void once they change)
+    roof_unit = None       # the dominant kernel's roofline unit when it differs from `unit`
 
     def config(self):
         return {"workload": self.name}
@@ -279,6 +281,10 @@ class Q4MLP(Workload):
 
     def __init__(self, B):
         self.B = B
+        if B > 32:  # beyond the streaming kernels: the 4-bit tile kernel, a matrix-core roofline
+            self.bound, self.roof_unit = "mfma", "TFLOP/s"
+            self.dominant = "q4_tile_dma_kernel 64 x 128 (gate|up all-to-sharded + SwiGLU)"
+            self.dominant_src = ("q4tile.hip", "internal.h")
 
     def setup(self):
         import numpy as np
@@ -312,6 +318,8 @@ class Q4MLP(Workload):
         wbytes = lambda rows, cols: rows * cols // 2 + 2 * 2 * rows * (cols // 64)
         self.units = wbytes(2 * F, D) + wbytes(D, F) + 2 * (B * D + 2 * B * F + B * D)
         self.dom_units = wbytes(2 * F, D) + 2 * (B * D + B * F)
+        if self.bound == "mfma":
+            self.dom_units = 2 * B * D * 2 * F
 
     def step(self, i, ev=None):
         sg = self.sg
@@ -874,16 +882,18 @@ def main():
 
     scale = 1e9 if wl.unit == "GB/s" else 1e12
     value = wl.units / (ms / 1e3) / scale
-    achieved = wl.dom_units / (dom_ms / 1e3) / scale
+    ru = wl.roof_unit or wl.unit  # the dominant kernel's roofline unit
+    rscale = 1e9 if ru == "GB/s" else 1e12
+    achieved = wl.dom_units / (dom_ms / 1e3) / rscale
     peak = HBM_PEAK_GBS if wl.bound == "hbm" else MFMA_PEAK_TFLOPS[wl.dtype]
     tag = wl.name + (f"-b{wl.B}" if isinstance(wl, Q4MLP) else "") + (
         "-steps" if isinstance(wl, Summa) and not wl.fused else "")
     traffic = load_traffic(wl, tag)
-    roofline = {"bound": wl.bound, "achieved": round(achieved, 2), "peak": peak, "unit": wl.unit,
+    roofline = {"bound": wl.bound, "achieved": round(achieved, 2), "peak": peak, "unit": ru,
                 "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": wl.dominant,
                 "kernel_us": round(dom_ms * 1e3, 2), "kernel_samples": n_samp, "kernel_timing": how,
-                "algorithmic": f"{wl.dom_units / (1e9 if wl.unit == 'GB/s' else 1e12):.4g} "
-                               f"{'GB' if wl.unit == 'GB/s' else 'TFLOP'} per launch"}
+                "algorithmic": f"{wl.dom_units / rscale:.4g} "
+                               f"{'GB' if ru == 'GB/s' else 'TFLOP'} per launch"}
 
     cpu = None
     if not args.no_cpu_baseline:
