@@ -140,13 +140,19 @@ sg_status common_checks(int mode, int segments, int P, int64_t out_dims, int64_t
 // ---------------------------------------------------------------------------
 // kernel choice
 // ---------------------------------------------------------------------------
-enum Kind { K_GENERIC, K_TILE0, K_TILE1, K_SKINNY, K_Q4, K_Q4TILE };
+enum Kind { K_GENERIC, K_TILE0, K_TILE1, K_SKINNY, K_Q4, K_Q4TILE, K_NW };
 
 int num_cus() { return sg::device_cus(); }
 
 // dense operands: the MFMA paths need 16-byte rows
 bool mfma_ok(const sg_layer* l, const void* x) {
     return l->dtype != SG_F32 && l->cols_r % 8 == 0 && aligned16(x) && aligned16(l->w);
+}
+
+// the few-token tile kernel: 33 to 256 tokens, 32-wide k tiles, weights
+// addressable through 32-bit offsets
+bool nw_ok(const sg_layer* l, int64_t B) {
+    return B > 32 && B <= 256 && l->cols_r % 32 == 0 && (double)l->P * l->rows_r * l->cols_r * 2 < 2.0e9;
 }
 
 // the streaming kernels keep one LDS slot per (rank, part): bounded ranks only
@@ -184,8 +190,11 @@ Kind choose(const sg_layer* l, int64_t B, const void* x, int swiglu = 0, int nse
     }
     if (!mfma_ok(l, x)) return K_GENERIC;
     if (B <= 32 && skinny_fits(l, B, swiglu, nseg)) return K_SKINNY;
-    // up to 256 tokens the 128 x 128 tiles (more workgroups); beyond, the
-    // ping-pong kernel (decode-MLP gate|up at 384 tokens: 187 -> 122 us)
+    // up to 128 tokens the few-token tiles (decode-MLP gate|up at 64 tokens:
+    // 98 us on the 128 x 128 tiles, 54 on them); from 129 to 256 the 128 x 128
+    // tiles (at 256: 108 against 119 us); beyond, the ping-pong kernel (at 384
+    // tokens: 187 us on the 128 x 128 tiles, 122 on it)
+    if (B <= 128 && nw_ok(l, B)) return K_NW;
     return B > 256 ? K_TILE0 : K_TILE1;
 }
 
@@ -199,6 +208,7 @@ bool want_split(const sg_layer* l, Kind k, int64_t B) {
     switch (k) {
     case K_TILE0: return sg::tile_count((int)B, (int)l->out_dims, 0) * 2 <= cus;
     case K_TILE1: return sg::tile_count((int)B, (int)l->out_dims, 1) * 2 <= cus;
+    case K_NW: return sg::tile_nw_count((int)B, (int)l->out_dims, 0) * 2 <= cus;
     // the 4-bit tile kernel (three workgroups per CU) splits up to one tile
     // per CU (decode-MLP down projection: 126 -> 45 us at 192 tokens, 143 ->
     // 101 us at 512)
@@ -211,6 +221,10 @@ sg::SplitLayout split_layout(const sg_layer* l, Kind k, int64_t B) {
     switch (k) {
     case K_TILE0: return sg::tile_split_layout((int)B, (int)l->out_dims, l->P, 0);
     case K_TILE1: return sg::tile_split_layout((int)B, (int)l->out_dims, l->P, 1);
+    case K_NW: {
+        const size_t t = (size_t)sg::tile_nw_count((int)B, (int)l->out_dims, 0);
+        return {t * (B <= 64 ? 64 : 128) * 128 * (size_t)sg::split_groups((int)t, l->P), t};
+    }
     case K_Q4TILE: {
         const size_t t = (size_t)sg::q4_tile_count((int)B, (int)l->out_dims);
         return {t * (size_t)sg::q4_tile_rows((int)B) * 128 * l->P, t};
@@ -226,9 +240,12 @@ Kind choose_row(const sg_layer* l, int64_t B) {
     if (l->quantized) return !l->qfrag ? K_GENERIC : (B <= 32 && q4_fits(l, B, 0) ? K_Q4 : K_Q4TILE);
     if (l->dtype == SG_F32 || l->cols_r % 8) return K_GENERIC;
     if (B <= 32 && skinny_fits(l, B, 0, l->P)) return K_SKINNY;
-    // the ping-pong kernel split into groups of ranks whenever the output
-    // gives too few tiles (decode-MLP down projection against the 128 x 128
-    // tiles: 93 -> 56 us at 64 tokens, 139 -> 69 us at 256)
+    // up to 256 tokens the few-token tiles, beyond them the ping-pong kernel,
+    // either split into groups of ranks whenever the output gives too few
+    // tiles (decode-MLP down projection at 64 tokens: 93 us on the split
+    // 128 x 128 tiles, 56 on the split ping-pong kernel, 36 on the few-token
+    // tiles; at 256 tokens 139, 69 and 58 us)
+    if (nw_ok(l, B)) return K_NW;
     return K_TILE0;
 }
 
@@ -243,6 +260,9 @@ hipError_t run(const sg::Problem& p, Kind k, hipStream_t st) {
     case K_SKINNY: return sg::launch_skinny(p, st);
     case K_Q4: return sg::launch_q4(p, st);
     case K_Q4TILE: return sg::launch_q4_tile(p, st);
+    // (a split call's workspace is laid out for this kernel: no fallback then)
+    case K_NW: return sg::tile_nw_fits(p) ? sg::launch_tile_nw(p, st)
+                      : p.split ? hipErrorInvalidValue : sg::launch_tile(p, st, 1);
     default: return sg::launch_generic(p, st);
     }
 }

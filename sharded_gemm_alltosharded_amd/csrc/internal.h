@@ -189,10 +189,19 @@ int device_cus();
 // sharded-to-all product into: the fewest that divide nseg and give every
 // compute unit a workgroup
 int tile_pp_groups(int M, int N, int nseg);
+// the fewest groups of consecutive segments (dividing nseg) that give every
+// compute unit a workgroup when each output tile runs once per group
+int split_groups(int tiles, int nseg);
 // second kernel of a split tile product: adds the groups' partial tiles in
 // order and stores them; layout 0: ping-pong 256 x 256 tiles, 1: register-
-// staged 128 x 128, 2: register-staged 256 x 256
+// staged 128 x 128, 2: register-staged 256 x 256, 3 and 4: few-token 64 x 128
+// and 128 x 128
 hipError_t launch_split_reduce(const Problem& p, int tiles_m, int tiles_n, int groups, int layout, hipStream_t s);
+// few-token tile kernel (tile_dma.hip): up to 256 tokens, 64- or 128-token
+// tiles of 128 weight rows
+int tile_nw_count(int M, int N, int swiglu);
+bool tile_nw_fits(const Problem& p);
+hipError_t launch_tile_nw(const Problem& p, hipStream_t s);
 
 // launch shapes of the streaming kernels (dynamic LDS bytes included)
 struct SkinnyShape {

@@ -405,8 +405,16 @@ hipError_t launch_split_reduce(const Problem& p, int tiles_m, int tiles_n, int g
         launch((split_reduce_kernel<128, 128, 64, 64, 256, false, RV>), dim3(ntiles, 16 / RV), dim3(256), 0, s, p,
                tiles_m, tiles_n, groups);
         break;
-    default:  // register-staged 256 x 256, 4 waves of 128 x 128: 64 float4 per thread
+    case 2:  // register-staged 256 x 256, 4 waves of 128 x 128: 64 float4 per thread
         launch((split_reduce_kernel<256, 256, 128, 128, 256, false, RV>), dim3(ntiles, 64 / RV), dim3(256), 0, s, p,
+               tiles_m, tiles_n, groups);
+        break;
+    case 3:  // few-token 64 x 128, 4 waves of 32 x 64: 8 float4 per thread
+        launch((split_reduce_kernel<64, 128, 32, 64, 256, true, RV>), dim3(ntiles, 8 / RV), dim3(256), 0, s, p,
+               tiles_m, tiles_n, groups);
+        break;
+    default:  // few-token 128 x 128, 4 waves of 64 x 64: 16 float4 per thread
+        launch((split_reduce_kernel<128, 128, 64, 64, 256, true, RV>), dim3(ntiles, 16 / RV), dim3(256), 0, s, p,
                tiles_m, tiles_n, groups);
         break;
     }
@@ -431,12 +439,14 @@ int device_cus() {
     return cus;
 }
 
-int tile_pp_groups(int M, int N, int nseg) {
-    const int tiles = tile_count(M, N, 0), cus = device_cus();
+int split_groups(int tiles, int nseg) {
+    const int cus = device_cus();
     for (int d = 1; d < nseg; ++d)
         if (nseg % d == 0 && tiles * d >= cus) return d;
     return nseg;
 }
+
+int tile_pp_groups(int M, int N, int nseg) { return split_groups(tile_count(M, N, 0), nseg); }
 
 // variant 0 splits into tile_pp_groups groups, variant 1 into nseg
 SplitLayout tile_split_layout(int M, int N, int nseg, int variant) {

@@ -342,6 +342,249 @@ __global__ __launch_bounds__(512) void tile_pp_kernel(Problem p, int tiles_m, in
     });
 }
 
+// Few-token tile kernel (33 to 256 tokens): TM = 64 or 128 tokens x 128
+// weight rows (SwiGLU: 64 gate rows and the 64 matching up rows), BK = 32, 4
+// waves of TM/2 tokens x 64 rows.  In this range a layer is bound by
+// streaming its weights, and the 256 x 256 tiles would waste most of their
+// MFMA work on padding rows, so the tile is narrow and the LDS holds a deep
+// ring of NS stages: k tile t + NS - 1 is issued while k tile t is read, one
+// workgroup barrier per k tile.  The loads, the LDS layout and the fragment
+// reads are the ping-pong kernel's (direct-to-LDS 16-byte loads through
+// buffer resources, rows XOR-swizzled by (row >> 2) & 3).  Every wave issues
+// the same number of loads for every k tile (past the last k tile, a repeat
+// of it into a stage never read), so the wait before each barrier is a
+// compile-time count.  SPLIT: as the ping-pong kernel (groups of consecutive
+// segments, partial tiles summed by split_reduce_kernel).
+template <int TM>
+struct NarrowShape {
+    static constexpr int BN = 128, BK = 32;
+    static constexpr int WTM = TM / 2, WTN = 64, NBM = WTM / 32, NBN = WTN / 32;
+    static constexpr int LA = TM / 64, LB = BN / 64, L = LA + LB;  // loads per thread per stage
+    static constexpr int SA = TM * BK, SB = BN * BK;               // elements per stage
+    static constexpr int NS = TM == 64 ? 8 : 6;                    // 96 KB of stages
+};
+
+template <int NBN, int NBM>
+__device__ __forceinline__ void wait_lds_n(u32x4 (&w)[NBN], u32x4 (&x)[NBM]) {
+    static_assert(NBN == 2 && (NBM == 1 || NBM == 2), "fragment counts of the few-token tiles");
+    if constexpr (NBM == 1)
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(w[0]), "+v"(w[1]), "+v"(x[0]));
+    else
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(w[0]), "+v"(w[1]), "+v"(x[0]), "+v"(x[1]));
+}
+
+template <bool F16, bool SWIGLU, bool SPLIT, int TM>
+__global__ __launch_bounds__(256) void tile_nw_kernel(Problem p, int tiles_m, int tiles_n) {
+    using S = NarrowShape<TM>;
+    constexpr int BN = S::BN, BK = S::BK, NW = 4, NS = S::NS;
+    constexpr int WTM = S::WTM, WTN = S::WTN, NBM = S::NBM, NBN = S::NBN;
+    constexpr int LA = S::LA, LB = S::LB, L = S::L, SA = S::SA, SB = S::SB;
+    constexpr int NOUT = SWIGLU ? BN / 2 : BN;
+    __shared__ __attribute__((aligned(1024))) uint16_t sA[NS * SA], sB[NS * SB];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave_m = wave & 1, wave_n = wave >> 1;
+
+    const int ntiles = tiles_m * tiles_n;
+    const int tile = xcd_remap(blockIdx.x, ntiles);
+    constexpr int GM = 4;
+    const int gidx = tile / (GM * tiles_n);
+    const int first_m = gidx * GM;
+    const int gsz = min(GM, tiles_m - first_m);
+    const int tin = tile - gidx * GM * tiles_n;
+    const int m0 = (first_m + tin % gsz) * TM;
+    const int64_t n0 = (int64_t)(tin / gsz) * NOUT;
+
+    // load i of wave w fills rows (4 i + w) * 16 .. + 16 of its operand
+    const int lr = lane >> 2, lc = lane & 3;
+    uint32_t aoff[LA], boff[LB];
+#pragma unroll
+    for (int i = 0; i < LA; ++i) {
+        const int row = (NW * i + wave) * 16 + lr;
+        const int m = min(m0 + row, p.M - 1);
+        aoff[i] = (uint32_t)(((int64_t)m * p.lda + (lc ^ swz4(row)) * 8) * 2);
+    }
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+        const int row = (NW * i + wave) * 16 + lr;
+        const int ch = lc ^ swz4(row);
+        int64_t wrow;
+        if constexpr (SWIGLU) {
+            const int64_t j = min(n0 + (row >> 6) * 32 + (row & 31), (int64_t)p.N - 1);
+            wrow = weight_row(p, j, (row >> 5) & 1);
+        } else {
+            wrow = min(n0 + row, (int64_t)p.N - 1);
+        }
+        boff[i] = (uint32_t)((p.wfrag ? frag_offset(wrow, ch * 8, p.wsteps) : wrow * p.ldw + ch * 8) * 2);
+    }
+    const int bk_step = p.wfrag ? 16 : 1;
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)p.A, 0, (int)a_extent(p), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)p.W, 0, (int)w_extent(p), 0x00020000);
+    const int ktiles_seg = p.Kseg / BK;
+    const int gsegs = SPLIT ? p.nseg / (int)gridDim.y : p.nseg;
+    const int nkt = ktiles_seg * gsegs;
+    const int seg_lo = SPLIT ? (int)blockIdx.y * gsegs : 0;
+
+    // k tile kt into stage kt mod NS; past the last k tile, the last again
+    auto issue = [&](int kt) {
+        uint16_t* a = sA + (kt % NS) * SA;
+        uint16_t* b = sB + (kt % NS) * SB;
+        const int kc = min(kt, nkt - 1);
+        const int s = seg_lo + kc / ktiles_seg;
+        const int k0 = (kc - (s - seg_lo) * ktiles_seg) * BK;
+        const uint32_t sa = (uint32_t)((s * p.a_seg + k0) * 2);
+        const uint32_t sw = (uint32_t)((s * p.w_seg + (int64_t)k0 * bk_step) * 2);
+#pragma unroll
+        for (int i = 0; i < LA; ++i) dma16(ra, aoff[i], sa, a + (NW * i + wave) * 16 * BK);
+#pragma unroll
+        for (int i = 0; i < LB; ++i) dma16(rw, boff[i], sw, b + (NW * i + wave) * 16 * BK);
+    };
+
+    f32x16 acc[NBN][NBM];
+#pragma unroll
+    for (int i = 0; i < NBN; ++i)
+#pragma unroll
+        for (int j = 0; j < NBM; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+    const int frow = lane & 31, fch = lane >> 5;
+    u32x4 w0[NBN], x0[NBM], w1[NBN], x1[NBM];
+    auto read = [&](int t, int kk, u32x4 (&wf)[NBN], u32x4 (&xf)[NBM]) {
+        const uint16_t* a = sA + (t % NS) * SA;
+        const uint16_t* b = sB + (t % NS) * SB;
+        const int c = kk * 2 + fch;
+#pragma unroll
+        for (int i = 0; i < NBN; ++i) {
+            const int row = wave_n * WTN + i * 32 + frow;
+            wf[i] = lds_read16(b + row * BK + ((c ^ swz4(row)) << 3));
+        }
+#pragma unroll
+        for (int j = 0; j < NBM; ++j) {
+            const int row = wave_m * WTM + j * 32 + frow;
+            xf[j] = lds_read16(a + row * BK + ((c ^ swz4(row)) << 3));
+        }
+    };
+
+    if (nkt > 0) {
+        for (int t = 0; t < NS - 1; ++t) issue(t);
+        for (int t = 0; t < nkt; ++t) {
+            // this wave's loads of k tile t have landed (those of the NS - 2
+            // later k tiles may be in flight); the barrier publishes k tile t
+            // and ends every wave's reads of k tile t - 1, whose stage the
+            // loads of k tile t + NS - 1 reuse
+            wait_vm<(NS - 2) * L>();
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            read(t, 0, w0, x0);
+            read(t, 1, w1, x1);
+            issue(t + NS - 1);
+            wait_lds_n<NBN, NBM>(w0, x0);
+            wait_lds_n<NBN, NBM>(w1, x1);
+#pragma unroll
+            for (int i = 0; i < NBN; ++i)
+#pragma unroll
+                for (int j = 0; j < NBM; ++j) acc[i][j] = mfma32<F16>(w0[i], x0[j], acc[i][j]);
+#pragma unroll
+            for (int i = 0; i < NBN; ++i)
+#pragma unroll
+                for (int j = 0; j < NBM; ++j) acc[i][j] = mfma32<F16>(w1[i], x1[j], acc[i][j]);
+        }
+        // no load may still be writing this workgroup's LDS when it ends
+        wait_vm<0>();
+    }
+
+    if constexpr (SPLIT) {
+        f32x4* mine = (f32x4*)(p.ws + ((int64_t)blockIdx.y * ntiles + tile) * (TM * BN));
+#pragma unroll
+        for (int i = 0; i < NBN; ++i)
+#pragma unroll
+            for (int j = 0; j < NBM; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                     acc[i][j][4 * q + 3]};
+                    mine[((i * NBM + j) * 4 + q) * 256 + tid] = v;
+                }
+        return;
+    }
+
+    // epilogue: lane l of a 32 x 32 block holds column l & 31 (token) and rows
+    // 8 blk + 4 (l >> 5) + e (weight rows) of the block
+    const int hi = lane >> 5;
+    static_for<0, NBN>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (SWIGLU && (i & 1)) return;
+        static_for<0, NBM>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            const int m = m0 + wave_m * WTM + j * 32 + (lane & 31);
+            if (m >= p.M) return;
+            static_for<0, 4>([&](auto bc) {
+                constexpr int blk = decltype(bc)::value;
+                int64_t n;
+                float v[4];
+                if constexpr (SWIGLU) {
+                    n = n0 + wave_n * 32 + 8 * blk + 4 * hi;  // blocks 2 wave_n (gate), 2 wave_n + 1 (up)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        v[e] = silu_f32(acc[i][j][4 * blk + e]) * acc[i | 1][j][4 * blk + e];  // i even: i | 1 = i + 1
+                } else {
+                    n = n0 + wave_n * WTN + i * 32 + 8 * blk + 4 * hi;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * blk + e];
+                }
+                store4(p, m, n, v);
+            });
+        });
+    });
+}
+
+// tiles of the few-token kernel
+int tile_nw_count(int M, int N, int swiglu) {
+    const int tm = M <= 64 ? 64 : 128, nout = swiglu ? 64 : 128;
+    return ((M + tm - 1) / tm) * ((N + nout - 1) / nout);
+}
+
+bool tile_nw_fits(const Problem& p) {
+    return !p.nn && !(p.split && p.swiglu) && !p.fp8 && !p.wq && p.Kseg % 32 == 0 && p.M <= 256 &&
+           a_extent(p) < (1LL << 31) && w_extent(p) < (1LL << 31);
+}
+
+template <int TM, bool SPLIT>
+static void launch_nw_tm(const Problem& p, hipStream_t s, dim3 grid, int tm, int tn) {
+    const bool f16 = p.dtype == SG_F16;
+    if (p.swiglu) {
+        if constexpr (!SPLIT) {
+            if (f16) launch(tile_nw_kernel<true, true, false, TM>, grid, dim3(256), 0, s, p, tm, tn);
+            else launch(tile_nw_kernel<false, true, false, TM>, grid, dim3(256), 0, s, p, tm, tn);
+        }
+    } else {
+        if (f16) launch(tile_nw_kernel<true, false, SPLIT, TM>, grid, dim3(256), 0, s, p, tm, tn);
+        else launch(tile_nw_kernel<false, false, SPLIT, TM>, grid, dim3(256), 0, s, p, tm, tn);
+    }
+}
+
+hipError_t launch_tile_nw(const Problem& p, hipStream_t s) {
+    if (p.M == 0 || p.N == 0) return hipSuccess;
+    if (!tile_nw_fits(p)) return hipErrorInvalidValue;
+    const int TMv = p.M <= 64 ? 64 : 128, nout = p.swiglu ? 64 : 128;
+    const int tm = (p.M + TMv - 1) / TMv, tn = (p.N + nout - 1) / nout;
+    const int groups = p.split ? split_groups(tm * tn, p.nseg) : 1;
+    const dim3 grid(tm * tn, groups);
+    if (TMv == 64) {
+        if (p.split) launch_nw_tm<64, true>(p, s, grid, tm, tn);
+        else launch_nw_tm<64, false>(p, s, grid, tm, tn);
+    } else {
+        if (p.split) launch_nw_tm<128, true>(p, s, grid, tm, tn);
+        else launch_nw_tm<128, false>(p, s, grid, tm, tn);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !p.split) return e;
+    return launch_split_reduce(p, tm, tn, groups, TMv == 64 ? 3 : 4, s);
+}
+
 bool tile_dma_fits(const Problem& p) {
     return !p.nn && !(p.split && p.swiglu) && !p.fp8 && !p.wq && p.Kseg % 32 == 0 && a_extent(p) < (1LL << 31) &&
            w_extent(p) < (1LL << 31);
