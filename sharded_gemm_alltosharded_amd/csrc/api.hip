@@ -190,11 +190,11 @@ Kind choose(const sg_layer* l, int64_t B, const void* x, int swiglu = 0, int nse
     }
     if (!mfma_ok(l, x)) return K_GENERIC;
     if (B <= 32 && skinny_fits(l, B, swiglu, nseg)) return K_SKINNY;
-    // up to 128 tokens the few-token tiles (decode-MLP gate|up at 64 tokens:
-    // 98 us on the 128 x 128 tiles, 54 on them); from 129 to 256 the 128 x 128
-    // tiles (at 256: 108 against 119 us); beyond, the ping-pong kernel (at 384
-    // tokens: 187 us on the 128 x 128 tiles, 122 on it)
-    if (B <= 128 && nw_ok(l, B)) return K_NW;
+    // up to 256 tokens the few-token tiles (decode-MLP gate|up at 64 tokens:
+    // 98 us on the 128 x 128 tiles, 54 on them; at 160, 113 against 95 us);
+    // beyond, the ping-pong kernel (at 384 tokens: 187 us on the 128 x 128
+    // tiles, 122 on it)
+    if (nw_ok(l, B)) return K_NW;
     return B > 256 ? K_TILE0 : K_TILE1;
 }
 
@@ -223,7 +223,7 @@ sg::SplitLayout split_layout(const sg_layer* l, Kind k, int64_t B) {
     case K_TILE1: return sg::tile_split_layout((int)B, (int)l->out_dims, l->P, 1);
     case K_NW: {
         const size_t t = (size_t)sg::tile_nw_count((int)B, (int)l->out_dims, 0);
-        return {t * (B <= 64 ? 64 : 128) * 128 * (size_t)sg::split_groups((int)t, l->P), t};
+        return {t * (size_t)sg::tile_nw_tm((int)B) * 128 * (size_t)sg::split_groups((int)t, l->P), t};
     }
     case K_Q4TILE: {
         const size_t t = (size_t)sg::q4_tile_count((int)B, (int)l->out_dims);

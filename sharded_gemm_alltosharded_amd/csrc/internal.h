@@ -194,11 +194,12 @@ int tile_pp_groups(int M, int N, int nseg);
 int split_groups(int tiles, int nseg);
 // second kernel of a split tile product: adds the groups' partial tiles in
 // order and stores them; layout 0: ping-pong 256 x 256 tiles, 1: register-
-// staged 128 x 128, 2: register-staged 256 x 256, 3 and 4: few-token 64 x 128
-// and 128 x 128
+// staged 128 x 128, 2: register-staged 256 x 256, 3, 4 and 5: few-token
+// 64 x 128, 128 x 128 and 256 x 128
 hipError_t launch_split_reduce(const Problem& p, int tiles_m, int tiles_n, int groups, int layout, hipStream_t s);
-// few-token tile kernel (tile_dma.hip): up to 256 tokens, 64- or 128-token
-// tiles of 128 weight rows
+// few-token tile kernel (tile_dma.hip): up to 256 tokens, 64-, 128- or
+// 256-token tiles (tile_nw_tm) of 128 weight rows
+int tile_nw_tm(int M);
 int tile_nw_count(int M, int N, int swiglu);
 bool tile_nw_fits(const Problem& p);
 hipError_t launch_tile_nw(const Problem& p, hipStream_t s);

@@ -413,8 +413,12 @@ hipError_t launch_split_reduce(const Problem& p, int tiles_m, int tiles_n, int g
         launch((split_reduce_kernel<64, 128, 32, 64, 256, true, RV>), dim3(ntiles, 8 / RV), dim3(256), 0, s, p,
                tiles_m, tiles_n, groups);
         break;
-    default:  // few-token 128 x 128, 4 waves of 64 x 64: 16 float4 per thread
+    case 4:  // few-token 128 x 128, 4 waves of 64 x 64: 16 float4 per thread
         launch((split_reduce_kernel<128, 128, 64, 64, 256, true, RV>), dim3(ntiles, 16 / RV), dim3(256), 0, s, p,
+               tiles_m, tiles_n, groups);
+        break;
+    default:  // few-token 256 x 128, 4 waves of 128 x 64: 32 float4 per thread
+        launch((split_reduce_kernel<256, 128, 128, 64, 256, true, RV>), dim3(ntiles, 32 / RV), dim3(256), 0, s, p,
                tiles_m, tiles_n, groups);
         break;
     }

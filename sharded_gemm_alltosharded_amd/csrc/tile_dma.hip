@@ -361,16 +361,18 @@ struct NarrowShape {
     static constexpr int WTM = TM / 2, WTN = 64, NBM = WTM / 32, NBN = WTN / 32;
     static constexpr int LA = TM / 64, LB = BN / 64, L = LA + LB;  // loads per thread per stage
     static constexpr int SA = TM * BK, SB = BN * BK;               // elements per stage
-    static constexpr int NS = TM == 64 ? 8 : 6;                    // 96 KB of stages
+    static constexpr int NS = TM == 64 ? 8 : TM == 128 ? 6 : 4;    // 96 KB of stages
 };
 
 template <int NBN, int NBM>
 __device__ __forceinline__ void wait_lds_n(u32x4 (&w)[NBN], u32x4 (&x)[NBM]) {
-    static_assert(NBN == 2 && (NBM == 1 || NBM == 2), "fragment counts of the few-token tiles");
+    static_assert(NBN == 2 && (NBM == 1 || NBM == 2 || NBM == 4), "fragment counts of the few-token tiles");
     if constexpr (NBM == 1)
         asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(w[0]), "+v"(w[1]), "+v"(x[0]));
-    else
+    else if constexpr (NBM == 2)
         asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(w[0]), "+v"(w[1]), "+v"(x[0]), "+v"(x[1]));
+    else
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(w[0]), "+v"(w[1]), "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]));
 }
 
 template <bool F16, bool SWIGLU, bool SPLIT, int TM>
@@ -541,9 +543,12 @@ __global__ __launch_bounds__(256) void tile_nw_kernel(Problem p, int tiles_m, in
     });
 }
 
+// token tile of the few-token kernel
+int tile_nw_tm(int M) { return M <= 64 ? 64 : M <= 128 ? 128 : 256; }
+
 // tiles of the few-token kernel
 int tile_nw_count(int M, int N, int swiglu) {
-    const int tm = M <= 64 ? 64 : 128, nout = swiglu ? 64 : 128;
+    const int tm = tile_nw_tm(M), nout = swiglu ? 64 : 128;
     return ((M + tm - 1) / tm) * ((N + nout - 1) / nout);
 }
 
@@ -569,20 +574,23 @@ static void launch_nw_tm(const Problem& p, hipStream_t s, dim3 grid, int tm, int
 hipError_t launch_tile_nw(const Problem& p, hipStream_t s) {
     if (p.M == 0 || p.N == 0) return hipSuccess;
     if (!tile_nw_fits(p)) return hipErrorInvalidValue;
-    const int TMv = p.M <= 64 ? 64 : 128, nout = p.swiglu ? 64 : 128;
+    const int TMv = tile_nw_tm(p.M), nout = p.swiglu ? 64 : 128;
     const int tm = (p.M + TMv - 1) / TMv, tn = (p.N + nout - 1) / nout;
     const int groups = p.split ? split_groups(tm * tn, p.nseg) : 1;
     const dim3 grid(tm * tn, groups);
     if (TMv == 64) {
         if (p.split) launch_nw_tm<64, true>(p, s, grid, tm, tn);
         else launch_nw_tm<64, false>(p, s, grid, tm, tn);
-    } else {
+    } else if (TMv == 128) {
         if (p.split) launch_nw_tm<128, true>(p, s, grid, tm, tn);
         else launch_nw_tm<128, false>(p, s, grid, tm, tn);
+    } else {
+        if (p.split) launch_nw_tm<256, true>(p, s, grid, tm, tn);
+        else launch_nw_tm<256, false>(p, s, grid, tm, tn);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !p.split) return e;
-    return launch_split_reduce(p, tm, tn, groups, TMv == 64 ? 3 : 4, s);
+    return launch_split_reduce(p, tm, tn, groups, TMv == 64 ? 3 : TMv == 128 ? 4 : 5, s);
 }
 
 bool tile_dma_fits(const Problem& p) {
