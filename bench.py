@@ -8,7 +8,8 @@ synthetic inputs already resident in HBM.  The default workload is the
 Llama-style gated MLP decode step (B=16 tokens, D=4096, F=14336, P=8 ranks on
 one GPU, bf16): gate/up all-to-sharded with the fused SwiGLU epilogue, then
 down sharded-to-all with the fused rank sum, through the fused MLP entry point
-(sg_mlp, the sharded h kept in its workspace).  Other workloads:
+(sg_mlp, the sharded h kept in its workspace); --batch sets other token
+counts (33-256 run the few-token tile kernel).  Other workloads:
 
     3   prefill: B=4096, P=4, fused QKV column shard (segments=3) + the MLP
     4   4-bit affine MLP (group 64), B in {1, 8, 32} (--batch; beyond 32 tokens the
@@ -54,7 +55,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--config", default="2", choices=["1", "2", "3", "4", "5a", "5b", "5c", "6", "7"])
-    ap.add_argument("--batch", type=int, default=1, help="tokens for the 4-bit workload (1, 8 or 32; more runs the 4-bit tile kernel)")
+    ap.add_argument("--batch", type=int, default=None,
+                    help="tokens: the 4-bit workload (1, 8 or 32, default 1; more runs the 4-bit tile kernel) or "
+                         "the decode MLP (default 16; 33-256 run the few-token tile kernel)")
     ap.add_argument("--summa", default="fused", choices=["fused", "steps"])
     ap.add_argument("--rank-share", action="store_true",
                     help="configs 2, 3, 4, 5b: only rank 0's share of the layers (P = 1, the per-GPU shapes "
@@ -126,13 +129,19 @@ def _dev_tensor(a, dtype):
 
 
 class DecodeMLP(Workload):
-    """Gated MLP decode: B=16, D=4096, F=14336, P=8, bf16."""
+    """Gated MLP decode: B=16 (or --batch), D=4096, F=14336, P=8, bf16."""
     B, D, F, P = 16, 4096, 14336, 8
     name = "llama-mlp-decode"
     metric = "sharded-MLP decode GB/s (% HBM peak)"
     rotate = 2
     dominant = "skinny_kernel (gate|up all-to-sharded + SwiGLU)"
     dominant_src = ("skinny.hip", "internal.h")
+
+    def __init__(self, B=16):
+        self.B = B
+        if B > 32:  # beyond the streaming kernels
+            self.dominant = "tile_nw_kernel (gate|up all-to-sharded + SwiGLU, few-token tiles)"
+            self.dominant_src = ("tile_dma.hip", "internal.h")
 
     def setup(self):
         import numpy as np
@@ -715,8 +724,8 @@ class BackwardMLP(Workload):
 
 
 def make(args) -> Workload:
-    wl = {"1": lambda: Tiny(), "2": lambda: DecodeMLP(), "3": lambda: PrefillMLP(),
-          "4": lambda: Q4MLP(args.batch), "5a": lambda: Summa(args.summa == "fused"),
+    wl = {"1": lambda: Tiny(), "2": lambda: DecodeMLP(args.batch or 16), "3": lambda: PrefillMLP(),
+          "4": lambda: Q4MLP(args.batch or 1), "5a": lambda: Summa(args.summa == "fused"),
           "5b": lambda: VocabHead(), "6": lambda: MxfpDecodeMLP(), "7": lambda: BackwardMLP(),
           "5c": lambda: SummaBackward()}[args.config]()
     if getattr(args, "rank_share", False):
@@ -886,7 +895,7 @@ def main():
     rscale = 1e9 if ru == "GB/s" else 1e12
     achieved = wl.dom_units / (dom_ms / 1e3) / rscale
     peak = HBM_PEAK_GBS if wl.bound == "hbm" else MFMA_PEAK_TFLOPS[wl.dtype]
-    tag = wl.name + (f"-b{wl.B}" if isinstance(wl, Q4MLP) else "") + (
+    tag = wl.name + (f"-b{wl.B}" if isinstance(wl, Q4MLP) or (isinstance(wl, DecodeMLP) and wl.B != 16) else "") + (
         "-steps" if isinstance(wl, Summa) and not wl.fused else "")
     traffic = load_traffic(wl, tag)
     roofline = {"bound": wl.bound, "achieved": round(achieved, 2), "peak": peak, "unit": ru,
