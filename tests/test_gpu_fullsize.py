@@ -49,6 +49,28 @@ def test_decode_mlp_full():
     assert torch.equal(sg.mlp(gu, dn, x), y)
 
 
+@pytest.mark.parametrize("B", [64, 256])
+def test_decode_mlp_more_tokens(B):
+    """The decode-MLP layers at 64 and 256 tokens (the few-token tiles; the
+    down layer split into rank groups, their partial tiles summed by the second
+    kernel): eight sampled tokens against the oracle, the fused entry point bit
+    for bit against the two calls."""
+    _case(f"decode MLP B={B} D=4096 F=14336 P=8")
+    D, F, P = 4096, 14336, 8
+    inp = synth.mlp_inputs(B, D, F, P, "bf16", seed=1)
+    gu = sg.shard_linear(to_dev(np.concatenate([inp.Wg, inp.Wu]), "bf16"), "all-to-sharded", segments=2, P=P)
+    dn = sg.shard_linear(to_dev(inp.Wd, "bf16"), "sharded-to-all", P=P)
+    x = to_dev(inp.X, "bf16")
+    h = sg.all_to_sharded(gu, x, swiglu=True)
+    y = sg.sharded_to_all(dn, h)
+    idx = sorted({0, 1, B // 2, B - 1, *np.random.default_rng(B).choice(B, 4, replace=False).tolist()})
+    X, Wg, Wu, Wd = (oracle.decode(a, "bf16") for a in (inp.X[idx], inp.Wg, inp.Wu, inp.Wd))
+    g, u = oracle.col(X, Wg, P=P), oracle.col(X, Wu, P=P)
+    assert_close(h[:, idx], oracle.swiglu(g, u, "f64"), "bf16", "h")
+    assert_close(y[idx], oracle.row(oracle.swiglu(g, u, "bf16"), Wd, P=P), "bf16", "y")
+    assert torch.equal(sg.mlp(gu, dn, x), y)
+
+
 def test_mxfp8_mlp_full():
     """MX FP8 decode MLP (the layers bench.py times for it): B=16, D=4096,
     F=14336, P=8, E4M3 codes with E8M0 scales per 32 inputs; every token."""
@@ -97,9 +119,11 @@ def q4_weights():
     return synth.q4_mlp_weights(4096, 14336, seed=20)
 
 
-@pytest.mark.parametrize("B", [1, 8, 32])
+@pytest.mark.parametrize("B", [1, 8, 32, 64, 512])
 def test_q4_mlp_full(q4_weights, B):
-    """4-bit affine MLP, D=4096, F=14336, P=4 (sampled tokens at B=32)."""
+    """4-bit affine MLP, D=4096, F=14336, P=4 (sampled tokens beyond 8): the
+    streaming kernels up to 32 tokens, the 4-bit tile kernels beyond (at 64
+    tokens the down layer split by rank, summed by the second kernel)."""
     _case(f"4-bit MLP B={B}")
     D, F, P = 4096, 14336, 4
     q = q4_weights
@@ -118,7 +142,7 @@ def test_q4_mlp_full(q4_weights, B):
     X = synth.normal(0, (B, D), 1.0, "bf16")
     h = sg.all_to_sharded(gu, to_dev(X, "bf16"), swiglu=True)
     y = sg.sharded_to_all(dn, h)
-    idx = np.arange(B) if B <= 8 else np.array([0, 5, 16, 31])
+    idx = np.arange(B) if B <= 8 else np.array(sorted({0, 5, 16, 31, B // 2 + 3, B - 1}))
     W = {k: oracle.deq4(*q[k][:3], 64) for k in ("gate", "up", "down")}
     Xs = oracle.decode(X[idx], "bf16")
     g, u = oracle.col(Xs, W["gate"], P=P), oracle.col(Xs, W["up"], P=P)
