@@ -525,7 +525,7 @@ def test_all_gather_input(B, P):
     assert_close(yb, oracle.col(xg, W, P=P, bias=b, dtype="bf16"), "bf16", "gathered-input col bf16")
 
 
-@pytest.mark.parametrize("B", [16, 600])
+@pytest.mark.parametrize("B", [16, 100, 600])
 def test_all_gather_input_swiglu(B):
     _print_case(B=B)
     D, F, P = 512, 1024, 4
