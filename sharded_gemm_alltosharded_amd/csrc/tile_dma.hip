@@ -546,6 +546,207 @@ __global__ __launch_bounds__(256) void tile_nw_kernel(Problem p, int tiles_m, in
 // token tile of the few-token kernel
 int tile_nw_tm(int M) { return M <= 64 ? 64 : M <= 128 ? 128 : 256; }
 
+
+// The few-token tile with 64-wide k tiles, for fragment-major weights whose
+// 16-row blocks are whole stored blocks (SwiGLU: rank widths a multiple of
+// 16): a wave-wide load then brings one stored 1 KB weight fragment verbatim
+// (eight whole 128-byte lines), or eight 128-byte activation rows (XOR-
+// swizzled by (row >> 1) & 7), where the 32-wide tiles load 64-byte halves of
+// sixteen activation rows.  Fewer cache lines per byte relieve the L1, which
+// stalled the address unit for ~44% of the kernel's cycles at 64 tokens
+// (decode gate|up at 64 tokens 54 -> 49 us, at 128 tokens 69 -> 58 us, the
+// same results bit for bit: the k order is unchanged).  Weight fragment f of
+// a stage holds (16-row block f >> 1, 32-wide step f & 1); lane l of a k16
+// step kk reads row r's chunk 2 (kk & 1) + (l >> 5) of fragment
+// (r >> 4, kk >> 1), which is lane (r & 15) + 16 chunk of it.
+__device__ __forceinline__ int swz8(int row) { return (row >> 1) & 7; }
+
+// wait for the k tile's fragment reads; ties every fragment register
+template <int NBN, int NBM>
+__device__ __forceinline__ void wait_lds_k64(u32x4 (&w)[4][NBN], u32x4 (&x)[4][NBM]) {
+    static_assert(NBN == 2 && (NBM == 1 || NBM == 2), "fragment counts");
+    if constexpr (NBM == 1)
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(w[0][0]), "+v"(w[0][1]), "+v"(w[1][0]), "+v"(w[1][1]), "+v"(w[2][0]), "+v"(w[2][1]),
+                       "+v"(w[3][0]), "+v"(w[3][1]), "+v"(x[0][0]), "+v"(x[1][0]), "+v"(x[2][0]), "+v"(x[3][0]));
+    else
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(w[0][0]), "+v"(w[0][1]), "+v"(w[1][0]), "+v"(w[1][1]), "+v"(w[2][0]), "+v"(w[2][1]),
+                       "+v"(w[3][0]), "+v"(w[3][1]), "+v"(x[0][0]), "+v"(x[1][0]), "+v"(x[2][0]), "+v"(x[3][0]),
+                       "+v"(x[0][1]), "+v"(x[1][1]), "+v"(x[2][1]), "+v"(x[3][1]));
+}
+
+template <int TM>
+struct Narrow64 {
+    static constexpr int BN = 128, BK = 64;
+    static constexpr int WTM = TM / 2, WTN = 64, NBM = WTM / 32, NBN = WTN / 32;
+    static constexpr int LA = TM / 32, LB = 4, L = LA + LB;  // loads per thread per stage
+    static constexpr int SA = TM * BK, SB = BN * BK;         // elements per stage
+    static constexpr int NS = TM == 64 ? 4 : 3;              // 96 KB of stages
+};
+
+template <bool F16, bool SWIGLU, bool SPLIT, int TM>
+__global__ __launch_bounds__(256) void tile_nw64_kernel(Problem p, int tiles_m, int tiles_n) {
+    using S = Narrow64<TM>;
+    constexpr int BN = S::BN, BK = S::BK, NW = 4, NS = S::NS;
+    constexpr int WTM = S::WTM, WTN = S::WTN, NBM = S::NBM, NBN = S::NBN;
+    constexpr int LA = S::LA, LB = S::LB, L = S::L, SA = S::SA, SB = S::SB;
+    constexpr int NOUT = SWIGLU ? BN / 2 : BN;
+    __shared__ __attribute__((aligned(1024))) uint16_t sA[NS * SA], sB[NS * SB];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave_m = wave & 1, wave_n = wave >> 1;
+    const int ntiles = tiles_m * tiles_n;
+    const int tile = xcd_remap(blockIdx.x, ntiles);
+    constexpr int GM = 4;
+    const int gidx = tile / (GM * tiles_n);
+    const int first_m = gidx * GM;
+    const int gsz = min(GM, tiles_m - first_m);
+    const int tin = tile - gidx * GM * tiles_n;
+    const int m0 = (first_m + tin % gsz) * TM;
+    const int64_t n0 = (int64_t)(tin / gsz) * NOUT;
+
+    // A: load i of wave w fills LDS rows (4 i + w) * 8 .. + 8 (128-byte rows);
+    // lane -> row lane >> 3, LDS chunk lane & 7, global chunk (lane & 7) ^ swz8(row).
+    // Rows past M read a clamped valid row (never stored).
+    uint32_t aoff[LA];
+#pragma unroll
+    for (int i = 0; i < LA; ++i) {
+        const int row = (NW * i + wave) * 8 + (lane >> 3);
+        const int m = min(m0 + row, p.M - 1);
+        aoff[i] = (uint32_t)(((int64_t)m * p.lda + (((lane & 7) ^ swz8(row)) << 3)) * 2);
+    }
+    // W: load i of wave w = fragment f = 4 i + w: 16-row block f >> 1, k step f & 1,
+    // copied verbatim (1 KB, lane at 16 lane)
+    uint32_t boff[LB];
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+        const int f = NW * i + wave, blk = f >> 1, st = f & 1;
+        const int row = blk * 16;  // first tile row of the block
+        int64_t wrow;
+        if constexpr (SWIGLU) {
+            const int64_t j = n0 + (row >> 6) * 32 + (row & 31);
+            const int64_t jc = j < p.N ? j : (int64_t)p.N - 16;
+            wrow = weight_row(p, jc, (row >> 5) & 1);
+        } else {
+            wrow = n0 + row < p.N ? n0 + row : (int64_t)p.N - 16;
+        }
+        boff[i] = (uint32_t)(frag_offset(wrow, 32 * st, p.wsteps) * 2 + lane * 16);
+    }
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)p.A, 0, (int)a_extent(p), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)p.W, 0, (int)w_extent(p), 0x00020000);
+    const int ktiles_seg = p.Kseg / BK;
+    const int gsegs = SPLIT ? p.nseg / (int)gridDim.y : p.nseg;
+    const int nkt = ktiles_seg * gsegs;
+    const int seg_lo = SPLIT ? (int)blockIdx.y * gsegs : 0;
+
+    auto issue = [&](int kt) {
+        uint16_t* a = sA + (kt % NS) * SA;
+        uint16_t* b = sB + (kt % NS) * SB;
+        const int kc = min(kt, nkt - 1);
+        const int s = seg_lo + kc / ktiles_seg;
+        const int k0 = (kc - (s - seg_lo) * ktiles_seg) * BK;
+        const uint32_t sa = (uint32_t)((s * p.a_seg + k0) * 2);
+        const uint32_t sw = (uint32_t)((s * p.w_seg + (int64_t)k0 * 16) * 2);
+#pragma unroll
+        for (int i = 0; i < LA; ++i) dma16(ra, aoff[i], sa, a + (NW * i + wave) * 8 * BK);
+#pragma unroll
+        for (int i = 0; i < LB; ++i) dma16(rw, boff[i], sw, b + (NW * i + wave) * 512);
+    };
+
+    f32x16 acc[NBN][NBM];
+#pragma unroll
+    for (int i = 0; i < NBN; ++i)
+#pragma unroll
+        for (int j = 0; j < NBM; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+    const int frow = lane & 31, fch = lane >> 5;
+    u32x4 wf[4][NBN], xf[4][NBM];
+    auto read = [&](int t, int kk) {
+        const uint16_t* a = sA + (t % NS) * SA;
+        const uint16_t* b = sB + (t % NS) * SB;
+#pragma unroll
+        for (int i = 0; i < NBN; ++i) {
+            const int r = wave_n * WTN + i * 32 + frow;
+            const int chunk = 2 * (kk & 1) + fch;
+            wf[kk][i] = lds_read16(b + ((r >> 4) * 2 + (kk >> 1)) * 512 + ((r & 15) + 16 * chunk) * 8);
+        }
+#pragma unroll
+        for (int j = 0; j < NBM; ++j) {
+            const int r = wave_m * WTM + j * 32 + frow;
+            const int c = 2 * kk + fch;
+            xf[kk][j] = lds_read16(a + r * BK + ((c ^ swz8(r)) << 3));
+        }
+    };
+
+    if (nkt > 0) {
+        for (int t = 0; t < NS - 1; ++t) issue(t);
+        for (int t = 0; t < nkt; ++t) {
+            wait_vm<(NS - 2) * L>();
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            read(t, 0);
+            read(t, 1);
+            read(t, 2);
+            read(t, 3);
+            issue(t + NS - 1);
+            wait_lds_k64<NBN, NBM>(wf, xf);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int i = 0; i < NBN; ++i)
+#pragma unroll
+                    for (int j = 0; j < NBM; ++j) acc[i][j] = mfma32<F16>(wf[kk][i], xf[kk][j], acc[i][j]);
+        }
+        wait_vm<0>();
+    }
+
+    if constexpr (SPLIT) {
+        f32x4* mine = (f32x4*)(p.ws + ((int64_t)blockIdx.y * ntiles + tile) * (TM * BN));
+#pragma unroll
+        for (int i = 0; i < NBN; ++i)
+#pragma unroll
+            for (int j = 0; j < NBM; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                     acc[i][j][4 * q + 3]};
+                    mine[((i * NBM + j) * 4 + q) * 256 + tid] = v;
+                }
+        return;
+    }
+    const int hi = lane >> 5;
+    static_for<0, NBN>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (SWIGLU && (i & 1)) return;
+        static_for<0, NBM>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            const int m = m0 + wave_m * WTM + j * 32 + (lane & 31);
+            if (m >= p.M) return;
+            static_for<0, 4>([&](auto bc) {
+                constexpr int blk = decltype(bc)::value;
+                int64_t n;
+                float v[4];
+                if constexpr (SWIGLU) {
+                    n = n0 + wave_n * 32 + 8 * blk + 4 * hi;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        v[e] = silu_f32(acc[i][j][4 * blk + e]) * acc[i | 1][j][4 * blk + e];
+                } else {
+                    n = n0 + wave_n * WTN + i * 32 + 8 * blk + 4 * hi;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * blk + e];
+                }
+                store4(p, m, n, v);
+            });
+        });
+    });
+}
+
 // tiles of the few-token kernel
 int tile_nw_count(int M, int N, int swiglu) {
     const int tm = tile_nw_tm(M), nout = swiglu ? 64 : 128;
@@ -557,9 +758,29 @@ bool tile_nw_fits(const Problem& p) {
            a_extent(p) < (1LL << 31) && w_extent(p) < (1LL << 31);
 }
 
+// the 64-wide k tiles: fragment-major weights whose 16-row blocks are whole
+// stored blocks (64- and 128-token tiles; the 256-token tile would need 144 KB)
+static bool nw64_ok(const Problem& p) {
+    return p.wfrag && p.Kseg % 64 == 0 && p.N % 16 == 0 && (!p.swiglu || p.floc % 16 == 0);
+}
+
 template <int TM, bool SPLIT>
 static void launch_nw_tm(const Problem& p, hipStream_t s, dim3 grid, int tm, int tn) {
     const bool f16 = p.dtype == SG_F16;
+    if constexpr (TM <= 128) {
+        if (nw64_ok(p)) {
+            if (p.swiglu) {
+                if constexpr (!SPLIT) {
+                    if (f16) launch(tile_nw64_kernel<true, true, false, TM>, grid, dim3(256), 0, s, p, tm, tn);
+                    else launch(tile_nw64_kernel<false, true, false, TM>, grid, dim3(256), 0, s, p, tm, tn);
+                }
+            } else {
+                if (f16) launch(tile_nw64_kernel<true, false, SPLIT, TM>, grid, dim3(256), 0, s, p, tm, tn);
+                else launch(tile_nw64_kernel<false, false, SPLIT, TM>, grid, dim3(256), 0, s, p, tm, tn);
+            }
+            return;
+        }
+    }
     if (p.swiglu) {
         if constexpr (!SPLIT) {
             if (f16) launch(tile_nw_kernel<true, true, false, TM>, grid, dim3(256), 0, s, p, tm, tn);

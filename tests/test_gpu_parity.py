@@ -98,7 +98,8 @@ COL_CASES = [
     ("bf16", 1, 256, 96, 1, 2), ("bf16", 5, 512, 192, 3, 2), ("bf16", 16, 4096, 448, 1, 8), ("bf16", 32, 200, 64, 2, 2),
     ("f16", 17, 1024, 320, 1, 4), ("bf16", 33, 264, 384, 1, 3), ("bf16", 130, 512, 640, 1, 4),
     ("bf16", 50, 1024, 512, 2, 4), ("f16", 100, 256, 384, 1, 2),
-    ("bf16", 64, 256, 200, 1, 2),  # out % 16 != 0: row-major weights on the few-token tiles
+    ("bf16", 64, 256, 200, 1, 2),  # out % 16 != 0: row-major weights on the few-token tiles (32-wide k)
+    ("bf16", 70, 96, 256, 1, 2),   # K = 96: the few-token tiles' 32-wide k tiles (64-wide elsewhere)
     ("f16", 300, 128, 1000, 1, 5), ("bf16", 520, 640, 768, 3, 2), ("bf16", 777, 256, 1100, 1, 2),
     ("bf16", 12, 24, 40, 1, 2), ("bf16", 3, 10, 4, 1, 2),  # K not a multiple of 8: generic path
 ]
