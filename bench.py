@@ -140,7 +140,7 @@ class DecodeMLP(Workload):
     def __init__(self, B=16):
         self.B = B
         if B > 32:  # beyond the streaming kernels
-            self.dominant = "tile_nw_kernel (gate|up all-to-sharded + SwiGLU, few-token tiles)"
+            self.dominant = "tile_nw64_kernel (gate|up all-to-sharded + SwiGLU, few-token tiles)"
             self.dominant_src = ("tile_dma.hip", "internal.h")
 
     def setup(self):
