@@ -174,9 +174,13 @@ bool q4_fits(const sg_layer* l, int64_t B, int swiglu) {
 Kind choose_mx(const sg_layer* l, int64_t B, const void* x, int swiglu, int nseg) {
     const bool ok = B <= 32 && l->wfrag && (l->cols_r / 32) % 4 == 0 && aligned16(x) && aligned16(l->w);
     if (ok && skinny_fits(l, B, swiglu, nseg)) return K_SKINNY;
-    // beyond 32 tokens the 128 x 128 tile kernel with the FP8 loader: its 256 x
-    // 256 form needs more registers than a wave has (measured on the MLP shapes
-    // at 512 tokens: gate|up 357 -> 324 us, down 372 -> 295 us)
+    // 33 to 128 tokens the few-token tiles with the FP8 loader after the LDS;
+    // beyond, the 128 x 128 tile kernel with the FP8 loader: its 256 x 256
+    // form needs more registers than a wave has (measured on the MLP shapes at
+    // 512 tokens: gate|up 357 -> 324 us, down 372 -> 295 us)
+    const bool blocks16 = (swiglu ? (l->rows_r / 2) % 16 : l->rows_r % 16) == 0;
+    if (B > 32 && B <= 128 && l->wfrag && l->cols_r % 128 == 0 && blocks16 && aligned16(x) && nw_ok(l, B))
+        return K_NW;
     if (B > 32 && aligned16(x) && l->cols_r % 8 == 0) return K_TILE1;
     return K_GENERIC;
 }

@@ -101,6 +101,23 @@ __device__ __forceinline__ u32x4 lds_read16(const uint16_t* p) {
     return r;
 }
 
+__device__ __forceinline__ u32x2 lds_read8(const uint8_t* p) {
+    const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+    u32x2 r;
+    asm volatile("ds_read_b64 %0, %1" : "=v"(r) : "v"(a));
+    return r;
+}
+__device__ __forceinline__ uint32_t lds_read4(const uint8_t* p) {
+    const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+    uint32_t r;
+    asm volatile("ds_read_b32 %0, %1" : "=v"(r) : "v"(a));
+    return r;
+}
+// one wave-wide 4-byte-per-lane load into LDS (dest + 4 lane)
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint8_t* lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, voff, soff, 0, 0);
+}
+
 // wait for every outstanding LDS read; ties the six fragments of one k step so
 // that no use of them is scheduled before the wait
 __device__ __forceinline__ void wait_lds(u32x4 (&w)[2], u32x4 (&x)[4]) {
@@ -747,15 +764,248 @@ __global__ __launch_bounds__(256) void tile_nw64_kernel(Problem p, int tiles_m, 
     });
 }
 
+// The few-token tile on MX FP8 weights (bf16 activations): 64 or 128 tokens
+// x 128 weight rows, 128-wide k tiles (one run of four 32-wide scale steps).
+// A stage holds the activations (rows of 256 bytes, 16-byte chunks XOR-
+// swizzled by row & 15), the sixteen stored 1 KB code fragments of the tile's
+// eight 16-row blocks (two 64-wide pairs each, verbatim) and the blocks' E8M0
+// scales of the run (8 x 64 bytes); all three arrive by direct-to-LDS loads,
+// three stages in flight.  After the LDS read, each lane's eight codes of a
+// k16 step become bf16 operands with v_cvt_scalef32_pk_bf16_fp8 and its row's
+// scale of that 32-wide step (exact, as in the streaming kernel), and meet the
+// activations in the bf16 MFMA.  Lane l of k16 step kk (pair kk >> 2, step
+// parity (kk >> 1) & 1) reads row r's chunk 2 (kk & 1) + (l >> 5) of the
+// pair's fragment: lane (r & 15) + 16 chunk of it, bytes 8 parity .. + 8.
+template <int TM>
+struct NarrowMx {
+    static constexpr int BN = 128, BK = 128;
+    static constexpr int WTM = TM / 2, WTN = 64, NBM = WTM / 32, NBN = WTN / 32;
+    static constexpr int SAB = TM * 256, SWB = BN * BK, SSB = 1024;  // bytes per stage
+    static constexpr int ST = SAB + SWB + SSB;
+    static constexpr int LA = SAB / 4096, LB = 4, L = LA + LB + 1;  // loads per thread per stage
+    static constexpr int NS = 3;
+};
+
+template <bool SWIGLU, bool SPLIT, int TM>
+__global__ __launch_bounds__(256) void tile_nw_mx_kernel(Problem p, int tiles_m, int tiles_n) {
+    using S = NarrowMx<TM>;
+    constexpr int BN = S::BN, BK = S::BK, NW = 4, NS = S::NS;
+    constexpr int WTM = S::WTM, WTN = S::WTN, NBM = S::NBM, NBN = S::NBN;
+    constexpr int SAB = S::SAB, SWB = S::SWB, ST = S::ST, LA = S::LA, LB = S::LB, L = S::L;
+    constexpr int NOUT = SWIGLU ? BN / 2 : BN;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * ST];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave_m = wave & 1, wave_n = wave >> 1;
+    const int ntiles = tiles_m * tiles_n;
+    const int tile = xcd_remap(blockIdx.x, ntiles);
+    constexpr int GM = 4;
+    const int gidx = tile / (GM * tiles_n);
+    const int first_m = gidx * GM;
+    const int gsz = min(GM, tiles_m - first_m);
+    const int tin = tile - gidx * GM * tiles_n;
+    const int m0 = (first_m + tin % gsz) * TM;
+    const int64_t n0 = (int64_t)(tin / gsz) * NOUT;
+
+    // first stored row of the tile's 16-row block b (blocks past N: the last)
+    auto block_row = [&](int b) -> int64_t {
+        const int row = b * 16;
+        if constexpr (SWIGLU) {
+            const int64_t j = n0 + (row >> 6) * 32 + (row & 31);
+            return weight_row(p, j < p.N ? j : (int64_t)p.N - 16, (row >> 5) & 1);
+        } else {
+            return n0 + row < p.N ? n0 + row : (int64_t)p.N - 16;
+        }
+    };
+    // activations: load i of wave w fills rows (4 i + w) * 4 .. + 4; lane -> row
+    // lane >> 4, LDS chunk lane & 15, global chunk (lane & 15) ^ (row & 15)
+    uint32_t aoff[LA];
+#pragma unroll
+    for (int i = 0; i < LA; ++i) {
+        const int row = (NW * i + wave) * 4 + (lane >> 4);
+        const int m = min(m0 + row, p.M - 1);
+        aoff[i] = (uint32_t)(((int64_t)m * p.lda + (((lane & 15) ^ (row & 15)) << 3)) * 2);
+    }
+    // codes: load i of wave w = fragment f = 4 i + w (block f >> 1, pair f & 1)
+    uint32_t coff[LB];
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+        const int f = NW * i + wave;
+        coff[i] = (uint32_t)(mx_code_offset(block_row(f >> 1), 64 * (f & 1), p.wsteps) + lane * 16);
+    }
+    // scales: waves 0 and 1 load blocks 4 w .. 4 w + 3 (16 rows x 4 bytes each);
+    // waves 2 and 3 repeat them into the stage's unused half
+    const int sb = 4 * (wave & 1) + (lane >> 4);
+    const uint32_t soffl = (uint32_t)mx_scale_offset(block_row(sb) + (lane & 15), 0, p.wsteps);
+
+    const int64_t rows = SWIGLU ? 2 * (int64_t)p.N : p.N, nblk = rows / 16;
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)p.A, 0, (int)a_extent(p), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)p.W, 0, (int)(((int64_t)p.nseg - 1) * p.w_seg + nblk * (p.wsteps / 2) * 1024), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)p.ms, 0, (int)(((int64_t)p.nseg - 1) * p.ms_seg + nblk * (p.wsteps / 4) * 64), 0x00020000);
+    const int ktiles_seg = p.Kseg / BK;
+    const int gsegs = SPLIT ? p.nseg / (int)gridDim.y : p.nseg;
+    const int nkt = ktiles_seg * gsegs;
+    const int seg_lo = SPLIT ? (int)blockIdx.y * gsegs : 0;
+
+    auto issue = [&](int kt) {
+        uint8_t* st = smem + (kt % NS) * ST;
+        const int kc = min(kt, nkt - 1);
+        const int s = seg_lo + kc / ktiles_seg;
+        const int k0 = (kc - (s - seg_lo) * ktiles_seg) * BK;
+        const uint32_t sa = (uint32_t)((s * p.a_seg + k0) * 2);
+        const uint32_t sw = (uint32_t)(s * p.w_seg + (int64_t)(k0 >> 6) * 1024);
+        const uint32_t ss = (uint32_t)(s * p.ms_seg + (int64_t)(k0 >> 7) * 64);
+#pragma unroll
+        for (int i = 0; i < LA; ++i) dma16(ra, aoff[i], sa, (uint16_t*)(st + (NW * i + wave) * 1024));
+#pragma unroll
+        for (int i = 0; i < LB; ++i) dma16(rw, coff[i], sw, (uint16_t*)(st + SAB + (NW * i + wave) * 1024));
+        dma4(rs, soffl, ss, st + SAB + SWB + wave * 256);
+    };
+
+    f32x16 acc[NBN][NBM];
+#pragma unroll
+    for (int i = 0; i < NBN; ++i)
+#pragma unroll
+        for (int j = 0; j < NBM; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+    const int frow = lane & 31, fch = lane >> 5;
+    // one half of a stage: k16 steps 4 hf .. 4 hf + 3 (the 64-wide pair hf)
+    auto half = [&](const uint8_t* st, int hf, const uint32_t (&sw)[NBN]) {
+        u32x2 cw[4][NBN];
+        u32x4 xf[4][NBM];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int kk = 4 * hf + q, chunk = 2 * (q & 1) + fch, sp = q >> 1;
+#pragma unroll
+            for (int i = 0; i < NBN; ++i) {
+                const int r = wave_n * WTN + i * 32 + frow;
+                cw[q][i] = lds_read8(st + SAB + ((r >> 4) * 2 + hf) * 1024 + ((r & 15) + 16 * chunk) * 16 + 8 * sp);
+            }
+#pragma unroll
+            for (int j = 0; j < NBM; ++j) {
+                const int r = wave_m * WTM + j * 32 + frow, c = 2 * kk + fch;
+                xf[q][j] = lds_read16((const uint16_t*)(st + r * 256 + ((c ^ (r & 15)) << 4)));
+            }
+        }
+        static_assert(NBN == 2 && (NBM == 1 || NBM == 2), "fragment counts of the few-token tiles");
+        if constexpr (NBM == 1)
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(cw[0][0]), "+v"(cw[0][1]), "+v"(cw[1][0]), "+v"(cw[1][1]), "+v"(cw[2][0]),
+                           "+v"(cw[2][1]), "+v"(cw[3][0]), "+v"(cw[3][1]), "+v"(xf[0][0]), "+v"(xf[1][0]),
+                           "+v"(xf[2][0]), "+v"(xf[3][0]));
+        else
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(cw[0][0]), "+v"(cw[0][1]), "+v"(cw[1][0]), "+v"(cw[1][1]), "+v"(cw[2][0]),
+                           "+v"(cw[2][1]), "+v"(cw[3][0]), "+v"(cw[3][1]), "+v"(xf[0][0]), "+v"(xf[1][0]),
+                           "+v"(xf[2][0]), "+v"(xf[3][0]), "+v"(xf[0][1]), "+v"(xf[1][1]), "+v"(xf[2][1]),
+                           "+v"(xf[3][1]));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int stp = 2 * hf + (q >> 1);  // 32-wide step of the run
+#pragma unroll
+            for (int i = 0; i < NBN; ++i) {
+                const u32x4 wf = mx8_to_bf16(cw[q][i], (sw[i] >> (8 * stp)) & 0xFFu);
+#pragma unroll
+                for (int j = 0; j < NBM; ++j) acc[i][j] = mfma32<false>(wf, xf[q][j], acc[i][j]);
+            }
+        }
+    };
+
+    if (nkt > 0) {
+        for (int t = 0; t < NS - 1; ++t) issue(t);
+        for (int t = 0; t < nkt; ++t) {
+            wait_vm<(NS - 2) * L>();
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            const uint8_t* st = smem + (t % NS) * ST;
+            uint32_t sw[NBN];
+#pragma unroll
+            for (int i = 0; i < NBN; ++i) {
+                const int r = wave_n * WTN + i * 32 + frow;
+                sw[i] = lds_read4(st + SAB + SWB + (r >> 4) * 64 + (r & 15) * 4);
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(sw[0]), "+v"(sw[1]));
+            half(st, 0, sw);
+            // every wave has read k tile t - 1: its stage takes k tile t + NS - 1
+            issue(t + NS - 1);
+            half(st, 1, sw);
+        }
+        wait_vm<0>();
+    }
+
+    if constexpr (SPLIT) {
+        f32x4* mine = (f32x4*)(p.ws + ((int64_t)blockIdx.y * ntiles + tile) * (TM * BN));
+#pragma unroll
+        for (int i = 0; i < NBN; ++i)
+#pragma unroll
+            for (int j = 0; j < NBM; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                     acc[i][j][4 * q + 3]};
+                    mine[((i * NBM + j) * 4 + q) * 256 + tid] = v;
+                }
+        return;
+    }
+    const int hi = lane >> 5;
+    static_for<0, NBN>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (SWIGLU && (i & 1)) return;
+        static_for<0, NBM>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            const int m = m0 + wave_m * WTM + j * 32 + (lane & 31);
+            if (m >= p.M) return;
+            static_for<0, 4>([&](auto bc) {
+                constexpr int blk = decltype(bc)::value;
+                int64_t n;
+                float v[4];
+                if constexpr (SWIGLU) {
+                    n = n0 + wave_n * 32 + 8 * blk + 4 * hi;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        v[e] = silu_f32(acc[i][j][4 * blk + e]) * acc[i | 1][j][4 * blk + e];
+                } else {
+                    n = n0 + wave_n * WTN + i * 32 + 8 * blk + 4 * hi;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * blk + e];
+                }
+                store4(p, m, n, v);
+            });
+        });
+    });
+}
+
 // tiles of the few-token kernel
 int tile_nw_count(int M, int N, int swiglu) {
     const int tm = tile_nw_tm(M), nout = swiglu ? 64 : 128;
     return ((M + tm - 1) / tm) * ((N + nout - 1) / nout);
 }
 
+// MX FP8 weights on the few-token tiles: fragment-major codes in whole stored
+// 16-row blocks, 128-wide k tiles, bf16 activations, up to 128 tokens
+static bool nw_mx_ok(const Problem& p) {
+    return p.wfrag && p.dtype == SG_BF16 && p.Kseg % 128 == 0 && p.N % 16 == 0 &&
+           (!p.swiglu || p.floc % 16 == 0) && p.M <= 128;
+}
+
 bool tile_nw_fits(const Problem& p) {
-    return !p.nn && !(p.split && p.swiglu) && !p.fp8 && !p.wq && p.Kseg % 32 == 0 && p.M <= 256 &&
-           a_extent(p) < (1LL << 31) && w_extent(p) < (1LL << 31);
+    return !p.nn && !(p.split && p.swiglu) && !p.wq && p.Kseg % 32 == 0 && p.M <= 256 &&
+           (!p.fp8 || nw_mx_ok(p)) && a_extent(p) < (1LL << 31) && w_extent(p) < (1LL << 31);
+}
+
+template <int TM, bool SPLIT>
+static void launch_nw_mx(const Problem& p, hipStream_t s, dim3 grid, int tm, int tn) {
+    if (p.swiglu) {
+        if constexpr (!SPLIT) launch(tile_nw_mx_kernel<true, false, TM>, grid, dim3(256), 0, s, p, tm, tn);
+    } else {
+        launch(tile_nw_mx_kernel<false, SPLIT, TM>, grid, dim3(256), 0, s, p, tm, tn);
+    }
 }
 
 // the 64-wide k tiles: fragment-major weights whose 16-row blocks are whole
@@ -799,7 +1049,15 @@ hipError_t launch_tile_nw(const Problem& p, hipStream_t s) {
     const int tm = (p.M + TMv - 1) / TMv, tn = (p.N + nout - 1) / nout;
     const int groups = p.split ? split_groups(tm * tn, p.nseg) : 1;
     const dim3 grid(tm * tn, groups);
-    if (TMv == 64) {
+    if (p.fp8) {  // nw_mx_ok: 64- or 128-token tiles
+        if (TMv == 64) {
+            if (p.split) launch_nw_mx<64, true>(p, s, grid, tm, tn);
+            else launch_nw_mx<64, false>(p, s, grid, tm, tn);
+        } else {
+            if (p.split) launch_nw_mx<128, true>(p, s, grid, tm, tn);
+            else launch_nw_mx<128, false>(p, s, grid, tm, tn);
+        }
+    } else if (TMv == 64) {
         if (p.split) launch_nw_tm<64, true>(p, s, grid, tm, tn);
         else launch_nw_tm<64, false>(p, s, grid, tm, tn);
     } else if (TMv == 128) {
