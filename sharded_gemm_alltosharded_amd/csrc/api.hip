@@ -174,12 +174,13 @@ bool q4_fits(const sg_layer* l, int64_t B, int swiglu) {
 Kind choose_mx(const sg_layer* l, int64_t B, const void* x, int swiglu, int nseg) {
     const bool ok = B <= 32 && l->wfrag && (l->cols_r / 32) % 4 == 0 && aligned16(x) && aligned16(l->w);
     if (ok && skinny_fits(l, B, swiglu, nseg)) return K_SKINNY;
-    // 33 to 128 tokens the few-token tiles with the FP8 loader after the LDS;
-    // beyond, the 128 x 128 tile kernel with the FP8 loader: its 256 x 256
+    // 33 to 256 tokens the few-token tiles with the FP8 conversion after the
+    // LDS (decode MLP shapes at 64 tokens: gate|up 155 -> 35 us, down 77 -> 26
+    // us); beyond, the 128 x 128 tile kernel with the FP8 loader: its 256 x 256
     // form needs more registers than a wave has (measured on the MLP shapes at
     // 512 tokens: gate|up 357 -> 324 us, down 372 -> 295 us)
     const bool blocks16 = (swiglu ? (l->rows_r / 2) % 16 : l->rows_r % 16) == 0;
-    if (B > 32 && B <= 128 && l->wfrag && l->cols_r % 128 == 0 && blocks16 && aligned16(x) && nw_ok(l, B))
+    if (B > 32 && l->wfrag && l->cols_r % 128 == 0 && blocks16 && aligned16(x) && nw_ok(l, B))
         return K_NW;
     if (B > 32 && aligned16(x) && l->cols_r % 8 == 0) return K_TILE1;
     return K_GENERIC;
@@ -212,7 +213,7 @@ bool want_split(const sg_layer* l, Kind k, int64_t B) {
     switch (k) {
     case K_TILE0: return sg::tile_count((int)B, (int)l->out_dims, 0) * 2 <= cus;
     case K_TILE1: return sg::tile_count((int)B, (int)l->out_dims, 1) * 2 <= cus;
-    case K_NW: return sg::tile_nw_count((int)B, (int)l->out_dims, 0) * 2 <= cus;
+    case K_NW: return sg::tile_nw_count((int)B, (int)l->out_dims, 0, l->mx) * 2 <= cus;
     // the 4-bit tile kernel (three workgroups per CU) splits up to one tile
     // per CU (decode-MLP down projection: 126 -> 45 us at 192 tokens, 143 ->
     // 101 us at 512)
@@ -226,8 +227,8 @@ sg::SplitLayout split_layout(const sg_layer* l, Kind k, int64_t B) {
     case K_TILE0: return sg::tile_split_layout((int)B, (int)l->out_dims, l->P, 0);
     case K_TILE1: return sg::tile_split_layout((int)B, (int)l->out_dims, l->P, 1);
     case K_NW: {
-        const size_t t = (size_t)sg::tile_nw_count((int)B, (int)l->out_dims, 0);
-        return {t * (size_t)sg::tile_nw_tm((int)B) * 128 * (size_t)sg::split_groups((int)t, l->P), t};
+        const size_t t = (size_t)sg::tile_nw_count((int)B, (int)l->out_dims, 0, l->mx);
+        return {t * (size_t)sg::tile_nw_tm((int)B, l->mx) * 128 * (size_t)sg::split_groups((int)t, l->P), t};
     }
     case K_Q4TILE: {
         const size_t t = (size_t)sg::q4_tile_count((int)B, (int)l->out_dims);

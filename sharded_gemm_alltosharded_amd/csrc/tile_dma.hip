@@ -561,7 +561,7 @@ __global__ __launch_bounds__(256) void tile_nw_kernel(Problem p, int tiles_m, in
 }
 
 // token tile of the few-token kernel
-int tile_nw_tm(int M) { return M <= 64 ? 64 : M <= 128 ? 128 : 256; }
+int tile_nw_tm(int M, bool fp8) { return M <= 64 ? 64 : (M <= 128 || fp8) ? 128 : 256; }
 
 
 // The few-token tile with 64-wide k tiles, for fragment-major weights whose
@@ -982,16 +982,16 @@ __global__ __launch_bounds__(256) void tile_nw_mx_kernel(Problem p, int tiles_m,
 }
 
 // tiles of the few-token kernel
-int tile_nw_count(int M, int N, int swiglu) {
-    const int tm = tile_nw_tm(M), nout = swiglu ? 64 : 128;
+int tile_nw_count(int M, int N, int swiglu, bool fp8) {
+    const int tm = tile_nw_tm(M, fp8), nout = swiglu ? 64 : 128;
     return ((M + tm - 1) / tm) * ((N + nout - 1) / nout);
 }
 
 // MX FP8 weights on the few-token tiles: fragment-major codes in whole stored
-// 16-row blocks, 128-wide k tiles, bf16 activations, up to 128 tokens
+// 16-row blocks, 128-wide k tiles, bf16 activations
 static bool nw_mx_ok(const Problem& p) {
     return p.wfrag && p.dtype == SG_BF16 && p.Kseg % 128 == 0 && p.N % 16 == 0 &&
-           (!p.swiglu || p.floc % 16 == 0) && p.M <= 128;
+           (!p.swiglu || p.floc % 16 == 0);
 }
 
 bool tile_nw_fits(const Problem& p) {
@@ -1045,11 +1045,11 @@ static void launch_nw_tm(const Problem& p, hipStream_t s, dim3 grid, int tm, int
 hipError_t launch_tile_nw(const Problem& p, hipStream_t s) {
     if (p.M == 0 || p.N == 0) return hipSuccess;
     if (!tile_nw_fits(p)) return hipErrorInvalidValue;
-    const int TMv = tile_nw_tm(p.M), nout = p.swiglu ? 64 : 128;
+    const int TMv = tile_nw_tm(p.M, p.fp8), nout = p.swiglu ? 64 : 128;
     const int tm = (p.M + TMv - 1) / TMv, tn = (p.N + nout - 1) / nout;
     const int groups = p.split ? split_groups(tm * tn, p.nseg) : 1;
     const dim3 grid(tm * tn, groups);
-    if (p.fp8) {  // nw_mx_ok: 64- or 128-token tiles
+    if (p.fp8) {  // 64- or 128-token tiles
         if (TMv == 64) {
             if (p.split) launch_nw_mx<64, true>(p, s, grid, tm, tn);
             else launch_nw_mx<64, false>(p, s, grid, tm, tn);

@@ -669,8 +669,8 @@ def test_slicing_mx_bit_exact(mode, out, inn, S, P):
         layer.shard(0, 3)  # no quantization biases
 
 
-# 33-128 tokens: the few-token tiles (codes converted after the LDS); beyond: the 128 x 128 tiles
-@pytest.mark.parametrize("B", [1, 8, 16, 32, 40, 100, 600])
+# 33-256 tokens: the few-token tiles (codes converted after the LDS); beyond: the 128 x 128 tiles
+@pytest.mark.parametrize("B", [1, 8, 16, 32, 40, 100, 200, 600])
 def test_mx_all_to_sharded(B):
     _print_case(B=B)
     D, out, P = 512, 384, 4
@@ -681,7 +681,7 @@ def test_mx_all_to_sharded(B):
         assert_close(y, oracle.col(X, Wd, P=P, gather=gather, dtype="bf16"), "f32", "mx col")
 
 
-@pytest.mark.parametrize("B", [1, 16, 32, 48, 128, 520])
+@pytest.mark.parametrize("B", [1, 16, 32, 48, 128, 250, 520])
 def test_mx_swiglu_and_row(B):
     _print_case(B=B)
     D, F, P = 512, 1024, 4
