@@ -207,8 +207,8 @@ size_t sg_mlp_workspace(const sg_layer* gate_up, const sg_layer* down, int64_t B
  * caller passes x and y as for sg_mlp; nothing is allocated or freed.
  * Errors: as sg_mlp, and SG_ERR_WORKSPACE when sg_mlp_workspace(gate_up,
  * down, B) exceeds the scratch (on 4096 x 14336 decode-MLP layers over 8
- * ranks the scratch holds every token count up to 32 for bf16 layers, up to
- * 64 for 4-bit ones: beyond, the down layer's rank split needs more).
+ * ranks the scratch holds every token count up to 64, bf16, MX FP8 and 4-bit
+ * layers alike: beyond, the down layer's rank split needs more).
  * All calls on one device share its scratch, so calls that overlap on one
  * GPU (other streams or threads) race: the caller serialises them. */
 #define SG_MLP_STATIC_SCRATCH_BYTES (16u << 20)
