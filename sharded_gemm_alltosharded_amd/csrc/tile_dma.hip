@@ -1,8 +1,12 @@
-// MFMA tile GEMM for gfx950 fed by direct global -> LDS loads (the
-// prefill-shaped sharded GEMMs: many tokens against a rank's weight rows).
-// Same product and epilogues as tile.hip's NT / SWIGLU modes; 256 x 256 output
-// tiles (SwiGLU: 256 tokens x 128 outputs from 256 interleaved gate/up rows),
-// BK = 32, 512 threads.
+// MFMA tile GEMMs for gfx950 fed by direct global -> LDS loads.  This file
+// holds the ping-pong kernel (tile_pp_kernel: the prefill-shaped sharded GEMMs,
+// many tokens against a rank's weight rows) and, further down, the few-token
+// kernels for 33 to 256 tokens (tile_nw_kernel, tile_nw64_kernel and, for MX
+// FP8 weights, tile_nw_mx_kernel), which reuse its loads and fragment reads.
+// Same products and epilogues as tile.hip's NT / SWIGLU modes.
+//
+// Ping-pong kernel: 256 x 256 output tiles (SwiGLU: 256 tokens x 128 outputs
+// from 256 interleaved gate/up rows), BK = 32, 512 threads.
 //
 // Schedule (ping-pong).  The 8 waves form two groups of four, waves 0-3 and
 // 4-7, so every SIMD hosts one wave of each.  Time runs in phases separated by
