@@ -149,10 +149,12 @@ bool mfma_ok(const sg_layer* l, const void* x) {
     return l->dtype != SG_F32 && l->cols_r % 8 == 0 && aligned16(x) && aligned16(l->w);
 }
 
-// the few-token tile kernel: 33 to 256 tokens, 32-wide k tiles, weights
-// addressable through 32-bit offsets
+// the few-token tile kernel: 33 to 256 tokens (MX FP8 layers: any count above
+// 32), 32-wide k tiles, weights and activations addressable through 32-bit
+// offsets
 bool nw_ok(const sg_layer* l, int64_t B) {
-    return B > 32 && B <= 256 && l->cols_r % 32 == 0 && (double)l->P * l->rows_r * l->cols_r * 2 < 2.0e9;
+    return B > 32 && (B <= 256 || l->mx) && l->cols_r % 32 == 0 &&
+           (double)l->P * l->rows_r * l->cols_r * 2 < 2.0e9 && (double)B * l->P * l->cols_r * 2 < 2.0e9;
 }
 
 // the streaming kernels keep one LDS slot per (rank, part): bounded ranks only
@@ -174,11 +176,12 @@ bool q4_fits(const sg_layer* l, int64_t B, int swiglu) {
 Kind choose_mx(const sg_layer* l, int64_t B, const void* x, int swiglu, int nseg) {
     const bool ok = B <= 32 && l->wfrag && (l->cols_r / 32) % 4 == 0 && aligned16(x) && aligned16(l->w);
     if (ok && skinny_fits(l, B, swiglu, nseg)) return K_SKINNY;
-    // 33 to 256 tokens the few-token tiles with the FP8 conversion after the
-    // LDS (decode MLP shapes at 64 tokens: gate|up 155 -> 35 us, down 77 -> 26
-    // us); beyond, the 128 x 128 tile kernel with the FP8 loader: its 256 x 256
-    // form needs more registers than a wave has (measured on the MLP shapes at
-    // 512 tokens: gate|up 357 -> 324 us, down 372 -> 295 us)
+    // beyond 32 tokens the few-token tiles with the FP8 conversion after the
+    // LDS, at every token count (decode MLP shapes at 64 tokens: gate|up 155 ->
+    // 35 us, down 77 -> 26 us against the 128 x 128 tile kernel with the FP8
+    // loader; at 512 tokens 329 -> 194 and 160 -> 85 us; at 4096 tokens 2221
+    // -> 1305 and 1079 -> 603 us); the tile kernel keeps the layers whose codes
+    // do not come in whole 16-row blocks of 128-wide k tiles
     const bool blocks16 = (swiglu ? (l->rows_r / 2) % 16 : l->rows_r % 16) == 0;
     if (B > 32 && l->wfrag && l->cols_r % 128 == 0 && blocks16 && aligned16(x) && nw_ok(l, B))
         return K_NW;

@@ -198,8 +198,8 @@ int split_groups(int tiles, int nseg);
 // 64 x 128, 128 x 128 and 256 x 128
 hipError_t launch_split_reduce(const Problem& p, int tiles_m, int tiles_n, int groups, int layout, hipStream_t s);
 // few-token tile kernel (tile_dma.hip): up to 256 tokens, 64-, 128- or
-// 256-token tiles (tile_nw_tm) of 128 weight rows; MX FP8 weights (fp8):
-// 64- or 128-token tiles
+// 256-token tiles (tile_nw_tm) of 128 weight rows; MX FP8 weights (fp8): any
+// token count, 64- or 128-token tiles
 int tile_nw_tm(int M, bool fp8 = false);
 int tile_nw_count(int M, int N, int swiglu, bool fp8 = false);
 bool tile_nw_fits(const Problem& p);

@@ -2,7 +2,8 @@
 // holds the ping-pong kernel (tile_pp_kernel: the prefill-shaped sharded GEMMs,
 // many tokens against a rank's weight rows) and, further down, the few-token
 // kernels for 33 to 256 tokens (tile_nw_kernel, tile_nw64_kernel and, for MX
-// FP8 weights, tile_nw_mx_kernel), which reuse its loads and fragment reads.
+// FP8 weights at any token count, tile_nw_mx_kernel), which reuse its loads
+// and fragment reads.
 // Same products and epilogues as tile.hip's NT / SWIGLU modes.
 //
 // Ping-pong kernel: 256 x 256 output tiles (SwiGLU: 256 tokens x 128 outputs
@@ -788,6 +789,10 @@ __global__ __launch_bounds__(256) void tile_nw64_kernel(Problem p, int tiles_m, 
 
 // The few-token tile on MX FP8 weights (bf16 activations): 64 or 128 tokens
 // x 128 weight rows, 128-wide k tiles (one run of four 32-wide scale steps).
+// It serves MX FP8 layers at every token count above 32: a 256-token tile
+// would need more LDS than three stages leave, and the 128 x 128 tile kernel
+// with a register-staged FP8 loader measured 1.7 to 1.9 times slower from 512
+// to 4096 tokens on the decode-MLP layer shapes.
 // A stage holds the activations (rows of 256 bytes, 16-byte chunks XOR-
 // swizzled by row & 15), the sixteen stored 1 KB code fragments of the tile's
 // eight 16-row blocks (two 64-wide pairs each, verbatim) and the blocks' E8M0
@@ -1017,7 +1022,7 @@ static bool nw_mx_ok(const Problem& p) {
 }
 
 bool tile_nw_fits(const Problem& p) {
-    return !p.nn && !(p.split && p.swiglu) && !p.wq && p.Kseg % 32 == 0 && p.M <= 256 &&
+    return !p.nn && !(p.split && p.swiglu) && !p.wq && p.Kseg % 32 == 0 && (p.M <= 256 || p.fp8) &&
            (!p.fp8 || nw_mx_ok(p)) && a_extent(p) < (1LL << 31) && w_extent(p) < (1LL << 31);
 }
 

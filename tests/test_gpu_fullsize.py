@@ -71,11 +71,14 @@ def test_decode_mlp_more_tokens(B):
     assert torch.equal(sg.mlp(gu, dn, x), y)
 
 
-def test_mxfp8_mlp_full():
-    """MX FP8 decode MLP (the layers bench.py times for it): B=16, D=4096,
-    F=14336, P=8, E4M3 codes with E8M0 scales per 32 inputs; every token."""
-    _case("MX FP8 decode MLP B=16 D=4096 F=14336 P=8")
-    B, D, F, P = 16, 4096, 14336, 8
+@pytest.mark.parametrize("B", [16, 512])
+def test_mxfp8_mlp_full(B):
+    """MX FP8 decode MLP (the layers bench.py times for it): D=4096, F=14336,
+    P=8, E4M3 codes with E8M0 scales per 32 inputs.  16 tokens (the streaming
+    kernels): every token; 512 tokens (the MX few-token tiles, the down layer
+    split into rank groups): eight sampled tokens."""
+    _case(f"MX FP8 decode MLP B={B} D=4096 F=14336 P=8")
+    D, F, P = 4096, 14336, 8
     X = synth.normal(90, (B, D), 1.0, "bf16")
     ws = [synth.uniform(91 + i, shp, 1 / 64, "f32") for i, shp in enumerate([(F, D), (F, D), (D, F)])]
     gc, gs = synth.quantize_mxfp8(np.concatenate([ws[0], ws[1]]))
@@ -85,11 +88,12 @@ def test_mxfp8_mlp_full():
     dn = sg.shard_mxfp8_linear(t(dc), t(ds), "sharded-to-all", P=P)
     h = sg.all_to_sharded(gu, to_dev(X, "bf16"), swiglu=True)
     y = sg.sharded_to_all(dn, h)
+    idx = list(range(B)) if B <= 16 else sorted({0, 1, B // 2, B - 1, *np.random.default_rng(B).choice(B, 4, replace=False).tolist()})
     Wgu, Wd = oracle.deq_mx8(gc, gs), oracle.deq_mx8(dc, ds)
-    Xd = oracle.decode(X, "bf16")
+    Xd = oracle.decode(X[idx], "bf16")
     g, u = oracle.col(Xd, Wgu[:F], P=P), oracle.col(Xd, Wgu[F:], P=P)
-    assert_close(h, oracle.swiglu(g, u, "f64"), "bf16", "h")
-    assert_close(y, oracle.row(oracle.swiglu(g, u, "bf16"), Wd, P=P), "bf16", "y")
+    assert_close(h[:, idx], oracle.swiglu(g, u, "f64"), "bf16", "h")
+    assert_close(y[idx], oracle.row(oracle.swiglu(g, u, "bf16"), Wd, P=P), "bf16", "y")
     assert torch.equal(sg.mlp(gu, dn, to_dev(X, "bf16")), y)  # the entry point bench.py times
 
 

@@ -669,8 +669,8 @@ def test_slicing_mx_bit_exact(mode, out, inn, S, P):
         layer.shard(0, 3)  # no quantization biases
 
 
-# 33-256 tokens: the few-token tiles (codes converted after the LDS); beyond: the 128 x 128 tiles
-@pytest.mark.parametrize("B", [1, 8, 16, 32, 40, 100, 200, 600])
+# beyond 32 tokens: the few-token tiles (codes converted after the LDS), 64- or 128-token tiles
+@pytest.mark.parametrize("B", [1, 8, 16, 32, 40, 100, 200, 600, 1100])
 def test_mx_all_to_sharded(B):
     _print_case(B=B)
     D, out, P = 512, 384, 4
@@ -695,6 +695,18 @@ def test_mx_swiglu_and_row(B):
     assert_close(h, oracle.swiglu(g, u, "f64"), "bf16", "mx h")
     y = sg.sharded_to_all(dn, h, out_dtype=torch.float32)
     assert_close(y, oracle.row(bits(h), Wdn, P=P, bias=bd, dtype="bf16"), "f32", "mx y")
+
+
+@pytest.mark.parametrize("B", [40, 600])
+def test_mx_tile_kernel(B):
+    """Inputs per rank not a multiple of 128 (480): the MX few-token tiles do
+    not take the layer, the 128 x 128 tile kernel with the FP8 loader does."""
+    _print_case(B=B)
+    D, out, P = 480, 256, 2
+    layer, _, _, Wd = _mx_layer(synth.uniform(85, (out, D), 1 / np.sqrt(D), "f32"), 0, P)
+    X = synth.normal(86, (B, D), 1.0, "bf16")
+    y = sg.all_to_sharded(layer, to_dev(X, "bf16"), gather=True, out_dtype=torch.float32)
+    assert_close(y, oracle.col(X, Wd, P=P, gather=True, dtype="bf16"), "f32", "mx tile kernel")
 
 
 def test_mx_row_major_layout():
