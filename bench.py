@@ -9,7 +9,7 @@ Llama-style gated MLP decode step (B=16 tokens, D=4096, F=14336, P=8 ranks on
 one GPU, bf16): gate/up all-to-sharded with the fused SwiGLU epilogue, then
 down sharded-to-all with the fused rank sum, through the fused MLP entry point
 (sg_mlp, the sharded h kept in its workspace); --batch sets other token
-counts (33-256 run the few-token tile kernel).  Other workloads:
+counts (17-256 run the few-token tile kernel).  Other workloads:
 
     3   prefill: B=4096, P=4, fused QKV column shard (segments=3) + the MLP
     4   4-bit affine MLP (group 64), B in {1, 8, 32} (--batch; beyond 32 tokens the
@@ -57,7 +57,7 @@ def parse():
     ap.add_argument("--config", default="2", choices=["1", "2", "3", "4", "5a", "5b", "5c", "6", "7"])
     ap.add_argument("--batch", type=int, default=None,
                     help="tokens: the 4-bit workload (1, 8 or 32, default 1; more runs the 4-bit tile kernel) or "
-                         "the decode MLP (default 16; 33-256 run the few-token tile kernel)")
+                         "the decode MLP (default 16; 17-256 run the few-token tile kernel)")
     ap.add_argument("--summa", default="fused", choices=["fused", "steps"])
     ap.add_argument("--rank-share", action="store_true",
                     help="configs 2, 3, 4, 5b: only rank 0's share of the layers (P = 1, the per-GPU shapes "
@@ -139,7 +139,7 @@ class DecodeMLP(Workload):
 
     def __init__(self, B=16):
         self.B = B
-        if B > 32:  # beyond the streaming kernels
+        if B > 16:  # beyond one token tile of the streaming kernel
             self.dominant = "tile_nw64_kernel (gate|up all-to-sharded + SwiGLU, few-token tiles)"
             self.dominant_src = ("tile_dma.hip", "internal.h")
 

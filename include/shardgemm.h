@@ -106,11 +106,13 @@ sg_status sg_shard_quantized_linear(const uint32_t* wq, const uint16_t* scales,
  *   act      activation dtype: SG_BF16 only (else SG_ERR_UNSUPPORTED).
  *   bias     (out_dims) bf16, or NULL (the layer bias, as for sg_shard_linear).
  * SG_ERR_NOT_DIVISIBLE when in_dims % 32, or for sharded-to-all when a scale
- * block would straddle two ranks ((in_dims/segments/P) % 32).  Up to 32 tokens
+ * block would straddle two ranks ((in_dims/segments/P) % 32).  Up to 16 tokens
  * run on the streaming kernel (codes converted to bf16 in registers) when the
  * shards tile into 16-row blocks and in/P (sharded-to-all) or in is a multiple
  * of 128; more tokens on the matrix-core tile kernels (codes converted to bf16
- * as they are staged); other calls take the generic kernel.  sg_layer_copy_shard returns
+ * after the LDS or as they are staged; 17 to 32 tokens stay on the streaming
+ * kernel for shards that the few-token tiles do not take); other calls take
+ * the generic kernel.  sg_layer_copy_shard returns
  * codes (what 0) and scales (what 2); sg_layer_info reports quantized = 2. */
 sg_status sg_shard_mxfp8_linear(const uint8_t* codes, const uint8_t* scales, int64_t out_dims,
                                 int64_t in_dims, sg_dtype act, const void* bias, int mode, int segments,
@@ -288,8 +290,8 @@ size_t sg_summa_backward_workspace(sg_dtype dtype, int64_t M, int64_t K, int64_t
 
 /* Bytes of workspace sg_sharded_to_all needs for B tokens (0 on bad input, and
  * when the call runs without one).  Non-zero when the output alone gives too
- * few tiles to fill the chip (beyond 32 tokens, dense 16-bit, MX FP8 and
- * 4-bit layers): groups of ranks are then workgroups of their own, their
+ * few tiles to fill the chip (dense 16-bit and MX FP8 layers beyond 16 tokens,
+ * 4-bit layers beyond 32): groups of ranks are then workgroups of their own, their
  * partial tiles stored in the workspace and summed in rank order by a second
  * kernel. */
 size_t sg_sharded_to_all_workspace(const sg_layer* layer, int64_t B);

@@ -149,11 +149,14 @@ bool mfma_ok(const sg_layer* l, const void* x) {
     return l->dtype != SG_F32 && l->cols_r % 8 == 0 && aligned16(x) && aligned16(l->w);
 }
 
-// the few-token tile kernel: 33 to 256 tokens (MX FP8 layers: any count above
-// 32), 32-wide k tiles, weights and activations addressable through 32-bit
-// offsets
+// the few-token tile kernel: 17 to 256 tokens (MX FP8 layers: any count above
+// 16), 32-wide k tiles, weights and activations addressable through 32-bit
+// offsets.  From 17 tokens the streaming kernels need a second token tile,
+// and the few-token tiles (64 tokens) win on the decode-MLP layer shapes:
+// separate calls at 17-32 tokens, dense gate|up 47-48 -> 45 us, down 28-41 ->
+// 27-28 us; MX FP8 gate|up 35-36 -> 32 us, down 24-32 -> 25 us.
 bool nw_ok(const sg_layer* l, int64_t B) {
-    return B > 32 && (B <= 256 || l->mx) && l->cols_r % 32 == 0 &&
+    return B > 16 && (B <= 256 || l->mx) && l->cols_r % 32 == 0 &&
            (double)l->P * l->rows_r * l->cols_r * 2 < 2.0e9 && (double)B * l->P * l->cols_r * 2 < 2.0e9;
 }
 
@@ -174,8 +177,6 @@ bool q4_fits(const sg_layer* l, int64_t B, int swiglu) {
 // fragment-major; more tokens on the tile kernels (codes converted to bf16 in
 // the loader), inputs with 16-byte rows; else the generic kernel
 Kind choose_mx(const sg_layer* l, int64_t B, const void* x, int swiglu, int nseg) {
-    const bool ok = B <= 32 && l->wfrag && (l->cols_r / 32) % 4 == 0 && aligned16(x) && aligned16(l->w);
-    if (ok && skinny_fits(l, B, swiglu, nseg)) return K_SKINNY;
     // beyond 32 tokens the few-token tiles with the FP8 conversion after the
     // LDS, at every token count (decode MLP shapes at 64 tokens: gate|up 155 ->
     // 35 us, down 77 -> 26 us against the 128 x 128 tile kernel with the FP8
@@ -183,8 +184,9 @@ Kind choose_mx(const sg_layer* l, int64_t B, const void* x, int swiglu, int nseg
     // -> 1305 and 1079 -> 603 us); the tile kernel keeps the layers whose codes
     // do not come in whole 16-row blocks of 128-wide k tiles
     const bool blocks16 = (swiglu ? (l->rows_r / 2) % 16 : l->rows_r % 16) == 0;
-    if (B > 32 && l->wfrag && l->cols_r % 128 == 0 && blocks16 && aligned16(x) && nw_ok(l, B))
-        return K_NW;
+    if (l->wfrag && l->cols_r % 128 == 0 && blocks16 && aligned16(x) && nw_ok(l, B)) return K_NW;
+    const bool ok = B <= 32 && l->wfrag && (l->cols_r / 32) % 4 == 0 && aligned16(x) && aligned16(l->w);
+    if (ok && skinny_fits(l, B, swiglu, nseg)) return K_SKINNY;
     if (B > 32 && aligned16(x) && l->cols_r % 8 == 0) return K_TILE1;
     return K_GENERIC;
 }
@@ -197,12 +199,12 @@ Kind choose(const sg_layer* l, int64_t B, const void* x, int swiglu = 0, int nse
         return (B <= 32 && nseg == 1 && q4_fits(l, B, swiglu)) ? K_Q4 : K_Q4TILE;
     }
     if (!mfma_ok(l, x)) return K_GENERIC;
-    if (B <= 32 && skinny_fits(l, B, swiglu, nseg)) return K_SKINNY;
     // up to 256 tokens the few-token tiles (decode-MLP gate|up at 64 tokens:
     // 98 us on the 128 x 128 tiles, 54 on them; at 160, 113 against 95 us);
     // beyond, the ping-pong kernel (at 384 tokens: 187 us on the 128 x 128
     // tiles, 122 on it)
     if (nw_ok(l, B)) return K_NW;
+    if (B <= 32 && skinny_fits(l, B, swiglu, nseg)) return K_SKINNY;
     return B > 256 ? K_TILE0 : K_TILE1;
 }
 
@@ -245,15 +247,18 @@ sg::SplitLayout split_layout(const sg_layer* l, Kind k, int64_t B) {
 // is checked separately; misaligned pointers fall back to the generic path)
 Kind choose_row(const sg_layer* l, int64_t B) {
     if (l->mx) return choose_mx(l, B, l->w, 0, l->P);
+    // 4-bit: the streaming kernels up to 32 tokens, as for the gate|up layer, so
+    // that the fused MLP (h fragment-major for the 16-row streaming kernel) and
+    // the separate calls run the same kernels
     if (l->quantized) return !l->qfrag ? K_GENERIC : (B <= 32 && q4_fits(l, B, 0) ? K_Q4 : K_Q4TILE);
     if (l->dtype == SG_F32 || l->cols_r % 8) return K_GENERIC;
-    if (B <= 32 && skinny_fits(l, B, 0, l->P)) return K_SKINNY;
     // up to 256 tokens the few-token tiles, beyond them the ping-pong kernel,
     // either split into groups of ranks whenever the output gives too few
     // tiles (decode-MLP down projection at 64 tokens: 93 us on the split
     // 128 x 128 tiles, 56 on the split ping-pong kernel, 36 on the few-token
     // tiles; at 256 tokens 139, 69 and 58 us)
     if (nw_ok(l, B)) return K_NW;
+    if (B <= 32 && skinny_fits(l, B, 0, l->P)) return K_SKINNY;
     return K_TILE0;
 }
 

@@ -92,9 +92,9 @@ def test_config1_mlp_fp32():
 # all-to-sharded
 # ---------------------------------------------------------------------------
 COL_CASES = [
-    # dtype, B, in, out, S, P   (path chosen by B: <= 32 streaming; 33-256 the few-token tiles of
-    # 64, 128 or 256 tokens when K is a multiple of 32, else the 128 x 128 tiles; beyond 256 the
-    # ping-pong kernel)
+    # dtype, B, in, out, S, P   (path chosen by B: <= 16 streaming; 17-256 the few-token tiles of
+    # 64, 128 or 256 tokens when K is a multiple of 32, else streaming up to 32 tokens and the
+    # 128 x 128 tiles beyond; beyond 256 the ping-pong kernel)
     ("bf16", 1, 256, 96, 1, 2), ("bf16", 5, 512, 192, 3, 2), ("bf16", 16, 4096, 448, 1, 8), ("bf16", 32, 200, 64, 2, 2),
     ("f16", 17, 1024, 320, 1, 4), ("bf16", 33, 264, 384, 1, 3), ("bf16", 130, 512, 640, 1, 4),
     ("bf16", 50, 1024, 512, 2, 4), ("f16", 100, 256, 384, 1, 2),
@@ -123,6 +123,7 @@ def test_all_to_sharded(case, gather):
 
 
 SWIGLU_CASES = [("bf16", 1, 256, 128, 2), ("bf16", 16, 512, 448, 4), ("f16", 31, 256, 96, 3),
+                ("f16", 24, 200, 96, 3),  # K = 200: streaming with two token tiles
                 ("bf16", 40, 256, 512, 2), ("bf16", 600, 384, 640, 4), ("f16", 513, 128, 384, 2),
                 ("f16", 120, 512, 768, 4), ("bf16", 100, 256, 400, 4),  # few-token tiles (100 outputs per rank)
                 ("f16", 200, 512, 768, 4)]  # few-token 256-token tiles
@@ -149,6 +150,8 @@ def test_swiglu_epilogue(case, gather):
 # ---------------------------------------------------------------------------
 ROW_CASES = [
     ("bf16", 1, 512, 96, 2), ("bf16", 16, 14336 // 4, 256, 8), ("f16", 29, 768, 200, 3), ("bf16", 8, 256, 64, 1),
+    ("bf16", 24, 200, 128, 5),     # 40 inputs per rank: streaming with two token tiles
+    ("bf16", 20, 1024, 4096, 8),   # few-token 64-token tiles from 17 tokens, rank split
     ("bf16", 100, 512, 256, 4),    # few-token 128-token tiles, rank split (2 tiles, 4 groups)
     ("bf16", 40, 1024, 4096, 8),   # few-token 64-token tiles, rank split (32 tiles, 8 groups)
     ("f16", 200, 512, 1024, 4),    # few-token 256-token tiles, rank split (8 tiles, 4 groups)
