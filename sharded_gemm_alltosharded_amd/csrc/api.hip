@@ -159,6 +159,15 @@ bool nw_ok(const sg_layer* l, int64_t B) {
     return B > 16 && (B <= 256 || l->mx) && l->cols_r % 32 == 0 &&
            (double)l->P * l->rows_r * l->cols_r * 2 < 2.0e9 && (double)B * l->P * l->cols_r * 2 < 2.0e9;
 }
+// ... and at 17 to 32 tokens only while one wave of workgroups covers the
+// layer's tiles: the vocabulary head (393 tiles of 64 tokens on 256 CUs) ran
+// 2% slower on them than on the streaming kernel, whose 16-row blocks balance
+// across the CUs
+bool nw_fills(const sg_layer* l, int64_t B, int swiglu) {
+    if (B > 32) return true;
+    const int n = (int)(swiglu ? l->out_dims / 2 : l->out_dims);
+    return sg::tile_nw_count((int)B, n, swiglu, l->mx) <= num_cus();
+}
 
 // the streaming kernels keep one LDS slot per (rank, part): bounded ranks only
 // nseg: K segments of the call (ranks of a sharded-to-all layer, or the input
@@ -184,7 +193,8 @@ Kind choose_mx(const sg_layer* l, int64_t B, const void* x, int swiglu, int nseg
     // -> 1305 and 1079 -> 603 us); the tile kernel keeps the layers whose codes
     // do not come in whole 16-row blocks of 128-wide k tiles
     const bool blocks16 = (swiglu ? (l->rows_r / 2) % 16 : l->rows_r % 16) == 0;
-    if (l->wfrag && l->cols_r % 128 == 0 && blocks16 && aligned16(x) && nw_ok(l, B)) return K_NW;
+    if (l->wfrag && l->cols_r % 128 == 0 && blocks16 && aligned16(x) && nw_ok(l, B) && nw_fills(l, B, swiglu))
+        return K_NW;
     const bool ok = B <= 32 && l->wfrag && (l->cols_r / 32) % 4 == 0 && aligned16(x) && aligned16(l->w);
     if (ok && skinny_fits(l, B, swiglu, nseg)) return K_SKINNY;
     if (B > 32 && aligned16(x) && l->cols_r % 8 == 0) return K_TILE1;
@@ -203,7 +213,7 @@ Kind choose(const sg_layer* l, int64_t B, const void* x, int swiglu = 0, int nse
     // 98 us on the 128 x 128 tiles, 54 on them; at 160, 113 against 95 us);
     // beyond, the ping-pong kernel (at 384 tokens: 187 us on the 128 x 128
     // tiles, 122 on it)
-    if (nw_ok(l, B)) return K_NW;
+    if (nw_ok(l, B) && nw_fills(l, B, swiglu)) return K_NW;
     if (B <= 32 && skinny_fits(l, B, swiglu, nseg)) return K_SKINNY;
     return B > 256 ? K_TILE0 : K_TILE1;
 }
@@ -257,7 +267,7 @@ Kind choose_row(const sg_layer* l, int64_t B) {
     // tiles (decode-MLP down projection at 64 tokens: 93 us on the split
     // 128 x 128 tiles, 56 on the split ping-pong kernel, 36 on the few-token
     // tiles; at 256 tokens 139, 69 and 58 us)
-    if (nw_ok(l, B)) return K_NW;
+    if (nw_ok(l, B) && nw_fills(l, B, 0)) return K_NW;
     if (B <= 32 && skinny_fits(l, B, 0, l->P)) return K_SKINNY;
     return K_TILE0;
 }
