@@ -139,11 +139,12 @@ sg_status sg_all_to_sharded(const sg_layer* layer, const void* x, int64_t B, voi
  *              SG_IN_SHARDED: x (P, B, in_dims/P), slice r holding columns
  *              [r in/P, (r+1) in/P) of the activation; every rank all-gathers it
  *              before its matmul (Case 2), which here is the K loop walking the P
- *              slices in order.  Dense and 4-bit layers: SG_ERR_UNSUPPORTED for
- *              MX FP8 layers, for fragment-stored dense weights when
- *              (in_dims/P) % 32 != 0, and for 4-bit layers when (in_dims/P) is
- *              not a multiple of 256 (fragment-stored codes) or 64 (row-major
- *              codes); SG_ERR_NOT_DIVISIBLE when P does not divide in_dims.
+ *              slices in order.  SG_ERR_UNSUPPORTED for fragment-stored dense
+ *              weights when (in_dims/P) % 32 != 0, for 4-bit layers when
+ *              (in_dims/P) is not a multiple of 256 (fragment-stored codes) or
+ *              64 (row-major codes), and for MX FP8 layers when it is not a
+ *              multiple of 128 (fragment-stored codes) or 32 (row-major codes);
+ *              SG_ERR_NOT_DIVISIBLE when P does not divide in_dims.
  *   out_layout SG_OUT_SHARDED: y (P, B, n_out/P) (gather = 0 of sg_all_to_sharded);
  *              SG_OUT_FULL: y (B, n_out), the rank-order all-gather (gather = 1).
  * Everything else as sg_all_to_sharded. */

@@ -580,7 +580,11 @@ sg_status sg_all_to_sharded_ex(const sg_layer* l, const void* x, int in_layout, 
         if (l->in_dims % l->P)
             return fail(SG_ERR_NOT_DIVISIBLE, "Cannot shard the input of size %lld across %d devices.",
                         (long long)l->in_dims, l->P);
-        if (l->mx) return fail(SG_ERR_UNSUPPORTED, "a sharded input is implemented for dense and 4-bit layers");
+        // MX FP8: no scale block may straddle two input shards, and in the
+        // fragment-major layout a row's scales come in runs of four blocks
+        if (l->mx && (l->in_dims / l->P) % (l->wfrag ? 128 : 32))
+            return fail(SG_ERR_UNSUPPORTED, "a sharded input on an MX FP8 layer needs in_dims / P to be a multiple of %d",
+                        l->wfrag ? 128 : 32);
         // 4-bit: no quantization group (in the stored layout, no run of four)
         // may straddle two input shards
         if (l->quantized && (l->in_dims / l->P) % (l->qfrag ? 256 : 64))
@@ -610,6 +614,7 @@ sg_status sg_all_to_sharded_ex(const sg_layer* l, const void* x, int in_layout, 
             p.q_seg = l->qfrag ? 4 * kr : kr / 8;
             p.g_seg = l->qfrag ? kr / 2 : kr / 64;
         }
+        if (l->mx) p.ms_seg = l->wfrag ? kr / 2 : kr / 32;  // (codes: w_seg bytes, as above)
     } else {
         p.lda = l->in_dims;
         p.Kseg = (int)l->cols_r;

@@ -868,10 +868,13 @@ __global__ __launch_bounds__(256) void tile_nw_mx_kernel(Problem p, int tiles_m,
 
     const int64_t rows = SWIGLU ? 2 * (int64_t)p.N : p.N, nblk = rows / 16;
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)p.A, 0, (int)a_extent(p), 0x00020000);
+    // extents: the last segment's k range of the last 16-row block
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)p.W, 0, (int)(((int64_t)p.nseg - 1) * p.w_seg + nblk * (p.wsteps / 2) * 1024), 0x00020000);
+        (void*)p.W, 0, (int)(((int64_t)p.nseg - 1) * p.w_seg + ((nblk - 1) * (p.wsteps / 2) + p.Kseg / 64) * 1024),
+        0x00020000);
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)p.ms, 0, (int)(((int64_t)p.nseg - 1) * p.ms_seg + nblk * (p.wsteps / 4) * 64), 0x00020000);
+        (void*)p.ms, 0, (int)(((int64_t)p.nseg - 1) * p.ms_seg + ((nblk - 1) * (p.wsteps / 4) + p.Kseg / 128) * 64),
+        0x00020000);
     const int ktiles_seg = p.Kseg / BK;
     const int gsegs = SPLIT ? p.nseg / (int)gridDim.y : p.nseg;
     const int nkt = ktiles_seg * gsegs;

@@ -566,6 +566,33 @@ def test_all_gather_input_q4(B):
     assert_close(y, ref, "f32", "q4 all-gather input")
 
 
+@pytest.mark.parametrize("B", [1, 16, 24, 100, 600])
+def test_all_gather_input_mx(B):
+    """An MX FP8 all-to-sharded layer fed its input as rank shards ([HSYM]
+    Case 2): the streaming kernel, the MX few-token tiles or (row-major codes,
+    out % 16 != 0) the generic kernel walk the P input slices as K segments."""
+    _print_case(B=B)
+    D, out, P = 1024, 384, 4
+    layer, _, _, Wd = _mx_layer(synth.uniform(68, (out, D), 1 / np.sqrt(D), "f32"), 0, P)
+    Xs = synth.normal(69, (P, B, D // P), 1.0, "bf16")
+    xg = oracle.all_gather(Xs)
+    for gather in (False, True):
+        y = sg.all_to_sharded(layer, to_dev(Xs, "bf16"), x_sharded=True, gather=gather, out_dtype=torch.float32)
+        assert_close(y, oracle.col(xg, Wd, P=P, gather=gather, dtype="bf16"), "f32", "mx all-gather input")
+    # SwiGLU over the gathered input
+    F = 512
+    ws = [synth.uniform(70 + i, (F, D), 1 / np.sqrt(D), "f32") for i in range(2)]
+    gu, _, _, Wgu = _mx_layer(np.concatenate(ws), 0, P, S=2)
+    h = sg.all_to_sharded(gu, to_dev(Xs, "bf16"), x_sharded=True, swiglu=True)
+    ref = oracle.swiglu(oracle.col(xg, Wgu[:F], P=P, dtype="bf16"), oracle.col(xg, Wgu[F:], P=P, dtype="bf16"), "f64")
+    assert_close(h, ref, "bf16", "mx all-gather input swiglu")
+    # row-major codes (72 outputs: not whole 16-row blocks per rank)
+    lr, _, _, Wr = _mx_layer(synth.uniform(72, (72, D), 1 / np.sqrt(D), "f32"), 0, 2)
+    Xr = synth.normal(73, (2, B, D // 2), 1.0, "bf16")
+    y = sg.all_to_sharded(lr, to_dev(Xr, "bf16"), x_sharded=True, gather=True, out_dtype=torch.float32)
+    assert_close(y, oracle.col(oracle.all_gather(Xr), Wr, P=2, gather=True, dtype="bf16"), "f32", "mx row-major")
+
+
 def test_all_gather_input_rejections():
     W = synth.uniform(53, (64, 96), 0.1, "bf16")
     layer = sg.shard_linear(to_dev(W, "bf16"), "all-to-sharded", P=2)  # in / P = 48: not 32-aligned
@@ -579,6 +606,10 @@ def test_all_gather_input_rejections():
     lq, _ = _q4_layer(synth.uniform(57, (128, 256), 1 / 16, "f32"), 0, 2)
     with pytest.raises(sg.ShardGemmError) as e:
         sg.all_to_sharded(lq, to_dev(synth.normal(58, (2, 4, 128), 1.0, "bf16"), "bf16"), x_sharded=True)
+    assert e.value.code == sg.ERR_UNSUPPORTED
+    lm, _, _, _ = _mx_layer(synth.uniform(59, (128, 384), 1 / 16, "f32"), 0, 2)  # fragment-major, 192 per shard
+    with pytest.raises(sg.ShardGemmError) as e:
+        sg.all_to_sharded(lm, to_dev(synth.normal(60, (2, 4, 192), 1.0, "bf16"), "bf16"), x_sharded=True)
     assert e.value.code == sg.ERR_UNSUPPORTED
 
 
