@@ -186,7 +186,7 @@ bool q4_fits(const sg_layer* l, int64_t B, int swiglu) {
 // fragment-major; more tokens on the tile kernels (codes converted to bf16 in
 // the loader), inputs with 16-byte rows; else the generic kernel
 Kind choose_mx(const sg_layer* l, int64_t B, const void* x, int swiglu, int nseg) {
-    // beyond 32 tokens the few-token tiles with the FP8 conversion after the
+    // from 17 tokens the few-token tiles with the FP8 conversion after the
     // LDS, at every token count (decode MLP shapes at 64 tokens: gate|up 155 ->
     // 35 us, down 77 -> 26 us against the 128 x 128 tile kernel with the FP8
     // loader; at 512 tokens 329 -> 194 and 160 -> 85 us; at 4096 tokens 2221
