@@ -21,6 +21,17 @@ FLAGS = [
     "-Wno-pass-failed", "-Wno-unknown-warning-option",
 ]
 
+# Per-file flags.  The 4-bit streaming kernels scale every group's MFMA result
+# on the vector unit; with the default register choice the MFMAs write the
+# accumulation registers and each group then copies them to ordinary ones
+# (about half of the loop's vector instructions).  The VGPR form of the MFMA
+# removes the copies (4-bit decode MLP at 32 tokens: gate|up 29.1 -> 27.1 us);
+# elsewhere it gained nothing measurable and spills in tile.hip.
+FILE_FLAGS = {
+    "q4.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "q4s.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
 
 def _objdir():
     d = os.path.join(HERE, "_build")
@@ -49,7 +60,7 @@ def build_library(verbose: bool = False, incremental: bool = False) -> str:
         objs.append(obj)
         if incremental and not _stale(os.path.join(CSRC, src), obj):
             continue
-        cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
     failed = []
     for src, p in procs:
