@@ -286,7 +286,7 @@ class Q4MLP(Workload):
     metric = "4-bit sharded-MLP GB/s (% HBM peak)"
     rotate = 6
     dominant = "q4_kernel (gate|up all-to-sharded + SwiGLU)"
-    dominant_src = ("q4.hip", "internal.h")
+    dominant_src = ("q4.hip", "q4_stream.h", "q4_wide.hip", "internal.h")
 
     def __init__(self, B):
         self.B = B

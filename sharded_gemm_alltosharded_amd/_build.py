@@ -9,7 +9,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libshardgemm.so")
-SOURCES = ["api.hip", "generic.hip", "tile.hip", "skinny.hip", "q4.hip", "q4s.hip", "layout.hip", "tile_dma.hip", "backward.hip", "q4tile.hip"]
+SOURCES = ["api.hip", "generic.hip", "tile.hip", "skinny.hip", "q4.hip", "q4_wide.hip", "q4s.hip", "layout.hip",
+           "tile_dma.hip", "backward.hip", "q4tile.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -21,15 +22,15 @@ FLAGS = [
     "-Wno-pass-failed", "-Wno-unknown-warning-option",
 ]
 
-# Per-file flags.  The 4-bit streaming kernels scale every group's MFMA result
+# Per-file flags.  The 4-bit streaming kernel scales every group's MFMA result
 # on the vector unit; with the default register choice the MFMAs write the
 # accumulation registers and each group then copies them to ordinary ones
 # (about half of the loop's vector instructions).  The VGPR form of the MFMA
-# removes the copies (4-bit decode MLP at 32 tokens: gate|up 29.1 -> 27.1 us);
-# elsewhere it gained nothing measurable and spills in tile.hip.
+# removes the copies; it pays for 17 to 32 tokens (q4_wide.hip) and measured
+# slower or no faster for fewer tokens, in the other 4-bit kernels and in the
+# dense ones (and spills in tile.hip).
 FILE_FLAGS = {
-    "q4.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-    "q4s.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "q4_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 
@@ -39,7 +40,8 @@ def _objdir():
     return d
 
 
-HEADERS = [os.path.join(CSRC, "internal.h"), os.path.join(os.path.dirname(HERE), "include", "shardgemm.h")]
+HEADERS = [os.path.join(CSRC, "internal.h"), os.path.join(CSRC, "q4_stream.h"),
+           os.path.join(os.path.dirname(HERE), "include", "shardgemm.h")]
 
 
 def _stale(src: str, obj: str) -> bool:
