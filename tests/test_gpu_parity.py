@@ -511,7 +511,7 @@ def test_wrong_layer_mode_is_rejected():
 # 3): an all-to-sharded layer fed sharded activations (all-gathered inside the
 # K loop), and a sharded-to-all layer whose summed output is reduce-scattered
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("B", [1, 16, 40, 600])
+@pytest.mark.parametrize("B", [1, 16, 24, 40, 600])
 @pytest.mark.parametrize("P", [2, 4])
 def test_all_gather_input(B, P):
     _print_case(B=B, P=P)
@@ -613,7 +613,7 @@ def test_all_gather_input_rejections():
     assert e.value.code == sg.ERR_UNSUPPORTED
 
 
-@pytest.mark.parametrize("B", [1, 16, 100, 600, 2048])
+@pytest.mark.parametrize("B", [1, 16, 24, 100, 600, 2048])
 @pytest.mark.parametrize("P", [2, 4])
 def test_reduce_scatter_output(B, P):
     """B = 100 and 2048 take the rank-split workspace path of the tile kernels."""
