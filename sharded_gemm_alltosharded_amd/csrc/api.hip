@@ -154,10 +154,12 @@ bool mfma_ok(const sg_layer* l, const void* x) {
 // offsets.  From 17 tokens the streaming kernels need a second token tile,
 // and the few-token tiles (64 tokens) win on the decode-MLP layer shapes:
 // separate calls at 17-32 tokens, dense gate|up 47-48 -> 45 us, down 28-41 ->
-// 27-28 us; MX FP8 gate|up 35-36 -> 32 us, down 24-32 -> 25 us.
+// 27-28 us; MX FP8 gate|up 35-36 -> 32 us, down 24-32 -> 25 us.  The tile
+// count (a 32-bit grid dimension) stays far below 2^31.
 bool nw_ok(const sg_layer* l, int64_t B) {
     return B > 16 && (B <= 256 || l->mx) && l->cols_r % 32 == 0 &&
-           (double)l->P * l->rows_r * l->cols_r * 2 < 2.0e9 && (double)B * l->P * l->cols_r * 2 < 2.0e9;
+           (double)l->P * l->rows_r * l->cols_r * 2 < 2.0e9 && (double)B * l->P * l->cols_r * 2 < 2.0e9 &&
+           (double)(B / 64 + 1) * (double)(l->out_dims / 64 + 1) < 1.0e9;
 }
 // ... and at 17 to 32 tokens only while one wave of workgroups covers the
 // layer's tiles: the vocabulary head (393 tiles of 64 tokens on 256 CUs) ran
