@@ -105,3 +105,30 @@ def test_mlp_static_quantized(Bs):
         ref = sg.mlp(gu, dn, x, out_dtype=torch.float32)
         torch.cuda.synchronize()
         assert torch.equal(y, ref), B
+
+
+def _mx(w, mode, P, S=1):
+    codes, scales = synth.quantize_mxfp8(w)
+    return sg.shard_mxfp8_linear(torch.from_numpy(codes).to(dev()), torch.from_numpy(scales).to(dev()), mode,
+                                 segments=S, P=P)
+
+
+@pytest.mark.parametrize("Bs", [(100, 24), (16, 8)], ids=lambda b: "-".join(map(str, b)))
+def test_mlp_static_mx(Bs):
+    """MX FP8 layers: the MX few-token tiles (the down layer split by rank
+    through partial tiles in the scratch) and the FP8 streaming kernel (h
+    fragment-major in the scratch), two calls in a row."""
+    D, F, P = 512, 1024, 4
+    print(f"case: mx D={D} F={F} P={P} B={Bs}", flush=True)
+    ws = [synth.uniform(80 + i, shp, 1 / np.sqrt(D), "f32") for i, shp in enumerate([(F, D), (F, D), (D, F)])]
+    gu, dn = _mx(np.concatenate([ws[0], ws[1]]), 0, P, S=2), _mx(ws[2], 1, P)
+    X = synth.normal(83, (max(Bs), D), 1.0, "bf16")
+    for B in Bs:
+        x = to_dev(X[:B], "bf16")
+        y = torch.empty((B, D), dtype=torch.float32, device=dev())
+        before = torch.cuda.memory_allocated()
+        sg.mlp_static(gu, dn, x, y)
+        assert torch.cuda.memory_allocated() == before
+        ref = sg.mlp(gu, dn, x, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref), B
