@@ -44,10 +44,21 @@ def _quantized(D, F, P, seed):
     return _q4(np.concatenate([ws[0], ws[1]]), "all-to-sharded", P, S=2), _q4(ws[2], "sharded-to-all", P)
 
 
+def _mx_pair(D, F, P, seed):
+    ws = [synth.uniform(seed + i, shp, 1 / np.sqrt(D), "f32") for i, shp in enumerate([(F, D), (F, D), (D, F)])]
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev())
+    gc, gs = synth.quantize_mxfp8(np.concatenate([ws[0], ws[1]]))
+    dc, ds = synth.quantize_mxfp8(ws[2])
+    return (sg.shard_mxfp8_linear(t(gc), t(gs), "all-to-sharded", segments=2, P=P),
+            sg.shard_mxfp8_linear(t(dc), t(ds), "sharded-to-all", P=P))
+
+
 # (kind, D, F, P, B): the few-token tiles with the down layer split by rank
 # (partial tiles, then the rank-order sum kernel); the streaming kernels with a
-# fragment-major h; the 4-bit tile kernels with the split down layer
-CASES = [("bf16", 256, 512, 2, 64), ("bf16", 512, 1024, 8, 16), ("q4", 512, 1024, 4, 40)]
+# fragment-major h; the 4-bit tile kernels with the split down layer; the MX
+# FP8 few-token tiles with the split down layer
+CASES = [("bf16", 256, 512, 2, 64), ("bf16", 512, 1024, 8, 16), ("q4", 512, 1024, 4, 40),
+         ("mx", 512, 1024, 4, 40)]
 
 
 def _replays(call, xs, out, x1, x2, ref1, ref2, eager2):
@@ -77,7 +88,12 @@ def _replays(call, xs, out, x1, x2, ref1, ref2, eager2):
 def test_mlp_graph_replays(case, static):
     kind, D, F, P, B = case
     print(f"case: {kind} D={D} F={F} P={P} B={B} static={static}", flush=True)
-    gu, dn = _quantized(D, F, P, seed=90) if kind == "q4" else _dense(D, F, P, kind, seed=91)
+    if kind == "q4":
+        gu, dn = _quantized(D, F, P, seed=90)
+    elif kind == "mx":
+        gu, dn = _mx_pair(D, F, P, seed=94)
+    else:
+        gu, dn = _dense(D, F, P, kind, seed=91)
     x1 = to_dev(synth.normal(92, (B, D), 1.0, "bf16"), "bf16")
     x2 = to_dev(synth.normal(93, (B, D), 1.0, "bf16"), "bf16")
     ref1 = sg.mlp(gu, dn, x1, out_dtype=torch.float32)
